@@ -1,0 +1,272 @@
+/*
+ * libmoe355 -- one MoE layer's forward pass on an AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument named *device* is device memory owned by the
+ * caller; the library allocates nothing on these paths and never synchronises
+ * the host.  Every call is asynchronous on the given HIP stream and returns
+ * after validating its arguments and enqueueing its kernels.  Shapes are fixed
+ * per call; how many entries of a list are valid is reported in device memory
+ * (the "counts" arrays), so a whole decode step can be enqueued without the
+ * host reading anything back.
+ *
+ * Errors: a call returns MOE355_OK (0) or a negative status.  Argument,
+ * shape, dtype and capacity problems are found on the host before anything is
+ * enqueued, and nothing is launched then.  A failed launch returns
+ * MOE355_EHIP.  moe355_last_error() gives a one-line description of the
+ * most recent failure on the calling host thread.
+ *
+ * Sources (cited by page title and section):
+ *   [FT-zh]  "FreeToken: Efficient Edge-Native MoE Serving with Bandwidth-Adaptive
+ *            Execution", Chinese digest -- Core method, Method steps, Technical novelty.
+ *   [FT-en]  the same paper's simplified English reader -- System Architecture,
+ *            Semantic-Aware Expert Caching, Elastic Memory Management, Figure 2.
+ *   [Edge0]  "The other half of the memory wall: serving a 35B MoE model from SSD
+ *            with trained route prediction" (translation) -- section 2 (MoE routing,
+ *            Quantization), section 3.1 (Problem, Executor paths, Math contract).
+ */
+#ifndef MOE355_H
+#define MOE355_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe355_status;
+#define MOE355_OK          0
+#define MOE355_EINVAL     (-1)   /* bad pointer, size or parameter            */
+#define MOE355_EHIP       (-2)   /* a HIP launch or runtime call failed        */
+#define MOE355_ENOTSUP    (-3)   /* shape or format this build does not handle */
+#define MOE355_ECAPACITY  (-4)   /* a caller buffer (list, workspace) too small */
+
+/* Static text for a status code. */
+const char* moe355_status_string(moe355_status s);
+/* Description of the latest failure on this host thread ("" if none). */
+const char* moe355_last_error(void);
+/* Library version string. */
+const char* moe355_version(void);
+
+/* Routing families [Edge0, section 2 "MoE routing"]. */
+#define MOE355_ROUTE_SOFTMAX_TOPK   0
+#define MOE355_ROUTE_SIGMOID_GROUP  1
+
+/* Expert weight formats. */
+#define MOE355_W_INT4_G64   0  /* int4 affine, group 64 along the input [Edge0, section 2 "Quantization"] */
+#define MOE355_W_MXFP4      1  /* OCP MX v1.0: e2m1 elements, e8m0 scale per 32 along the input */
+
+/*
+ * One MoE layer's shape and routing (the model description the Edge0 page
+ * calls MoESpec, section 3 Figure 1).  n_group / topk_group / route_scale are
+ * read only for MOE355_ROUTE_SIGMOID_GROUP.
+ */
+typedef struct {
+    int32_t hidden;      /* H */
+    int32_t inter;       /* I, expert intermediate size */
+    int32_t n_experts;   /* E */
+    int32_t top_k;       /* k */
+    int32_t route;       /* MOE355_ROUTE_* */
+    int32_t n_group;
+    int32_t topk_group;
+    float   route_scale;
+    int32_t wfmt;        /* MOE355_W_* */
+} moe355_layer_desc;
+
+/*
+ * Bytes of one expert, S.  One expert is a contiguous blob: for gate [I,H],
+ * up [I,H] and down [H,I] in that order, int4 stores q uint8 [out, in/2]
+ * (element 2c in the low nibble of byte c), s bf16 [out, in/64] and
+ * b bf16 [out, in/64] (weight = s*q + b); MXFP4 stores q uint8 [out, in/2]
+ * (e2m1 codes, same nibble order) and e uint8 [out, in/32] (scale 2^(e-127)).
+ * Returns 0 for an invalid descriptor.
+ */
+int64_t moe355_expert_bytes(const moe355_layer_desc* d);
+
+/*
+ * The HBM expert cache [FT-zh, Core method: N slots shared by every MoE layer,
+ * each holding the complete tensors of one (layer, expert); the pool stays the
+ * source of truth].  All arrays are device memory owned by the caller.
+ *   slot_table [n_layers*n_experts] int32: slot of (l, e) or -1.
+ *   slot_owner [n_slots] int32: l*E+e held by the slot, or -1.
+ *   slot_ts    [n_slots] int64: tick of the last router selection, 0 = never used.
+ *   slot_data  [n_slots * slot_bytes].
+ * A fresh cache is table = -1, owner = -1, ts = 0.
+ */
+typedef struct {
+    int32_t  n_slots;
+    int32_t  n_layers;
+    int32_t  n_experts;
+    int64_t  slot_bytes;
+    int32_t* slot_table;
+    int32_t* slot_owner;
+    int64_t* slot_ts;
+    uint8_t* slot_data;
+} moe355_cache;
+
+/*
+ * Miss handling [FT-zh, Core method: q* = m * B_P / B_H; FT-en, Semantic-Aware
+ * Expert Caching: rounded to nearest].  q = min(m, floor((2*q_num*m + q_den) /
+ * (2*q_den))); q_num = q_den = 1 is pure fill.  K is the number of LRU victims
+ * one scan returns [FT-en, Elastic Memory Management]; at most min(q, K) misses
+ * are filled, the rest are computed in place from the pool.
+ */
+typedef struct {
+    int32_t K;
+    int32_t q_num;
+    int32_t q_den;
+} moe355_evict_policy;
+
+/*
+ * Per-call lists, each of `capacity` int32 device entries, plus
+ * counts[6] = {n_uniq, n_hit, n_miss, n_fill, n_inplace, n_victims}.
+ * uniq, hit_expert, miss, fill_expert and inplace hold expert ids in ascending
+ * order; hit_slot / fill_slot pair with hit_expert / fill_expert; victims are
+ * slots in ascending (ts, slot) order.  Entries past the counts are unspecified.
+ */
+typedef struct {
+    int32_t* uniq;
+    int32_t* hit_expert;
+    int32_t* hit_slot;
+    int32_t* miss;
+    int32_t* fill_expert;
+    int32_t* fill_slot;
+    int32_t* inplace;
+    int32_t* victims;
+    int32_t* counts;
+    int32_t  capacity;
+} moe355_classify_out;
+
+/*
+ * logits[t, e] = sum_h x[t, h] * w_router[e, h], fp32 accumulation.
+ * x: device bf16 [T, H]; w_router: device fp32 [E, H]; logits: device fp32 [T, E].
+ */
+moe355_status moe355_router_logits(const moe355_layer_desc* d, const void* x_bf16,
+                                   const float* w_router, int32_t T, float* logits,
+                                   hipStream_t stream);
+
+/*
+ * Routing [Edge0, section 2 "MoE routing"].
+ *   softmax-top-k: the k largest fp32 logits (ties to the lower expert id),
+ *     w_j = exp(l_j - l_max) / sum over the kept of exp(l - l_max).
+ *   sigmoid-group: s = sigmoid(l) in fp64; groups are n_group blocks of E/n_group
+ *     consecutive experts ranked by the sum of their two largest s (fp64, ties to
+ *     the lower group); the best topk_group groups are kept; the k largest logits
+ *     inside them are chosen (ties to the lower id); w = s / sum(s) * route_scale.
+ * ids are written in descending score order.
+ * logits: device fp32 [T, E]; topk_ids: device int32 [T, k]; topk_w: device fp32 [T, k].
+ * Limits: E <= 512, k <= 32 and k <= E; for sigmoid-group E/n_group must hold
+ * at least 2 experts and the group size must split evenly over lanes
+ * (E/n_group a power of two, or a multiple of ceil(E/64)).
+ */
+moe355_status moe355_route(const moe355_layer_desc* d, const float* logits, int32_t T,
+                           int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/*
+ * Dedup only: uniq = sorted distinct ids of ids[0..n_ids), counts[0] = their
+ * number; the other counts are set to 0.  Used when no cache is present
+ * (whole layer resident).  out->capacity must be >= min(n_ids, E).
+ */
+moe355_status moe355_dedup(const int32_t* ids, int32_t n_ids, int32_t n_experts,
+                           moe355_classify_out* out, hipStream_t stream);
+
+/*
+ * One layer call's cache bookkeeping, as one single-workgroup kernel
+ * [FT-zh, Core method and Method steps; FT-en, Elastic Memory Management]:
+ * dedup the n_ids routed ids of `layer`; split them into hits (slot_table >= 0)
+ * and misses; stamp hits with `tick`; compute q; scan every slot's timestamp once
+ * and take the K smallest (ts, slot) among slots with ts < tick as victims;
+ * for i < min(q, n_victims): evict victim i's owner (its table entry -> -1), map
+ * miss i to victim i, set owner and ts = tick.  Remaining misses go to `inplace`.
+ * The caller must use a tick larger than every earlier one (e.g. step*L + l + 1).
+ * Limits: n_slots <= 16384, n_experts <= 1024, 0 < tick < 2^31,
+ * out->capacity >= max(min(n_ids, E), K).
+ */
+moe355_status moe355_classify_evict(const moe355_cache* c, int32_t layer, int64_t tick,
+                                    const int32_t* ids, int32_t n_ids,
+                                    const moe355_evict_policy* p, moe355_classify_out* out,
+                                    hipStream_t stream);
+
+/*
+ * Batch copy of the filled experts [FT-zh, Core method: batch copy inside the
+ * graph]: for i < counts[3], S bytes from pool + (layer*E + fill_expert[i]) * S
+ * to slot_data + fill_slot[i] * S.  pool: device [n_layers * E * S].
+ * max_fill bounds counts[3] (use the policy's K).
+ */
+moe355_status moe355_cache_fill(const moe355_cache* c, const uint8_t* pool, int32_t layer,
+                                const moe355_classify_out* out, int32_t max_fill,
+                                hipStream_t stream);
+
+/*
+ * Elastic rebuild at a safe point [FT-en, Elastic Memory Management: the slot
+ * count follows the memory budget and excess slots are evicted without a
+ * restart]: `to` (to->n_slots slots, same n_layers / n_experts / slot_bytes)
+ * receives the to->n_slots occupied slots of `from` that are last in
+ * (ts, slot) order, packed into slots 0.. in ascending old-slot order with
+ * their timestamps and bytes; remaining slots of `to` are empty.  `from` is
+ * read only.  The two caches must not share memory.
+ */
+moe355_status moe355_cache_rebuild(const moe355_cache* from, moe355_cache* to,
+                                   hipStream_t stream);
+
+/*
+ * Prefill bucketing: a stable sort of the T*k pairs p = t*k + j by expert id.
+ * perm: device int32 [T*k]; offsets: device int32 [E+1] (offsets[e] = first
+ * position of expert e, offsets[E] = T*k).  ws: device scratch of
+ * moe355_workspace_bytes(d, T, MOE355_MODE_PERMUTE) bytes.
+ */
+moe355_status moe355_permute(const moe355_layer_desc* d, const int32_t* topk_ids, int32_t T,
+                             int32_t* perm, int32_t* offsets, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/*
+ * Decode expert FFN with the combine fused [Edge0, section 3.1 "Math contract":
+ * down(silu(gate(x)) * up(x)); FT-zh, Core method: partial sums merge exactly]:
+ *   out[t] = sum_j topk_w[t, j] * down_e(silu(gate_e(x_t)) * up_e(x_t)),  e = topk_ids[t, j].
+ * The distinct experts are read from uniq / counts[0] of `exp` (filled by
+ * moe355_classify_evict or moe355_dedup); each expert's bytes are read once per
+ * call, from its cache slot when cache != NULL and slot_table[layer*E+e] >= 0,
+ * else from pool + (layer*E + e) * S (pool = one layer's buffer with layer = 0
+ * for a whole-layer call).  x: device bf16 [T, H]; out: device fp32 [T, H];
+ * ws: device scratch of moe355_workspace_bytes(d, T, MOE355_MODE_DECODE) bytes.
+ * Limits: T*k <= 256, H and I multiples of 256.
+ */
+moe355_status moe355_expert_ffn_decode(const moe355_layer_desc* d, const void* x_bf16,
+                                       int32_t T, const int32_t* topk_ids, const float* topk_w,
+                                       const moe355_cache* cache, const uint8_t* pool,
+                                       int32_t layer, const moe355_classify_out* exp,
+                                       float* out, void* ws, size_t ws_bytes,
+                                       hipStream_t stream);
+
+/*
+ * Prefill expert FFN: a grouped GEMM over each expert's token bucket (from
+ * moe355_permute) on the matrix cores, with the whole layer resident
+ * [Edge0, section 3.1 "Executor paths": the whole-layer path loads all experts
+ * of a layer for prefill; FT-zh, Method steps].  Same result as the decode
+ * call.  layer_w: device [E * S].  out: device fp32 [T, H].
+ * ws: moe355_workspace_bytes(d, T, MOE355_MODE_PREFILL) bytes.
+ */
+moe355_status moe355_expert_ffn_prefill(const moe355_layer_desc* d, const void* x_bf16,
+                                        int32_t T, const int32_t* topk_ids, const float* topk_w,
+                                        const uint8_t* layer_w, const int32_t* perm,
+                                        const int32_t* offsets, float* out, void* ws,
+                                        size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Unfused combine: out[t, n] = sum_j topk_w[t, j] * y[t*k + j, n], j ascending.
+ * y: device fp32 [T*k, H]; out: device fp32 [T, H].
+ */
+moe355_status moe355_combine(int32_t T, int32_t H, int32_t k, const float* y,
+                             const float* topk_w, float* out, hipStream_t stream);
+
+#define MOE355_MODE_DECODE   0
+#define MOE355_MODE_PREFILL  1
+#define MOE355_MODE_PERMUTE  2
+/* Scratch bytes a call of the given mode needs for T tokens. */
+size_t moe355_workspace_bytes(const moe355_layer_desc* d, int32_t T, int32_t mode);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE355_H */

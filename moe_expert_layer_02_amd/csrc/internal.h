@@ -1,0 +1,69 @@
+// Internal helpers shared by the libmoe355 translation units (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe355.h"
+
+namespace moe355 {
+
+// ---- host-side status -------------------------------------------------------
+moe355_status fail(moe355_status s, const char* fmt, ...);
+moe355_status check_launch(const char* what);
+inline moe355_status ok() { return MOE355_OK; }
+
+#define MOE355_REQUIRE(cond, code, ...) \
+    do { if (!(cond)) return ::moe355::fail((code), __VA_ARGS__); } while (0)
+
+// Bytes of one expert blob and the offsets of its tensors (canonical layout).
+struct ExpertLayout {
+    int64_t bytes = 0;
+    // per matrix m (0 gate, 1 up, 2 down): packed codes, then scales (s or e), then biases
+    int64_t q_off[3] = {0, 0, 0};
+    int64_t s_off[3] = {0, 0, 0};
+    int64_t b_off[3] = {0, 0, 0};
+};
+bool expert_layout(const moe355_layer_desc* d, ExpertLayout* L);
+moe355_status check_desc(const moe355_layer_desc* d);
+
+// ---- device helpers ---------------------------------------------------------
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Order-preserving map of a float to uint32 (-0.0 folded onto +0.0 first).
+__device__ __forceinline__ uint32_t f32_order_key(float v) {
+    uint32_t u = __float_as_uint(v + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_xor(T v, int mask) {
+    return __shfl_xor(v, mask, WAVE);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        uint64_t o = __shfl_xor(v, m, WAVE);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);
+    return v;
+}
+
+// Sum over aligned segments of `width` lanes (width a power of two <= 64).
+__device__ __forceinline__ float segment_sum_f32(float v, int width) {
+    for (int m = width >> 1; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);
+    return v;
+}
+
+}  // namespace moe355

@@ -1,0 +1,178 @@
+"""Torch-tensor front end of the libmoe355 calls.
+
+Each function takes device tensors, hands their addresses and the current HIP
+stream to the C call of the same name, and raises ``Moe355Error`` on a
+non-zero status.  Nothing here computes any part of the layer.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from .abi import (Cache, ClassifyOut, EvictPolicy, LayerDesc, MODE_DECODE, MODE_PERMUTE,
+                  MODE_PREFILL, check, load)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libmoe355 takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libmoe355 takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def version() -> str:
+    return load().moe355_version().decode()
+
+
+def expert_bytes(desc: LayerDesc) -> int:
+    return int(load().moe355_expert_bytes(ctypes.byref(desc)))
+
+
+def workspace_bytes(desc: LayerDesc, T: int, mode: int) -> int:
+    return int(load().moe355_workspace_bytes(ctypes.byref(desc), T, mode))
+
+
+def router_logits(desc, x_bf16, w_router, logits, stream=None):
+    _need(x_bf16, torch.bfloat16, "x")
+    _need(w_router, torch.float32, "w_router")
+    _need(logits, torch.float32, "logits")
+    T = x_bf16.shape[0]
+    check(load().moe355_router_logits(ctypes.byref(desc), _ptr(x_bf16), _ptr(w_router), T,
+                                      _ptr(logits), _stream(stream)), "moe355_router_logits")
+
+
+def route(desc, logits, topk_ids, topk_w, stream=None):
+    _need(logits, torch.float32, "logits")
+    _need(topk_ids, torch.int32, "topk_ids")
+    _need(topk_w, torch.float32, "topk_w")
+    T = logits.shape[0]
+    check(load().moe355_route(ctypes.byref(desc), _ptr(logits), T, _ptr(topk_ids), _ptr(topk_w),
+                              _stream(stream)), "moe355_route")
+
+
+class DeviceClassifyOut:
+    """Caller-owned per-call lists (``capacity`` int32 each) plus counts[6]."""
+
+    NAMES = ("uniq", "hit_expert", "hit_slot", "miss", "fill_expert", "fill_slot", "inplace",
+             "victims")
+
+    def __init__(self, capacity: int, device="cuda"):
+        self.capacity = capacity
+        self.buf = torch.full((len(self.NAMES), max(capacity, 1)), -1, dtype=torch.int32,
+                              device=device)
+        self.counts = torch.zeros(6, dtype=torch.int32, device=device)
+        self.struct = ClassifyOut(*[self.buf[i].data_ptr() for i in range(len(self.NAMES))],
+                                  self.counts.data_ptr(), capacity)
+
+    def list(self, name: str):
+        return self.buf[self.NAMES.index(name)]
+
+    def host(self) -> dict:
+        """Copy the lists to the host, trimmed to their counts (synchronises)."""
+        b = self.buf.cpu()
+        c = self.counts.cpu().tolist()
+        n = {"uniq": c[0], "hit_expert": c[1], "hit_slot": c[1], "miss": c[2],
+             "fill_expert": c[3], "fill_slot": c[3], "inplace": c[4], "victims": c[5]}
+        out = {k: b[i, :n[k]].tolist() for i, k in enumerate(self.NAMES)}
+        out["counts"] = c
+        return out
+
+
+class DeviceCache:
+    """The HBM expert cache: slot table, owner, timestamps and slot bytes."""
+
+    def __init__(self, n_slots: int, n_layers: int, n_experts: int, slot_bytes: int,
+                 device="cuda", with_data: bool = True):
+        self.table = torch.full((n_layers * n_experts,), -1, dtype=torch.int32, device=device)
+        self.owner = torch.full((n_slots,), -1, dtype=torch.int32, device=device)
+        self.ts = torch.zeros((n_slots,), dtype=torch.int64, device=device)
+        self.data = (torch.empty((n_slots * slot_bytes,), dtype=torch.uint8, device=device)
+                     if with_data else None)
+        self.struct = Cache(n_slots, n_layers, n_experts, slot_bytes, self.table.data_ptr(),
+                            self.owner.data_ptr(), self.ts.data_ptr(),
+                            self.data.data_ptr() if self.data is not None else None)
+
+    @property
+    def n_slots(self) -> int:
+        return self.struct.n_slots
+
+
+def dedup(ids, n_experts: int, out: DeviceClassifyOut, stream=None):
+    _need(ids, torch.int32, "ids")
+    check(load().moe355_dedup(_ptr(ids), ids.numel(), n_experts, ctypes.byref(out.struct),
+                              _stream(stream)), "moe355_dedup")
+
+
+def classify_evict(cache: DeviceCache, layer: int, tick: int, ids, policy: EvictPolicy,
+                   out: DeviceClassifyOut, stream=None):
+    _need(ids, torch.int32, "ids")
+    check(load().moe355_classify_evict(ctypes.byref(cache.struct), layer, tick, _ptr(ids),
+                                       ids.numel(), ctypes.byref(policy),
+                                       ctypes.byref(out.struct), _stream(stream)),
+          "moe355_classify_evict")
+
+
+def cache_fill(cache: DeviceCache, pool, layer: int, out: DeviceClassifyOut, max_fill: int,
+               stream=None):
+    _need(pool, torch.uint8, "pool")
+    check(load().moe355_cache_fill(ctypes.byref(cache.struct), _ptr(pool), layer,
+                                   ctypes.byref(out.struct), max_fill, _stream(stream)),
+          "moe355_cache_fill")
+
+
+def cache_rebuild(src: DeviceCache, dst: DeviceCache, stream=None):
+    check(load().moe355_cache_rebuild(ctypes.byref(src.struct), ctypes.byref(dst.struct),
+                                      _stream(stream)), "moe355_cache_rebuild")
+
+
+def permute(desc, topk_ids, perm, offsets, ws, stream=None):
+    _need(topk_ids, torch.int32, "topk_ids")
+    T = topk_ids.shape[0]
+    check(load().moe355_permute(ctypes.byref(desc), _ptr(topk_ids), T, _ptr(perm), _ptr(offsets),
+                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+          "moe355_permute")
+
+
+def expert_ffn_decode(desc, x_bf16, topk_ids, topk_w, cache, pool, layer: int,
+                      experts: DeviceClassifyOut, out, ws, stream=None):
+    _need(x_bf16, torch.bfloat16, "x")
+    _need(out, torch.float32, "out")
+    T = x_bf16.shape[0]
+    cptr = ctypes.byref(cache.struct) if cache is not None else None
+    check(load().moe355_expert_ffn_decode(ctypes.byref(desc), _ptr(x_bf16), T, _ptr(topk_ids),
+                                          _ptr(topk_w), cptr, _ptr(pool), layer,
+                                          ctypes.byref(experts.struct), _ptr(out), _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(stream)),
+          "moe355_expert_ffn_decode")
+
+
+def expert_ffn_prefill(desc, x_bf16, topk_ids, topk_w, layer_w, perm, offsets, out, ws,
+                       stream=None):
+    _need(x_bf16, torch.bfloat16, "x")
+    _need(out, torch.float32, "out")
+    T = x_bf16.shape[0]
+    check(load().moe355_expert_ffn_prefill(ctypes.byref(desc), _ptr(x_bf16), T, _ptr(topk_ids),
+                                           _ptr(topk_w), _ptr(layer_w), _ptr(perm), _ptr(offsets),
+                                           _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                           _stream(stream)), "moe355_expert_ffn_prefill")
+
+
+def combine(y, topk_w, out, stream=None):
+    T, k = topk_w.shape
+    H = out.shape[1]
+    check(load().moe355_combine(T, H, k, _ptr(y), _ptr(topk_w), _ptr(out), _stream(stream)),
+          "moe355_combine")

@@ -81,9 +81,9 @@ class CacheSim:
             self.ts[s] = tick
         q = q_split(len(miss), q_num, q_den)
         # one scan over every slot's timestamp: the K oldest eligible slots
-        eligible = [(int(self.ts[s]), s) for s in range(self.N) if self.ts[s] < tick]
-        eligible.sort()
-        victims = [s for _, s in eligible[:K]]
+        eligible = np.nonzero(self.ts < tick)[0]              # ascending slot ids
+        order = np.argsort(self.ts[eligible], kind="stable")    # by ts, then slot
+        victims = [int(s) for s in eligible[order][:K]]
         q_eff = min(q, len(victims))
         fill_e = miss[:q_eff]
         fill_s = victims[:q_eff]

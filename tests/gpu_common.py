@@ -1,0 +1,53 @@
+"""Helpers shared by the GPU parity tests (imported lazily, safe on CPU)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from workloads import configs as C
+from workloads import experts as wx
+
+# spec tolerances for the layer output
+REL_L2 = 1e-2
+MAX_ABS = 2e-2
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def desc_of(w: C.Workload):
+    import moe_expert_layer_02_amd as m
+    return m.LayerDesc(w.hidden, w.inter, w.n_experts, w.top_k, w.route, w.n_group,
+                       w.topk_group, w.route_scale, w.wfmt)
+
+
+def check_close(got, want, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = got - want
+    rel = np.linalg.norm(err) / max(np.linalg.norm(want), 1e-30)
+    mx = np.abs(err).max() if err.size else 0.0
+    say(f"{what}: rel_l2={rel:.3e} max_abs={mx:.3e} (|ref| max {np.abs(want).max():.3e})")
+    assert rel <= REL_L2, f"{what}: rel L2 {rel:.3e} > {REL_L2}"
+    assert mx <= MAX_ABS, f"{what}: max abs {mx:.3e} > {MAX_ABS}"
+    return rel, mx
+
+
+class BlobSource:
+    """CPU regeneration of expert bytes (independent of the GPU producer)."""
+
+    def __init__(self, w: C.Workload, seed: int | None = None):
+        self.w = w
+        self.seed = C.seed(w.cid, 0) if seed is None else seed
+        self.cache = {}
+
+    def __call__(self, layer: int, e: int):
+        g = layer * self.w.n_experts + e
+        if g not in self.cache:
+            self.cache[g] = wx.expert_blob(self.seed, g, self.w.wfmt, self.w.hidden, self.w.inter)
+        return self.cache[g]

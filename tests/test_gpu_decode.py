@@ -1,0 +1,183 @@
+"""Decode expert FFN parity on the GPU against the oracle: small shapes that
+span several row tiles with ragged token counts, both weight formats, the
+tiny whole-layer workload end to end, sampled calls of the full-size decode
+workloads (experts read from cache slots and from the pool), and edge cases
+(one expert shared by every token, the largest T*k, empty batch)."""
+import numpy as np
+import pytest
+
+from oracle import ffn as offn
+from oracle import route as oroute
+from workloads import configs as C
+from workloads import experts as wx
+from workloads import traces as tr
+
+from gpu_common import BlobSource, check_close, desc_of, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _x_dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _decode_whole_layer(w, x_bits, ids_np, wt_np, seed=None):
+    """GPU decode FFN with every expert of one layer resident (no cache)."""
+    import torch
+    import moe_expert_layer_02_amd as m
+    from workloads import gpu as wg
+    seed = C.seed(w.cid, 0) if seed is None else seed
+    S = wx.expert_bytes(w.wfmt, w.hidden, w.inter)
+    layer = torch.empty(w.n_experts * S, dtype=torch.uint8, device="cuda")
+    wg.fill_experts(layer, 0, w.n_experts, w.wfmt, w.hidden, w.inter, seed)
+    T = x_bits.shape[0]
+    desc = desc_of(w)
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).cuda()
+    wt = torch.from_numpy(np.ascontiguousarray(wt_np, dtype=np.float32)).cuda()
+    exp = m.DeviceClassifyOut(max(1, min(T * w.top_k, w.n_experts)))
+    m.dedup(ids, w.n_experts, exp)
+    out = torch.full((T, w.hidden), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(m.workspace_bytes(desc, T, m.MODE_DECODE), dtype=torch.uint8, device="cuda")
+    m.expert_ffn_decode(desc, _x_dev(x_bits), ids, wt, None, layer, 0, exp, out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _oracle_layer(w, x_bits, ids, wt, seed=None, tokens=None, layer=0):
+    src = BlobSource(w, seed)
+    return offn.moe_layer(tr.x_as_f32(x_bits), ids, wt, lambda e: src(layer, e), w.wfmt,
+                          w.hidden, w.inter, tokens=tokens)
+
+
+SMALL = [
+    # (H, I, E, k, T, wfmt)
+    (256, 128, 16, 2, 4, C.WFMT_INT4_G64),
+    (512, 256, 32, 3, 5, C.WFMT_INT4_G64),
+    (1024, 512, 24, 4, 7, C.WFMT_MXFP4),
+    (2048, 512, 64, 8, 3, C.WFMT_INT4_G64),
+    (2048, 1024, 40, 6, 9, C.WFMT_MXFP4),
+    (4096, 2048, 16, 6, 2, C.WFMT_MXFP4),
+    (4096, 256, 20, 5, 4, C.WFMT_INT4_G64),
+]
+
+
+@pytest.mark.parametrize("H,I,E,k,T,wfmt", SMALL)
+def test_decode_small_shapes(H, I, E, k, T, wfmt):
+    w = C.Workload(cid=100 + H // 256 + I // 64 + E, name="small", hidden=H, inter=I,
+                   n_experts=E, top_k=k, route=0, wfmt=wfmt)
+    say(f"decode small H={H} I={I} E={E} k={k} T={T} fmt={wfmt}")
+    rng = np.random.default_rng(H + I + E + k + T)
+    x_bits = tr.bf16_normal(rng, (T, H))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    ids, wt = oroute.softmax_topk(logits, k)
+    got = _decode_whole_layer(w, x_bits, ids, wt)
+    want = _oracle_layer(w, x_bits, ids, wt)
+    check_close(got, want, f"decode H={H} I={I} fmt={wfmt}")
+
+
+def test_decode_tiny_workload_end_to_end():
+    """Tiny workload: x . W_r^T -> softmax top-2 -> dedup -> expert FFN, all on the GPU."""
+    import torch
+    import moe_expert_layer_02_amd as m
+    w = C.TINY
+    x_bits, wr = tr.tiny_inputs(w)
+    lg = torch.empty((w.t_decode, w.n_experts), dtype=torch.float32, device="cuda")
+    m.router_logits(desc_of(w), _x_dev(x_bits), torch.from_numpy(wr).cuda(), lg)
+    ids = torch.empty((w.t_decode, w.top_k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((w.t_decode, w.top_k), dtype=torch.float32, device="cuda")
+    m.route(desc_of(w), lg, ids, wt)
+    torch.cuda.synchronize()
+    got = _decode_whole_layer(w, x_bits, ids.cpu().numpy(), wt.cpu().numpy())
+    ref_logits = oroute.router_logits(tr.x_as_f32(x_bits), wr)
+    rid, rw = oroute.softmax_topk(ref_logits, w.top_k)
+    assert (ids.cpu().numpy() == rid).all()
+    want = _oracle_layer(w, x_bits, rid, rw)
+    check_close(got, want, "tiny workload")
+
+
+def test_decode_one_expert_shared_by_all_tokens():
+    w = C.Workload(cid=120, name="shared", hidden=2048, inter=512, n_experts=32, top_k=4,
+                   route=0, wfmt=C.WFMT_INT4_G64)
+    T = 13
+    rng = np.random.default_rng(3)
+    x_bits = tr.bf16_normal(rng, (T, w.hidden))
+    ids = np.stack([np.r_[5, rng.choice([e for e in range(32) if e != 5], 3, replace=False)]
+                    for _ in range(T)]).astype(np.int32)
+    wt = rng.random((T, 4)).astype(np.float32)
+    got = _decode_whole_layer(w, x_bits, ids, wt)
+    check_close(got, _oracle_layer(w, x_bits, ids, wt), "one shared expert")
+
+
+def test_decode_largest_pair_count():
+    w = C.Workload(cid=121, name="maxpairs", hidden=1024, inter=256, n_experts=64, top_k=8,
+                   route=0, wfmt=C.WFMT_MXFP4)
+    T = 32   # T*k = 256, the decode limit
+    rng = np.random.default_rng(4)
+    x_bits = tr.bf16_normal(rng, (T, w.hidden))
+    ids, wt = oroute.softmax_topk(rng.standard_normal((T, 64)).astype(np.float32), 8)
+    got = _decode_whole_layer(w, x_bits, ids, wt)
+    check_close(got, _oracle_layer(w, x_bits, ids, wt), "T*k=256")
+
+
+def test_decode_empty_batch_is_noop():
+    import torch
+    import moe_expert_layer_02_amd as m
+    w = C.QWEN_DECODE
+    desc = desc_of(w)
+    e = torch.empty(0, dtype=torch.int32, device="cuda")
+    exp = m.DeviceClassifyOut(8)
+    out = torch.empty((0, w.hidden), dtype=torch.float32, device="cuda")
+    x = torch.empty((0, w.hidden), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    pool = torch.empty(16, dtype=torch.uint8, device="cuda")
+    m.expert_ffn_decode(desc, x, e.view(0, 8), torch.empty((0, 8), device="cuda"), None, pool, 0,
+                        exp, out, ws)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("cid,steps,sample", [(2, 6, [(0, 0), (2, 17), (5, 39)]),
+                                              (4, 3, [(1, 5), (2, 23)])])
+def test_decode_full_size_sampled_calls(cid, steps, sample):
+    """Whole decode steps at full size through the cache; sampled calls checked."""
+    import torch
+    import moe_expert_layer_02_amd as m
+    from workloads import gpu as wg
+    w = C.ALL[cid]
+    say(f"decode full size {w.name}: {steps} steps, sampled {sample}")
+    desc = desc_of(w)
+    trace = tr.DecodeTrace(w, steps)
+    pool = wg.make_pool(w)
+    S = wx.expert_bytes(w.wfmt, w.hidden, w.inter)
+    cache = m.DeviceCache(w.n_slots, w.n_layers, w.n_experts, S)
+    K = w.victims_k
+    policy = m.EvictPolicy(K, w.q_num, w.q_den)
+    exp = m.DeviceClassifyOut(max(K, min(w.t_decode * w.top_k, w.n_experts)))
+    ids = torch.empty((w.t_decode, w.top_k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((w.t_decode, w.top_k), dtype=torch.float32, device="cuda")
+    out = torch.empty((w.t_decode, w.hidden), dtype=torch.float32, device="cuda")
+    ws = torch.empty(m.workspace_bytes(desc, w.t_decode, m.MODE_DECODE), dtype=torch.uint8,
+                     device="cuda")
+    src = BlobSource(w)
+    rng = np.random.default_rng(cid)
+    for s in range(steps):
+        for l in range(w.n_layers):
+            x_bits = tr.decode_x(w, s, l)
+            lg = torch.from_numpy(trace.logits[s, l]).cuda()
+            m.route(desc, lg, ids, wt)
+            m.classify_evict(cache, l, s * w.n_layers + l + 1, ids, policy, exp)
+            m.cache_fill(cache, pool, l, exp, K)
+            m.expert_ffn_decode(desc, _x_dev(x_bits), ids, wt, cache, pool, l, exp, out, ws)
+            if (s, l) in sample:
+                torch.cuda.synchronize()
+                h = exp.host()
+                got = out.cpu().numpy()
+                rid, rw = oroute.route(trace.logits[s, l], w.top_k, w.route, w.n_group,
+                                       w.topk_group, w.route_scale)
+                assert (ids.cpu().numpy() == rid).all()
+                toks = sorted(rng.choice(w.t_decode, size=min(2, w.t_decode), replace=False))
+                want = offn.moe_layer(tr.x_as_f32(x_bits), rid, rw, lambda e: src(l, e), w.wfmt,
+                                      w.hidden, w.inter, tokens=toks)
+                say(f"call ({s},{l}): hits {h['counts'][1]} fills {h['counts'][3]} "
+                    f"in-place {h['counts'][4]}")
+                check_close(got[toks], want, f"{w.name} call ({s},{l}) tokens {toks}")
