@@ -72,6 +72,14 @@ def cpu_baseline_decode(w, trace, n_calls: int, budget_s: float):
 
 
 def bench_decode(args, w):
+    """Timed region: K decode steps, each one replay of a captured graph holding
+    the step's 40 (or 24) decode_layer calls -- route + classify/evict in one
+    kernel, then the expert FFN with fill-through and the combine -- after the
+    step's inputs (logits, activations, tick base) are staged in HBM.
+
+    Roofline: the expert FFN kernel timed with HIP events in a second, eager
+    pass over the same trace (route, classify_evict, cache_fill as separate
+    calls, then the FFN between two events on the same stream)."""
     import torch
     import moe_expert_layer_02_amd as m
     from workloads import experts as wx
@@ -84,59 +92,106 @@ def bench_decode(args, w):
                        w.topk_group, w.route_scale, w.wfmt)
     S = wx.expert_bytes(w.wfmt, w.hidden, w.inter)
     L, T = w.n_layers, w.t_decode
-    n_steps_trace = w.steps
-    trace = tr.DecodeTrace(w, n_steps_trace)
+    n_trace = w.steps
+    trace = tr.DecodeTrace(w, n_trace)
     pool = wg.make_pool(w)
-    cache = m.DeviceCache(w.n_slots, L, w.n_experts, S)
     K = w.victims_k
     policy = m.EvictPolicy(K, w.q_num, w.q_den)
-    logits = torch.from_numpy(trace.logits).to(dev)                       # [steps, L, T, E]
-    xs = torch.stack([torch.stack([_x_dev(tr.decode_x(w, s, l), torch) for l in range(L)])
-                      for s in range(n_steps_trace)])                       # [steps, L, T, H]
-    ids = torch.empty((L, T, w.top_k), dtype=torch.int32, device=dev)
-    wt = torch.empty((L, T, w.top_k), dtype=torch.float32, device=dev)
     cap = max(K, min(T * w.top_k, w.n_experts))
-    # one set of per-layer lists per timed step, so the counts are read once at the end
-    lists_by_step = [[m.DeviceClassifyOut(cap) for _ in range(L)] for _ in range(args.steps + 1)]
-    out = torch.empty((L, T, w.hidden), dtype=torch.float32, device=dev)
-    ws = torch.empty(m.workspace_bytes(desc, T, m.MODE_DECODE), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
+    logits_all = torch.from_numpy(trace.logits).to(dev)                      # [steps, L, T, E]
+    xs_all = torch.stack([torch.stack([_x_dev(tr.decode_x(w, s, l), torch) for l in range(L)])
+                          for s in range(n_trace)])                           # [steps, L, T, H]
 
-    def step(s, events=None, slot=0):
-        ts = s % n_steps_trace
-        lists = lists_by_step[slot]
-        for l in range(L):
-            tick = s * L + l + 1
-            m.route(desc, logits[ts, l], ids[l], wt[l])
-            m.classify_evict(cache, l, tick, ids[l], policy, lists[l])
-            m.cache_fill(cache, pool, l, lists[l], K)
-            if events is not None:
-                events[l][0].record(stream)
-            m.expert_ffn_decode(desc, xs[ts, l], ids[l], wt[l], cache, pool, l, lists[l], out[l],
-                                ws)
-            if events is not None:
-                events[l][1].record(stream)
+    class Step:
+        def __init__(self):
+            self.cache = m.DeviceCache(w.n_slots, L, w.n_experts, S)
+            self.logits = torch.empty_like(logits_all[0])
+            self.x = torch.empty_like(xs_all[0])
+            self.tick = torch.zeros(1, dtype=torch.int64, device=dev)
+            self.ids = torch.empty((L, T, w.top_k), dtype=torch.int32, device=dev)
+            self.wt = torch.empty((L, T, w.top_k), dtype=torch.float32, device=dev)
+            self.lists = [m.DeviceClassifyOut(cap) for _ in range(L)]
+            self.out = torch.empty((L, T, w.hidden), dtype=torch.float32, device=dev)
+            self.ws = torch.zeros(m.workspace_bytes(desc, T, m.MODE_DECODE), dtype=torch.uint8,
+                                  device=dev)
+
+        def stage(self, s):
+            self.logits.copy_(logits_all[s % n_trace])
+            self.x.copy_(xs_all[s % n_trace])
+            self.tick.fill_(s * L)
+
+        def layers(self):
+            for l in range(L):
+                m.decode_layer(desc, self.cache, pool, l, self.tick, l + 1, self.logits[l],
+                               self.x[l], policy, self.ids[l], self.wt[l], self.lists[l],
+                               self.out[l], self.ws)
+
+    warm = Step()                       # first launches (occupancy queries) outside capture
+    warm.stage(0)
+    warm.layers()
+    torch.cuda.synchronize()
+    del warm
+    st = Step()
+    st.stage(0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st.layers()
+    torch.cuda.synchronize()
 
     for s in range(args.warmup):
-        step(s)
+        st.stage(s)
+        graph.replay()
     torch.cuda.synchronize()
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in range(L)] for _ in range(args.steps)]
+    uniq_per_step = []
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, ev[i], slot=i + 1)
+        st.stage(args.warmup + i)
+        graph.replay()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    dt = t1 - t0
-    n_uniq = sum(int(lists_by_step[i + 1][l].counts[0].item())
-                 for i in range(args.steps) for l in range(L))
-    ffn_ms = [e0.elapsed_time(e1) for row in ev for e0, e1 in row]
-    ffn_avg_s = float(np.mean(ffn_ms)) / 1e3
+    dt = time.perf_counter() - t0
+    # distinct experts per call, from the trace's target sets (the routed top-k sets;
+    # checked below against the device counts of the last step)
+    for i in range(args.steps):
+        s = (args.warmup + i) % n_trace
+        for l in range(L):
+            uniq_per_step.append(len(np.unique(trace.targets[s, l])))
+    n_uniq = int(np.sum(uniq_per_step))
+    last = (args.warmup + args.steps - 1) % n_trace
+    for l in range(L):
+        assert int(st.lists[l].counts[0].item()) == len(np.unique(trace.targets[last, l]))
     bytes_total = n_uniq * S
     n_calls = args.steps * L
-    per_call_bytes = bytes_total / n_calls
-    achieved = per_call_bytes / ffn_avg_s / 1e9
     value = bytes_total / dt / 1e9
+
+    # roofline pass: the FFN kernel alone between two events, eager, same trace
+    rp = Step()
+    ids = torch.empty((T, w.top_k), dtype=torch.int32, device=dev)
+    wt = torch.empty((T, w.top_k), dtype=torch.float32, device=dev)
+    lst = m.DeviceClassifyOut(cap)
+    stream = torch.cuda.current_stream()
+    ev = []
+    rp_steps = min(args.steps, 10)
+    u_rp = 0
+    for s in range(args.warmup + rp_steps):
+        rp.stage(s)
+        for l in range(L):
+            m.route(desc, rp.logits[l], ids, wt)
+            m.classify_evict(rp.cache, l, s * L + l + 1, ids, policy, lst)
+            m.cache_fill(rp.cache, pool, l, lst, K)
+            timed = s >= args.warmup
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            m.expert_ffn_decode(desc, rp.x[l], ids, wt, rp.cache, pool, l, lst, rp.out[l], rp.ws)
+            if timed:
+                e1.record(stream)
+                ev.append((e0, e1))
+                u_rp += len(np.unique(trace.targets[s % n_trace, l]))
+    torch.cuda.synchronize()
+    ffn_avg_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    per_call_bytes = u_rp * S / len(ev)
+    achieved = per_call_bytes / ffn_avg_s / 1e9
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt / args.steps * 1e3, 4),
@@ -145,11 +200,13 @@ def bench_decode(args, w):
         "config": {"workload": w.name, "layers": L, "tokens_per_step": T, "hidden": w.hidden,
                    "inter": w.inter, "experts": w.n_experts, "top_k": w.top_k,
                    "weights": "int4_g64" if w.wfmt == 0 else "mxfp4", "cache_slots": w.n_slots,
-                   "expert_bytes": S, "parallelism": "single_gpu"},
-        "roofline": {"bound": "hbm", "kernel": "expert_ffn_decode",
+                   "expert_bytes": S, "layer_calls_timed": n_calls, "parallelism": "single_gpu",
+                   "step": "one replay of a captured graph of decode_layer calls"},
+        "roofline": {"bound": "hbm", "kernel": "ffn_decode_kernel (expert_ffn_decode)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": round(per_call_bytes), "avg_launch_us": round(ffn_avg_s * 1e6, 2)},
+                     "bytes_per_launch": round(per_call_bytes),
+                     "avg_launch_us": round(ffn_avg_s * 1e6, 2), "launches_timed": len(ev)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_decode(w, trace, n_calls=args.cpu_calls,
@@ -157,12 +214,119 @@ def bench_decode(args, w):
     return res
 
 
+MFMA_PEAK_BF16_TFLOPS = 2500.0
+
+
+def cpu_baseline_prefill(w, x_bits, ids, wt, budget_s: float):
+    """The oracle (fp32, NumPy BLAS) on a bounded sample of the prefill layer's tokens."""
+    from oracle import ffn as offn
+    from workloads import configs as C
+    from workloads import experts as wx
+    from workloads import traces as tr
+    n_tok = 256
+    toks = np.arange(n_tok)
+    blobs = {int(e): wx.expert_blob(C.seed(w.cid, 0), int(e), w.wfmt, w.hidden, w.inter)
+             for e in np.unique(ids[toks])}
+    x = tr.x_as_f32(x_bits[toks])
+    t0 = time.perf_counter()
+    offn.moe_layer(x, ids[toks], wt[toks], blobs.__getitem__, w.wfmt, w.hidden, w.inter,
+                   dtype=np.float32)
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = os.cpu_count() or 1
+    return {"value": round(n_tok / dt, 2), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"first {n_tok} of {w.t_prefill} tokens, fp32 NumPy dequant of their "
+                      f"{len(blobs)} experts + GEMMs + combine, {dt:.1f} s"}
+
+
+def bench_prefill(args, w):
+    import torch
+    import moe_expert_layer_02_amd as m
+    from workloads import experts as wx
+    from workloads import gpu as wg
+    from workloads import traces as tr
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    desc = m.LayerDesc(w.hidden, w.inter, w.n_experts, w.top_k, w.route, w.n_group,
+                       w.topk_group, w.route_scale, w.wfmt)
+    S = wx.expert_bytes(w.wfmt, w.hidden, w.inter)
+    T, k = w.t_prefill, w.top_k
+    x_bits = tr.prefill_x(w)
+    logits_np = tr.prefill_logits(w)
+    layer = torch.empty(w.n_experts * S, dtype=torch.uint8, device=dev)
+    wg.fill_experts(layer, 0, w.n_experts, w.wfmt, w.hidden, w.inter, C_seed(w))
+    x = _x_dev(x_bits, torch)
+    logits = torch.from_numpy(logits_np).to(dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wt = torch.empty((T, k), dtype=torch.float32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    offsets = torch.empty(w.n_experts + 1, dtype=torch.int32, device=dev)
+    wsp = torch.empty(m.workspace_bytes(desc, T, m.MODE_PERMUTE), dtype=torch.uint8, device=dev)
+    ws = torch.empty(m.workspace_bytes(desc, T, m.MODE_PREFILL), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, w.hidden), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        m.route(desc, logits, ids, wt)
+        m.permute(desc, ids, perm, offsets, wsp)
+        if events is not None:
+            events[0].record(stream)
+        m.expert_ffn_prefill(desc, x, ids, wt, layer, perm, offsets, out, ws)
+        if events is not None:
+            events[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ffn_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    flops = 6.0 * w.hidden * w.inter * T * k          # algorithmic: gate, up, down
+    achieved = flops / ffn_s / 1e12
+    res = {
+        "metric": METRIC, "value": round(T * args.steps / dt, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(dt / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16-mfma/f32-acc", "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "hidden": w.hidden, "inter": w.inter,
+                   "experts": w.n_experts, "top_k": k,
+                   "weights": "int4_g64" if w.wfmt == 0 else "mxfp4",
+                   "parallelism": "single_gpu"},
+        "roofline": {"bound": "mfma", "kernel": "expert_ffn_prefill",
+                     "achieved": round(achieved, 1), "peak": MFMA_PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": flops,
+                     "avg_launch_us": round(ffn_s * 1e6, 1)},
+    }
+    if not args.no_cpu_baseline:
+        torch.cuda.synchronize()
+        res["cpu_baseline"] = cpu_baseline_prefill(w, x_bits, ids.cpu().numpy(), wt.cpu().numpy(),
+                                                   args.cpu_budget)
+    return res
+
+
+def C_seed(w):
+    from workloads import configs as C
+    return C.seed(w.cid, 0)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen_decode", choices=["qwen_decode", "ds_decode"])
+    ap.add_argument("--workload", default="qwen_decode",
+                    choices=["qwen_decode", "ds_decode", "qwen_prefill", "ds_prefill"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-calls", type=int, default=160)
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -172,8 +336,9 @@ def main():
               "single-GPU by design", file=sys.stderr)
         sys.exit(2)
     from workloads import configs as C
-    w = {"qwen_decode": C.QWEN_DECODE, "ds_decode": C.DS_DECODE}[args.workload]
-    res = bench_decode(args, w)
+    w = {"qwen_decode": C.QWEN_DECODE, "ds_decode": C.DS_DECODE, "qwen_prefill": C.QWEN_PREFILL,
+         "ds_prefill": C.DS_STRESS}[args.workload]
+    res = bench_prefill(args, w) if args.workload.endswith("prefill") else bench_decode(args, w)
     print(json.dumps(res), flush=True)
 
 

@@ -124,6 +124,14 @@ typedef struct {
  * uniq, hit_expert, miss, fill_expert and inplace hold expert ids in ascending
  * order; hit_slot / fill_slot pair with hit_expert / fill_expert; victims are
  * slots in ascending (ts, slot) order.  Entries past the counts are unspecified.
+ *
+ * plan [capacity][4] int32 and pairs [pair_capacity] int32 describe the call for
+ * the expert FFN, one row per distinct expert uniq[u]:
+ *   plan[u] = {slot holding the expert after the call or -1 (read from the pool),
+ *              1 if this call fills that slot else 0,
+ *              first index into pairs, number of pairs};
+ * pairs lists the routed (token, slot) pairs t*k + j grouped by u.
+ * pair_capacity must be >= the call's number of routed ids.
  */
 typedef struct {
     int32_t* uniq;
@@ -136,6 +144,9 @@ typedef struct {
     int32_t* victims;
     int32_t* counts;
     int32_t  capacity;
+    int32_t* plan;
+    int32_t* pairs;
+    int32_t  pair_capacity;
 } moe355_classify_out;
 
 /*
@@ -180,7 +191,7 @@ moe355_status moe355_dedup(const int32_t* ids, int32_t n_ids, int32_t n_experts,
  * for i < min(q, n_victims): evict victim i's owner (its table entry -> -1), map
  * miss i to victim i, set owner and ts = tick.  Remaining misses go to `inplace`.
  * The caller must use a tick larger than every earlier one (e.g. step*L + l + 1).
- * Limits: n_slots <= 16384, n_experts <= 1024, 0 < tick < 2^31,
+ * Limits: n_slots <= 16384, n_experts <= 1024, n_ids <= 1024, 0 < tick < 2^31,
  * out->capacity >= max(min(n_ids, E), K).
  */
 moe355_status moe355_classify_evict(const moe355_cache* c, int32_t layer, int64_t tick,
@@ -229,8 +240,12 @@ moe355_status moe355_permute(const moe355_layer_desc* d, const int32_t* topk_ids
  * call, from its cache slot when cache != NULL and slot_table[layer*E+e] >= 0,
  * else from pool + (layer*E + e) * S (pool = one layer's buffer with layer = 0
  * for a whole-layer call).  x: device bf16 [T, H]; out: device fp32 [T, H];
- * ws: device scratch of moe355_workspace_bytes(d, T, MOE355_MODE_DECODE) bytes.
- * Limits: T*k <= 256, H and I multiples of 256.
+ * ws: device scratch of moe355_workspace_bytes(d, T, MOE355_MODE_DECODE) bytes
+ * (calls sharing one workspace must not overlap).  exp->plan and exp->pairs
+ * (written by moe355_classify_evict or moe355_dedup) are required.  Two
+ * kernels: gate/up (which also zeroes out), then down with the combine as fp32
+ * atomic additions, so the order of a token's k additions is not fixed.
+ * Limits: T*k <= 256; H and I in {128, 256, 512, 1024, 2048, 4096}.
  */
 moe355_status moe355_expert_ffn_decode(const moe355_layer_desc* d, const void* x_bf16,
                                        int32_t T, const int32_t* topk_ids, const float* topk_w,
@@ -238,6 +253,30 @@ moe355_status moe355_expert_ffn_decode(const moe355_layer_desc* d, const void* x
                                        int32_t layer, const moe355_classify_out* exp,
                                        float* out, void* ws, size_t ws_bytes,
                                        hipStream_t stream);
+
+/*
+ * One whole decode layer call in two kernels [FT-zh, Method steps: per layer a
+ * single device kernel routes, deduplicates, classifies, splits the misses and
+ * picks the LRU victims; the GPU computes G = H u F while F is copied into its
+ * slots; everything replays inside one captured graph with no host
+ * involvement]: route T tokens from `logits`, run the bookkeeping of
+ * moe355_classify_evict, then the expert FFN of moe355_expert_ffn_decode with
+ * the combine.  The experts filled in this call are read from the pool and
+ * their bytes are written to their victim slots by the FFN itself (the same end
+ * state as moe355_cache_fill, one fewer pass over those bytes).
+ *   tick = *tick_base + tick_add when tick_base (device int64) is non-null,
+ *   else tick_add; it must exceed every earlier tick.
+ * logits: device fp32 [T, E]; x: device bf16 [T, H]; topk_ids / topk_w: device
+ * [T, k] outputs; lists: the call's classify lists (capacity >= max(min(T*k, E),
+ * K)); out: device fp32 [T, H]; ws as for moe355_expert_ffn_decode (zeroed
+ * before first use).  Limits: 1 <= T*k <= 256, plus those of the two calls.
+ */
+moe355_status moe355_decode_layer(const moe355_layer_desc* d, const moe355_cache* c,
+                                  const uint8_t* pool, int32_t layer, const int64_t* tick_base,
+                                  int64_t tick_add, const float* logits, const void* x_bf16,
+                                  int32_t T, const moe355_evict_policy* p, int32_t* topk_ids,
+                                  float* topk_w, moe355_classify_out* lists, float* out, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
 
 /*
  * Prefill expert FFN: a grouped GEMM over each expert's token bucket (from

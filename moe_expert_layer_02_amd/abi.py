@@ -38,7 +38,8 @@ class EvictPolicy(ctypes.Structure):
 class ClassifyOut(ctypes.Structure):
     _fields_ = [("uniq", c_ptr), ("hit_expert", c_ptr), ("hit_slot", c_ptr), ("miss", c_ptr),
                 ("fill_expert", c_ptr), ("fill_slot", c_ptr), ("inplace", c_ptr),
-                ("victims", c_ptr), ("counts", c_ptr), ("capacity", c_i32)]
+                ("victims", c_ptr), ("counts", c_ptr), ("capacity", c_i32), ("plan", c_ptr),
+                ("pairs", c_ptr), ("pair_capacity", c_i32)]
 
 
 class Moe355Error(RuntimeError):
@@ -65,6 +66,9 @@ _SIGS = {
     "moe355_expert_ffn_decode": (c_i32, [_P(LayerDesc), c_ptr, c_i32, c_ptr, c_ptr, _P(Cache),
                                          c_ptr, c_i32, _P(ClassifyOut), c_ptr, c_ptr,
                                          ctypes.c_size_t, c_ptr]),
+    "moe355_decode_layer": (c_i32, [_P(LayerDesc), _P(Cache), c_ptr, c_i32, c_ptr, c_i64, c_ptr,
+                                    c_ptr, c_i32, _P(EvictPolicy), c_ptr, c_ptr, _P(ClassifyOut),
+                                    c_ptr, c_ptr, ctypes.c_size_t, c_ptr]),
     "moe355_expert_ffn_prefill": (c_i32, [_P(LayerDesc), c_ptr, c_i32, c_ptr, c_ptr, c_ptr,
                                           c_ptr, c_ptr, c_ptr, c_ptr, ctypes.c_size_t, c_ptr]),
     "moe355_combine": (c_i32, [c_i32, c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr]),

@@ -74,6 +74,7 @@ moe355_status check_desc(const moe355_layer_desc* d) {
 
 size_t permute_ws_bytes(int E, int T, int k);
 size_t prefill_ws_bytes(const moe355_layer_desc* d, int T);
+size_t decode_ws_bytes(const moe355_layer_desc* d, int T);
 
 }  // namespace moe355
 
@@ -102,9 +103,8 @@ extern "C" int64_t moe355_expert_bytes(const moe355_layer_desc* d) {
 
 extern "C" size_t moe355_workspace_bytes(const moe355_layer_desc* d, int32_t T, int32_t mode) {
     if (check_desc(d) != MOE355_OK || T < 0) return 0;
-    const size_t tk = static_cast<size_t>(T) * d->top_k;
     switch (mode) {
-        case MOE355_MODE_DECODE: return tk * d->inter * sizeof(float) + 256;
+        case MOE355_MODE_DECODE: return decode_ws_bytes(d, T);
         case MOE355_MODE_PREFILL: return prefill_ws_bytes(d, T);
         case MOE355_MODE_PERMUTE: return permute_ws_bytes(d->n_experts, T, d->top_k);
         default: return 0;

@@ -15,7 +15,7 @@
 // (ts, slot) keys among slots with ts < tick are found by an 8-bit-digit radix
 // select over LDS histograms, then ranked by counting.  Owning the whole call
 // in one workgroup keeps the table updates free of cross-workgroup atomics.
-#include "internal.h"
+#include "route_dev.h"
 
 namespace moe355 {
 namespace {
@@ -139,9 +139,38 @@ __device__ uint64_t radix_select(int n, uint32_t rank, KeyFn key_of, SelectScrat
     return prefix;
 }
 
+}  // namespace
+
+struct ClassifyParams {
+    int dedup_only;
+    int32_t* table;
+    int table_len;
+    int32_t* owner;
+    int64_t* slot_ts;
+    int N, E, layer;
+    const int64_t* tick_dev;   // tick = *tick_dev + tick_add when set, else tick_add
+    int64_t tick_add;
+    const int32_t* ids;
+    int n_ids;
+    int K, q_num, q_den;
+    // optional routing of the call's tokens before the bookkeeping
+    const float* logits;
+    int T, k, route_kind, n_group, topk_group;
+    float route_scale;
+    int32_t* ids_out;
+    float* w_out;
+    int32_t *uniq, *hit_e, *hit_s, *miss, *fill_e, *fill_s, *inplace, *victims, *counts;
+    int32_t *plan, *pairs;     // optional: the FFN's per-expert plan and grouped pairs
+};
+
+namespace {
+
 struct ClassifyShared {
     uint32_t ts[MAX_SLOTS];
     int32_t mark[MAX_EXPERTS];
+    int32_t upos[MAX_EXPERTS];   // expert -> its index u in uniq
+    int32_t pcnt[MAX_EXPERTS];   // routed pairs per u
+    int32_t pbeg[MAX_EXPERTS];   // first index of u's pairs
     int32_t miss[MAX_LIST];
     uint64_t sel_key[MAX_LIST];
     int32_t victims[MAX_LIST];
@@ -150,21 +179,43 @@ struct ClassifyShared {
     SelectScratch sc;
 };
 
-__global__ void __launch_bounds__(CL_THREADS)
-classify_kernel(int dedup_only, int32_t* __restrict__ table, int table_len,
-                int32_t* __restrict__ owner, int64_t* __restrict__ slot_ts, int N, int E,
-                int layer, uint32_t tick,
-                const int32_t* __restrict__ ids, int n_ids, int K, int q_num, int q_den,
-                int32_t* __restrict__ o_uniq, int32_t* __restrict__ o_hit_e,
-                int32_t* __restrict__ o_hit_s, int32_t* __restrict__ o_miss,
-                int32_t* __restrict__ o_fill_e, int32_t* __restrict__ o_fill_s,
-                int32_t* __restrict__ o_inplace, int32_t* __restrict__ o_victims,
-                int32_t* __restrict__ o_counts) {
-    __shared__ ClassifyShared sh;
-    const int tid = threadIdx.x;
+}  // namespace
 
-    for (int e = tid; e < E; e += CL_THREADS) sh.mark[e] = 0;
+// One layer call: optional routing of T tokens, then dedup, hit/miss, victims.
+__global__ void __launch_bounds__(CL_THREADS) classify_kernel(ClassifyParams cp) {
+    __shared__ ClassifyShared sh;
+    __shared__ int32_t routed[MAX_LIST];
+    const int tid = threadIdx.x;
+    int32_t* __restrict__ table = cp.table;
+    int32_t* __restrict__ owner = cp.owner;
+    int64_t* __restrict__ slot_ts = cp.slot_ts;
+    const int N = cp.N, E = cp.E, layer = cp.layer, K = cp.K, table_len = cp.table_len;
+    const int dedup_only = cp.dedup_only;
+    const uint32_t tick = cp.tick_dev ? static_cast<uint32_t>(*cp.tick_dev + cp.tick_add)
+                                      : static_cast<uint32_t>(cp.tick_add);
+    const int32_t* ids = cp.ids;
+    const int n_ids = cp.n_ids;
+
+    for (int e = tid; e < E; e += CL_THREADS) {
+        sh.mark[e] = 0;
+        sh.pcnt[e] = 0;
+    }
     if (tid == 0) sh.n_sel = 0;
+    if (cp.logits) {
+        // route the call's tokens first: one wavefront per token
+        for (int t = tid / WAVE; t < cp.T; t += CL_WAVES) {
+            float w;
+            const int e = route_token(cp.logits + static_cast<int64_t>(t) * E, E, cp.k,
+                                      cp.route_kind, cp.n_group, cp.topk_group, cp.route_scale, &w);
+            const int lane = tid & (WAVE - 1);
+            if (lane < cp.k) {
+                cp.ids_out[t * cp.k + lane] = e;
+                cp.w_out[t * cp.k + lane] = w;
+                routed[t * cp.k + lane] = e;
+            }
+        }
+        ids = routed;
+    }
     __syncthreads();
     for (int i = tid; i < n_ids; i += CL_THREADS) {
         int e = ids[i];
@@ -190,21 +241,50 @@ classify_kernel(int dedup_only, int32_t* __restrict__ table, int table_len,
     const uint32_t n_uniq = static_cast<uint32_t>(tot & 0x1FFFFF);
     const uint32_t n_hit = static_cast<uint32_t>((tot >> 21) & 0x1FFFFF);
     const uint32_t n_miss = static_cast<uint32_t>((tot >> 42) & 0x1FFFFF);
-    if (m) o_uniq[pos & 0x1FFFFF] = e;
+    const int my_u = static_cast<int>(pos & 0x1FFFFF);
+    if (m) {
+        cp.uniq[my_u] = e;
+        sh.upos[e] = my_u;
+    }
+    __syncthreads();
+
+    // ---- the routed pairs of each distinct expert, grouped by u (n_ids <= threads) ----
+    const bool with_plan = cp.plan != nullptr && cp.pairs != nullptr;
+    int pair_u = -1, pair_local = 0;
+    if (with_plan && tid < n_ids) {
+        const int pe = ids[tid];
+        if (pe >= 0 && pe < E) {
+            pair_u = sh.upos[pe];
+            pair_local = atomicAdd(&sh.pcnt[pair_u], 1);
+        }
+    }
+    __syncthreads();
+    {
+        uint64_t ptot;
+        const uint64_t pb = block_excl_scan(
+            (with_plan && tid < static_cast<int>(n_uniq)) ? static_cast<uint64_t>(sh.pcnt[tid]) : 0ull,
+            sh.wave_tot, &ptot);
+        if (tid < static_cast<int>(n_uniq)) sh.pbeg[tid] = static_cast<int32_t>(pb);
+    }
+    __syncthreads();
+    if (pair_u >= 0) cp.pairs[sh.pbeg[pair_u] + pair_local] = tid;
+
     if (dedup_only) {
-        if (tid < 6) o_counts[tid] = tid == 0 ? static_cast<int32_t>(n_uniq) : 0;
+        if (tid < 6) cp.counts[tid] = tid == 0 ? static_cast<int32_t>(n_uniq) : 0;
+        if (with_plan && m)
+            reinterpret_cast<int4*>(cp.plan)[my_u] = make_int4(-1, 0, sh.pbeg[my_u], sh.pcnt[my_u]);
         return;
     }
     if (is_hit) {
         const uint32_t p = (pos >> 21) & 0x1FFFFF;
-        o_hit_e[p] = e;
-        o_hit_s[p] = slot;
+        cp.hit_e[p] = e;
+        cp.hit_s[p] = slot;
         sh.ts[slot] = tick;  // recency moves on a router selection
         slot_ts[slot] = tick;
     }
     if (is_miss) {
         const uint32_t p = (pos >> 42) & 0x1FFFFF;
-        o_miss[p] = e;
+        cp.miss[p] = e;
         sh.miss[p] = e;
     }
     __syncthreads();
@@ -237,13 +317,13 @@ classify_kernel(int dedup_only, int32_t* __restrict__ table, int table_len,
             for (uint32_t j = 0; j < n_vic; ++j) r += sh.sel_key[j] < k ? 1u : 0u;
             const int s = static_cast<int>(k & ((1ull << sbits) - 1));
             sh.victims[r] = s;
-            o_victims[r] = s;
+            cp.victims[r] = s;
         }
         __syncthreads();
     }
 
     // ---- q split and slot update -------------------------------------------
-    const int64_t q_raw = (2ll * q_num * n_miss + q_den) / (2ll * q_den);
+    const int64_t q_raw = (2ll * cp.q_num * n_miss + cp.q_den) / (2ll * cp.q_den);
     const uint32_t q = static_cast<uint32_t>(q_raw < n_miss ? q_raw : n_miss);
     const uint32_t q_eff = q < n_vic ? q : n_vic;
     for (uint32_t i = tid; i < q_eff; i += CL_THREADS) {
@@ -255,19 +335,29 @@ classify_kernel(int dedup_only, int32_t* __restrict__ table, int table_len,
         table[layer * E + ex] = v;
         owner[v] = layer * E + ex;
         slot_ts[v] = tick;
-        o_fill_e[i] = ex;
-        o_fill_s[i] = v;
+        cp.fill_e[i] = ex;
+        cp.fill_s[i] = v;
     }
-    for (uint32_t i = q_eff + tid; i < n_miss; i += CL_THREADS) o_inplace[i - q_eff] = sh.miss[i];
+    for (uint32_t i = q_eff + tid; i < n_miss; i += CL_THREADS) cp.inplace[i - q_eff] = sh.miss[i];
+    if (with_plan && m) {
+        // where the FFN reads this expert from after the call, and whether it is filled now
+        const uint32_t p_miss = static_cast<uint32_t>((pos >> 42) & 0x1FFFFF);
+        const bool filled = is_miss && p_miss < q_eff;
+        const int final_slot = is_hit ? slot : (filled ? sh.victims[p_miss] : -1);
+        reinterpret_cast<int4*>(cp.plan)[my_u] =
+            make_int4(final_slot, filled ? 1 : 0, sh.pbeg[my_u], sh.pcnt[my_u]);
+    }
     if (tid == 0) {
-        o_counts[0] = static_cast<int32_t>(n_uniq);
-        o_counts[1] = static_cast<int32_t>(n_hit);
-        o_counts[2] = static_cast<int32_t>(n_miss);
-        o_counts[3] = static_cast<int32_t>(q_eff);
-        o_counts[4] = static_cast<int32_t>(n_miss - q_eff);
-        o_counts[5] = static_cast<int32_t>(n_vic);
+        cp.counts[0] = static_cast<int32_t>(n_uniq);
+        cp.counts[1] = static_cast<int32_t>(n_hit);
+        cp.counts[2] = static_cast<int32_t>(n_miss);
+        cp.counts[3] = static_cast<int32_t>(q_eff);
+        cp.counts[4] = static_cast<int32_t>(n_miss - q_eff);
+        cp.counts[5] = static_cast<int32_t>(n_vic);
     }
 }
+
+namespace {
 
 // Copy the filled experts' bytes from the pool into their slots.
 __global__ void __launch_bounds__(256)
@@ -364,8 +454,14 @@ rebuild_copy_kernel(const int32_t* __restrict__ f_table, int table_len, int f_n,
 
 constexpr int64_t COPY_CHUNK = 64 * 1024;
 
-moe355_status check_out(const moe355_classify_out* o, bool full) {
+}  // namespace
+
+moe355_status check_out(const moe355_classify_out* o, bool full, int n_ids) {
     MOE355_REQUIRE(o && o->uniq && o->counts, MOE355_EINVAL, "classify_out: null list");
+    MOE355_REQUIRE((o->plan == nullptr) == (o->pairs == nullptr), MOE355_EINVAL,
+                   "classify_out: plan and pairs go together");
+    MOE355_REQUIRE(o->pairs == nullptr || o->pair_capacity >= n_ids, MOE355_ECAPACITY,
+                   "classify_out: pair capacity %d < %d routed ids", o->pair_capacity, n_ids);
     if (full)
         MOE355_REQUIRE(o->hit_expert && o->hit_slot && o->miss && o->fill_expert && o->fill_slot &&
                            o->inplace && o->victims,
@@ -388,42 +484,24 @@ moe355_status check_cache(const moe355_cache* c) {
     return MOE355_OK;
 }
 
-}  // namespace
-}  // namespace moe355
-
-using namespace moe355;
-
-extern "C" moe355_status moe355_dedup(const int32_t* ids, int32_t n_ids, int32_t n_experts,
-                                      moe355_classify_out* out, hipStream_t stream) {
-    moe355_status st = check_out(out, false);
-    if (st) return st;
-    MOE355_REQUIRE(n_ids >= 0 && (n_ids == 0 || ids), MOE355_EINVAL, "dedup: n_ids=%d", n_ids);
-    MOE355_REQUIRE(n_experts >= 1 && n_experts <= MAX_EXPERTS, MOE355_ENOTSUP,
-                   "dedup: n_experts=%d", n_experts);
-    const int need = n_ids < n_experts ? n_ids : n_experts;
-    MOE355_REQUIRE(out->capacity >= need, MOE355_ECAPACITY, "dedup: capacity %d < %d",
-                   out->capacity, need);
-    classify_kernel<<<1, CL_THREADS, 0, stream>>>(
-        1, nullptr, 0, nullptr, nullptr, 0, n_experts, 0, 0, ids, n_ids, 0, 1, 1, out->uniq, nullptr,
-        nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, out->counts);
-    return check_launch("dedup");
-}
-
-extern "C" moe355_status moe355_classify_evict(const moe355_cache* c, int32_t layer, int64_t tick,
-                                               const int32_t* ids, int32_t n_ids,
-                                               const moe355_evict_policy* p,
-                                               moe355_classify_out* out, hipStream_t stream) {
+// classify_evict with an optional route phase (route != null: ids are produced
+// from route->logits) and an optional device-resident tick base.
+moe355_status classify_call(const moe355_cache* c, int32_t layer, const int64_t* tick_dev,
+                            int64_t tick, const int32_t* ids, int32_t n_ids,
+                            const moe355_evict_policy* p, moe355_classify_out* out,
+                            const RouteArgs* route, hipStream_t stream) {
     moe355_status st = check_cache(c);
     if (st) return st;
-    st = check_out(out, true);
+    st = check_out(out, true, n_ids);
     if (st) return st;
     MOE355_REQUIRE(p, MOE355_EINVAL, "classify_evict: null policy");
     MOE355_REQUIRE(layer >= 0 && layer < c->n_layers, MOE355_EINVAL, "classify_evict: layer=%d",
                    layer);
-    MOE355_REQUIRE(tick > 0 && tick < (1ll << 31), MOE355_ENOTSUP,
-                   "classify_evict: tick=%lld outside (0, 2^31)", static_cast<long long>(tick));
-    MOE355_REQUIRE(n_ids >= 0 && (n_ids == 0 || ids), MOE355_EINVAL, "classify_evict: n_ids=%d",
-                   n_ids);
+    if (!tick_dev)
+        MOE355_REQUIRE(tick > 0 && tick < (1ll << 31), MOE355_ENOTSUP,
+                       "classify_evict: tick=%lld outside (0, 2^31)", static_cast<long long>(tick));
+    MOE355_REQUIRE(n_ids >= 0 && n_ids <= MAX_LIST && (n_ids == 0 || ids || route), MOE355_EINVAL,
+                   "classify_evict: n_ids=%d", n_ids);
     MOE355_REQUIRE(p->K >= 0 && p->q_num >= 0 && p->q_den >= 1, MOE355_EINVAL,
                    "classify_evict: policy K=%d q=%d/%d", p->K, p->q_num, p->q_den);
     MOE355_REQUIRE(static_cast<int64_t>(p->q_num) * 2 * MAX_EXPERTS < (1ll << 62), MOE355_EINVAL,
@@ -432,13 +510,84 @@ extern "C" moe355_status moe355_classify_evict(const moe355_cache* c, int32_t la
     const int need = need_u > p->K ? need_u : p->K;
     MOE355_REQUIRE(out->capacity >= need, MOE355_ECAPACITY,
                    "classify_evict: list capacity %d < %d", out->capacity, need);
-    classify_kernel<<<1, CL_THREADS, 0, stream>>>(
-        0, c->slot_table, c->n_layers * c->n_experts, c->slot_owner, c->slot_ts, c->n_slots,
-        c->n_experts, layer,
-        static_cast<uint32_t>(tick), ids, n_ids, p->K, p->q_num, p->q_den, out->uniq,
-        out->hit_expert, out->hit_slot, out->miss, out->fill_expert, out->fill_slot, out->inplace,
-        out->victims, out->counts);
+    ClassifyParams cp{};
+    cp.dedup_only = 0;
+    cp.table = c->slot_table;
+    cp.table_len = c->n_layers * c->n_experts;
+    cp.owner = c->slot_owner;
+    cp.slot_ts = c->slot_ts;
+    cp.N = c->n_slots;
+    cp.E = c->n_experts;
+    cp.layer = layer;
+    cp.tick_dev = tick_dev;
+    cp.tick_add = tick;
+    cp.ids = ids;
+    cp.n_ids = n_ids;
+    cp.K = p->K;
+    cp.q_num = p->q_num;
+    cp.q_den = p->q_den;
+    if (route) {
+        cp.logits = route->logits;
+        cp.T = route->T;
+        cp.k = route->k;
+        cp.route_kind = route->kind;
+        cp.n_group = route->n_group;
+        cp.topk_group = route->topk_group;
+        cp.route_scale = route->scale;
+        cp.ids_out = route->ids_out;
+        cp.w_out = route->w_out;
+    }
+    cp.uniq = out->uniq;
+    cp.hit_e = out->hit_expert;
+    cp.hit_s = out->hit_slot;
+    cp.miss = out->miss;
+    cp.fill_e = out->fill_expert;
+    cp.fill_s = out->fill_slot;
+    cp.inplace = out->inplace;
+    cp.victims = out->victims;
+    cp.counts = out->counts;
+    cp.plan = out->plan;
+    cp.pairs = out->pairs;
+    classify_kernel<<<1, CL_THREADS, 0, stream>>>(cp);
     return check_launch("classify_evict");
+}
+
+namespace {
+}  // namespace
+}  // namespace moe355
+
+using namespace moe355;
+
+extern "C" moe355_status moe355_dedup(const int32_t* ids, int32_t n_ids, int32_t n_experts,
+                                      moe355_classify_out* out, hipStream_t stream) {
+    moe355_status st = check_out(out, false, n_ids);
+    if (st) return st;
+    MOE355_REQUIRE(n_ids >= 0 && n_ids <= MAX_LIST && (n_ids == 0 || ids), MOE355_EINVAL,
+                   "dedup: n_ids=%d outside [0, %d]", n_ids, MAX_LIST);
+    MOE355_REQUIRE(n_experts >= 1 && n_experts <= MAX_EXPERTS, MOE355_ENOTSUP,
+                   "dedup: n_experts=%d", n_experts);
+    const int need = n_ids < n_experts ? n_ids : n_experts;
+    MOE355_REQUIRE(out->capacity >= need, MOE355_ECAPACITY, "dedup: capacity %d < %d",
+                   out->capacity, need);
+    ClassifyParams cp{};
+    cp.dedup_only = 1;
+    cp.E = n_experts;
+    cp.ids = ids;
+    cp.n_ids = n_ids;
+    cp.q_den = 1;
+    cp.uniq = out->uniq;
+    cp.counts = out->counts;
+    cp.plan = out->plan;
+    cp.pairs = out->pairs;
+    classify_kernel<<<1, CL_THREADS, 0, stream>>>(cp);
+    return check_launch("dedup");
+}
+
+extern "C" moe355_status moe355_classify_evict(const moe355_cache* c, int32_t layer, int64_t tick,
+                                               const int32_t* ids, int32_t n_ids,
+                                               const moe355_evict_policy* p,
+                                               moe355_classify_out* out, hipStream_t stream) {
+    return classify_call(c, layer, nullptr, tick, ids, n_ids, p, out, nullptr, stream);
 }
 
 extern "C" moe355_status moe355_cache_fill(const moe355_cache* c, const uint8_t* pool,

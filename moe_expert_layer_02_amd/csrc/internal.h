@@ -26,6 +26,26 @@ struct ExpertLayout {
 };
 bool expert_layout(const moe355_layer_desc* d, ExpertLayout* L);
 moe355_status check_desc(const moe355_layer_desc* d);
+moe355_status check_cache(const moe355_cache* c);
+moe355_status check_out(const moe355_classify_out* o, bool full, int n_ids);
+
+// Routing of a call's tokens folded into the cache bookkeeping kernel.
+struct RouteArgs {
+    const float* logits;   // [T, E]
+    int T, k, kind, n_group, topk_group;
+    float scale;
+    int32_t* ids_out;      // [T, k]
+    float* w_out;          // [T, k]
+};
+moe355_status classify_call(const moe355_cache* c, int32_t layer, const int64_t* tick_dev,
+                            int64_t tick, const int32_t* ids, int32_t n_ids,
+                            const moe355_evict_policy* p, moe355_classify_out* out,
+                            const RouteArgs* route, hipStream_t stream);
+moe355_status decode_ffn(const moe355_layer_desc* d, const void* x_bf16, int32_t T,
+                         const int32_t* topk_ids, const float* topk_w, const moe355_cache* cache,
+                         const uint8_t* pool, int32_t layer, const moe355_classify_out* exp,
+                         bool fill_through, float* out, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
 
 // ---- device helpers ---------------------------------------------------------
 constexpr int WAVE = 64;

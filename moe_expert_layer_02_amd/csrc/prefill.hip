@@ -621,16 +621,23 @@ extern "C" moe355_status moe355_expert_ffn_prefill(const moe355_layer_desc* d, c
                    "expert_ffn_prefill: LDS need %zu / %zu bytes", lds_gu, lds_dn);
     auto gu = int4 ? gate_up_mfma<MOE355_W_INT4_G64> : gate_up_mfma<MOE355_W_MXFP4>;
     auto dn = int4 ? down_mfma<MOE355_W_INT4_G64> : down_mfma<MOE355_W_MXFP4>;
-    if (lds_gu > 64 * 1024 &&
-        hipFuncSetAttribute(reinterpret_cast<const void*>(gu),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(lds_gu)) != hipSuccess)
-        return fail(MOE355_EHIP, "expert_ffn_prefill: LDS %zu bytes refused", lds_gu);
-    if (lds_dn > 64 * 1024 &&
-        hipFuncSetAttribute(reinterpret_cast<const void*>(dn),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(lds_dn)) != hipSuccess)
-        return fail(MOE355_EHIP, "expert_ffn_prefill: LDS %zu bytes refused", lds_dn);
+    // raise the dynamic LDS limit once per kernel when a shape needs more than 64 KB
+    static size_t granted[2][2] = {{64 * 1024, 64 * 1024}, {64 * 1024, 64 * 1024}};
+    const int fi = int4 ? 0 : 1;
+    if (lds_gu > granted[fi][0]) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(gu),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                static_cast<int>(lds_gu)) != hipSuccess)
+            return fail(MOE355_EHIP, "expert_ffn_prefill: LDS %zu bytes refused", lds_gu);
+        granted[fi][0] = lds_gu;
+    }
+    if (lds_dn > granted[fi][1]) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(dn),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                static_cast<int>(lds_dn)) != hipSuccess)
+            return fail(MOE355_EHIP, "expert_ffn_prefill: LDS %zu bytes refused", lds_dn);
+        granted[fi][1] = lds_dn;
+    }
     gu<<<blocks, 256, lds_gu, stream>>>(p);
     st = check_launch("expert_ffn_prefill gate_up");
     if (st) return st;

@@ -70,13 +70,16 @@ class DeviceClassifyOut:
     NAMES = ("uniq", "hit_expert", "hit_slot", "miss", "fill_expert", "fill_slot", "inplace",
              "victims")
 
-    def __init__(self, capacity: int, device="cuda"):
+    def __init__(self, capacity: int, pair_capacity: int = 1024, device="cuda"):
         self.capacity = capacity
         self.buf = torch.full((len(self.NAMES), max(capacity, 1)), -1, dtype=torch.int32,
                               device=device)
         self.counts = torch.zeros(6, dtype=torch.int32, device=device)
+        self.plan = torch.zeros((max(capacity, 1), 4), dtype=torch.int32, device=device)
+        self.pairs = torch.zeros(max(pair_capacity, 1), dtype=torch.int32, device=device)
         self.struct = ClassifyOut(*[self.buf[i].data_ptr() for i in range(len(self.NAMES))],
-                                  self.counts.data_ptr(), capacity)
+                                  self.counts.data_ptr(), capacity, self.plan.data_ptr(),
+                                  self.pairs.data_ptr(), pair_capacity)
 
     def list(self, name: str):
         return self.buf[self.NAMES.index(name)]
@@ -89,6 +92,8 @@ class DeviceClassifyOut:
              "fill_expert": c[3], "fill_slot": c[3], "inplace": c[4], "victims": c[5]}
         out = {k: b[i, :n[k]].tolist() for i, k in enumerate(self.NAMES)}
         out["counts"] = c
+        out["plan"] = self.plan[:c[0]].cpu().tolist()
+        out["pairs"] = self.pairs.cpu().tolist()
         return out
 
 
@@ -158,6 +163,23 @@ def expert_ffn_decode(desc, x_bf16, topk_ids, topk_w, cache, pool, layer: int,
                                           ctypes.byref(experts.struct), _ptr(out), _ptr(ws),
                                           ws.numel() * ws.element_size(), _stream(stream)),
           "moe355_expert_ffn_decode")
+
+
+def decode_layer(desc, cache: DeviceCache, pool, layer: int, tick_base, tick_add: int, logits,
+                 x_bf16, policy: EvictPolicy, topk_ids, topk_w, lists: DeviceClassifyOut, out, ws,
+                 stream=None):
+    """route + classify_evict + expert FFN (fill-through) for one layer call."""
+    _need(logits, torch.float32, "logits")
+    _need(x_bf16, torch.bfloat16, "x")
+    if tick_base is not None:
+        _need(tick_base, torch.int64, "tick_base")
+    T = x_bf16.shape[0]
+    check(load().moe355_decode_layer(ctypes.byref(desc), ctypes.byref(cache.struct), _ptr(pool),
+                                     layer, _ptr(tick_base), tick_add, _ptr(logits), _ptr(x_bf16),
+                                     T, ctypes.byref(policy), _ptr(topk_ids), _ptr(topk_w),
+                                     ctypes.byref(lists.struct), _ptr(out), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)),
+          "moe355_decode_layer")
 
 
 def expert_ffn_prefill(desc, x_bf16, topk_ids, topk_w, layer_w, perm, offsets, out, ws,

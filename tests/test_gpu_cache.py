@@ -35,6 +35,9 @@ class TraceRunner:
         n_calls = steps * w.n_layers
         self.lists = torch.full((n_calls, len(KEYS), self.cap), -1, dtype=torch.int32, device="cuda")
         self.counts = torch.zeros((n_calls, 6), dtype=torch.int32, device="cuda")
+        self.plan = torch.zeros((n_calls, self.cap, 4), dtype=torch.int32, device="cuda")
+        self.pairs = torch.zeros((n_calls, w.t_decode * w.top_k), dtype=torch.int32,
+                                 device="cuda")
         self.desc = desc_of(w)
         self.ids = torch.empty((w.t_decode, w.top_k), dtype=torch.int32, device="cuda")
         self.wt = torch.empty((w.t_decode, w.top_k), dtype=torch.float32, device="cuda")
@@ -45,8 +48,11 @@ class TraceRunner:
         o.capacity = self.cap
         o.buf = self.lists[call]
         o.counts = self.counts[call]
+        o.plan = self.plan[call]
+        o.pairs = self.pairs[call]
         o.struct = m.ClassifyOut(*[o.buf[i].data_ptr() for i in range(len(KEYS))],
-                                 o.counts.data_ptr(), self.cap)
+                                 o.counts.data_ptr(), self.cap, o.plan.data_ptr(),
+                                 o.pairs.data_ptr(), self.pairs.shape[1])
         return o
 
     def call(self, call_idx, layer, tick, logits_np, policy):
@@ -76,6 +82,7 @@ def _run_trace(w, steps, with_pool, shrink_step=-1, shrink_slots=0):
     sim = ocache.CacheSim(w.n_slots, w.n_layers, w.n_experts)
     policy = m.EvictPolicy(runner.K, w.q_num, w.q_den)
     expected = []
+    routed = []
     for s in range(steps):
         if s == shrink_step:
             torch.cuda.synchronize()
@@ -100,14 +107,18 @@ def _run_trace(w, steps, with_pool, shrink_step=-1, shrink_slots=0):
             ids, _ = oroute.route(trace.logits[s, l], w.top_k, w.route, w.n_group, w.topk_group,
                                   w.route_scale)
             expected.append(sim.classify_evict(l, tick, ids, runner.K, w.q_num, w.q_den))
+            routed.append(ids.ravel())
     torch.cuda.synchronize()
     lists = runner.lists.cpu().numpy()
     counts = runner.counts.cpu().numpy()
+    plans = runner.plan.cpu().numpy()
+    pairs = runner.pairs.cpu().numpy()
     for call, exp in enumerate(expected):
         got, c = runner.host_call(call, lists, counts)
         assert c == exp["counts"], (call, c, exp["counts"])
         for k in KEYS:
             assert got[k] == exp[k], (call, k, got[k], exp[k])
+        _check_plan(exp, plans[call], pairs[call], routed[call])
     assert np.array_equal(runner.cache.table.cpu().numpy(), sim.table)
     assert np.array_equal(runner.cache.owner.cpu().numpy(), sim.owner)
     assert np.array_equal(runner.cache.ts.cpu().numpy(), sim.ts)
@@ -117,6 +128,20 @@ def _run_trace(w, steps, with_pool, shrink_step=-1, shrink_slots=0):
     if with_pool:
         _check_slot_bytes(runner, pool, w)
     return runner, pool
+
+
+def _check_plan(exp, plan, pairs, ids):
+    """plan[u] = (slot after the call or -1, filled now, first pair, pair count)."""
+    slot_of = dict(zip(exp["hit_expert"], exp["hit_slot"]))
+    fill_of = dict(zip(exp["fill_expert"], exp["fill_slot"]))
+    begin = 0
+    for u, e in enumerate(exp["uniq"]):
+        want_slot = slot_of.get(e, fill_of.get(e, -1))
+        want = [want_slot, 1 if e in fill_of else 0, begin, int((ids == e).sum())]
+        assert plan[u].tolist() == want, (u, e, plan[u].tolist(), want)
+        grp = sorted(pairs[begin:begin + want[3]].tolist())
+        assert grp == [i for i in range(len(ids)) if ids[i] == e]
+        begin += want[3]
 
 
 def _check_slot_bytes(runner, pool, w):

@@ -38,7 +38,7 @@ def _decode_whole_layer(w, x_bits, ids_np, wt_np, seed=None):
     exp = m.DeviceClassifyOut(max(1, min(T * w.top_k, w.n_experts)))
     m.dedup(ids, w.n_experts, exp)
     out = torch.full((T, w.hidden), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(m.workspace_bytes(desc, T, m.MODE_DECODE), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(m.workspace_bytes(desc, T, m.MODE_DECODE), dtype=torch.uint8, device="cuda")
     m.expert_ffn_decode(desc, _x_dev(x_bits), ids, wt, None, layer, 0, exp, out, ws)
     torch.cuda.synchronize()
     return out.cpu().numpy()
@@ -129,7 +129,7 @@ def test_decode_empty_batch_is_noop():
     exp = m.DeviceClassifyOut(8)
     out = torch.empty((0, w.hidden), dtype=torch.float32, device="cuda")
     x = torch.empty((0, w.hidden), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
     pool = torch.empty(16, dtype=torch.uint8, device="cuda")
     m.expert_ffn_decode(desc, x, e.view(0, 8), torch.empty((0, 8), device="cuda"), None, pool, 0,
                         exp, out, ws)
@@ -156,7 +156,7 @@ def test_decode_full_size_sampled_calls(cid, steps, sample):
     ids = torch.empty((w.t_decode, w.top_k), dtype=torch.int32, device="cuda")
     wt = torch.empty((w.t_decode, w.top_k), dtype=torch.float32, device="cuda")
     out = torch.empty((w.t_decode, w.hidden), dtype=torch.float32, device="cuda")
-    ws = torch.empty(m.workspace_bytes(desc, w.t_decode, m.MODE_DECODE), dtype=torch.uint8,
+    ws = torch.zeros(m.workspace_bytes(desc, w.t_decode, m.MODE_DECODE), dtype=torch.uint8,
                      device="cuda")
     src = BlobSource(w)
     rng = np.random.default_rng(cid)

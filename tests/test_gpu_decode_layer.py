@@ -1,0 +1,151 @@
+"""The fused decode-layer call (route + classify_evict in one kernel, then the
+expert FFN with fill-through) on the GPU: every call of decode traces
+bit-exact against the oracle's simulator on the integer outputs, sampled layer
+outputs against the oracle, every cache slot holding its owner's pool bytes
+afterwards (the fill happened inside the FFN), and a whole decode step captured
+as a graph and replayed, each replay checked against eager execution."""
+import numpy as np
+import pytest
+
+from oracle import cache as ocache
+from oracle import ffn as offn
+from oracle import route as oroute
+from workloads import configs as C
+from workloads import experts as wx
+from workloads import traces as tr
+
+from gpu_common import BlobSource, check_close, desc_of, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _x_dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+class LayerRunner:
+    def __init__(self, w, n_slots, pool):
+        import torch
+        import moe_expert_layer_02_amd as m
+        self.m, self.torch, self.w = m, torch, w
+        self.desc = desc_of(w)
+        self.S = wx.expert_bytes(w.wfmt, w.hidden, w.inter)
+        self.cache = m.DeviceCache(n_slots, w.n_layers, w.n_experts, self.S)
+        self.pool = pool
+        self.K = min(w.t_decode * w.top_k, w.n_experts, n_slots)
+        self.policy = m.EvictPolicy(self.K, w.q_num, w.q_den)
+        self.cap = max(self.K, min(w.t_decode * w.top_k, w.n_experts))
+        L, T = w.n_layers, w.t_decode
+        self.lists = [m.DeviceClassifyOut(self.cap) for _ in range(L)]
+        self.ids = torch.empty((L, T, w.top_k), dtype=torch.int32, device="cuda")
+        self.wt = torch.empty((L, T, w.top_k), dtype=torch.float32, device="cuda")
+        self.out = torch.empty((L, T, w.hidden), dtype=torch.float32, device="cuda")
+        self.ws = torch.zeros(m.workspace_bytes(self.desc, T, m.MODE_DECODE), dtype=torch.uint8,
+                              device="cuda")
+        self.tick = torch.zeros(1, dtype=torch.int64, device="cuda")
+        self.logits = torch.empty((L, T, w.n_experts), dtype=torch.float32, device="cuda")
+        self.x = torch.empty((L, T, w.hidden), dtype=torch.bfloat16, device="cuda")
+
+    def stage(self, step, logits_np, xs):
+        self.logits.copy_(self.torch.from_numpy(logits_np))
+        self.x.copy_(xs)
+        self.tick.fill_(step * self.w.n_layers)
+
+    def step(self):
+        for l in range(self.w.n_layers):
+            self.m.decode_layer(self.desc, self.cache, self.pool, l, self.tick, l + 1,
+                                self.logits[l], self.x[l], self.policy, self.ids[l], self.wt[l],
+                                self.lists[l], self.out[l], self.ws)
+
+
+def _xs(w, s):
+    import torch
+    return torch.stack([_x_dev(tr.decode_x(w, s, l)) for l in range(w.n_layers)])
+
+
+@pytest.mark.parametrize("cid,steps,sample", [(2, 64, [(0, 3), (63, 39)]), (4, 24, [(5, 7)]),
+                                              (5, 24, [(23, 0)])])
+def test_decode_layer_trace(cid, steps, sample):
+    import torch
+    from workloads import gpu as wg
+    w = C.ALL[cid]
+    say(f"decode_layer trace {w.name}: {steps} steps")
+    trace = tr.DecodeTrace(w, steps)
+    pool = wg.make_pool(w)
+    run = LayerRunner(w, w.n_slots, pool)
+    sim = ocache.CacheSim(w.n_slots, w.n_layers, w.n_experts)
+    src = BlobSource(w)
+    for s in range(steps):
+        xs = _xs(w, s)
+        run.stage(s, trace.logits[s], xs)
+        run.step()
+        torch.cuda.synchronize()
+        for l in range(w.n_layers):
+            rid, rw = oroute.route(trace.logits[s, l], w.top_k, w.route, w.n_group, w.topk_group,
+                                   w.route_scale)
+            exp = sim.classify_evict(l, s * w.n_layers + l + 1, rid, run.K, w.q_num, w.q_den)
+            got = run.lists[l].host()
+            assert got["counts"] == exp["counts"], (s, l, got["counts"], exp["counts"])
+            for key in ("uniq", "hit_expert", "hit_slot", "miss", "fill_expert", "fill_slot",
+                        "inplace", "victims"):
+                assert got[key] == exp[key], (s, l, key)
+            assert np.array_equal(run.ids[l].cpu().numpy(), rid)
+            if (s, l) in sample:
+                toks = list(range(min(2, w.t_decode)))
+                want = offn.moe_layer(tr.x_as_f32(tr.decode_x(w, s, l)), rid, rw,
+                                      lambda e: src(l, e), w.wfmt, w.hidden, w.inter, tokens=toks)
+                check_close(run.out[l].cpu().numpy()[toks], want, f"{w.name} call ({s},{l})")
+    assert np.array_equal(run.cache.table.cpu().numpy(), sim.table)
+    assert np.array_equal(run.cache.ts.cpu().numpy(), sim.ts)
+    S = run.S
+    owner = run.cache.owner.cpu().numpy()
+    data, pv = run.cache.data.view(-1, S), pool.view(-1, S)
+    occ = np.nonzero(owner >= 0)[0]
+    for i in range(0, len(occ), 64):
+        sl = torch.from_numpy(occ[i:i + 64]).cuda()
+        ow = torch.from_numpy(owner[occ[i:i + 64]].astype(np.int64)).cuda()
+        assert torch.equal(data.index_select(0, sl), pv.index_select(0, ow)), "slot bytes differ"
+    say(f"{w.name}: {steps * w.n_layers} calls bit-exact, {len(occ)} slots hold their pool bytes")
+
+
+def test_decode_step_graph_replay_matches_eager():
+    import torch
+    from workloads import gpu as wg
+    w = C.QWEN_DECODE
+    steps = 6
+    trace = tr.DecodeTrace(w, steps)
+    pool = wg.make_pool(w)
+    # one eager step on a throwaway cache, so no kernel is launched for the
+    # first time (occupancy query) while the graph is being captured
+    warm = LayerRunner(w, w.n_slots, pool)
+    warm.stage(0, trace.logits[0], _xs(w, 0))
+    warm.step()
+    torch.cuda.synchronize()
+    del warm
+    eager = LayerRunner(w, w.n_slots, pool)
+    graphed = LayerRunner(w, w.n_slots, pool)
+    graphed.stage(0, trace.logits[0], _xs(w, 0))
+    torch.cuda.synchronize()
+    snap = [t.clone() for t in (graphed.cache.table, graphed.cache.owner, graphed.cache.ts)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graphed.step()
+    torch.cuda.synchronize()
+    # capturing records the launches without running them
+    for a, b in zip(snap, (graphed.cache.table, graphed.cache.owner, graphed.cache.ts)):
+        assert torch.equal(a, b)
+    for s in range(steps):
+        xs = _xs(w, s)
+        eager.stage(s, trace.logits[s], xs)
+        eager.step()
+        torch.cuda.synchronize()
+        graphed.stage(s, trace.logits[s], xs)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(eager.ids, graphed.ids), s
+        # the combine adds a token's k contributions with atomics in no fixed order
+        torch.testing.assert_close(graphed.out, eager.out, rtol=1e-6, atol=1e-5)
+        assert torch.equal(eager.cache.table, graphed.cache.table), s
+        assert torch.equal(eager.cache.ts, graphed.cache.ts), s
+        say(f"graph replay {s} matches eager")
