@@ -1,6 +1,6 @@
-// Decode expert FFN: one kernel per layer call that streams each distinct
-// expert's packed weights from HBM once, dequantises them in registers and
-// writes the routing-weighted layer output.
+// Decode expert FFN: streams each distinct expert's packed weights from HBM
+// once, dequantises them in registers, and runs the products on MFMA so that
+// one pass over an expert serves up to 16 of its routed tokens at the same cost.
 //
 // [Edge0, section 3.1 "Math contract"]: y = down(silu(gate(x)) * up(x)) per
 // routed expert over its quantised weights.  [FT-zh, Core method / Method
@@ -8,57 +8,66 @@
 // read from the pool, the partial sums merge exactly, and the misses chosen for
 // filling are batch-copied into their victim slots.
 //
-// Two launches:
-//   gate/up: a work item is (distinct expert, tile of I rows).  Each wavefront
-//     owns a fixed 16-byte column chunk of every row (32 weights per lane),
-//     keeps its tokens' activations for that chunk in registers and issues all
-//     of its row loads first; a block walks a contiguous range of items, so
-//     consecutive items share an expert and its converted activations.  int4
-//     uses v_dot2_f32_f16 on exact fp16 nibbles (1024 + q with 1024 removed in
-//     packed fp16) against fp16 activations and applies s * sum(q x) +
-//     b * sum(x) per 64-group; MXFP4 converts codes with the gfx950 scaled
-//     fp4 -> fp16 conversion and scales each 32-block by 2^(e-127).
-//     h = silu(g) * u goes to the workspace in fp32.  This launch also zeroes the
-//     layer output.
-//   down + combine: a work item is (distinct expert, tile of H rows).  The
-//     expert's h slices are loaded once per item and reused across its rows;
-//     each row's dot product meets the routing weight and is added into the
-//     layer output with an fp32 atomic (k additions per output element).
+// Products.  v_mfma_f32_16x16x32 with the weights as the A operand (16 rows x
+// 32 inputs) and the routed tokens as B (32 inputs x 16 tokens).  A wavefront
+// load of 16 rows x 64 bytes (one "slab" of 128 inputs) gives every lane one
+// 16-byte chunk, which feeds four MFMA steps.
+//   int4 g64 (f16 MFMA): the A value is s * (q - 8), exact in f16 for any bf16
+//     scale (|q - 8| <= 8 keeps the product within 11 significant bits); the
+//     bias term sum_g (b_g + 8 s_g) * sum_{k in g} x_k goes through one more
+//     MFMA per slab on hi/lo f16 splits of both factors.  x is converted to
+//     f16 (exact for bf16 values in f16's range).
+//   MXFP4 (bf16 MFMA): the gfx950 scaled fp4 -> bf16 conversion applies the
+//     e8m0 block scale and is exact; x is bf16 already.
+// h = silu(g) * u crosses into the down projection as a hi/lo pair of 16-bit
+// values (f16 for int4, bf16 for MXFP4), and the down pass runs both halves.
 //
-// Before anything else every block stages the call's plan (for each distinct
-// expert: where its bytes live, whether this call fills a cache slot with it,
-// and its routed pairs) in LDS, so every weight load is independent of the
-// others.  With fill-through on, an expert that this call fills into a cache
-// slot is read from the pool and its bytes are written to the slot by the lanes
-// that read them, which replaces the separate pool -> slot copy.
-#include <stdlib.h>
-
+// Two launches:
+//   gate/up: a block item is (distinct expert, tile of I rows); the block's
+//     four wavefronts split H into KW parts (and the rows into 4/KW groups),
+//     reduce their partial sums through LDS and write h.  It also zeroes the
+//     layer output.
+//   down + combine: a wavefront item is (distinct expert, tile of H rows) over
+//     all of I; each row's result meets the routing weight and is added into
+//     the fp32 layer output with an atomic (k additions per element).
+// Each block stages the call's plan (for each distinct expert: where its bytes
+// live, whether this call fills a cache slot with it, its routed pairs) in LDS
+// first, so every weight load is independent of the others, and each
+// wavefront keeps the next slab's loads in flight while it computes one.  With
+// fill-through on, an expert that this call fills into a cache slot is read
+// from the pool and the lanes that read its bytes also write them to the slot.
 #include "internal.h"
 
 namespace moe355 {
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int SLAB = 128;   // inputs per wavefront load (16 rows x 64 bytes)
+constexpr int TOK = 16;     // tokens per MFMA pass
 
 struct DecodeParams {
-    const uint16_t* x;
-    const int32_t* ids;
-    const float* w;
+    const uint16_t* x;       // [T][H] bf16
+    const float* w;          // [T*k] routing weights
     const int32_t* uniq;
     const int32_t* counts;
-    const int32_t* table;
     const uint8_t* slots;
     const uint8_t* pool;
     const int32_t* plan;     // [n_plan][4]: slot or -1, filled now, first pair, pair count
     const int32_t* pairs;    // routed pairs grouped by expert
     int n_plan;              // plan rows loaded (>= number of distinct experts)
+    int has_cache;
     int fill_through;
     int64_t S;
     int E, layer, T, k, H, I;
     int64_t q_off[3], s_off[3], b_off[3];
-    float* h;
-    float* out;
+    uint16_t* h_hi;          // [T*k][I] high half of h (f16 for int4, bf16 for MXFP4)
+    uint16_t* h_lo;          // [T*k][I] remainder h - h_hi
+    float* out;              // [T][H]
 };
 
 struct ExpertRef {
@@ -78,22 +87,19 @@ struct PlanLds {
 // Where distinct expert u's bytes are read from (and written to, with fill-through).
 __device__ __forceinline__ ExpertRef expert_ref(const DecodeParams& p, const PlanLds& pl, int u) {
     const int4 row = pl.plan[u];
-    const uint8_t* from_pool = p.pool + (static_cast<int64_t>(p.layer) * p.E + pl.uniq[u]) * p.S;
     ExpertRef r;
     r.dst = nullptr;
-    r.src = from_pool;
-    if (p.table && row.x >= 0) {
+    r.src = p.pool + (static_cast<int64_t>(p.layer) * p.E + pl.uniq[u]) * p.S;
+    if (p.has_cache && row.x >= 0) {
         uint8_t* slot = const_cast<uint8_t*>(p.slots) + static_cast<int64_t>(row.x) * p.S;
-        if (p.fill_through && row.y) {
+        if (p.fill_through && row.y)
             r.dst = slot;        // filled by this call: read the pool, write the slot
-        } else {
+        else
             r.src = slot;
-        }
     }
     return r;
 }
 
-// Every block stages the plan first: one round trip, then loads are independent.
 __device__ __forceinline__ void stage_plan(const DecodeParams& p, PlanLds& pl) {
     if (threadIdx.x < p.n_plan) {
         pl.plan[threadIdx.x] = reinterpret_cast<const int4*>(p.plan)[threadIdx.x];
@@ -104,175 +110,201 @@ __device__ __forceinline__ void stage_plan(const DecodeParams& p, PlanLds& pl) {
     __syncthreads();
 }
 
+__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint32_t ldg4(const void* p) { return *reinterpret_cast<const uint32_t*>(p); }
+__device__ __forceinline__ uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ uint32_t as_u32(bf16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+
+template <int FMT>
+__device__ __forceinline__ f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+    if (FMT == MOE355_W_INT4_G64)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                      __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
     return e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);
 }
 
-__device__ __forceinline__ half2_t as_half2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+// f16 pair from two fp32 values that are exact in f16.
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
 
-__device__ __forceinline__ uint4 ldg16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
-
-// The 32 bf16 activations under one 16-byte weight chunk as fp16 pairs, paired
-// the way the chunk's codes unpack; returns their fp32 sum.
-template <int FMT>
-__device__ __forceinline__ float load_x_pairs(const uint16_t* xs, half2_t xh[16]) {
-    const uint4* v = reinterpret_cast<const uint4*>(xs);
-    float xf[32];
+// int4: f16(s * (q - 8)) for the 8 codes of one dword, in the order
+// (0,4,1,5,2,6,3,7) of their place in the dword.  |q - 8| <= 8 keeps every
+// product of a bf16 scale within f16's 11 significant bits, so each value is
+// exact; the offset moves into the bias (b + 8 s).
+__device__ __forceinline__ uint4 a_int4(uint32_t d, half2_t s2) {
+    const half2_t off = {static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
+    uint32_t v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint4 q = v[i];
-        const uint32_t d[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            xf[8 * i + 2 * j] = __uint_as_float(d[j] << 16);
-            xf[8 * i + 2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
-        }
+        const half2_t q = as_h2(((d >> (4 * i)) & 0x000F000Fu) | 0x64006400u);  // 1024 + q
+        v[i] = as_u32((q + off) * s2);
     }
-    float sum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) sum += xf[i];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        // int4: dword d unpacks to pairs (8d+s, 8d+4+s); MXFP4: natural pairs
-        const int a = FMT == MOE355_W_INT4_G64 ? 8 * (i / 4) + (i % 4) : 2 * i;
-        const int b = FMT == MOE355_W_INT4_G64 ? a + 4 : a + 1;
-        half2_t t;
-        t.x = static_cast<_Float16>(xf[a]);
-        t.y = static_cast<_Float16>(xf[b]);
-        xh[i] = t;
-    }
-    return sum;
+    return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// Exact fp16 nibbles of one int4 chunk, pairs (8d+s, 8d+4+s).
-__device__ __forceinline__ void unpack_int4_f16(uint4 w, half2_t q[16]) {
-    const uint32_t d4[4] = {w.x, w.y, w.z, w.w};
-    const half2_t k1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            q[4 * d + s] = as_half2(((d4[d] >> (4 * s)) & 0x000F000Fu) | 0x64006400u) - k1024;
+// MXFP4: the 8 codes of one dword, scaled by 2^(e-127), exact in bf16, natural order.
+__device__ __forceinline__ uint4 a_fp4(uint32_t d, float scale) {
+    return make_uint4(as_u32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 0)),
+                      as_u32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 1)),
+                      as_u32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 2)),
+                      as_u32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3)));
 }
 
-// fp16 e2m1 values of one MXFP4 chunk, natural pairs (2i, 2i+1).
-__device__ __forceinline__ void unpack_fp4_f16(uint4 w, half2_t q[16]) {
-    const uint32_t d4[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        q[4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d4[d], 1.0f, 0);
-        q[4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d4[d], 1.0f, 1);
-        q[4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d4[d], 1.0f, 2);
-        q[4 * d + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d4[d], 1.0f, 3);
-    }
+// 8 bf16 activations (natural order) as f16 in the int4 A order, plus their sum.
+__device__ __forceinline__ uint4 b_x_f16(uint4 v, float* sum) {
+    const half2_t one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    const uint32_t p0 = pk_f16(__uint_as_float(v.x << 16), __uint_as_float(v.z << 16));
+    const uint32_t p1 = pk_f16(__uint_as_float(v.x & 0xFFFF0000u), __uint_as_float(v.z & 0xFFFF0000u));
+    const uint32_t p2 = pk_f16(__uint_as_float(v.y << 16), __uint_as_float(v.w << 16));
+    const uint32_t p3 = pk_f16(__uint_as_float(v.y & 0xFFFF0000u), __uint_as_float(v.w & 0xFFFF0000u));
+    float s = *sum;
+    s = __builtin_amdgcn_fdot2(as_h2(p0), one, s, false);
+    s = __builtin_amdgcn_fdot2(as_h2(p1), one, s, false);
+    s = __builtin_amdgcn_fdot2(as_h2(p2), one, s, false);
+    s = __builtin_amdgcn_fdot2(as_h2(p3), one, s, false);
+    *sum = s;
+    return make_uint4(p0, p1, p2, p3);
 }
 
-__device__ __forceinline__ float dot16(const half2_t q[16], const half2_t x[16]) {
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) a = __builtin_amdgcn_fdot2(q[i], x[i], a, false);
-    return a;
+__device__ __forceinline__ float sum_f16x8(uint4 v, float s) {
+    const half2_t one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    s = __builtin_amdgcn_fdot2(as_h2(v.x), one, s, false);
+    s = __builtin_amdgcn_fdot2(as_h2(v.y), one, s, false);
+    s = __builtin_amdgcn_fdot2(as_h2(v.z), one, s, false);
+    s = __builtin_amdgcn_fdot2(as_h2(v.w), one, s, false);
+    return s;
+}
+
+// The slab's two group sums of a lane's 32 values (chunks 0,1 -> first group,
+// chunks 2,3 -> second), as the bias MFMA's B operand: lanes of chunk 0 hold
+// [hi0, hi1, lo0, lo1, hi0, hi1, 0, 0]; every other lane holds zeros.
+__device__ __forceinline__ uint4 bias_b_operand(float part, int gq) {
+    float v = part + __shfl_xor(part, 16, WAVE);
+    const float o = __shfl_xor(v, 32, WAVE);
+    const float g0 = gq < 2 ? v : o, g1 = gq < 2 ? o : v;
+    const _Float16 h0 = static_cast<_Float16>(g0), h1 = static_cast<_Float16>(g1);
+    const _Float16 l0 = static_cast<_Float16>(g0 - static_cast<float>(h0));
+    const _Float16 l1 = static_cast<_Float16>(g1 - static_cast<float>(h1));
+    if (gq != 0) return make_uint4(0u, 0u, 0u, 0u);
+    const half2_t hi = {h0, h1}, lo = {l0, l1};
+    return make_uint4(as_u32(hi), as_u32(lo), as_u32(hi), 0u);
+}
+
+// The bias MFMA's A operand for one row and the slab's two groups: b' = b + 8 s
+// (exact in fp32) as an f16 hi/lo pair, laid out [h0, h1, h0, h1, l0, l1, 0, 0]
+// against the B operand above (the lo x lo term is below f16's resolution).
+__device__ __forceinline__ uint4 bias_a_operand(uint32_t bd, uint32_t sd, int gq) {
+    if (gq != 0) return make_uint4(0u, 0u, 0u, 0u);
+    const float b0 = __uint_as_float(bd << 16) + 8.0f * __uint_as_float(sd << 16);
+    const float b1 = __uint_as_float(bd & 0xFFFF0000u) + 8.0f * __uint_as_float(sd & 0xFFFF0000u);
+    const _Float16 h0 = static_cast<_Float16>(b0), h1 = static_cast<_Float16>(b1);
+    const _Float16 l0 = static_cast<_Float16>(b0 - static_cast<float>(h0));
+    const _Float16 l1 = static_cast<_Float16>(b1 - static_cast<float>(h1));
+    const half2_t hi = {h0, h1}, lo = {l0, l1};
+    return make_uint4(as_u32(hi), as_u32(hi), as_u32(lo), 0u);
+}
+
+// int4 scale of this lane's chunk as an f16 pair (s, s).
+__device__ __forceinline__ half2_t int4_scale(uint32_t sd, int gq) {
+    const float s = __uint_as_float(gq < 2 ? (sd << 16) : (sd & 0xFFFF0000u));
+    const _Float16 sh = static_cast<_Float16>(s);
+    return half2_t{sh, sh};
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-// One row chunk of a matrix: packed codes plus its scale (and bias for int4).
-struct Chunk {
-    uint4 q;
-    uint32_t s, b;
+// Loads of one slab for one matrix and RT row tiles: codes, scale dword, bias dword.
+template <int RT>
+struct WSlab {
+    uint4 q[RT];
+    uint32_t sc[RT];
+    uint32_t bi[RT];
 };
 
-// Load (and with fill-through, copy) the chunk `ch` (16 bytes) of row r of matrix m.
+// Byte offsets of row r's slab at input kb: codes, scale/exponent dword, bias dword.
+struct SlabOff {
+    int64_t q, s;
+};
 template <int FMT>
-__device__ __forceinline__ Chunk load_chunk(const DecodeParams& p, const ExpertRef& ref, int m,
-                                            int64_t row_bytes, int L, int r, int ch) {
-    Chunk c;
-    const int64_t qo = p.q_off[m] + r * row_bytes + ch * 16;
-    c.q = ldg16(ref.src + qo);
-    if (FMT == MOE355_W_INT4_G64) {
-        const int64_t g = static_cast<int64_t>(r) * (L / 64) + ch / 2;
-        c.s = reinterpret_cast<const uint16_t*>(ref.src + p.s_off[m])[g];
-        c.b = reinterpret_cast<const uint16_t*>(ref.src + p.b_off[m])[g];
-        if (ref.dst) {
-            *reinterpret_cast<uint4*>(ref.dst + qo) = c.q;
-            if ((ch & 1) == 0) {
-                reinterpret_cast<uint16_t*>(ref.dst + p.s_off[m])[g] = static_cast<uint16_t>(c.s);
-                reinterpret_cast<uint16_t*>(ref.dst + p.b_off[m])[g] = static_cast<uint16_t>(c.b);
-            }
-        }
-    } else {
-        const int64_t eo = p.s_off[m] + static_cast<int64_t>(r) * (L / 32) + ch;
-        c.s = ref.src[eo];
-        c.b = 0;
-        if (ref.dst) {
-            *reinterpret_cast<uint4*>(ref.dst + qo) = c.q;
-            ref.dst[eo] = static_cast<uint8_t>(c.s);
-        }
-    }
-    return c;
+__device__ __forceinline__ SlabOff slab_off(int r, int kdim, int kb, int gq) {
+    SlabOff o;
+    o.q = static_cast<int64_t>(r) * (kdim / 2) + kb / 2 + 16 * gq;
+    o.s = FMT == MOE355_W_INT4_G64 ? static_cast<int64_t>(r) * (kdim / 32) + kb / 32
+                                   : static_cast<int64_t>(r) * (kdim / 32) + kb / 32;
+    return o;
 }
 
-// Convert one pair group's activations (one or two tokens) for this lane's chunks.
-template <int FMT, int NC>
-__device__ __forceinline__ void load_group_x(const DecodeParams& p, int t0, int t1, int ch0,
-                                             half2_t xh[2][NC][16], float xs[2][NC]) {
+template <int FMT, int RT>
+__device__ __forceinline__ void load_wslab(const DecodeParams& p, const uint8_t* src, int m,
+                                           int row0, int kdim, int kb, int ln, int gq,
+                                           WSlab<RT>& w) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int64_t col = static_cast<int64_t>(ch0 + c * WAVE) * 32;
-        xs[0][c] = load_x_pairs<FMT>(p.x + static_cast<int64_t>(t0) * p.H + col, xh[0][c]);
-        if (t1 >= 0) xs[1][c] = load_x_pairs<FMT>(p.x + static_cast<int64_t>(t1) * p.H + col, xh[1][c]);
+    for (int t = 0; t < RT; ++t) {
+        const SlabOff o = slab_off<FMT>(row0 + 16 * t + ln, kdim, kb, gq);
+        w.q[t] = ldg16(src + p.q_off[m] + o.q);
+        w.sc[t] = ldg4(src + p.s_off[m] + o.s);
+        w.bi[t] = 0u;
+        if (FMT == MOE355_W_INT4_G64 && gq == 0) w.bi[t] = ldg4(src + p.b_off[m] + o.s);
     }
 }
 
-// gate . x and up . x for one row (LA loads of it) and one or two tokens.
-template <int FMT, int NC, int LA>
-__device__ __forceinline__ void gate_up_rows(const DecodeParams& p, const Chunk wc[2][LA][NC],
-                                             const half2_t xh[2][NC][16], const float xs[2][NC],
-                                             bool two, int seg, int ch0, int r0, int rpw,
-                                             int pr0, int pr1) {
+// Fill-through: write a slab's bytes (codes by every lane, scale words once per row).
+template <int FMT, int RT>
+__device__ __forceinline__ void store_wslab(const DecodeParams& p, uint8_t* dst, int m, int row0,
+                                            int kdim, int kb, int ln, int gq, const WSlab<RT>& w) {
 #pragma unroll
-    for (int l = 0; l < LA; ++l) {
-        float acc[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                half2_t q[16];
-                float s, b;
-                if (FMT == MOE355_W_INT4_G64) {
-                    unpack_int4_f16(wc[m][l][c].q, q);
-                    s = bf16_to_f32(static_cast<uint16_t>(wc[m][l][c].s));
-                    b = bf16_to_f32(static_cast<uint16_t>(wc[m][l][c].b));
-                } else {
-                    unpack_fp4_f16(wc[m][l][c].q, q);
-                    s = e8m0_to_f32(wc[m][l][c].s);
-                    b = 0.0f;
-                }
-                const float d0 = dot16(q, xh[0][c]);
-                acc[m][0] += FMT == MOE355_W_INT4_G64 ? fmaf(s, d0, b * xs[0][c]) : s * d0;
-                if (two) {
-                    const float d1 = dot16(q, xh[1][c]);
-                    acc[m][1] += FMT == MOE355_W_INT4_G64 ? fmaf(s, d1, b * xs[1][c]) : s * d1;
-                }
-            }
-            acc[m][0] = segment_sum_f32(acc[m][0], seg);
-            if (two) acc[m][1] = segment_sum_f32(acc[m][1], seg);
-        }
-        if (ch0 == 0) {
-            const int r = r0 + l * rpw;
-            p.h[static_cast<int64_t>(pr0) * p.I + r] = silu(acc[0][0]) * acc[1][0];
-            if (two) p.h[static_cast<int64_t>(pr1) * p.I + r] = silu(acc[0][1]) * acc[1][1];
+    for (int t = 0; t < RT; ++t) {
+        const SlabOff o = slab_off<FMT>(row0 + 16 * t + ln, kdim, kb, gq);
+        *reinterpret_cast<uint4*>(dst + p.q_off[m] + o.q) = w.q[t];
+        if (gq == 0) {
+            *reinterpret_cast<uint32_t*>(dst + p.s_off[m] + o.s) = w.sc[t];
+            if (FMT == MOE355_W_INT4_G64)
+                *reinterpret_cast<uint32_t*>(dst + p.b_off[m] + o.s) = w.bi[t];
         }
     }
 }
 
-// NC: 16-byte chunks per lane per row (H / 2048, or 1 for rows narrower than a
-// wavefront); LA: row loads per wavefront per work item.
-template <int FMT, int NC, int LA>
-__global__ void __launch_bounds__(256) gate_up_kernel(DecodeParams p, int seg) {
+// acc[t] += W_slab(row tile t) . B over the slab's four MFMA steps (B given per step).
+template <int FMT, int RT>
+__device__ __forceinline__ void mma_slab(const WSlab<RT>& w, const uint4 b[4], int gq,
+                                         f32x4 acc[RT]) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const uint32_t d4[4] = {w.q[t].x, w.q[t].y, w.q[t].z, w.q[t].w};
+        if (FMT == MOE355_W_INT4_G64) {
+            const half2_t s2 = int4_scale(w.sc[t], gq);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[t] = mma<FMT>(a_int4(d4[j], s2), b[j], acc[t]);
+        } else {
+            const float scale = e8m0_to_f32((w.sc[t] >> (8 * gq)) & 0xFFu);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[t] = mma<FMT>(a_fp4(d4[j], scale), b[j], acc[t]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// gate/up.  KW wavefronts share a row tile and split H; RT tiles of 16 rows each.
+template <int FMT, int KW, int RT>
+struct GuStage {
+    WSlab<RT> g, u;
+    uint4 x[4];
+};
+
+template <int FMT, int KW, int RT>
+__global__ void __launch_bounds__(256) gate_up_kernel(DecodeParams p) {
+    constexpr int RW = 4 / KW;
     __shared__ PlanLds pl;
-    const int lane = threadIdx.x & (WAVE - 1);
-    const int wv = threadIdx.x / WAVE;
+    __shared__ f32x4 red[2][4][RT][2][WAVE];
+    const int lane = threadIdx.x & (WAVE - 1), ln = lane & 15, gq = lane >> 4;
+    const int wv = threadIdx.x / WAVE, kw = wv % KW, rw = wv / KW;
     stage_plan(p, pl);
     {   // zero the layer output for the down launch's atomics
         const int64_t n = static_cast<int64_t>(p.T) * p.H;
@@ -280,209 +312,277 @@ __global__ void __launch_bounds__(256) gate_up_kernel(DecodeParams p, int seg) {
              i += static_cast<int64_t>(gridDim.x) * blockDim.x)
             p.out[i] = 0.0f;
     }
-    const int rpw = WAVE / seg;
-    const int wave_rows = LA * rpw;
-    const int item_rows = 4 * wave_rows;
-    const int tiles = p.I / item_rows;
+    const int H = p.H;
+    const int kpart = H / KW, NS = kpart / SLAB, kbase = kw * kpart;
+    const int tile_rows = RW * RT * 16;
+    const int tiles = p.I / tile_rows;
     const int n_items = pl.n_uniq * tiles;
     const int per = (n_items + gridDim.x - 1) / gridDim.x;
-    const int sub = lane / seg, ch0 = lane % seg;
-    const int64_t row_bytes = p.H / 2;
-    half2_t xh[2][NC][16];
-    float xs[2][NC];
-    int cached_u = -1;   // expert whose first pair group sits in xh / xs
-    const int i_end = min(n_items, (static_cast<int>(blockIdx.x) + 1) * per);
-    for (int item = blockIdx.x * per; item < i_end; ++item) {
-        const int u = item / tiles;
-        const int tile = item - u * tiles;
-        const int r0 = tile * item_rows + wv * wave_rows + sub;
+    const int i_beg = blockIdx.x * per;
+    const int i_end = min(n_items, i_beg + per);
+    if (i_beg >= i_end) return;
+
+    // unit = (item, token group); stage = (unit, slab)
+    auto tokens_of = [&](int item) { return pl.plan[item / tiles].w; };
+    auto load = [&](GuStage<FMT, KW, RT>& st, int item, int tg, int s) {
+        const int u = item / tiles, tile = item - u * tiles;
         const ExpertRef ref = expert_ref(p, pl, u);
-        Chunk wc[2][LA][NC];
+        const int row0 = tile * tile_rows + rw * RT * 16;
+        const int kb = kbase + s * SLAB;
+        load_wslab<FMT, RT>(p, ref.src, 0, row0, H, kb, ln, gq, st.g);
+        load_wslab<FMT, RT>(p, ref.src, 1, row0, H, kb, ln, gq, st.u);
+        const int n = tg * TOK + ln;
+        const int4 pr = pl.plan[u];
+        if (n < pr.w) {
+            const int t = pl.pairs[pr.z + n] / p.k;
+            const uint16_t* xs = p.x + static_cast<int64_t>(t) * H + kb + 32 * gq;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st.x[i] = ldg16(xs + 8 * i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st.x[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    f32x4 acc[2][RT];
+    auto zero_acc = [&]() {
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int l = 0; l < LA; ++l)
+            for (int t = 0; t < RT; ++t) acc[m][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    };
+    auto compute = [&](const GuStage<FMT, KW, RT>& st, int item, int tg, int s) {
+        uint4 b[4];
+        float part = 0.0f;
 #pragma unroll
-                for (int c = 0; c < NC; ++c)
-                    wc[m][l][c] = load_chunk<FMT>(p, ref, m, row_bytes, p.H, r0 + l * rpw,
-                                                  ch0 + c * WAVE);
-        const int pb = pl.plan[u].z, pc = pl.plan[u].w;
-        for (int g = 0; g < pc; g += 2) {
-            const int pr0 = pl.pairs[pb + g];
-            const int pr1 = g + 1 < pc ? pl.pairs[pb + g + 1] : -1;
-            if (g > 0 || cached_u != u) {
-                load_group_x<FMT, NC>(p, pr0 / p.k, pr1 >= 0 ? pr1 / p.k : -1, ch0, xh, xs);
-                cached_u = g == 0 ? u : -1;
-            }
-            if (pr1 >= 0)
-                gate_up_rows<FMT, NC, LA>(p, wc, xh, xs, true, seg, ch0, r0, rpw, pr0, pr1);
-            else
-                gate_up_rows<FMT, NC, LA>(p, wc, xh, xs, false, seg, ch0, r0, rpw, pr0, -1);
-        }
-    }
-}
-
-// One pair's h slice for this lane's chunks, with its fp32 sum.
-template <int NC>
-__device__ __forceinline__ void load_h(const DecodeParams& p, int pr, int ch0, float hv[NC][32],
-                                       float hs[NC]) {
+        for (int j = 0; j < 4; ++j)
+            b[j] = FMT == MOE355_W_INT4_G64 ? b_x_f16(st.x[j], &part) : st.x[j];
+        mma_slab<FMT, RT>(st.g, b, gq, acc[0]);
+        mma_slab<FMT, RT>(st.u, b, gq, acc[1]);
+        if (FMT == MOE355_W_INT4_G64) {
+            const uint4 bb = bias_b_operand(part, gq);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const float4* hp = reinterpret_cast<const float4*>(
-            p.h + static_cast<int64_t>(pr) * p.I + (ch0 + c * WAVE) * 32);
-        hs[c] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float4 v = hp[i];
-            hv[c][4 * i + 0] = v.x;
-            hv[c][4 * i + 1] = v.y;
-            hv[c][4 * i + 2] = v.z;
-            hv[c][4 * i + 3] = v.w;
-            hs[c] += (v.x + v.y) + (v.z + v.w);
-        }
-    }
-}
-
-// down_row . h for one 16-byte chunk (32 weights) against this lane's h slice.
-template <int FMT>
-__device__ __forceinline__ float down_chunk_dot(const Chunk& ch, const float hv[32], float hs) {
-    const uint32_t d4[4] = {ch.q.x, ch.q.y, ch.q.z, ch.q.w};
-    float dq = 0.0f;
-    if (FMT == MOE355_W_INT4_G64) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const uint32_t lo = d4[d] & 0x0F0F0F0Fu;
-            const uint32_t hi = (d4[d] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                dq = fmaf(static_cast<float>((lo >> (8 * b)) & 0xFFu), hv[8 * d + 2 * b], dq);
-                dq = fmaf(static_cast<float>((hi >> (8 * b)) & 0xFFu), hv[8 * d + 2 * b + 1], dq);
+            for (int t = 0; t < RT; ++t) {
+                acc[0][t] = mma<FMT>(bias_a_operand(st.g.bi[t], st.g.sc[t], gq), bb, acc[0][t]);
+                acc[1][t] = mma<FMT>(bias_a_operand(st.u.bi[t], st.u.sc[t], gq), bb, acc[1][t]);
             }
         }
-        return fmaf(bf16_to_f32(static_cast<uint16_t>(ch.s)), dq,
-                    bf16_to_f32(static_cast<uint16_t>(ch.b)) * hs);
-    } else {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const float2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d4[d], 1.0f, 0);
-            const float2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d4[d], 1.0f, 1);
-            const float2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d4[d], 1.0f, 2);
-            const float2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d4[d], 1.0f, 3);
-            dq = fmaf(v0.x, hv[8 * d + 0], dq);
-            dq = fmaf(v0.y, hv[8 * d + 1], dq);
-            dq = fmaf(v1.x, hv[8 * d + 2], dq);
-            dq = fmaf(v1.y, hv[8 * d + 3], dq);
-            dq = fmaf(v2.x, hv[8 * d + 4], dq);
-            dq = fmaf(v2.y, hv[8 * d + 5], dq);
-            dq = fmaf(v3.x, hv[8 * d + 6], dq);
-            dq = fmaf(v3.y, hv[8 * d + 7], dq);
+        if (tg == 0) {
+            const int u = item / tiles;
+            const ExpertRef ref = expert_ref(p, pl, u);
+            if (ref.dst) {
+                const int row0 = (item - u * tiles) * tile_rows + rw * RT * 16;
+                const int kb = kbase + s * SLAB;
+                store_wslab<FMT, RT>(p, ref.dst, 0, row0, H, kb, ln, gq, st.g);
+                store_wslab<FMT, RT>(p, ref.dst, 1, row0, H, kb, ln, gq, st.u);
+            }
         }
-        return e8m0_to_f32(ch.s) * dq;
-    }
-}
-
-// Down rows [r0 + l*rpw] for one or two pairs whose h slices are in registers.
-template <int FMT, int NC, int LC>
-__device__ __forceinline__ void down_rows(const DecodeParams& p, const Chunk wc[LC][NC],
-                                          const float hv[2][NC][32], const float hs[2][NC],
-                                          bool two, int seg, int ch0, int r0, int rpw, float* o0,
-                                          float w0, float* o1, float w1) {
-#pragma unroll
-    for (int l = 0; l < LC; ++l) {
-        float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            a0 += down_chunk_dot<FMT>(wc[l][c], hv[0][c], hs[0][c]);
-            if (two) a1 += down_chunk_dot<FMT>(wc[l][c], hv[1][c], hs[1][c]);
-        }
-        a0 = segment_sum_f32(a0, seg);
-        if (two) a1 = segment_sum_f32(a1, seg);
-        if (ch0 == 0) {
-            unsafeAtomicAdd(o0 + r0 + l * rpw, w0 * a0);
-            if (two) unsafeAtomicAdd(o1 + r0 + l * rpw, w1 * a1);
-        }
-    }
-}
-
-// A work item is (distinct expert, tile of H rows); each wavefront streams nch
-// chunks of LC row loads, prefetching the next chunk while it computes one, with
-// the h slices of up to two routed pairs held in registers for the whole item.
-template <int FMT, int NC, int LC>
-__global__ void __launch_bounds__(256) down_kernel(DecodeParams p, int seg, int nch) {
-    __shared__ PlanLds pl;
-    const int lane = threadIdx.x & (WAVE - 1);
-    const int wv = threadIdx.x / WAVE;
-    stage_plan(p, pl);
-    const int rpw = WAVE / seg;
-    const int wave_rows = LC * nch * rpw;
-    const int item_rows = 4 * wave_rows;
-    const int tiles = p.H / item_rows;
-    const int n_items = pl.n_uniq * tiles;
-    const int per = (n_items + gridDim.x - 1) / gridDim.x;
-    const int sub = lane / seg, ch0 = lane % seg;
-    const int64_t row_bytes = p.I / 2;
-    const int i_end = min(n_items, (static_cast<int>(blockIdx.x) + 1) * per);
-    for (int item = blockIdx.x * per; item < i_end; ++item) {
+    };
+    int ebuf = 0;
+    auto epilogue = [&](int item, int tg) {
         const int u = item / tiles;
-        const int tile = item - u * tiles;
-        const int rbase = tile * item_rows + wv * wave_rows + sub;
-        const ExpertRef ref = expert_ref(p, pl, u);
-        const int pb = pl.plan[u].z, pc = pl.plan[u].w;
-        for (int g = 0; g < pc; g += 2) {
-            const int pr0 = pl.pairs[pb + g];
-            const int pr1 = g + 1 < pc ? pl.pairs[pb + g + 1] : -1;
-            const bool two = pr1 >= 0;
-            float hv[2][NC][32], hs[2][NC];
-            load_h<NC>(p, pr0, ch0, hv[0], hs[0]);
-            if (two) load_h<NC>(p, pr1, ch0, hv[1], hs[1]);
-            float* o0 = p.out + static_cast<int64_t>(pr0 / p.k) * p.H;
-            float* o1 = two ? p.out + static_cast<int64_t>(pr1 / p.k) * p.H : o0;
-            const float w0 = p.w[pr0], w1 = two ? p.w[pr1] : 0.0f;
-            // only the first pair group copies the bytes into a filled slot
-            ExpertRef rf = ref;
-            if (g > 0) rf.dst = nullptr;
-            Chunk cur[LC][NC], nxt[LC][NC];
+        const int4 pr = pl.plan[u];
+        if (KW > 1) {
+            if (kw != 0) {
 #pragma unroll
-            for (int l = 0; l < LC; ++l)
+                for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int c = 0; c < NC; ++c)
-                    cur[l][c] = load_chunk<FMT>(p, rf, 2, row_bytes, p.I, rbase + l * rpw,
-                                                ch0 + c * WAVE);
-#pragma unroll 1
-            for (int ci = 0; ci < nch; ++ci) {
-                const int r0 = rbase + ci * LC * rpw;
-                if (ci + 1 < nch) {
+                    for (int t = 0; t < RT; ++t) red[ebuf][wv][t][m][lane] = acc[m][t];
+            }
+            __syncthreads();
+            if (kw == 0) {
 #pragma unroll
-                    for (int l = 0; l < LC; ++l)
+                for (int o = 1; o < KW; ++o)
 #pragma unroll
-                        for (int c = 0; c < NC; ++c)
-                            nxt[l][c] = load_chunk<FMT>(p, rf, 2, row_bytes, p.I,
-                                                        r0 + (LC + l) * rpw, ch0 + c * WAVE);
-                }
-                if (two)
-                    down_rows<FMT, NC, LC>(p, cur, hv, hs, true, seg, ch0, r0, rpw, o0, w0, o1, w1);
-                else
-                    down_rows<FMT, NC, LC>(p, cur, hv, hs, false, seg, ch0, r0, rpw, o0, w0, o1, w1);
-                if (ci + 1 < nch) {
+                    for (int m = 0; m < 2; ++m)
 #pragma unroll
-                    for (int l = 0; l < LC; ++l)
+                        for (int t = 0; t < RT; ++t) acc[m][t] += red[ebuf][wv + o][t][m][lane];
+            }
+            ebuf ^= 1;
+        }
+        const int n = tg * TOK + ln;
+        if (kw == 0 && n < pr.w) {
+            const int pair = pl.pairs[pr.z + n];
+            const int row0 = (item - u * tiles) * tile_rows + rw * RT * 16;
 #pragma unroll
-                        for (int c = 0; c < NC; ++c) cur[l][c] = nxt[l][c];
+            for (int t = 0; t < RT; ++t) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float hv = silu(acc[0][t][r]) * acc[1][t][r];
+                    const int row = row0 + 16 * t + 4 * gq + r;
+                    uint16_t hi, lo;
+                    int64_t at;
+                    if (FMT == MOE355_W_INT4_G64) {
+                        const _Float16 a = static_cast<_Float16>(hv);
+                        const _Float16 b = static_cast<_Float16>(hv - static_cast<float>(a));
+                        hi = __builtin_bit_cast(uint16_t, a);
+                        lo = __builtin_bit_cast(uint16_t, b);
+                        // stored in the int4 A order inside each block of 8 rows
+                        at = static_cast<int64_t>(pair) * p.I + (row & ~7) + 2 * r + (gq & 1);
+                    } else {
+                        const __bf16 a = static_cast<__bf16>(hv);
+                        const __bf16 b = static_cast<__bf16>(hv - static_cast<float>(a));
+                        hi = __builtin_bit_cast(uint16_t, a);
+                        lo = __builtin_bit_cast(uint16_t, b);
+                        at = static_cast<int64_t>(pair) * p.I + row;
+                    }
+                    p.h_hi[at] = hi;
+                    p.h_lo[at] = lo;
                 }
             }
         }
+        zero_acc();
+    };
+
+    zero_acc();
+    GuStage<FMT, KW, RT> sa, sb;
+    int item = i_beg, tg = 0, s = 0;
+    load(sa, item, tg, 0);
+    // advance (item, tg, s) to the next stage; false past the block's last item
+    auto next = [&](int& it, int& g, int& sl) -> bool {
+        if (++sl < NS) return true;
+        sl = 0;
+        if ((g + 1) * TOK < tokens_of(it)) {
+            ++g;
+            return true;
+        }
+        g = 0;
+        return ++it < i_end;
+    };
+    for (;;) {
+        int it2 = item, g2 = tg, s2 = s;
+        bool more = next(it2, g2, s2);
+        if (more) load(sb, it2, g2, s2);
+        compute(sa, item, tg, s);
+        if (s == NS - 1) epilogue(item, tg);
+        if (!more) break;
+        item = it2; tg = g2; s = s2;
+        it2 = item; g2 = tg; s2 = s;
+        more = next(it2, g2, s2);
+        if (more) load(sa, it2, g2, s2);
+        compute(sb, item, tg, s);
+        if (s == NS - 1) epilogue(item, tg);
+        if (!more) break;
+        item = it2; tg = g2; s = s2;
     }
 }
 
-// Row geometry: lanes per row segment and 16-byte chunks per lane for rows of L weights.
-void row_geometry(int L, int* seg, int* nc) {
-    const int chunks = L / 32;
-    if (chunks >= WAVE) {
-        *seg = WAVE;
-        *nc = chunks / WAVE;
-    } else {
-        *seg = chunks;
-        *nc = 1;
+// ---------------------------------------------------------------------------
+// down + combine.  Wavefront items of RT tiles of 16 rows over all of I.
+template <int FMT, int RT>
+struct DnStage {
+    WSlab<RT> w;
+    uint4 hh[4], hl[4];
+};
+
+template <int FMT, int RT>
+__global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
+    __shared__ PlanLds pl;
+    const int lane = threadIdx.x & (WAVE - 1), ln = lane & 15, gq = lane >> 4;
+    stage_plan(p, pl);
+    const int I = p.I, NS = I / SLAB;
+    const int tile_rows = RT * 16;
+    const int tiles = p.H / tile_rows;
+    const int n_items = pl.n_uniq * tiles;
+    const int n_waves = gridDim.x * (blockDim.x / WAVE);
+    const int gw = blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
+    const int per = (n_items + n_waves - 1) / n_waves;
+    const int i_beg = gw * per;
+    const int i_end = min(n_items, i_beg + per);
+    if (i_beg >= i_end) return;
+
+    auto tokens_of = [&](int item) { return pl.plan[item / tiles].w; };
+    auto load = [&](DnStage<FMT, RT>& st, int item, int tg, int s) {
+        const int u = item / tiles, tile = item - u * tiles;
+        const ExpertRef ref = expert_ref(p, pl, u);
+        const int kb = s * SLAB;
+        load_wslab<FMT, RT>(p, ref.src, 2, tile * tile_rows, I, kb, ln, gq, st.w);
+        const int n = tg * TOK + ln;
+        const int4 pr = pl.plan[u];
+        if (n < pr.w) {
+            const int64_t o = static_cast<int64_t>(pl.pairs[pr.z + n]) * I + kb + 32 * gq;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                st.hh[i] = ldg16(p.h_hi + o + 8 * i);
+                st.hl[i] = ldg16(p.h_lo + o + 8 * i);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                st.hh[i] = make_uint4(0u, 0u, 0u, 0u);
+                st.hl[i] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    };
+    f32x4 acc[RT];
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    };
+    auto compute = [&](const DnStage<FMT, RT>& st, int item, int tg, int s) {
+        mma_slab<FMT, RT>(st.w, st.hh, gq, acc);
+        mma_slab<FMT, RT>(st.w, st.hl, gq, acc);
+        if (FMT == MOE355_W_INT4_G64) {
+            float part = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part = sum_f16x8(st.hl[i], sum_f16x8(st.hh[i], part));
+            const uint4 bb = bias_b_operand(part, gq);
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+                acc[t] = mma<FMT>(bias_a_operand(st.w.bi[t], st.w.sc[t], gq), bb, acc[t]);
+        }
+        if (tg == 0) {
+            const int u = item / tiles;
+            const ExpertRef ref = expert_ref(p, pl, u);
+            if (ref.dst)
+                store_wslab<FMT, RT>(p, ref.dst, 2, (item - u * tiles) * tile_rows, I, s * SLAB, ln,
+                                     gq, st.w);
+        }
+    };
+    auto epilogue = [&](int item, int tg) {
+        const int u = item / tiles;
+        const int4 pr = pl.plan[u];
+        const int n = tg * TOK + ln;
+        if (n < pr.w) {
+            const int pair = pl.pairs[pr.z + n];
+            const float wt = p.w[pair];
+            float* o = p.out + static_cast<int64_t>(pair / p.k) * p.H + (item - u * tiles) * tile_rows;
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) unsafeAtomicAdd(o + 16 * t + 4 * gq + r, wt * acc[t][r]);
+        }
+        zero_acc();
+    };
+
+    zero_acc();
+    DnStage<FMT, RT> sa, sb;
+    int item = i_beg, tg = 0, s = 0;
+    load(sa, item, tg, 0);
+    auto next = [&](int& it, int& g, int& sl) -> bool {
+        if (++sl < NS) return true;
+        sl = 0;
+        if ((g + 1) * TOK < tokens_of(it)) {
+            ++g;
+            return true;
+        }
+        g = 0;
+        return ++it < i_end;
+    };
+    for (;;) {
+        int it2 = item, g2 = tg, s2 = s;
+        bool more = next(it2, g2, s2);
+        if (more) load(sb, it2, g2, s2);
+        compute(sa, item, tg, s);
+        if (s == NS - 1) epilogue(item, tg);
+        if (!more) break;
+        item = it2; tg = g2; s = s2;
+        it2 = item; g2 = tg; s2 = s;
+        more = next(it2, g2, s2);
+        if (more) load(sa, it2, g2, s2);
+        compute(sb, item, tg, s);
+        if (s == NS - 1) epilogue(item, tg);
+        if (!more) break;
+        item = it2; tg = g2; s = s2;
     }
 }
 
@@ -504,41 +604,40 @@ int device_cus() {
     return cus;
 }
 
-template <int FMT, int NCA, int LA, int NCB, int LC>
-moe355_status launch_two(const DecodeParams& p, int segA, int segB, int max_uniq,
-                         hipStream_t stream) {
-    const int rpw_b = WAVE / segB;
-    const int rows_a = 4 * LA * (WAVE / segA);
-    MOE355_REQUIRE(p.I % rows_a == 0 && p.H % (4 * LC * rpw_b) == 0, MOE355_ENOTSUP,
-                   "expert_ffn_decode: H=%d I=%d do not tile", p.H, p.I);
-    const int cap = device_cus() * 2;        // two resident blocks per CU
-    // down: as many row chunks per item as keep at least two items per CU (reuse
-    // of the h slices grows with the chunks), at most 8
-    const int base_tiles = p.H / (4 * LC * rpw_b);
-    int nch = 8;
-    while (nch > 1 && (base_tiles % nch != 0 || max_uniq * (base_tiles / nch) < 2 * device_cus()))
-        nch >>= 1;
-    const int items_a = max_uniq * (p.I / rows_a);
-    const int items_b = max_uniq * (base_tiles / nch);
-    gate_up_kernel<FMT, NCA, LA><<<items_a < cap ? items_a : cap, 256, 0, stream>>>(p, segA);
-    moe355_status st = check_launch("expert_ffn_decode gate_up");
-    if (st) return st;
-    down_kernel<FMT, NCB, LC><<<items_b < cap ? items_b : cap, 256, 0, stream>>>(p, segB, nch);
-    return check_launch("expert_ffn_decode down");
+template <int FMT, int KW>
+moe355_status launch_gate_up(const DecodeParams& p, int max_uniq, hipStream_t stream) {
+    constexpr int RW = 4 / KW;
+    const int cap = device_cus() * 2;   // two resident blocks per CU
+    // two row tiles per wavefront when that still leaves two items per block slot
+    const int items2 = max_uniq * (p.I / (RW * 32));
+    if (items2 >= 2 * cap && p.I % (RW * 32) == 0) {
+        gate_up_kernel<FMT, KW, 2><<<items2 < cap ? items2 : cap, 256, 0, stream>>>(p);
+    } else {
+        const int items1 = max_uniq * (p.I / (RW * 16));
+        gate_up_kernel<FMT, KW, 1><<<items1 < cap ? items1 : cap, 256, 0, stream>>>(p);
+    }
+    return check_launch("expert_ffn_decode gate_up");
 }
 
 template <int FMT>
 moe355_status launch_decode(const DecodeParams& p, int max_uniq, hipStream_t stream) {
-    int segA, ncA, segB, ncB;
-    row_geometry(p.H, &segA, &ncA);
-    row_geometry(p.I, &segB, &ncB);
-    // gate/up: 4 row loads per wavefront and item (2 with two chunks per row);
-    // down: chunks of 4 row loads per wavefront (2 with two chunks per row)
-    if (ncA == 1 && ncB == 1) return launch_two<FMT, 1, 4, 1, 4>(p, segA, segB, max_uniq, stream);
-    if (ncA == 2 && ncB == 1) return launch_two<FMT, 2, 2, 1, 4>(p, segA, segB, max_uniq, stream);
-    if (ncA == 2 && ncB == 2) return launch_two<FMT, 2, 2, 2, 2>(p, segA, segB, max_uniq, stream);
-    if (ncA == 1 && ncB == 2) return launch_two<FMT, 1, 4, 2, 2>(p, segA, segB, max_uniq, stream);
-    return fail(MOE355_ENOTSUP, "expert_ffn_decode: H=%d I=%d", p.H, p.I);
+    moe355_status st;
+    // wavefronts splitting H: 4 when H >= 512
+    if (p.H >= 512) st = launch_gate_up<FMT, 4>(p, max_uniq, stream);
+    else if (p.H == 256) st = launch_gate_up<FMT, 2>(p, max_uniq, stream);
+    else st = launch_gate_up<FMT, 1>(p, max_uniq, stream);
+    if (st) return st;
+    const int slots = device_cus() * 8;   // eight resident wavefronts per CU
+    const int items2 = max_uniq * (p.H / 32);
+    if (items2 >= 2 * slots) {
+        const int waves = items2 < slots ? items2 : slots;
+        down_kernel<FMT, 2><<<(waves + 3) / 4, 256, 0, stream>>>(p);
+    } else {
+        const int items1 = max_uniq * (p.H / 16);
+        const int waves = items1 < slots ? items1 : slots;
+        down_kernel<FMT, 1><<<(waves + 3) / 4, 256, 0, stream>>>(p);
+    }
+    return check_launch("expert_ffn_decode down");
 }
 
 __global__ void combine_kernel(int T, int H, int k, const float* __restrict__ y,
@@ -557,7 +656,7 @@ __global__ void combine_kernel(int T, int H, int k, const float* __restrict__ y,
 
 size_t decode_ws_bytes(const moe355_layer_desc* d, int T) {
     const size_t tk = static_cast<size_t>(T) * d->top_k;
-    return 256 + tk * d->inter * sizeof(float);
+    return 256 + 2 * tk * d->inter * sizeof(uint16_t);   // h as hi and lo halves
 }
 
 // Shared by the public decode call and the fused decode-layer call.
@@ -582,7 +681,6 @@ moe355_status decode_ffn(const moe355_layer_desc* d, const void* x_bf16, int32_t
     expert_layout(d, &L);
     DecodeParams p{};
     p.x = static_cast<const uint16_t*>(x_bf16);
-    p.ids = topk_ids;
     p.w = topk_w;
     p.uniq = exp->uniq;
     p.counts = exp->counts;
@@ -599,14 +697,16 @@ moe355_status decode_ffn(const moe355_layer_desc* d, const void* x_bf16, int32_t
         p.s_off[m] = L.s_off[m];
         p.b_off[m] = L.b_off[m];
     }
-    p.h = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + 256);
+    const size_t tkI = static_cast<size_t>(T) * d->top_k * d->inter;
+    p.h_hi = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + 256);
+    p.h_lo = p.h_hi + tkI;
     p.out = out;
     if (cache) {
         MOE355_REQUIRE(cache->slot_table && cache->slot_data && cache->slot_bytes == L.bytes &&
                            cache->n_experts == d->n_experts && layer >= 0 &&
                            layer < cache->n_layers,
                        MOE355_EINVAL, "expert_ffn_decode: cache does not match the layer");
-        p.table = cache->slot_table;
+        p.has_cache = 1;
         p.slots = cache->slot_data;
         p.fill_through = fill_through ? 1 : 0;
     } else {
