@@ -73,9 +73,12 @@ def cpu_baseline_decode(w, trace, n_calls: int, budget_s: float):
 
 def bench_decode(args, w):
     """Timed region: K decode steps, each one replay of a captured graph holding
-    the step's 40 (or 24) decode_layer calls -- route + classify/evict in one
-    kernel, then the expert FFN with fill-through and the combine -- after the
-    step's inputs (logits, activations, tick base) are staged in HBM.
+    the step's 40 (or 24) layer calls, after the step's inputs (logits,
+    activations, tick base) are staged in HBM.  Layer call order "fused":
+    decode_layer (route + classify/evict in one kernel, then the expert FFN with
+    fill-through and the combine).  Order "split": route_plan and the FFN on the
+    main stream, evict_fill (LRU update + fill copy) on a second stream that the
+    next layer's route_plan waits for.
 
     Roofline: the expert FFN kernel timed with HIP events in a second, eager
     pass over the same trace (route, classify_evict, cache_fill as separate
@@ -101,6 +104,7 @@ def bench_decode(args, w):
     logits_all = torch.from_numpy(trace.logits).to(dev)                      # [steps, L, T, E]
     xs_all = torch.stack([torch.stack([_x_dev(tr.decode_x(w, s, l), torch) for l in range(L)])
                           for s in range(n_trace)])                           # [steps, L, T, H]
+    order = args.order if args.order != "auto" else "fused"
 
     class Step:
         def __init__(self):
@@ -114,6 +118,8 @@ def bench_decode(args, w):
             self.out = torch.empty((L, T, w.hidden), dtype=torch.float32, device=dev)
             self.ws = torch.zeros(m.workspace_bytes(desc, T, m.MODE_DECODE), dtype=torch.uint8,
                                   device=dev)
+            self.side = torch.cuda.Stream()
+            self.planned = [torch.cuda.Event() for _ in range(L)]
 
         def stage(self, s):
             self.logits.copy_(logits_all[s % n_trace])
@@ -121,10 +127,25 @@ def bench_decode(args, w):
             self.tick.fill_(s * L)
 
         def layers(self):
+            main = torch.cuda.current_stream()
+            if order == "fused":
+                for l in range(L):
+                    m.decode_layer(desc, self.cache, pool, l, self.tick, l + 1, self.logits[l],
+                                   self.x[l], policy, self.ids[l], self.wt[l], self.lists[l],
+                                   self.out[l], self.ws)
+                return
+            self.side.wait_stream(main)
             for l in range(L):
-                m.decode_layer(desc, self.cache, pool, l, self.tick, l + 1, self.logits[l],
-                               self.x[l], policy, self.ids[l], self.wt[l], self.lists[l],
-                               self.out[l], self.ws)
+                main.wait_stream(self.side)          # previous layer's slot update and fill
+                m.route_plan(desc, self.cache, l, self.logits[l], self.ids[l], self.wt[l],
+                             self.lists[l])
+                self.planned[l].record(main)
+                m.expert_ffn_decode(desc, self.x[l], self.ids[l], self.wt[l], self.cache, pool, l,
+                                    self.lists[l], self.out[l], self.ws)
+                self.side.wait_event(self.planned[l])
+                m.evict_fill(desc, self.cache, pool, l, self.tick, l + 1, self.ids[l], policy,
+                             self.lists[l], stream=self.side)
+            main.wait_stream(self.side)
 
     warm = Step()                       # first launches (occupancy queries) outside capture
     warm.stage(0)
@@ -201,7 +222,7 @@ def bench_decode(args, w):
                    "inter": w.inter, "experts": w.n_experts, "top_k": w.top_k,
                    "weights": "int4_g64" if w.wfmt == 0 else "mxfp4", "cache_slots": w.n_slots,
                    "expert_bytes": S, "layer_calls_timed": n_calls, "parallelism": "single_gpu",
-                   "step": "one replay of a captured graph of decode_layer calls"},
+                   "order": order, "step": "one replay of a captured graph of the step's layer calls"},
         "roofline": {"bound": "hbm", "kernel": "ffn_decode_kernel (expert_ffn_decode)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
@@ -327,6 +348,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen_decode",
                     choices=["qwen_decode", "ds_decode", "qwen_prefill", "ds_prefill"])
+    ap.add_argument("--order", default="auto", choices=["auto", "fused", "split"],
+                    help="decode layer call order (auto: fused)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-calls", type=int, default=160)
     ap.add_argument("--cpu-budget", type=float, default=20.0)

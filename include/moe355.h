@@ -268,8 +268,8 @@ moe355_status moe355_expert_ffn_decode(const moe355_layer_desc* d, const void* x
  *   else tick_add; it must exceed every earlier tick.
  * logits: device fp32 [T, E]; x: device bf16 [T, H]; topk_ids / topk_w: device
  * [T, k] outputs; lists: the call's classify lists (capacity >= max(min(T*k, E),
- * K)); out: device fp32 [T, H]; ws as for moe355_expert_ffn_decode (zeroed
- * before first use).  Limits: 1 <= T*k <= 256, plus those of the two calls.
+ * K)); out: device fp32 [T, H]; ws as for moe355_expert_ffn_decode.
+ * Limits: 1 <= T*k <= 256, plus those of the two calls.
  */
 moe355_status moe355_decode_layer(const moe355_layer_desc* d, const moe355_cache* c,
                                   const uint8_t* pool, int32_t layer, const int64_t* tick_base,
@@ -277,6 +277,36 @@ moe355_status moe355_decode_layer(const moe355_layer_desc* d, const moe355_cache
                                   int32_t T, const moe355_evict_policy* p, int32_t* topk_ids,
                                   float* topk_w, moe355_classify_out* lists, float* out, void* ws,
                                   size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The same layer call with the cache bookkeeping off the critical path
+ * [FT-zh, Core method: VRAM only changes speed, never results; FT-zh, Method
+ * steps: the filled experts are batch-copied into their victim slots].  Three
+ * calls replace moe355_decode_layer:
+ *   1. moe355_route_plan on the compute stream: route T tokens from `logits`,
+ *      deduplicate, classify hits and misses against the slot table (read only)
+ *      and write lists->uniq / hit / miss, counts[0..2] (counts[3..5] = 0), the
+ *      pairs and a plan in which hits read their slots and misses the pool.
+ *   2. moe355_expert_ffn_decode on the compute stream with `lists` and the cache.
+ *   3. moe355_evict_fill on a second stream, ordered after call 1: stamps the
+ *      hits with the tick, selects the K LRU victims, splits the misses by q,
+ *      updates slot_table / slot_owner / slot_ts, writes lists->fill / inplace /
+ *      victims and counts[3..5], and copies the filled experts from the pool
+ *      into their victim slots.  It never touches the slots this call reads.
+ * The next call that reads the slot table (any layer) must be ordered after
+ * call 3.  The results equal moe355_decode_layer's; the filled experts' bytes
+ * are read twice (once by the FFN, once by the copy).
+ * Arguments as for moe355_decode_layer; T*k <= 256.
+ */
+moe355_status moe355_route_plan(const moe355_layer_desc* d, const moe355_cache* c, int32_t layer,
+                                const float* logits, int32_t T, int32_t* topk_ids, float* topk_w,
+                                moe355_classify_out* lists, hipStream_t stream);
+
+moe355_status moe355_evict_fill(const moe355_layer_desc* d, const moe355_cache* c,
+                                const uint8_t* pool, int32_t layer, const int64_t* tick_base,
+                                int64_t tick_add, const int32_t* topk_ids, int32_t T,
+                                const moe355_evict_policy* p, moe355_classify_out* lists,
+                                hipStream_t stream);
 
 /*
  * Prefill expert FFN: a grouped GEMM over each expert's token bucket (from

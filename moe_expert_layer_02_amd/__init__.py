@@ -15,14 +15,16 @@ from .abi import (LayerDesc, Cache, EvictPolicy, ClassifyOut, ROUTE_SOFTMAX_TOPK
                   ROUTE_SIGMOID_GROUP, W_INT4_G64, W_MXFP4, MODE_DECODE, MODE_PREFILL,
                   MODE_PERMUTE, Moe355Error, lib_path, load)
 from .ops import (router_logits, route, dedup, classify_evict, cache_fill, cache_rebuild,
-                  permute, expert_ffn_decode, decode_layer, expert_ffn_prefill, combine, workspace_bytes,
+                  permute, expert_ffn_decode, decode_layer, route_plan, evict_fill,
+                  expert_ffn_prefill, combine, workspace_bytes,
                   expert_bytes, version, DeviceCache, DeviceClassifyOut)
 
 __all__ = [
     "LayerDesc", "Cache", "EvictPolicy", "ClassifyOut", "ROUTE_SOFTMAX_TOPK",
     "ROUTE_SIGMOID_GROUP", "W_INT4_G64", "W_MXFP4", "MODE_DECODE", "MODE_PREFILL", "MODE_PERMUTE",
     "Moe355Error", "lib_path", "load", "router_logits", "route", "dedup", "classify_evict",
-    "cache_fill", "cache_rebuild", "permute", "expert_ffn_decode", "decode_layer",
+    "cache_fill", "cache_rebuild", "permute", "expert_ffn_decode", "decode_layer", "route_plan",
+    "evict_fill",
     "expert_ffn_prefill",
     "combine", "workspace_bytes", "expert_bytes", "version", "DeviceCache", "DeviceClassifyOut",
 ]

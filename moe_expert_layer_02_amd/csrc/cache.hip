@@ -15,6 +15,8 @@
 // (ts, slot) keys among slots with ts < tick are found by an 8-bit-digit radix
 // select over LDS histograms, then ranked by counting.  Owning the whole call
 // in one workgroup keeps the table updates free of cross-workgroup atomics.
+#include <type_traits>
+
 #include "route_dev.h"
 
 namespace moe355 {
@@ -79,23 +81,17 @@ struct SelectScratch {
 };
 
 // Key of slot s: valid(s) ? (ts(s) << sbits | s) : none.  Returns the `rank`-th
-// smallest valid key (1-based); all keys are distinct.  `rank` must be in
-// [1, number of valid keys].
+// smallest valid key (1-based); all keys are distinct and below 2^bits.  `rank`
+// must be in [1, number of valid keys].  Two barriers per 8-bit digit: wave 0
+// scans the histogram, picks the digit and clears the histogram for the next.
 template <typename KeyFn>
-__device__ uint64_t radix_select(int n, uint32_t rank, KeyFn key_of, SelectScratch* sc) {
-    uint64_t mx = 0;
-    for (int s = threadIdx.x; s < n; s += CL_THREADS) {
-        uint64_t k;
-        if (key_of(s, &k)) mx = k > mx ? k : mx;
-    }
-    mx = block_max_u64(mx, sc->red);
-    const int bits = mx ? 64 - __clzll(static_cast<long long>(mx)) : 1;
-    int shift = ((bits - 1) / 8) * 8;
+__device__ uint64_t radix_select(int n, uint32_t rank, int bits, KeyFn key_of, SelectScratch* sc) {
+    for (int i = threadIdx.x; i < 256; i += CL_THREADS) sc->hist[i] = 0;
+    __syncthreads();
+    int shift = ((bits > 0 ? bits - 1 : 0) / 8) * 8;
     uint64_t prefix = 0, pmask = 0;
     uint32_t remaining = rank;
     for (; shift >= 0; shift -= 8) {
-        for (int i = threadIdx.x; i < 256; i += CL_THREADS) sc->hist[i] = 0;
-        __syncthreads();
         for (int s = threadIdx.x; s < n; s += CL_THREADS) {
             uint64_t k;
             if (key_of(s, &k) && (k & pmask) == prefix)
@@ -110,6 +106,8 @@ __device__ uint64_t radix_select(int n, uint32_t rank, KeyFn key_of, SelectScrat
                 c[i] = sc->hist[lane * 4 + i];
                 local += c[i];
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc->hist[lane * 4 + i] = 0;
             uint32_t inc = local;
 #pragma unroll
             for (int d = 1; d < WAVE; d <<= 1) {
@@ -134,7 +132,6 @@ __device__ uint64_t radix_select(int n, uint32_t rank, KeyFn key_of, SelectScrat
         prefix |= static_cast<uint64_t>(sc->pick[0]) << shift;
         pmask |= 255ull << shift;
         remaining = sc->pick[1];
-        __syncthreads();
     }
     return prefix;
 }
@@ -142,7 +139,7 @@ __device__ uint64_t radix_select(int n, uint32_t rank, KeyFn key_of, SelectScrat
 }  // namespace
 
 struct ClassifyParams {
-    int dedup_only;
+    int mode;                  // ClassifyMode (internal.h)
     int32_t* table;
     int table_len;
     int32_t* owner;
@@ -165,44 +162,103 @@ struct ClassifyParams {
 
 namespace {
 
+constexpr int OWN_SLOTS = 4096;   // owners staged in LDS for caches up to this size
+
 struct ClassifyShared {
     uint32_t ts[MAX_SLOTS];
+    int32_t own[OWN_SLOTS];
+    int32_t tab[MAX_EXPERTS];    // this layer's row of the slot table
     int32_t mark[MAX_EXPERTS];
     int32_t upos[MAX_EXPERTS];   // expert -> its index u in uniq
     int32_t pcnt[MAX_EXPERTS];   // routed pairs per u
     int32_t pbeg[MAX_EXPERTS];   // first index of u's pairs
+    int32_t ids[MAX_LIST];       // the call's routed ids
+    int32_t plocal[MAX_LIST];    // a pair's place inside its expert's group
     int32_t miss[MAX_LIST];
     uint64_t sel_key[MAX_LIST];
+    int32_t sel_owner[MAX_LIST];
     int32_t victims[MAX_LIST];
-    uint64_t wave_tot[CL_WAVES];
-    uint32_t n_sel;
-    SelectScratch sc;
+    int32_t vic_owner[MAX_LIST];
+    uint32_t hist[256];
 };
+
+// Inclusive prefix sum over the 64 lanes (DPP row shifts and row broadcasts).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
+// Exclusive prefix sum and total over the 64 lanes.
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t* total) {
+    const uint32_t inc = wave_incl_scan(v);
+    *total = __builtin_amdgcn_readlane(inc, 63);
+    return inc - v;
+}
+
+// Orders this wavefront's LDS accesses before the ones that follow: a compiler
+// barrier plus a wait for outstanding LDS operations only (global stores stay
+// in flight).
+__device__ __forceinline__ void wave_lds_sync() {
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
 
 }  // namespace
 
-// One layer call: optional routing of T tokens, then dedup, hit/miss, victims.
+// One layer call.  All 16 wavefronts request the slot timestamps, owners and
+// this layer's table row at once and route the call's tokens (one wavefront
+// per token); then a single wavefront does the bookkeeping with DPP scans and
+// LDS histograms, so no step after routing waits on a workgroup barrier.
+// SPT = slots per thread held in registers while routing runs (caches up to
+// SPT * CL_THREADS slots); SPT = 0 stores the timestamps before routing.
+// SPL = slots per lane the bookkeeping wavefront holds in registers (caches up
+// to 64 * SPL slots); SPL = 0 reads them from LDS.
+template <int SPT, int SPL>
 __global__ void __launch_bounds__(CL_THREADS) classify_kernel(ClassifyParams cp) {
     __shared__ ClassifyShared sh;
-    __shared__ int32_t routed[MAX_LIST];
     const int tid = threadIdx.x;
     int32_t* __restrict__ table = cp.table;
     int32_t* __restrict__ owner = cp.owner;
     int64_t* __restrict__ slot_ts = cp.slot_ts;
     const int N = cp.N, E = cp.E, layer = cp.layer, K = cp.K, table_len = cp.table_len;
-    const int dedup_only = cp.dedup_only;
-    const uint32_t tick = cp.tick_dev ? static_cast<uint32_t>(*cp.tick_dev + cp.tick_add)
-                                      : static_cast<uint32_t>(cp.tick_add);
-    const int32_t* ids = cp.ids;
-    const int n_ids = cp.n_ids;
+    const int mode = cp.mode;
+    const bool dedup_only = mode == CLASSIFY_DEDUP;
+    const bool plan_only = mode == CLASSIFY_PLAN;     // no cache state changes
+    const bool evict_only = mode == CLASSIFY_EVICT;   // the plan is another call's
+    const bool need_slots = mode == CLASSIFY_FULL || evict_only;
+    const bool own_lds = N <= OWN_SLOTS;
+    const int n_ids = cp.logits ? cp.T * cp.k : cp.n_ids;
 
+    // ---- every wavefront: requests, routing, clears ---------------------------
+    constexpr int R = SPT > 0 ? SPT : 1;
+    int64_t ts_r[R];
+    int32_t own_r[R];
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+        const int sl = tid + j * CL_THREADS;
+        ts_r[j] = 0;
+        own_r[j] = -1;
+        if (need_slots && sl < N) {
+            ts_r[j] = slot_ts[sl];
+            if (own_lds) own_r[j] = owner[sl];
+        }
+    }
+    if (SPT == 0 && need_slots) {
+        for (int sl = tid; sl < N; sl += CL_THREADS) {
+            sh.ts[sl] = static_cast<uint32_t>(slot_ts[sl]);
+            if (own_lds) sh.own[sl] = owner[sl];
+        }
+    }
     for (int e = tid; e < E; e += CL_THREADS) {
+        sh.tab[e] = dedup_only ? -1 : table[layer * E + e];
         sh.mark[e] = 0;
         sh.pcnt[e] = 0;
     }
-    if (tid == 0) sh.n_sel = 0;
     if (cp.logits) {
-        // route the call's tokens first: one wavefront per token
         for (int t = tid / WAVE; t < cp.T; t += CL_WAVES) {
             float w;
             const int e = route_token(cp.logits + static_cast<int64_t>(t) * E, E, cp.k,
@@ -211,125 +267,255 @@ __global__ void __launch_bounds__(CL_THREADS) classify_kernel(ClassifyParams cp)
             if (lane < cp.k) {
                 cp.ids_out[t * cp.k + lane] = e;
                 cp.w_out[t * cp.k + lane] = w;
-                routed[t * cp.k + lane] = e;
+                sh.ids[t * cp.k + lane] = e;
             }
         }
-        ids = routed;
+    } else {
+        for (int i = tid; i < n_ids; i += CL_THREADS) sh.ids[i] = cp.ids[i];
     }
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+        const int sl = tid + j * CL_THREADS;
+        if (need_slots && sl < N) {
+            sh.ts[sl] = static_cast<uint32_t>(ts_r[j]);
+            if (own_lds) sh.own[sl] = own_r[j];
+        }
+    }
+    const uint32_t tick = cp.tick_dev ? static_cast<uint32_t>(*cp.tick_dev + cp.tick_add)
+                                      : static_cast<uint32_t>(cp.tick_add);
     __syncthreads();
-    for (int i = tid; i < n_ids; i += CL_THREADS) {
-        int e = ids[i];
+    if (tid >= WAVE) return;
+
+    // ---- one wavefront from here on ------------------------------------------
+    const int lane = tid;
+    const bool with_plan = cp.plan != nullptr && cp.pairs != nullptr && !evict_only;
+    for (int i = lane; i < n_ids; i += WAVE) {
+        const int e = sh.ids[i];
         if (e >= 0 && e < E) sh.mark[e] = 1;  // ids out of range are ignored
     }
-    if (!dedup_only)
-        for (int s = tid; s < N; s += CL_THREADS) sh.ts[s] = static_cast<uint32_t>(slot_ts[s]);
-    __syncthreads();
+    wave_lds_sync();
 
-    // E <= CL_THREADS: thread e handles expert e
-    const int e = tid;
-    const int m = (e < E) ? sh.mark[e] : 0;
-    int slot = -1;
-    if (m && !dedup_only) {
-        slot = table[layer * E + e];
-        if (slot >= N) slot = -1;  // a table entry outside the cache counts as absent
-    }
-    const uint64_t is_hit = (m && slot >= 0) ? 1 : 0;
-    const uint64_t is_miss = (m && slot < 0) ? 1 : 0;
-    const uint64_t packed = static_cast<uint64_t>(m) | (is_hit << 21) | (is_miss << 42);
-    uint64_t tot;
-    const uint64_t pos = block_excl_scan(packed, sh.wave_tot, &tot);
-    const uint32_t n_uniq = static_cast<uint32_t>(tot & 0x1FFFFF);
-    const uint32_t n_hit = static_cast<uint32_t>((tot >> 21) & 0x1FFFFF);
-    const uint32_t n_miss = static_cast<uint32_t>((tot >> 42) & 0x1FFFFF);
-    const int my_u = static_cast<int>(pos & 0x1FFFFF);
-    if (m) {
-        cp.uniq[my_u] = e;
-        sh.upos[e] = my_u;
-    }
-    __syncthreads();
-
-    // ---- the routed pairs of each distinct expert, grouped by u (n_ids <= threads) ----
-    const bool with_plan = cp.plan != nullptr && cp.pairs != nullptr;
-    int pair_u = -1, pair_local = 0;
-    if (with_plan && tid < n_ids) {
-        const int pe = ids[tid];
-        if (pe >= 0 && pe < E) {
-            pair_u = sh.upos[pe];
-            pair_local = atomicAdd(&sh.pcnt[pair_u], 1);
-        }
-    }
-    __syncthreads();
-    {
-        uint64_t ptot;
-        const uint64_t pb = block_excl_scan(
-            (with_plan && tid < static_cast<int>(n_uniq)) ? static_cast<uint64_t>(sh.pcnt[tid]) : 0ull,
-            sh.wave_tot, &ptot);
-        if (tid < static_cast<int>(n_uniq)) sh.pbeg[tid] = static_cast<int32_t>(pb);
-    }
-    __syncthreads();
-    if (pair_u >= 0) cp.pairs[sh.pbeg[pair_u] + pair_local] = tid;
-
-    if (dedup_only) {
-        if (tid < 6) cp.counts[tid] = tid == 0 ? static_cast<int32_t>(n_uniq) : 0;
-        if (with_plan && m)
-            reinterpret_cast<int4*>(cp.plan)[my_u] = make_int4(-1, 0, sh.pbeg[my_u], sh.pcnt[my_u]);
-        return;
-    }
-    if (is_hit) {
-        const uint32_t p = (pos >> 21) & 0x1FFFFF;
-        cp.hit_e[p] = e;
-        cp.hit_s[p] = slot;
-        sh.ts[slot] = tick;  // recency moves on a router selection
-        slot_ts[slot] = tick;
-    }
-    if (is_miss) {
-        const uint32_t p = (pos >> 42) & 0x1FFFFF;
-        cp.miss[p] = e;
-        sh.miss[p] = e;
-    }
-    __syncthreads();
-
-    // ---- one scan of every slot's timestamp: the K oldest eligible slots ----
-    const int sbits = N > 1 ? 32 - __clz(N - 1) : 1;
-    auto key_of = [&](int s, uint64_t* k) -> bool {
-        uint32_t t = sh.ts[s];
-        *k = (static_cast<uint64_t>(t) << sbits) | static_cast<uint32_t>(s);
-        return t < tick;
+    // distinct experts, hits and misses; lane owns experts [e0, e0 + epl)
+    const int epl = (E + WAVE - 1) / WAVE;
+    const int e0 = lane * epl, e1 = min(E, e0 + epl);
+    auto slot_of = [&](int e) {
+        const int sl = sh.tab[e];
+        return (sl >= 0 && sl < N) ? sl : -1;  // an entry outside the cache counts as absent
     };
-    uint32_t local = 0;
-    for (int s = tid; s < N; s += CL_THREADS) local += sh.ts[s] < tick ? 1u : 0u;
-    const uint32_t n_elig = block_sum_u32(local, sh.sc.red32);
-    const uint32_t n_vic = n_elig < static_cast<uint32_t>(K) ? n_elig : static_cast<uint32_t>(K);
-    if (n_vic > 0) {
-        uint64_t thr = ~0ull;
-        if (n_elig > n_vic) thr = radix_select(N, n_vic, key_of, &sh.sc);
-        for (int s = tid; s < N; s += CL_THREADS) {
-            uint64_t k;
-            if (key_of(s, &k) && k <= thr) {
-                const uint32_t at = atomicAdd(&sh.n_sel, 1u);
-                if (at < MAX_LIST) sh.sel_key[at] = k;
+    uint32_t cu = 0, ch = 0, cm = 0;
+    for (int e = e0; e < e1; ++e) {
+        if (!sh.mark[e]) continue;
+        ++cu;
+        if (slot_of(e) >= 0) ++ch;
+        else ++cm;
+    }
+    uint32_t n_uniq, n_hit, n_miss;
+    const uint32_t bu = wave_excl_scan(cu, &n_uniq);
+    const uint32_t bh = wave_excl_scan(ch, &n_hit);
+    const uint32_t bm = wave_excl_scan(cm, &n_miss);
+    {
+        uint32_t u = bu, h = bh, mi = bm;
+        for (int e = e0; e < e1; ++e) {
+            if (!sh.mark[e]) continue;
+            if (!evict_only) cp.uniq[u] = e;
+            sh.upos[e] = static_cast<int32_t>(u++);
+            const int sl = slot_of(e);
+            if (dedup_only) continue;
+            if (sl >= 0) {
+                if (!evict_only) {
+                    cp.hit_e[h] = e;
+                    cp.hit_s[h] = sl;
+                }
+                ++h;
+                if (!plan_only) {
+                    sh.ts[sl] = tick;  // recency moves on a router selection
+                    slot_ts[sl] = tick;
+                }
+            } else {
+                if (!evict_only) cp.miss[mi] = e;
+                sh.miss[mi++] = e;
             }
         }
-        __syncthreads();
-        for (uint32_t i = tid; i < n_vic; i += CL_THREADS) {
+    }
+    wave_lds_sync();
+
+    // the routed pairs of each distinct expert, grouped by u
+    if (with_plan) {
+        for (int i = lane; i < n_ids; i += WAVE) {
+            const int e = sh.ids[i];
+            sh.plocal[i] = (e >= 0 && e < E) ? atomicAdd(&sh.pcnt[sh.upos[e]], 1) : -1;
+        }
+        wave_lds_sync();
+        const int upl = (static_cast<int>(n_uniq) + WAVE - 1) / WAVE;
+        const int u0 = lane * upl, u1 = min(static_cast<int>(n_uniq), u0 + upl);
+        uint32_t c = 0, tot;
+        for (int u = u0; u < u1; ++u) c += sh.pcnt[u];
+        uint32_t b = wave_excl_scan(c, &tot);
+        for (int u = u0; u < u1; ++u) {
+            sh.pbeg[u] = static_cast<int32_t>(b);
+            b += sh.pcnt[u];
+        }
+        wave_lds_sync();
+        for (int i = lane; i < n_ids; i += WAVE) {
+            const int e = sh.ids[i];
+            if (e >= 0 && e < E) cp.pairs[sh.pbeg[sh.upos[e]] + sh.plocal[i]] = i;
+        }
+    }
+
+    if (dedup_only) {
+        if (lane < 6) cp.counts[lane] = lane == 0 ? static_cast<int32_t>(n_uniq) : 0;
+        if (with_plan)
+            for (int u = lane; u < static_cast<int>(n_uniq); u += WAVE)
+                reinterpret_cast<int4*>(cp.plan)[u] = make_int4(-1, 0, sh.pbeg[u], sh.pcnt[u]);
+        return;
+    }
+    if (plan_only) {
+        // hits are read from their slots, misses from the pool; the cache is
+        // updated later by the evict-only call
+        if (with_plan) {
+            for (int e = e0; e < e1; ++e) {
+                if (!sh.mark[e]) continue;
+                const int u = sh.upos[e];
+                reinterpret_cast<int4*>(cp.plan)[u] = make_int4(slot_of(e), 0, sh.pbeg[u], sh.pcnt[u]);
+            }
+        }
+        if (lane < 6) {
+            const uint32_t c3[3] = {n_uniq, n_hit, n_miss};
+            cp.counts[lane] = lane < 3 ? static_cast<int32_t>(c3[lane]) : 0;
+        }
+        return;
+    }
+
+    // ---- one scan of every slot's timestamp: the K oldest eligible slots -----
+    wave_lds_sync();   // hit stamps are in LDS
+    const int sbits = N > 1 ? 32 - __clz(N - 1) : 1;
+    const int spl = SPL > 0 ? SPL : (N + WAVE - 1) / WAVE;
+    const int s0 = lane * spl, s1 = min(N, s0 + spl);
+    // Victims: the n_vic smallest (ts << sbits | slot) keys among eligible slots.
+    // With 32-bit keys (tick << sbits fits) each lane holds its timestamps in
+    // registers; otherwise it reads them from LDS.
+    const bool narrow = (static_cast<uint64_t>(tick) << sbits) < (1ull << 32);
+    uint32_t n_elig = 0, n_vic = 0;
+    auto select = [&](auto key_zero, auto in_regs) {
+        using KT = decltype(key_zero);
+        constexpr bool REGS = decltype(in_regs)::value && SPL > 0;
+        constexpr int RL = REGS ? SPL : 1;
+        uint32_t tsr[RL];
+        if constexpr (REGS) {
+#pragma unroll
+            for (int j = 0; j < SPL; j += 4) {
+                if (s0 + j + 3 < N) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(&sh.ts[s0 + j]);
+                    tsr[j] = v.x; tsr[j + 1] = v.y; tsr[j + 2] = v.z; tsr[j + 3] = v.w;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) tsr[j + i] = s0 + j + i < N ? sh.ts[s0 + j + i] : ~0u;
+                }
+            }
+        }
+        // calls f(slot, ts) for each of this lane's slots
+        auto for_slots = [&](auto f) {
+            if constexpr (REGS) {
+#pragma unroll
+                for (int j = 0; j < SPL; ++j) f(s0 + j, tsr[j]);
+            } else {
+                for (int sl = s0; sl < s1; ++sl) f(sl, sh.ts[sl]);
+            }
+        };
+        uint32_t ce = 0;
+        for_slots([&](int sl, uint32_t t) { ce += (sl < N && t < tick) ? 1u : 0u; });
+        wave_excl_scan(ce, &n_elig);
+        n_vic = n_elig < static_cast<uint32_t>(K) ? n_elig : static_cast<uint32_t>(K);
+        if (n_vic == 0) return;
+        constexpr int KB = 8 * sizeof(KT);
+        auto key = [&](int sl, uint32_t t) { return (static_cast<KT>(t) << sbits) | static_cast<KT>(sl); };
+        KT thr = ~static_cast<KT>(0);
+        if (n_elig > n_vic) {
+            const uint64_t top = static_cast<uint64_t>(tick) << sbits;
+            const int bits = 64 - __clzll(static_cast<long long>(top));
+            KT prefix = 0, pmask = 0;
+            uint32_t remaining = n_vic;
+            for (int shift = ((bits - 1) / 8) * 8; shift >= 0; shift -= 8) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sh.hist[lane * 4 + i] = 0;
+                wave_lds_sync();
+                for_slots([&](int sl, uint32_t t) {
+                    const KT k = key(sl, t);
+                    if (sl < N && t < tick && (k & pmask) == prefix)
+                        atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
+                });
+                wave_lds_sync();
+                uint32_t c4[4], local = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    c4[i] = sh.hist[lane * 4 + i];
+                    local += c4[i];
+                }
+                uint32_t tot;
+                const uint32_t before = wave_excl_scan(local, &tot);
+                // the lane whose range of the histogram crosses `remaining`
+                const bool mine = before < remaining && remaining <= before + local;
+                uint32_t digit = 0, rem = 0;
+                if (mine) {
+                    uint32_t acc = before;
+                    for (int i = 0; i < 4; ++i) {
+                        if (acc + c4[i] >= remaining) {
+                            digit = lane * 4 + i;
+                            rem = remaining - acc;
+                            break;
+                        }
+                        acc += c4[i];
+                    }
+                }
+                const int src = __builtin_ctzll(__ballot(mine));
+                digit = __builtin_amdgcn_readlane(digit, src);
+                rem = __builtin_amdgcn_readlane(rem, src);
+                prefix |= static_cast<KT>(digit) << shift;
+                pmask |= static_cast<KT>(255) << shift;
+                remaining = rem;
+            }
+            thr = prefix;
+        }
+        static_assert(KB == 32 || KB == 64, "key width");
+        // collect the selected keys in slot order, then rank them by key
+        uint32_t cs = 0;
+        for_slots([&](int sl, uint32_t t) { cs += (sl < N && t < tick && key(sl, t) <= thr) ? 1u : 0u; });
+        uint32_t n_sel;
+        uint32_t at = wave_excl_scan(cs, &n_sel);
+        for_slots([&](int sl, uint32_t t) {
+            if (sl < N && t < tick && key(sl, t) <= thr) {
+                sh.sel_key[at] = static_cast<uint64_t>(key(sl, t));
+                sh.sel_owner[at] = own_lds ? sh.own[sl] : owner[sl];
+                ++at;
+            }
+        });
+    };
+    if (narrow)
+        select(uint32_t{0}, std::true_type{});
+    else
+        select(uint64_t{0}, std::false_type{});
+    if (n_vic > 0) {
+        wave_lds_sync();
+        for (uint32_t i = lane; i < n_vic; i += WAVE) {
             const uint64_t k = sh.sel_key[i];
             uint32_t r = 0;
             for (uint32_t j = 0; j < n_vic; ++j) r += sh.sel_key[j] < k ? 1u : 0u;
-            const int s = static_cast<int>(k & ((1ull << sbits) - 1));
-            sh.victims[r] = s;
-            cp.victims[r] = s;
+            const int sl = static_cast<int>(k & ((1ull << sbits) - 1));
+            sh.victims[r] = sl;
+            sh.vic_owner[r] = sh.sel_owner[i];
+            cp.victims[r] = sl;
         }
-        __syncthreads();
+        wave_lds_sync();
     }
 
     // ---- q split and slot update -------------------------------------------
     const int64_t q_raw = (2ll * cp.q_num * n_miss + cp.q_den) / (2ll * cp.q_den);
     const uint32_t q = static_cast<uint32_t>(q_raw < n_miss ? q_raw : n_miss);
     const uint32_t q_eff = q < n_vic ? q : n_vic;
-    for (uint32_t i = tid; i < q_eff; i += CL_THREADS) {
+    for (uint32_t i = lane; i < q_eff; i += WAVE) {
         const int v = sh.victims[i];
         const int ex = sh.miss[i];
-        const int old = owner[v];
+        const int old = sh.vic_owner[i];
         // evict; `old` is never one of this call's misses
         if (old >= 0 && old < table_len) table[old] = -1;
         table[layer * E + ex] = v;
@@ -338,19 +524,29 @@ __global__ void __launch_bounds__(CL_THREADS) classify_kernel(ClassifyParams cp)
         cp.fill_e[i] = ex;
         cp.fill_s[i] = v;
     }
-    for (uint32_t i = q_eff + tid; i < n_miss; i += CL_THREADS) cp.inplace[i - q_eff] = sh.miss[i];
-    if (with_plan && m) {
-        // where the FFN reads this expert from after the call, and whether it is filled now
-        const uint32_t p_miss = static_cast<uint32_t>((pos >> 42) & 0x1FFFFF);
-        const bool filled = is_miss && p_miss < q_eff;
-        const int final_slot = is_hit ? slot : (filled ? sh.victims[p_miss] : -1);
-        reinterpret_cast<int4*>(cp.plan)[my_u] =
-            make_int4(final_slot, filled ? 1 : 0, sh.pbeg[my_u], sh.pcnt[my_u]);
+    for (uint32_t i = q_eff + lane; i < n_miss; i += WAVE) cp.inplace[i - q_eff] = sh.miss[i];
+    if (with_plan) {
+        // where the FFN reads each expert from after the call, and whether it is filled now
+        uint32_t mi = bm;
+        for (int e = e0; e < e1; ++e) {
+            if (!sh.mark[e]) continue;
+            const int u = sh.upos[e];
+            const int sl = slot_of(e);
+            int final_slot = sl, filled = 0;
+            if (sl < 0) {
+                filled = mi < q_eff ? 1 : 0;
+                final_slot = filled ? sh.victims[mi] : -1;
+                ++mi;
+            }
+            reinterpret_cast<int4*>(cp.plan)[u] = make_int4(final_slot, filled, sh.pbeg[u], sh.pcnt[u]);
+        }
     }
-    if (tid == 0) {
-        cp.counts[0] = static_cast<int32_t>(n_uniq);
-        cp.counts[1] = static_cast<int32_t>(n_hit);
-        cp.counts[2] = static_cast<int32_t>(n_miss);
+    if (lane == 0) {
+        if (!evict_only) {
+            cp.counts[0] = static_cast<int32_t>(n_uniq);
+            cp.counts[1] = static_cast<int32_t>(n_hit);
+            cp.counts[2] = static_cast<int32_t>(n_miss);
+        }
         cp.counts[3] = static_cast<int32_t>(q_eff);
         cp.counts[4] = static_cast<int32_t>(n_miss - q_eff);
         cp.counts[5] = static_cast<int32_t>(n_vic);
@@ -400,7 +596,16 @@ rebuild_select_kernel(const int32_t* __restrict__ f_table, const int32_t* __rest
     // keep keys greater than the (n_occ - t_n)-th smallest occupied key
     uint64_t thr = 0;
     bool keep_all = n_occ <= static_cast<uint32_t>(t_n);
-    if (!keep_all) thr = radix_select(f_n, n_occ - t_n, key_of, &sh.sc);
+    if (!keep_all) {
+        uint64_t mx = 0;
+        for (int s = tid; s < f_n; s += CL_THREADS) {
+            uint64_t k;
+            if (key_of(s, &k)) mx = k > mx ? k : mx;
+        }
+        mx = block_max_u64(mx, sh.sc.red);
+        const int bits = mx ? 64 - __clzll(static_cast<long long>(mx)) : 1;
+        thr = radix_select(f_n, n_occ - t_n, bits, key_of, &sh.sc);
+    }
 
     // new slot = rank of the kept slot in ascending old-slot order; each thread
     // owns a contiguous run of old slots so the scan follows slot order
@@ -489,7 +694,7 @@ moe355_status check_cache(const moe355_cache* c) {
 moe355_status classify_call(const moe355_cache* c, int32_t layer, const int64_t* tick_dev,
                             int64_t tick, const int32_t* ids, int32_t n_ids,
                             const moe355_evict_policy* p, moe355_classify_out* out,
-                            const RouteArgs* route, hipStream_t stream) {
+                            const RouteArgs* route, ClassifyMode mode, hipStream_t stream) {
     moe355_status st = check_cache(c);
     if (st) return st;
     st = check_out(out, true, n_ids);
@@ -511,7 +716,7 @@ moe355_status classify_call(const moe355_cache* c, int32_t layer, const int64_t*
     MOE355_REQUIRE(out->capacity >= need, MOE355_ECAPACITY,
                    "classify_evict: list capacity %d < %d", out->capacity, need);
     ClassifyParams cp{};
-    cp.dedup_only = 0;
+    cp.mode = mode;
     cp.table = c->slot_table;
     cp.table_len = c->n_layers * c->n_experts;
     cp.owner = c->slot_owner;
@@ -548,7 +753,13 @@ moe355_status classify_call(const moe355_cache* c, int32_t layer, const int64_t*
     cp.counts = out->counts;
     cp.plan = out->plan;
     cp.pairs = out->pairs;
-    classify_kernel<<<1, CL_THREADS, 0, stream>>>(cp);
+    const int N = cp.N;
+    if (N <= 512) classify_kernel<1, 8><<<1, CL_THREADS, 0, stream>>>(cp);
+    else if (N <= 1024) classify_kernel<1, 16><<<1, CL_THREADS, 0, stream>>>(cp);
+    else if (N <= 2048) classify_kernel<2, 32><<<1, CL_THREADS, 0, stream>>>(cp);
+    else if (N <= 4096) classify_kernel<4, 0><<<1, CL_THREADS, 0, stream>>>(cp);
+    else if (N <= 8192) classify_kernel<8, 0><<<1, CL_THREADS, 0, stream>>>(cp);
+    else classify_kernel<0, 0><<<1, CL_THREADS, 0, stream>>>(cp);
     return check_launch("classify_evict");
 }
 
@@ -570,7 +781,7 @@ extern "C" moe355_status moe355_dedup(const int32_t* ids, int32_t n_ids, int32_t
     MOE355_REQUIRE(out->capacity >= need, MOE355_ECAPACITY, "dedup: capacity %d < %d",
                    out->capacity, need);
     ClassifyParams cp{};
-    cp.dedup_only = 1;
+    cp.mode = CLASSIFY_DEDUP;
     cp.E = n_experts;
     cp.ids = ids;
     cp.n_ids = n_ids;
@@ -579,7 +790,7 @@ extern "C" moe355_status moe355_dedup(const int32_t* ids, int32_t n_ids, int32_t
     cp.counts = out->counts;
     cp.plan = out->plan;
     cp.pairs = out->pairs;
-    classify_kernel<<<1, CL_THREADS, 0, stream>>>(cp);
+    classify_kernel<1, 8><<<1, CL_THREADS, 0, stream>>>(cp);
     return check_launch("dedup");
 }
 
@@ -587,12 +798,13 @@ extern "C" moe355_status moe355_classify_evict(const moe355_cache* c, int32_t la
                                                const int32_t* ids, int32_t n_ids,
                                                const moe355_evict_policy* p,
                                                moe355_classify_out* out, hipStream_t stream) {
-    return classify_call(c, layer, nullptr, tick, ids, n_ids, p, out, nullptr, stream);
+    return classify_call(c, layer, nullptr, tick, ids, n_ids, p, out, nullptr, CLASSIFY_FULL,
+                         stream);
 }
 
-extern "C" moe355_status moe355_cache_fill(const moe355_cache* c, const uint8_t* pool,
-                                           int32_t layer, const moe355_classify_out* out,
-                                           int32_t max_fill, hipStream_t stream) {
+namespace moe355 {
+moe355_status fill_call(const moe355_cache* c, const uint8_t* pool, int32_t layer,
+                        const moe355_classify_out* out, int32_t max_fill, hipStream_t stream) {
     moe355_status st = check_cache(c);
     if (st) return st;
     MOE355_REQUIRE(pool && c->slot_data && out && out->fill_expert && out->fill_slot && out->counts,
@@ -610,6 +822,13 @@ extern "C" moe355_status moe355_cache_fill(const moe355_cache* c, const uint8_t*
                                           out->fill_expert, out->fill_slot, out->counts,
                                           COPY_CHUNK);
     return check_launch("cache_fill");
+}
+}  // namespace moe355
+
+extern "C" moe355_status moe355_cache_fill(const moe355_cache* c, const uint8_t* pool,
+                                           int32_t layer, const moe355_classify_out* out,
+                                           int32_t max_fill, hipStream_t stream) {
+    return fill_call(c, pool, layer, out, max_fill, stream);
 }
 
 extern "C" moe355_status moe355_cache_rebuild(const moe355_cache* from, moe355_cache* to,

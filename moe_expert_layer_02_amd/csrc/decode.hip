@@ -33,7 +33,8 @@
 // Each block stages the call's plan (for each distinct expert: where its bytes
 // live, whether this call fills a cache slot with it, its routed pairs) in LDS
 // first, so every weight load is independent of the others, and each
-// wavefront keeps the next slab's loads in flight while it computes one.  With
+// wavefront keeps the loads of the next two or three slabs in flight while it
+// computes one.  With
 // fill-through on, an expert that this call fills into a cache slot is read
 // from the pool and the lanes that read its bytes also write them to the slot.
 #include "internal.h"
@@ -81,6 +82,7 @@ struct PlanLds {
     int4 plan[MAX_PLAN];
     int32_t uniq[MAX_PLAN];
     int32_t pairs[MAX_PLAN];
+    float w[MAX_PLAN];       // routing weight of each pair
     int32_t n_uniq;
 };
 
@@ -105,7 +107,10 @@ __device__ __forceinline__ void stage_plan(const DecodeParams& p, PlanLds& pl) {
         pl.plan[threadIdx.x] = reinterpret_cast<const int4*>(p.plan)[threadIdx.x];
         pl.uniq[threadIdx.x] = p.uniq[threadIdx.x];
     }
-    if (threadIdx.x < p.T * p.k) pl.pairs[threadIdx.x] = p.pairs[threadIdx.x];
+    if (threadIdx.x < p.T * p.k) {
+        pl.pairs[threadIdx.x] = p.pairs[threadIdx.x];
+        pl.w[threadIdx.x] = p.w[threadIdx.x];
+    }
     if (threadIdx.x == 0) pl.n_uniq = p.counts[0];
     __syncthreads();
 }
@@ -250,8 +255,8 @@ __device__ __forceinline__ void load_wslab(const DecodeParams& p, const uint8_t*
         const SlabOff o = slab_off<FMT>(row0 + 16 * t + ln, kdim, kb, gq);
         w.q[t] = ldg16(src + p.q_off[m] + o.q);
         w.sc[t] = ldg4(src + p.s_off[m] + o.s);
-        w.bi[t] = 0u;
-        if (FMT == MOE355_W_INT4_G64 && gq == 0) w.bi[t] = ldg4(src + p.b_off[m] + o.s);
+        // every lane loads (a broadcast within the row); only chunk-0 lanes use it
+        w.bi[t] = FMT == MOE355_W_INT4_G64 ? ldg4(src + p.b_off[m] + o.s) : 0u;
     }
 }
 
@@ -298,7 +303,13 @@ struct GuStage {
     uint4 x[4];
 };
 
-template <int FMT, int KW, int RT>
+// Position in a block's or wavefront's stream of stages: (item, token group, slab).
+struct Cursor {
+    int item, tg, s;
+    bool valid;
+};
+
+template <int FMT, int KW, int RT, int D>
 __global__ void __launch_bounds__(256) gate_up_kernel(DecodeParams p) {
     constexpr int RW = 4 / KW;
     __shared__ PlanLds pl;
@@ -324,24 +335,24 @@ __global__ void __launch_bounds__(256) gate_up_kernel(DecodeParams p) {
 
     // unit = (item, token group); stage = (unit, slab)
     auto tokens_of = [&](int item) { return pl.plan[item / tiles].w; };
+    // Loads are unconditional so that the compiler can count the ones still in
+    // flight: a cursor past the block's end re-reads its last item, and token
+    // columns with no pair read the expert's first token (their MFMA columns are
+    // never used).
     auto load = [&](GuStage<FMT, KW, RT>& st, int item, int tg, int s) {
-        const int u = item / tiles, tile = item - u * tiles;
+        const int it = min(item, i_end - 1);
+        const int u = it / tiles, tile = it - u * tiles;
         const ExpertRef ref = expert_ref(p, pl, u);
         const int row0 = tile * tile_rows + rw * RT * 16;
         const int kb = kbase + s * SLAB;
         load_wslab<FMT, RT>(p, ref.src, 0, row0, H, kb, ln, gq, st.g);
         load_wslab<FMT, RT>(p, ref.src, 1, row0, H, kb, ln, gq, st.u);
-        const int n = tg * TOK + ln;
         const int4 pr = pl.plan[u];
-        if (n < pr.w) {
-            const int t = pl.pairs[pr.z + n] / p.k;
-            const uint16_t* xs = p.x + static_cast<int64_t>(t) * H + kb + 32 * gq;
+        const int n = tg * TOK + ln;
+        const int t = pl.pairs[pr.z + (n < pr.w ? n : 0)] / p.k;
+        const uint16_t* xs = p.x + static_cast<int64_t>(t) * H + kb + 32 * gq;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) st.x[i] = ldg16(xs + 8 * i);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) st.x[i] = make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int i = 0; i < 4; ++i) st.x[i] = ldg16(xs + 8 * i);
     };
     f32x4 acc[2][RT];
     auto zero_acc = [&]() {
@@ -434,35 +445,39 @@ __global__ void __launch_bounds__(256) gate_up_kernel(DecodeParams p) {
     };
 
     zero_acc();
-    GuStage<FMT, KW, RT> sa, sb;
-    int item = i_beg, tg = 0, s = 0;
-    load(sa, item, tg, 0);
-    // advance (item, tg, s) to the next stage; false past the block's last item
-    auto next = [&](int& it, int& g, int& sl) -> bool {
-        if (++sl < NS) return true;
-        sl = 0;
-        if ((g + 1) * TOK < tokens_of(it)) {
-            ++g;
-            return true;
+    auto advance = [&](Cursor& c) {
+        if (!c.valid) return;
+        if (++c.s < NS) return;
+        c.s = 0;
+        if ((c.tg + 1) * TOK < tokens_of(c.item)) {
+            ++c.tg;
+            return;
         }
-        g = 0;
-        return ++it < i_end;
+        c.tg = 0;
+        c.valid = ++c.item < i_end;
     };
-    for (;;) {
-        int it2 = item, g2 = tg, s2 = s;
-        bool more = next(it2, g2, s2);
-        if (more) load(sb, it2, g2, s2);
-        compute(sa, item, tg, s);
-        if (s == NS - 1) epilogue(item, tg);
-        if (!more) break;
-        item = it2; tg = g2; s = s2;
-        it2 = item; g2 = tg; s2 = s;
-        more = next(it2, g2, s2);
-        if (more) load(sa, it2, g2, s2);
-        compute(sb, item, tg, s);
-        if (s == NS - 1) epilogue(item, tg);
-        if (!more) break;
-        item = it2; tg = g2; s = s2;
+    // D stages in a ring: the loads of the next D-1 stages stay in flight while
+    // one is computed
+    GuStage<FMT, KW, RT> st[D];
+    Cursor lc{i_beg, 0, 0, true}, cc = lc;
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) {
+        load(st[d], lc.item, lc.tg, lc.s);
+        advance(lc);
+    }
+    bool done = false;
+    while (!done) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (!done) {
+                load(st[(d + D - 1) % D], lc.item, lc.tg, lc.s);
+                advance(lc);
+                compute(st[d], cc.item, cc.tg, cc.s);
+                if (cc.s == NS - 1) epilogue(cc.item, cc.tg);
+                advance(cc);
+                done = !cc.valid;
+            }
+        }
     }
 }
 
@@ -474,7 +489,7 @@ struct DnStage {
     uint4 hh[4], hl[4];
 };
 
-template <int FMT, int RT>
+template <int FMT, int RT, int D>
 __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
     __shared__ PlanLds pl;
     const int lane = threadIdx.x & (WAVE - 1), ln = lane & 15, gq = lane >> 4;
@@ -491,26 +506,20 @@ __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
     if (i_beg >= i_end) return;
 
     auto tokens_of = [&](int item) { return pl.plan[item / tiles].w; };
+    // unconditional loads, as in gate/up
     auto load = [&](DnStage<FMT, RT>& st, int item, int tg, int s) {
-        const int u = item / tiles, tile = item - u * tiles;
+        const int it = min(item, i_end - 1);
+        const int u = it / tiles, tile = it - u * tiles;
         const ExpertRef ref = expert_ref(p, pl, u);
         const int kb = s * SLAB;
         load_wslab<FMT, RT>(p, ref.src, 2, tile * tile_rows, I, kb, ln, gq, st.w);
-        const int n = tg * TOK + ln;
         const int4 pr = pl.plan[u];
-        if (n < pr.w) {
-            const int64_t o = static_cast<int64_t>(pl.pairs[pr.z + n]) * I + kb + 32 * gq;
+        const int n = tg * TOK + ln;
+        const int64_t o = static_cast<int64_t>(pl.pairs[pr.z + (n < pr.w ? n : 0)]) * I + kb + 32 * gq;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                st.hh[i] = ldg16(p.h_hi + o + 8 * i);
-                st.hl[i] = ldg16(p.h_lo + o + 8 * i);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                st.hh[i] = make_uint4(0u, 0u, 0u, 0u);
-                st.hl[i] = make_uint4(0u, 0u, 0u, 0u);
-            }
+        for (int i = 0; i < 4; ++i) {
+            st.hh[i] = ldg16(p.h_hi + o + 8 * i);
+            st.hl[i] = ldg16(p.h_lo + o + 8 * i);
         }
     };
     f32x4 acc[RT];
@@ -544,7 +553,7 @@ __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
         const int n = tg * TOK + ln;
         if (n < pr.w) {
             const int pair = pl.pairs[pr.z + n];
-            const float wt = p.w[pair];
+            const float wt = pl.w[pair];
             float* o = p.out + static_cast<int64_t>(pair / p.k) * p.H + (item - u * tiles) * tile_rows;
 #pragma unroll
             for (int t = 0; t < RT; ++t)
@@ -555,34 +564,39 @@ __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
     };
 
     zero_acc();
-    DnStage<FMT, RT> sa, sb;
-    int item = i_beg, tg = 0, s = 0;
-    load(sa, item, tg, 0);
-    auto next = [&](int& it, int& g, int& sl) -> bool {
-        if (++sl < NS) return true;
-        sl = 0;
-        if ((g + 1) * TOK < tokens_of(it)) {
-            ++g;
-            return true;
+    auto advance = [&](Cursor& c) {
+        if (!c.valid) return;
+        if (++c.s < NS) return;
+        c.s = 0;
+        if ((c.tg + 1) * TOK < tokens_of(c.item)) {
+            ++c.tg;
+            return;
         }
-        g = 0;
-        return ++it < i_end;
+        c.tg = 0;
+        c.valid = ++c.item < i_end;
     };
-    for (;;) {
-        int it2 = item, g2 = tg, s2 = s;
-        bool more = next(it2, g2, s2);
-        if (more) load(sb, it2, g2, s2);
-        compute(sa, item, tg, s);
-        if (s == NS - 1) epilogue(item, tg);
-        if (!more) break;
-        item = it2; tg = g2; s = s2;
-        it2 = item; g2 = tg; s2 = s;
-        more = next(it2, g2, s2);
-        if (more) load(sa, it2, g2, s2);
-        compute(sb, item, tg, s);
-        if (s == NS - 1) epilogue(item, tg);
-        if (!more) break;
-        item = it2; tg = g2; s = s2;
+    // D stages in a ring: the loads of the next D-1 stages stay in flight while
+    // one is computed
+    DnStage<FMT, RT> st[D];
+    Cursor lc{i_beg, 0, 0, true}, cc = lc;
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) {
+        load(st[d], lc.item, lc.tg, lc.s);
+        advance(lc);
+    }
+    bool done = false;
+    while (!done) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (!done) {
+                load(st[(d + D - 1) % D], lc.item, lc.tg, lc.s);
+                advance(lc);
+                compute(st[d], cc.item, cc.tg, cc.s);
+                if (cc.s == NS - 1) epilogue(cc.item, cc.tg);
+                advance(cc);
+                done = !cc.valid;
+            }
+        }
     }
 }
 
@@ -608,13 +622,14 @@ template <int FMT, int KW>
 moe355_status launch_gate_up(const DecodeParams& p, int max_uniq, hipStream_t stream) {
     constexpr int RW = 4 / KW;
     const int cap = device_cus() * 2;   // two resident blocks per CU
-    // two row tiles per wavefront when that still leaves two items per block slot
+    // two row tiles per wavefront (three stages in flight) when that still leaves
+    // two items per block slot; else one tile with four stages in flight
     const int items2 = max_uniq * (p.I / (RW * 32));
     if (items2 >= 2 * cap && p.I % (RW * 32) == 0) {
-        gate_up_kernel<FMT, KW, 2><<<items2 < cap ? items2 : cap, 256, 0, stream>>>(p);
+        gate_up_kernel<FMT, KW, 2, 3><<<items2 < cap ? items2 : cap, 256, 0, stream>>>(p);
     } else {
         const int items1 = max_uniq * (p.I / (RW * 16));
-        gate_up_kernel<FMT, KW, 1><<<items1 < cap ? items1 : cap, 256, 0, stream>>>(p);
+        gate_up_kernel<FMT, KW, 1, 4><<<items1 < cap ? items1 : cap, 256, 0, stream>>>(p);
     }
     return check_launch("expert_ffn_decode gate_up");
 }
@@ -631,11 +646,11 @@ moe355_status launch_decode(const DecodeParams& p, int max_uniq, hipStream_t str
     const int items2 = max_uniq * (p.H / 32);
     if (items2 >= 2 * slots) {
         const int waves = items2 < slots ? items2 : slots;
-        down_kernel<FMT, 2><<<(waves + 3) / 4, 256, 0, stream>>>(p);
+        down_kernel<FMT, 2, 3><<<(waves + 3) / 4, 256, 0, stream>>>(p);
     } else {
         const int items1 = max_uniq * (p.H / 16);
         const int waves = items1 < slots ? items1 : slots;
-        down_kernel<FMT, 1><<<(waves + 3) / 4, 256, 0, stream>>>(p);
+        down_kernel<FMT, 1, 4><<<(waves + 3) / 4, 256, 0, stream>>>(p);
     }
     return check_launch("expert_ffn_decode down");
 }

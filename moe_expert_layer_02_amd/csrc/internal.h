@@ -37,10 +37,19 @@ struct RouteArgs {
     int32_t* ids_out;      // [T, k]
     float* w_out;          // [T, k]
 };
+// What one bookkeeping launch does.
+enum ClassifyMode {
+    CLASSIFY_FULL = 0,    // route?, dedup, hit/miss, victims, slot update, plan with fills
+    CLASSIFY_DEDUP = 1,   // dedup and plan only, no cache
+    CLASSIFY_PLAN = 2,    // route?, dedup, hit/miss and a plan reading misses from the pool
+    CLASSIFY_EVICT = 3,   // hit stamps, victims, slot update and fill lists for a planned call
+};
 moe355_status classify_call(const moe355_cache* c, int32_t layer, const int64_t* tick_dev,
                             int64_t tick, const int32_t* ids, int32_t n_ids,
                             const moe355_evict_policy* p, moe355_classify_out* out,
-                            const RouteArgs* route, hipStream_t stream);
+                            const RouteArgs* route, ClassifyMode mode, hipStream_t stream);
+moe355_status fill_call(const moe355_cache* c, const uint8_t* pool, int32_t layer,
+                        const moe355_classify_out* out, int32_t max_fill, hipStream_t stream);
 moe355_status decode_ffn(const moe355_layer_desc* d, const void* x_bf16, int32_t T,
                          const int32_t* topk_ids, const float* topk_w, const moe355_cache* cache,
                          const uint8_t* pool, int32_t layer, const moe355_classify_out* exp,

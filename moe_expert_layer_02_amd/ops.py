@@ -182,6 +182,30 @@ def decode_layer(desc, cache: DeviceCache, pool, layer: int, tick_base, tick_add
           "moe355_decode_layer")
 
 
+def route_plan(desc, cache: DeviceCache, layer: int, logits, topk_ids, topk_w,
+               lists: DeviceClassifyOut, stream=None):
+    """Route + dedup + hit/miss + FFN plan (hits from slots, misses from the pool)."""
+    _need(logits, torch.float32, "logits")
+    T = logits.shape[0]
+    check(load().moe355_route_plan(ctypes.byref(desc), ctypes.byref(cache.struct), layer,
+                                   _ptr(logits), T, _ptr(topk_ids), _ptr(topk_w),
+                                   ctypes.byref(lists.struct), _stream(stream)),
+          "moe355_route_plan")
+
+
+def evict_fill(desc, cache: DeviceCache, pool, layer: int, tick_base, tick_add: int, topk_ids,
+               policy: EvictPolicy, lists: DeviceClassifyOut, stream=None):
+    """Hit stamps, K LRU victims, slot update and the pool -> slot copy of a planned call."""
+    _need(topk_ids, torch.int32, "topk_ids")
+    if tick_base is not None:
+        _need(tick_base, torch.int64, "tick_base")
+    T = topk_ids.shape[0]
+    check(load().moe355_evict_fill(ctypes.byref(desc), ctypes.byref(cache.struct), _ptr(pool),
+                                   layer, _ptr(tick_base), tick_add, _ptr(topk_ids), T,
+                                   ctypes.byref(policy), ctypes.byref(lists.struct),
+                                   _stream(stream)), "moe355_evict_fill")
+
+
 def expert_ffn_prefill(desc, x_bf16, topk_ids, topk_w, layer_w, perm, offsets, out, ws,
                        stream=None):
     _need(x_bf16, torch.bfloat16, "x")

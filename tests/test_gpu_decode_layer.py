@@ -1,9 +1,11 @@
-"""The fused decode-layer call (route + classify_evict in one kernel, then the
-expert FFN with fill-through) on the GPU: every call of decode traces
-bit-exact against the oracle's simulator on the integer outputs, sampled layer
-outputs against the oracle, every cache slot holding its owner's pool bytes
-afterwards (the fill happened inside the FFN), and a whole decode step captured
-as a graph and replayed, each replay checked against eager execution."""
+"""The decode-layer calls on the GPU, in both orders the library offers:
+"fused" (route + classify_evict in one kernel, then the expert FFN with
+fill-through) and "split" (route + plan, the FFN reading misses from the pool,
+and the LRU update + fill copy on a second stream that the next layer waits
+for).  Every call of decode traces bit-exact against the oracle's simulator on
+the integer outputs, sampled layer outputs against the oracle, every cache slot
+holding its owner's pool bytes afterwards, and a whole decode step captured as
+a graph and replayed, each replay checked against eager execution."""
 import numpy as np
 import pytest
 
@@ -25,10 +27,12 @@ def _x_dev(bits):
 
 
 class LayerRunner:
-    def __init__(self, w, n_slots, pool):
+    def __init__(self, w, n_slots, pool, mode="fused"):
         import torch
         import moe_expert_layer_02_amd as m
-        self.m, self.torch, self.w = m, torch, w
+        self.m, self.torch, self.w, self.mode = m, torch, w, mode
+        self.side = torch.cuda.Stream()
+        self.planned = [torch.cuda.Event() for _ in range(w.n_layers)]
         self.desc = desc_of(w)
         self.S = wx.expert_bytes(w.wfmt, w.hidden, w.inter)
         self.cache = m.DeviceCache(n_slots, w.n_layers, w.n_experts, self.S)
@@ -53,10 +57,27 @@ class LayerRunner:
         self.tick.fill_(step * self.w.n_layers)
 
     def step(self):
+        m = self.m
+        main = self.torch.cuda.current_stream()
+        if self.mode == "split":
+            self.side.wait_stream(main)   # staged inputs
         for l in range(self.w.n_layers):
-            self.m.decode_layer(self.desc, self.cache, self.pool, l, self.tick, l + 1,
-                                self.logits[l], self.x[l], self.policy, self.ids[l], self.wt[l],
-                                self.lists[l], self.out[l], self.ws)
+            if self.mode == "fused":
+                m.decode_layer(self.desc, self.cache, self.pool, l, self.tick, l + 1,
+                               self.logits[l], self.x[l], self.policy, self.ids[l], self.wt[l],
+                               self.lists[l], self.out[l], self.ws)
+                continue
+            main.wait_stream(self.side)   # the previous layer's slot update and fill
+            m.route_plan(self.desc, self.cache, l, self.logits[l], self.ids[l], self.wt[l],
+                         self.lists[l])
+            self.planned[l].record(main)
+            m.expert_ffn_decode(self.desc, self.x[l], self.ids[l], self.wt[l], self.cache,
+                                self.pool, l, self.lists[l], self.out[l], self.ws)
+            self.side.wait_event(self.planned[l])
+            m.evict_fill(self.desc, self.cache, self.pool, l, self.tick, l + 1, self.ids[l],
+                         self.policy, self.lists[l], stream=self.side)
+        if self.mode == "split":
+            main.wait_stream(self.side)
 
 
 def _xs(w, s):
@@ -64,16 +85,17 @@ def _xs(w, s):
     return torch.stack([_x_dev(tr.decode_x(w, s, l)) for l in range(w.n_layers)])
 
 
+@pytest.mark.parametrize("mode", ["fused", "split"])
 @pytest.mark.parametrize("cid,steps,sample", [(2, 64, [(0, 3), (63, 39)]), (4, 24, [(5, 7)]),
                                               (5, 24, [(23, 0)])])
-def test_decode_layer_trace(cid, steps, sample):
+def test_decode_layer_trace(cid, steps, sample, mode):
     import torch
     from workloads import gpu as wg
     w = C.ALL[cid]
-    say(f"decode_layer trace {w.name}: {steps} steps")
+    say(f"decode_layer trace {w.name} ({mode}): {steps} steps")
     trace = tr.DecodeTrace(w, steps)
     pool = wg.make_pool(w)
-    run = LayerRunner(w, w.n_slots, pool)
+    run = LayerRunner(w, w.n_slots, pool, mode)
     sim = ocache.CacheSim(w.n_slots, w.n_layers, w.n_experts)
     src = BlobSource(w)
     for s in range(steps):
@@ -109,7 +131,8 @@ def test_decode_layer_trace(cid, steps, sample):
     say(f"{w.name}: {steps * w.n_layers} calls bit-exact, {len(occ)} slots hold their pool bytes")
 
 
-def test_decode_step_graph_replay_matches_eager():
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_decode_step_graph_replay_matches_eager(mode):
     import torch
     from workloads import gpu as wg
     w = C.QWEN_DECODE
@@ -118,13 +141,13 @@ def test_decode_step_graph_replay_matches_eager():
     pool = wg.make_pool(w)
     # one eager step on a throwaway cache, so no kernel is launched for the
     # first time (occupancy query) while the graph is being captured
-    warm = LayerRunner(w, w.n_slots, pool)
+    warm = LayerRunner(w, w.n_slots, pool, mode)
     warm.stage(0, trace.logits[0], _xs(w, 0))
     warm.step()
     torch.cuda.synchronize()
     del warm
-    eager = LayerRunner(w, w.n_slots, pool)
-    graphed = LayerRunner(w, w.n_slots, pool)
+    eager = LayerRunner(w, w.n_slots, pool, mode)
+    graphed = LayerRunner(w, w.n_slots, pool, mode)
     graphed.stage(0, trace.logits[0], _xs(w, 0))
     torch.cuda.synchronize()
     snap = [t.clone() for t in (graphed.cache.table, graphed.cache.owner, graphed.cache.ts)]
@@ -148,4 +171,4 @@ def test_decode_step_graph_replay_matches_eager():
         torch.testing.assert_close(graphed.out, eager.out, rtol=1e-6, atol=1e-5)
         assert torch.equal(eager.cache.table, graphed.cache.table), s
         assert torch.equal(eager.cache.ts, graphed.cache.ts), s
-        say(f"graph replay {s} matches eager")
+        say(f"graph replay {s} ({mode}) matches eager")
