@@ -60,78 +60,6 @@ struct PrefillParams {
     float* out;
 };
 
-__device__ __forceinline__ f32x16 mfma(uint4 a, uint4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    bf16x2 v;
-    v.x = static_cast<__bf16>(lo);
-    v.y = static_cast<__bf16>(hi);
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-// 8 consecutive fp32 values as hi and lo bf16 parts (v = hi + lo to ~16 bits).
-__device__ __forceinline__ void split8(const float* v, uint4& hi, uint4& lo) {
-    float h[8], l[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        h[i] = static_cast<float>(static_cast<__bf16>(v[i]));
-        l[i] = v[i] - h[i];
-    }
-    hi = make_uint4(pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3]), pack_bf16(h[4], h[5]),
-                    pack_bf16(h[6], h[7]));
-    lo = make_uint4(pack_bf16(l[0], l[1]), pack_bf16(l[2], l[3]), pack_bf16(l[4], l[5]),
-                    pack_bf16(l[6], l[7]));
-}
-
-// 32 int4 nibbles (16 bytes, element 2c = low nibble of byte c) -> 32 exact bf16.
-__device__ __forceinline__ void nibbles_to_bf16(uint4 q, uint4 out[4]) {
-    const uint32_t d[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = d[i] & 0x0F0F0F0Fu, hi = (d[i] >> 4) & 0x0F0F0F0Fu;
-        float f[8];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            f[2 * b] = static_cast<float>((lo >> (8 * b)) & 0xFFu);
-            f[2 * b + 1] = static_cast<float>((hi >> (8 * b)) & 0xFFu);
-        }
-        // small integers are exact in bf16: the top half of the fp32 pattern
-        out[i] = make_uint4(
-            (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u),
-            (__float_as_uint(f[2]) >> 16) | (__float_as_uint(f[3]) & 0xFFFF0000u),
-            (__float_as_uint(f[4]) >> 16) | (__float_as_uint(f[5]) & 0xFFFF0000u),
-            (__float_as_uint(f[6]) >> 16) | (__float_as_uint(f[7]) & 0xFFFF0000u));
-    }
-}
-
-// 32 e2m1 codes (one MX block) times 2^(e-127) -> 32 exact bf16.
-__device__ __forceinline__ void fp4_to_bf16(uint4 q, uint32_t e, uint4 out[4]) {
-    const float sc = e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);
-    const uint32_t d[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        out[i] = make_uint4(
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], sc, 0)),
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], sc, 1)),
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], sc, 2)),
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], sc, 3)));
-    }
-}
-
-__device__ __forceinline__ float bf16_sum8(uint4 v) {
-    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s += __uint_as_float(d[i] << 16) + __uint_as_float(d[i] & 0xFFFF0000u);
-    return s;
-}
-
-// LDS tile of 128 rows x 64 bf16, 16-byte chunk c of row r at (c ^ (r & 7)).
-__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7)); }
-
 // Persistent tile loop: the work of a call split into NXCD contiguous ranges.
 struct TileRange {
     int begin, end, step;
@@ -178,12 +106,8 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Shared pieces of the two GEMMs.  Block tile: 128 pair rows x 256 weight rows,
-// K staged 64 at a time in double-buffered, XOR-swizzled LDS (one barrier per
-// stage); wavefront (wm, wn) of the 2 x 2 grid computes 64 x 128 of it with 2 x 4
-// MFMA 32x32 tiles.
+// Shared pieces of the two GEMMs.
 
-constexpr int BN = 256;     // weight rows per tile
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -238,50 +162,6 @@ __device__ __forceinline__ float f16x8_sum(uint4 v, float s) {
     s = __builtin_amdgcn_fdot2(as_h2(v.z), one, s, false);
     s = __builtin_amdgcn_fdot2(as_h2(v.w), one, s, false);
     return s;
-}
-
-// One staging thread's weight row for one stage: 64 codes, its scale(s).
-struct WRow {
-    uint4 q[2];
-    uint32_t sc;   // int4: bf16 scale of the group; MXFP4: the two e8m0 bytes
-};
-
-template <int FMT>
-__device__ __forceinline__ WRow load_wrow(const uint8_t* W, const PrefillParams& p, int m,
-                                          int row, int kdim, int kk) {
-    WRow r;
-    const uint8_t* q = W + p.q_off[m] + static_cast<int64_t>(row) * (kdim / 2) + kk * 32;
-    r.q[0] = reinterpret_cast<const uint4*>(q)[0];
-    r.q[1] = reinterpret_cast<const uint4*>(q)[1];
-    if (FMT == MOE355_W_INT4_G64)
-        r.sc = reinterpret_cast<const uint16_t*>(W + p.s_off[m])[static_cast<int64_t>(row) * (kdim / 64) + kk];
-    else
-        r.sc = reinterpret_cast<const uint16_t*>(W + p.s_off[m] + static_cast<int64_t>(row) * (kdim / 32))[kk];
-    return r;
-}
-
-// Dequantise one staged row into 8 LDS chunks (exact values: f16 for int4, bf16 for MXFP4).
-template <int FMT>
-__device__ __forceinline__ void store_wrow(uint4* Bs, int r, const WRow& w) {
-    const uint32_t d[8] = {w.q[0].x, w.q[0].y, w.q[0].z, w.q[0].w,
-                           w.q[1].x, w.q[1].y, w.q[1].z, w.q[1].w};
-    if (FMT == MOE355_W_INT4_G64) {
-        const _Float16 sh = static_cast<_Float16>(__uint_as_float(w.sc << 16));
-        const half2v s2 = {sh, sh};
-#pragma unroll
-        for (int c = 0; c < 8; ++c) Bs[swz(r, c)] = int4_dword_f16(d[c], s2);
-    } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const uint32_t e = (w.sc >> (8 * (c >> 2))) & 0xFFu;   // chunks 0-3: block 0
-            const float sc = e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);
-            Bs[swz(r, c)] = make_uint4(
-                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[c], sc, 0)),
-                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[c], sc, 1)),
-                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[c], sc, 2)),
-                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[c], sc, 3)));
-        }
-    }
 }
 
 // The bias MFMA operands for 8 groups [g0, g0+8): b' = b + 8 s of weight row n
@@ -355,43 +235,79 @@ __global__ void __launch_bounds__(256) x16_kernel(const uint16_t* __restrict__ x
 }
 
 // ---------------------------------------------------------------------------
-// The GEMM pipeline shared by gate/up and down.  A (activation rows) travels
-// global -> LDS by direct loads into a ring of PD stages, in the swizzled layout
-// (lane i of a load lands at +16 i, so each lane fetches the chunk that belongs
-// there); B (weight rows) travels global -> registers, PD stages ahead, straight
-// in MFMA operand order, and is dequantised just before its MFMAs.  Wavefront w
-// computes all 128 rows x 64 weight rows (two 32-wide column tiles).  Within a
-// 64-wide stage, lane half hh holds inputs [32 hh, 32 hh + 32) and MFMA step s
+// The GEMM pipeline shared by gate/up and down.  Both operands travel global ->
+// LDS by direct loads (global_load_lds: lane i of a load lands 16 i bytes, or 4 i
+// for a dword load, past the LDS address in M0) into a ring of PD stage slots,
+// PD - 1 stages ahead of the MFMAs; one barrier per stage.
+//   A (activation rows): 128 rows x 64 inputs; 16-byte chunk c of row r sits at
+//     chunk (c ^ (r & 7)) of the row, so each lane fetches the chunk that belongs
+//     where it lands and the MFMA reads are free of bank conflicts.
+//   B (weight rows): per wavefront 2 column tiles x 64 lanes x 16 bytes of codes
+//     in MFMA operand order, then one dword per lane and tile holding its scale.
+// Within a stage, lane half hh holds inputs [32 hh, 32 hh + 32) and MFMA step s
 // takes inputs 32 hh + 8 s + [0, 8) from both operands.
+//
+// The loads are issued from inline assembly.  The compiler's wait-count pass
+// cannot tell the ring slots apart, so for its own form of these loads it waits
+// for every one in flight before the first LDS read of a stage, which turns the
+// ring into a fully serialised load -> compute sequence.  Hidden from it, the
+// only waits on them are the explicit per-stage ones below (vector-memory
+// operations of one wavefront complete in issue order, so "at most n in flight"
+// means all but the last n loads have landed).
 
-constexpr int PD = 3;        // stages in flight
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-__device__ __forceinline__ lds_ptr_t to_lds(const void* q) {
-    return (lds_ptr_t)(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(q)));
+// A wavefront-uniform pointer held in scalar registers.
+__device__ __forceinline__ const void* uniform_ptr(const void* q) {
+    const uint64_t v = reinterpret_cast<uint64_t>(q);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima).
+// Direct loads of base + voff (32-bit byte offset, per lane) into LDS at lds;
+// base and lds are wavefront-uniform.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :: "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+
+// Wait until at most N of this wavefront's loads are in flight and its LDS reads
+// are done, then meet the other wavefronts.
 template <int N>
-__device__ __forceinline__ void wait_vm() {
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+// The same with N = OPS * min(R, rem) for a runtime rem >= 0.
+template <int OPS, int R>
+__device__ __forceinline__ void stage_wait(int rem) {
+    if constexpr (R == 0) {
+        stage_barrier<0>();
+    } else {
+        if (rem >= R) stage_barrier<R * OPS>();
+        else stage_wait<OPS, R - 1>(rem);
+    }
 }
 
-// One stage of one lane's weight rows: 16 bytes of codes per column tile and its scale.
-struct BRaw {
-    uint4 q[2];
-    uint32_t sc[2];   // int4: bf16 scale of the group; MXFP4: e8m0 of this lane's 32 inputs
-};
+__device__ __forceinline__ uint32_t lds_addr(const void* q) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(q));
+}
 
-// B operand of MFMA step s for one column tile.
+// B operand of MFMA step s from one lane's 16 code bytes; sc is the lane's scale
+// dword (int4: two bf16 group scales, kk odd takes the high one; MXFP4: four e8m0
+// bytes, byte 2 (kk & 1) + hh is this lane's).
 template <int FMT>
-__device__ __forceinline__ uint4 b_operand(const uint4& q, uint32_t sc, int s) {
+__device__ __forceinline__ uint4 b_operand(const uint4& q, uint32_t sc, int kk, int hh, int s) {
     const uint32_t d = s == 0 ? q.x : s == 1 ? q.y : s == 2 ? q.z : q.w;
     if (FMT == MOE355_W_INT4_G64) {
-        const _Float16 sh = static_cast<_Float16>(__uint_as_float(sc << 16));
+        const uint32_t b = (kk & 1) ? (sc & 0xFFFF0000u) : (sc << 16);
+        const _Float16 sh = static_cast<_Float16>(__uint_as_float(b));
         return int4_dword_f16(d, half2v{sh, sh});
     }
-    const float scale = sc ? __uint_as_float(sc << 23) : __uint_as_float(0x00400000u);
+    const uint32_t e = (sc >> (8 * (2 * (kk & 1) + hh))) & 0xFFu;
+    const float scale = e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);
     return make_uint4(
         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 0)),
         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 1)),
@@ -405,35 +321,39 @@ __device__ __forceinline__ uint4 a_operand(const uint4* A, int mt, int ln, int h
     return A[r * 8 + (c ^ (r & 7))];
 }
 
-// Weight-row pointers of one lane for matrix m, row n, reduction length kdim.
-template <int FMT>
-struct BRow {
-    const uint8_t* q;
-    const uint8_t* s;
-    __device__ void init(const uint8_t* W, const PrefillParams& p, int m, int n, int kdim, int hh) {
-        q = W + p.q_off[m] + static_cast<int64_t>(n) * (kdim / 2) + hh * 16;
-        s = FMT == MOE355_W_INT4_G64 ? W + p.s_off[m] + static_cast<int64_t>(n) * (kdim / 32)
-                                     : W + p.s_off[m] + static_cast<int64_t>(n) * (kdim / 32) + hh;
-    }
-    __device__ void load(int kk, uint4* qv, uint32_t* sc) const {
-        *qv = *reinterpret_cast<const uint4*>(q + kk * 32);
-        *sc = FMT == MOE355_W_INT4_G64 ? reinterpret_cast<const uint16_t*>(s)[kk] : s[2 * kk];
-    }
-};
+// Stage slot layouts (bytes).  gate/up: A = 128 rows x 64 inputs; B codes
+// [wavefront][4 column tiles][64 lanes] x 16 bytes; scales [wavefront][2][64]
+// dwords, load j holding the scale dwords of the wavefront's weight rows
+// 64 j + [0, 64), so column tile c finds its row ln at 32 (c & 1) + ln of load c / 2.
+constexpr int GU_A = 0, GU_B = 16384, GU_S = 32768, GU_SLOT = 34816, GU_PD = 4;
+// down: A = hi and lo parts of 128 rows x 64 inputs of h; B as above.
+constexpr int DN_AH = 0, DN_AL = 16384, DN_B = 32768, DN_S = 49152, DN_SLOT = 51200, DN_PD = 3;
+constexpr int GU_FEAT = 256;   // features per gate/up tile: 64 per wavefront
+constexpr int DN_COLS = 512;   // output columns per down tile: 128 per wavefront
+
+// The scale dword of column tile c for this lane, from a slot's scale region.
+__device__ __forceinline__ uint32_t tile_scale(const uint32_t* S, int wv, int c, int ln) {
+    return S[(2 * wv + (c >> 1)) * 64 + 32 * (c & 1) + ln];
+}
 
 // ---------------------------------------------------------------------------
-// gate/up: A = the tile's 128 gathered token rows (int4: the f16 copy of x),
-// B = gate and up rows of features [f0 + 32 w, +32) for wavefront w.  Writes
-// h = silu(g) * u as a hi/lo 16-bit pair, and for int4 the group sums of h.
+// gate/up: A = the tile's 128 gathered token rows (int4: the f16 copy of x); B =
+// for wavefront w the gate rows (column tiles 0, 1) and up rows (tiles 2, 3) of
+// features fw + [0, 64), fw = f0 + 64 w.  The MFMAs take the weights as their
+// first operand, so an accumulator holds 32 features x 32 tokens and a lane holds
+// runs of 4 consecutive features of one token: h = silu(g) * u leaves as 8-byte
+// stores straight from registers (hi and lo 16-bit parts), and for int4 the
+// group sums of h need one exchange between the lane halves.
 template <int FMT>
 __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
+    constexpr int PD = GU_PD, D = PD - 1, OPS = 10;   // loads per stage per wavefront
     extern __shared__ uint4 smem[];
-    uint4* ring = smem;                                           // [PD][128 x 8 chunks]
-    int32_t* rtok = reinterpret_cast<int32_t*>(smem + PD * 1024); // token of each tile row
-    float* part = reinterpret_cast<float*>(rtok + BM);            // [4][64] h sums (int4)
-    const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
-    const int ln = lane & 31, hh = lane >> 5;
-    const int H = p.H, G = H / 64, KS = H / BK;
+    uint8_t* ring = reinterpret_cast<uint8_t*>(smem);                  // [PD][GU_SLOT]
+    int32_t* rtok = reinterpret_cast<int32_t*>(ring + PD * GU_SLOT);   // token of each tile row
+    const int tid = threadIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / WAVE);
+    const int H = p.H, I = p.I, G = H / 64, KS = H / BK;
+    const uint32_t ring_lds = lds_addr(ring);
 
     {   // zero the layer output for the down kernel's atomics
         const int64_t n = static_cast<int64_t>(p.T) * H;
@@ -442,178 +362,235 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
             p.out[i] = 0.0f;
     }
 
-    const int FX = p.I / 128;
+    const int FX = (I + GU_FEAT - 1) / GU_FEAT;
     const TileRange tr = tile_range(*p.n_tiles * FX);
-    const uint16_t* xs = FMT == MOE355_W_INT4_G64 ? p.xf : p.x;
+    const void* xs = uniform_ptr(FMT == MOE355_W_INT4_G64 ? p.xf : p.x);
     for (int t = tr.begin; t < tr.end; t += tr.step) {
-        const int y = t / FX, f0 = (t - y * FX) * 128;
+        const int y = t / FX;
         const int e = p.tile_e[y], m0 = p.tile_m0[y];
         const int pbase = p.offsets[e] + m0;
         const int rows = min(BM, p.offsets[e + 1] - pbase);
-        const uint8_t* W = p.W + static_cast<int64_t>(e) * p.S;
+        const void* W = uniform_ptr(p.W + static_cast<int64_t>(e) * p.S);
+        const int fw = (t - y * FX) * GU_FEAT + 64 * wv;
+        // The lane index is made opaque once per tile so that the compiler
+        // recomputes lane-derived addresses here instead of hoisting dozens of
+        // them out of the tile loop (they would spill, and every reload of a
+        // spill waits for all memory operations in flight).
+        int lane = tid & (WAVE - 1);
+        asm volatile("" : "+v"(lane));
+        const int ln = lane & 31, hh = lane >> 5;
+        const bool live = fw < I;            // the last tile of a small I may leave wavefronts idle
+        const int fr = live ? fw : 0;        // (they compute on row 0 and store nothing)
         __syncthreads();   // the previous tile is done with the LDS
         // rows past the bucket re-read its first row (their outputs are dropped)
         if (tid < BM) rtok[tid] = p.perm[pbase + (tid < rows ? tid : 0)] / p.k;
         __syncthreads();
-        int aoff[4];   // this lane's direct-load sources: 4 blocks of 8 rows of the tile
+        uint32_t aoff[4];   // this lane's A sources: 4 blocks of 8 rows of the tile
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 8 * (4 * wv + j) + lane / 8, c = (lane % 8) ^ (lane / 8);
-            aoff[j] = rtok[r] * H + c * 8;
+            aoff[j] = static_cast<uint32_t>(rtok[r]) * static_cast<uint32_t>(2 * H) + c * 16;
         }
-        BRow<FMT> brow[2];
-        brow[0].init(W, p, 0, f0 + 32 * wv + ln, H, hh);   // gate
-        brow[1].init(W, p, 1, f0 + 32 * wv + ln, H, hh);   // up
+        uint32_t bq[4], bsc[2];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            bq[c] = static_cast<uint32_t>(p.q_off[c >> 1] + static_cast<int64_t>(fr + 32 * (c & 1) + ln) * (H / 2) + hh * 16);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            bsc[j] = static_cast<uint32_t>(p.s_off[j] + static_cast<int64_t>(fr + lane) * (H / 32));
 
-        f32x16 R[4][2];
+        f32x16 R[4][4];   // [column tile][row tile]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) R[i][0] = R[i][1] = f32x16{};
-        BRaw braw[PD];
-        auto issue = [&](int kk, int slot, BRaw& b) {
-            uint4* dst = ring + slot * 1024 + 4 * wv * 64;
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                __builtin_amdgcn_global_load_lds(xs + aoff[j] + kk * BK, to_lds(dst + j * 64), 16, 0, 0);
-            brow[0].load(kk, &b.q[0], &b.sc[0]);
-            brow[1].load(kk, &b.q[1], &b.sc[1]);
+            for (int i = 0; i < 4; ++i) R[c][i] = f32x16{};
+        auto issue = [&](int kk, int slot) {
+            const uint32_t sl = ring_lds + slot * GU_SLOT;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dma16(xs, aoff[j] + kk * 128, sl + GU_A + (4 * wv + j) * 1024);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) dma16(W, bq[c] + kk * 32, sl + GU_B + (4 * wv + c) * 1024);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) dma4(W, bsc[j] + (kk >> 1) * 4, sl + GU_S + (2 * wv + j) * 256);
         };
-        auto compute = [&](int slot, const BRaw& b) {
-            const uint4* A = ring + slot * 1024;
+        auto compute = [&](int kk, int slot) {
+            const uint8_t* sp = ring + slot * GU_SLOT;
+            const uint4* A = reinterpret_cast<const uint4*>(sp + GU_A);
+            const uint4* Bq = reinterpret_cast<const uint4*>(sp + GU_B) + 4 * wv * 64 + lane;
+            const uint32_t* S = reinterpret_cast<const uint32_t*>(sp + GU_S);
+            uint4 q[4];
+            uint32_t sc[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                q[c] = Bq[c * 64];
+                sc[c] = tile_scale(S, wv, c, ln);
+            }
+            // A fragments are read one MFMA step ahead of their use: with one
+            // wavefront per SIMD nothing else hides the LDS latency
+            uint4 a[2][4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) a[0][mt] = a_operand(A, mt, ln, hh, 0);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const uint4 b0 = b_operand<FMT>(b.q[0], b.sc[0], s);
-                const uint4 b1 = b_operand<FMT>(b.q[1], b.sc[1], s);
+                if (s + 1 < 4) {
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    const uint4 a = a_operand(A, mt, ln, hh, s);
-                    R[mt][0] = mma<FMT>(a, b0, R[mt][0]);
-                    R[mt][1] = mma<FMT>(a, b1, R[mt][1]);
+                    for (int mt = 0; mt < 4; ++mt) a[(s + 1) & 1][mt] = a_operand(A, mt, ln, hh, s + 1);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint4 b = b_operand<FMT>(q[c], sc[c], kk, hh, s);
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) R[c][mt] = mma<FMT>(b, a[s & 1][mt], R[c][mt]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
-        issue(0, 0, braw[0]);
-        if (KS > 1) issue(1, 1, braw[1]);
-        for (int kb = 0; kb < KS; kb += PD) {
 #pragma unroll
-            for (int d = 0; d < PD; ++d) {
-                const int kk = kb + d;
-                if (kk < KS) {
-                    // this stage's loads are done once only the next stage's 8 remain
-                    if (kk + 1 < KS) wait_vm<8>();
-                    else wait_vm<0>();
-                    __syncthreads();
-                    if (kk + 2 < KS) issue(kk + 2, (d + 2) % PD, braw[(d + 2) % PD]);
-                    compute(d, braw[d]);
-                }
-            }
+        for (int kk = 0; kk < D; ++kk)
+            if (kk < KS) issue(kk, kk);
+        int slot = 0;
+#pragma nounroll
+        for (int kk = 0; kk < KS; ++kk) {
+            stage_wait<OPS, D - 1>(KS - 1 - kk);   // stage kk has landed everywhere
+            const int next = slot == 0 ? PD - 1 : slot - 1;   // (slot + D) % PD: the slot read last stage
+            if (kk + D < KS) issue(kk + D, next);
+            compute(kk, slot);
+            slot = slot == PD - 1 ? 0 : slot + 1;
         }
 
         if (FMT == MOE355_W_INT4_G64) {
-            // bias: R += sum_g xsum[m, g] * (b + 8 s)[n, g], both factors as f16 hi + lo
+            // bias: R += sum_g (b + 8 s)[n, g] * xsum[m, g], both factors as f16 hi + lo
             for (int g0 = 0; g0 < G; g0 += 16) {
                 const int gl = g0 + 8 * hh;
-                uint4 bh[2], bl[2];
-                bias_b(W, p, 0, f0 + 32 * wv + ln, G, gl, &bh[0], &bl[0]);
-                bias_b(W, p, 1, f0 + 32 * wv + ln, G, gl, &bh[1], &bl[1]);
+                uint4 bh[4], bl[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) bias_b(static_cast<const uint8_t*>(W), p, c >> 1, fr + 32 * (c & 1) + ln, G, gl, &bh[c], &bl[c]);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     uint4 xh, xl;
                     bias_a(p.xsum + static_cast<int64_t>(rtok[mt * 32 + ln]) * G, G, gl, &xh, &xl);
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) {
-                        R[mt][ct] = mma<FMT>(xh, bh[ct], R[mt][ct]);
-                        R[mt][ct] = mma<FMT>(xl, bh[ct], R[mt][ct]);
-                        R[mt][ct] = mma<FMT>(xh, bl[ct], R[mt][ct]);
+                    for (int c = 0; c < 4; ++c) {
+                        R[c][mt] = mma<FMT>(bh[c], xh, R[c][mt]);
+                        R[c][mt] = mma<FMT>(bh[c], xl, R[c][mt]);
+                        R[c][mt] = mma<FMT>(bl[c], xh, R[c][mt]);
                     }
                 }
             }
         }
 
-        // h = silu(g) * u as hi + lo 16-bit values, 64 rows at a time through the
-        // ring (each wavefront its own 32 columns), stored as 16-byte row pieces
-        __syncthreads();   // every wavefront is done reading the ring
-        uint16_t* th = reinterpret_cast<uint16_t*>(ring) + wv * (2 * 64 * 32);   // [64][32] hi
-        uint16_t* tl = th + 64 * 32;                                              // lo
-        // int4: the down GEMM's operand order inside blocks of 8 columns
-        const int col = FMT == MOE355_W_INT4_G64 ? (ln & ~7) + 2 * (ln & 3) + ((ln >> 2) & 1) : ln;
+        // h = silu(g) * u.  Lane (ln, hh) holds, for token row 32 mt + ln, features
+        // fw + 32 ft + 8 q + 4 hh + [0, 4) in R[ft][mt][4 q + 0..3] (g) and R[2 + ft] (u).
+        // int4 stores each block of 8 features in the down GEMM's operand order
+        // (0, 4, 1, 5, 2, 6, 3, 7): lane half 0 writes positions 0-3 = features
+        // 0, 4, 1, 5 and half 1 positions 4-7 = features 2, 6, 3, 7, after trading
+        // features 2, 3 (half 0) for 4, 5 (half 1).
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
+        for (int mt = 0; mt < 4; ++mt) {
+            const int r = mt * 32 + ln;
+            const bool keep = live && r < rows;
+            const int64_t row = static_cast<int64_t>(pbase + r) * I;
+            float gsum = 0.0f;
 #pragma unroll
-            for (int mq = 0; mq < 2; ++mq) {
-                const int mt = 2 * half + mq;
+            for (int ft = 0; ft < 2; ++ft) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int rl = mq * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-                    const float g = R[mt][0][i], u = R[mt][1][i];
-                    const float hv = g / (1.0f + __expf(-g)) * u;
-                    uint16_t hi, lo;
-                    if (FMT == MOE355_W_INT4_G64) {
-                        const _Float16 a = static_cast<_Float16>(hv);
-                        hi = __builtin_bit_cast(uint16_t, a);
-                        lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(hv - static_cast<float>(a)));
-                    } else {
-                        const __bf16 a = static_cast<__bf16>(hv);
-                        hi = __builtin_bit_cast(uint16_t, a);
-                        lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(hv - static_cast<float>(a)));
+                for (int q = 0; q < 4; ++q) {
+                    uint32_t hw[2], lw[2];   // this lane's 4 values as packed hi and lo pairs
+                    uint16_t hi[4], lo[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float g = R[ft][mt][4 * q + j], u = R[2 + ft][mt][4 * q + j];
+                        const float hv = g / (1.0f + __expf(-g)) * u;
+                        if (FMT == MOE355_W_INT4_G64) {
+                            const _Float16 x1 = static_cast<_Float16>(hv);
+                            const _Float16 x2 = static_cast<_Float16>(hv - static_cast<float>(x1));
+                            hi[j] = __builtin_bit_cast(uint16_t, x1);
+                            lo[j] = __builtin_bit_cast(uint16_t, x2);
+                            gsum += static_cast<float>(x1) + static_cast<float>(x2);
+                        } else {
+                            const __bf16 x1 = static_cast<__bf16>(hv);
+                            hi[j] = __builtin_bit_cast(uint16_t, x1);
+                            lo[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(hv - static_cast<float>(x1)));
+                        }
                     }
-                    th[rl * 32 + col] = hi;
-                    tl[rl * 32 + col] = lo;
-                }
-            }
-            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wavefront's region only
-            // 64 rows x 64 bytes per half: 4 pieces of 16 bytes per row
-#pragma unroll
-            for (int q = lane; q < 256; q += WAVE) {
-                const int rl = q >> 2, c = q & 3, r = half * 64 + rl;
-                if (r < rows) {
-                    const int64_t at = static_cast<int64_t>(pbase + r) * p.I + f0 + 32 * wv + 8 * c;
-                    *reinterpret_cast<uint4*>(p.h_hi + at) = reinterpret_cast<const uint4*>(th + rl * 32)[c];
-                    *reinterpret_cast<uint4*>(p.h_lo + at) = reinterpret_cast<const uint4*>(tl + rl * 32)[c];
+                    if (FMT == MOE355_W_INT4_G64) {
+                        const uint32_t gh = hh ? (hi[0] | (static_cast<uint32_t>(hi[1]) << 16))
+                                               : (hi[2] | (static_cast<uint32_t>(hi[3]) << 16));
+                        const uint32_t gl = hh ? (lo[0] | (static_cast<uint32_t>(lo[1]) << 16))
+                                               : (lo[2] | (static_cast<uint32_t>(lo[3]) << 16));
+                        const uint32_t rh = __shfl_xor(gh, 32, WAVE), rl = __shfl_xor(gl, 32, WAVE);
+                        if (hh == 0) {
+                            hw[0] = hi[0] | (rh << 16);
+                            hw[1] = hi[1] | (rh & 0xFFFF0000u);
+                            lw[0] = lo[0] | (rl << 16);
+                            lw[1] = lo[1] | (rl & 0xFFFF0000u);
+                        } else {
+                            hw[0] = (rh & 0xFFFFu) | (static_cast<uint32_t>(hi[2]) << 16);
+                            hw[1] = (rh >> 16) | (static_cast<uint32_t>(hi[3]) << 16);
+                            lw[0] = (rl & 0xFFFFu) | (static_cast<uint32_t>(lo[2]) << 16);
+                            lw[1] = (rl >> 16) | (static_cast<uint32_t>(lo[3]) << 16);
+                        }
+                    } else {
+                        hw[0] = hi[0] | (static_cast<uint32_t>(hi[1]) << 16);
+                        hw[1] = hi[2] | (static_cast<uint32_t>(hi[3]) << 16);
+                        lw[0] = lo[0] | (static_cast<uint32_t>(lo[1]) << 16);
+                        lw[1] = lo[2] | (static_cast<uint32_t>(lo[3]) << 16);
+                    }
+                    if (keep) {
+                        const int64_t at = row + fw + 32 * ft + 8 * q + 4 * hh;
+                        *reinterpret_cast<uint2*>(p.h_hi + at) = make_uint2(hw[0], hw[1]);
+                        *reinterpret_cast<uint2*>(p.h_lo + at) = make_uint2(lw[0], lw[1]);
+                    }
                 }
             }
             if (FMT == MOE355_W_INT4_G64) {
-                // this wavefront's share of each row's group sum (32 of a group's 64 columns)
-                float sum = 0.0f;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    sum = f16x8_sum(reinterpret_cast<const uint4*>(th + lane * 32)[c], sum);
-                    sum = f16x8_sum(reinterpret_cast<const uint4*>(tl + lane * 32)[c], sum);
-                }
-                part[wv * 64 + lane] = sum;
-                __syncthreads();
-                if ((wv & 1) == 0) {
-                    const int r = half * 64 + lane;
-                    if (r < rows)
-                        p.hsum[static_cast<int64_t>(pbase + r) * (p.I / 64) + f0 / 64 + wv / 2] =
-                            part[wv * 64 + lane] + part[(wv + 1) * 64 + lane];
-                }
+                // the row's sum over the wavefront's 64 features: one int4 group of h
+                gsum += __shfl_xor(gsum, 32, WAVE);
+                if (keep && hh == 0) p.hsum[static_cast<int64_t>(pbase + r) * (I / 64) + fw / 64] = gsum;
             }
-            __syncthreads();   // the ring region is rewritten by the next half
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// down + combine: A = the tile's 128 rows of h (hi and lo), B = down rows
-// [n0 + 64 w, +64) for wavefront w; the weighted rows are added into the
-// output with fp32 atomics.
+// down + combine: A = the tile's 128 rows of h (hi and lo); B = down rows
+// nw + [0, 128) for wavefront w, nw = n0 + 128 w, as 4 column tiles; the
+// weighted rows are added into the output with fp32 atomics (a lane holds one
+// output column of 16 rows per row tile, so each atomic instruction covers 128
+// contiguous bytes of 2 rows).
 template <int FMT>
 __global__ void __launch_bounds__(256) down_mfma(PrefillParams p) {
+    constexpr int PD = DN_PD, D = PD - 1, OPS = 14;   // loads per stage per wavefront
     extern __shared__ uint4 smem[];
-    uint4* ring = smem;                                           // [PD][hi 128 x 8, lo 128 x 8]
-    int32_t* rtok = reinterpret_cast<int32_t*>(smem + PD * 2048);
+    uint8_t* ring = reinterpret_cast<uint8_t*>(smem);                  // [PD][DN_SLOT]
+    int32_t* rtok = reinterpret_cast<int32_t*>(ring + PD * DN_SLOT);
     float* rw = reinterpret_cast<float*>(rtok + BM);
-    const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
-    const int ln = lane & 31, hh = lane >> 5;
-    const int I = p.I, Gd = I / 64, KS = I / BK;
-    const int FX = p.H / BN;
+    const int tid = threadIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / WAVE);
+    const int H = p.H, I = p.I, Gd = I / 64, KS = I / BK;
+    const int FX = (H + DN_COLS - 1) / DN_COLS;
+    const uint32_t ring_lds = lds_addr(ring);
     const TileRange tr = tile_range(*p.n_tiles * FX);
     for (int t = tr.begin; t < tr.end; t += tr.step) {
-        const int y = t / FX, n0 = (t - y * FX) * BN;
+        const int y = t / FX;
         const int e = p.tile_e[y], m0 = p.tile_m0[y];
         const int pbase = p.offsets[e] + m0;
         const int rows = min(BM, p.offsets[e + 1] - pbase);
-        const uint8_t* W = p.W + static_cast<int64_t>(e) * p.S;
+        const void* W = uniform_ptr(p.W + static_cast<int64_t>(e) * p.S);
+        const uint8_t* Wb = p.W + static_cast<int64_t>(e) * p.S;
+        const int nw = (t - y * FX) * DN_COLS + 128 * wv;
+        // The lane index is made opaque once per tile so that the compiler
+        // recomputes lane-derived addresses here instead of hoisting dozens of
+        // them out of the tile loop (they would spill, and every reload of a
+        // spill waits for all memory operations in flight).
+        int lane = tid & (WAVE - 1);
+        asm volatile("" : "+v"(lane));
+        const int ln = lane & 31, hh = lane >> 5;
+        const bool live = nw < H;            // idle wavefronts of a small H compute on row 0
+        const int nr = live ? nw : 0;
+        const void* hb = uniform_ptr(p.h_hi + static_cast<int64_t>(pbase) * I);   // h rows are the bucket's pairs
+        const void* lb = uniform_ptr(p.h_lo + static_cast<int64_t>(pbase) * I);
         __syncthreads();   // the previous tile is done with the LDS
         if (tid < BM) {
             if (tid < rows) {
@@ -625,99 +602,126 @@ __global__ void __launch_bounds__(256) down_mfma(PrefillParams p) {
                 rw[tid] = 0.0f;
             }
         }
-        int aoff[4];   // h rows are the bucket's pairs, contiguous from pbase
+        uint32_t aoff[4];   // rows past the bucket re-read its first row
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 8 * (4 * wv + j) + lane / 8, c = (lane % 8) ^ (lane / 8);
-            aoff[j] = (pbase + (r < rows ? r : 0)) * I + c * 8;
+            aoff[j] = static_cast<uint32_t>(r < rows ? r : 0) * static_cast<uint32_t>(2 * I) + c * 16;
         }
-        BRow<FMT> brow[2];
-        brow[0].init(W, p, 2, n0 + 64 * wv + ln, I, hh);
-        brow[1].init(W, p, 2, n0 + 64 * wv + 32 + ln, I, hh);
-
-        f32x16 R[4][2];
+        uint32_t bq[4], bsc[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) R[i][0] = R[i][1] = f32x16{};
-        BRaw braw[PD];
-        auto issue = [&](int kk, int slot, BRaw& b) {
-            uint4* dst = ring + slot * 2048 + 4 * wv * 64;
+        for (int c = 0; c < 4; ++c)
+            bq[c] = static_cast<uint32_t>(p.q_off[2] + static_cast<int64_t>(nr + 32 * c + ln) * (I / 2) + hh * 16);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            bsc[j] = static_cast<uint32_t>(p.s_off[2] + static_cast<int64_t>(nr + 64 * j + lane) * (I / 32));
+
+        f32x16 R[4][4];   // [row tile][column tile]
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) R[i][c] = f32x16{};
+        auto issue = [&](int kk, int slot) {
+            const uint32_t sl = ring_lds + slot * DN_SLOT;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                __builtin_amdgcn_global_load_lds(p.h_hi + aoff[j] + kk * BK, to_lds(dst + j * 64), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(p.h_lo + aoff[j] + kk * BK, to_lds(dst + 1024 + j * 64), 16, 0, 0);
+                dma16(hb, aoff[j] + kk * 128, sl + DN_AH + (4 * wv + j) * 1024);
+                dma16(lb, aoff[j] + kk * 128, sl + DN_AL + (4 * wv + j) * 1024);
             }
-            brow[0].load(kk, &b.q[0], &b.sc[0]);
-            brow[1].load(kk, &b.q[1], &b.sc[1]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) dma16(W, bq[c] + kk * 32, sl + DN_B + (4 * wv + c) * 1024);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) dma4(W, bsc[j] + (kk >> 1) * 4, sl + DN_S + (2 * wv + j) * 256);
         };
-        auto compute = [&](int slot, const BRaw& b) {
-            const uint4* Ah = ring + slot * 2048;
-            const uint4* Al = Ah + 1024;
+        auto compute = [&](int kk, int slot) {
+            const uint8_t* sp = ring + slot * DN_SLOT;
+            const uint4* Ah = reinterpret_cast<const uint4*>(sp + DN_AH);
+            const uint4* Al = reinterpret_cast<const uint4*>(sp + DN_AL);
+            const uint4* Bq = reinterpret_cast<const uint4*>(sp + DN_B) + 4 * wv * 64 + lane;
+            const uint32_t* S = reinterpret_cast<const uint32_t*>(sp + DN_S);
+            uint4 q[4];
+            uint32_t sc[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const uint4 b0 = b_operand<FMT>(b.q[0], b.sc[0], s);
-                const uint4 b1 = b_operand<FMT>(b.q[1], b.sc[1], s);
+            for (int c = 0; c < 4; ++c) {
+                q[c] = Bq[c * 64];
+                sc[c] = tile_scale(S, wv, c, ln);
+            }
+            // half-step u: MFMA step u / 2 on the hi (u even) or lo (u odd) part of
+            // h; its A fragments are read one half-step ahead of their use
+            uint4 a[2][4], b[4];
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    const uint4 ah = a_operand(Ah, mt, ln, hh, s);
-                    const uint4 al = a_operand(Al, mt, ln, hh, s);
-                    R[mt][0] = mma<FMT>(ah, b0, R[mt][0]);
-                    R[mt][1] = mma<FMT>(ah, b1, R[mt][1]);
-                    R[mt][0] = mma<FMT>(al, b0, R[mt][0]);
-                    R[mt][1] = mma<FMT>(al, b1, R[mt][1]);
+            for (int mt = 0; mt < 4; ++mt) a[0][mt] = a_operand(Ah, mt, ln, hh, 0);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (u + 1 < 8) {
+                    const uint4* An = ((u + 1) & 1) ? Al : Ah;
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) a[(u + 1) & 1][mt] = a_operand(An, mt, ln, hh, (u + 1) >> 1);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if ((u & 1) == 0) b[c] = b_operand<FMT>(q[c], sc[c], kk, hh, u >> 1);
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) R[mt][c] = mma<FMT>(a[u & 1][mt], b[c], R[mt][c]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
-        issue(0, 0, braw[0]);
-        if (KS > 1) issue(1, 1, braw[1]);
-        for (int kb = 0; kb < KS; kb += PD) {
 #pragma unroll
-            for (int d = 0; d < PD; ++d) {
-                const int kk = kb + d;
-                if (kk < KS) {
-                    // this stage's loads are done once only the next stage's 12 remain
-                    if (kk + 1 < KS) wait_vm<12>();
-                    else wait_vm<0>();
-                    __syncthreads();
-                    if (kk + 2 < KS) issue(kk + 2, (d + 2) % PD, braw[(d + 2) % PD]);
-                    compute(d, braw[d]);
-                }
-            }
+        for (int kk = 0; kk < D; ++kk)
+            if (kk < KS) issue(kk, kk);
+        int slot = 0;
+#pragma nounroll
+        for (int kk = 0; kk < KS; ++kk) {
+            stage_wait<OPS, D - 1>(KS - 1 - kk);
+            const int next = slot == 0 ? PD - 1 : slot - 1;
+            if (kk + D < KS) issue(kk + D, next);
+            compute(kk, slot);
+            slot = slot == PD - 1 ? 0 : slot + 1;
         }
 
         if (FMT == MOE355_W_INT4_G64) {
             for (int g0 = 0; g0 < Gd; g0 += 16) {
                 const int gl = g0 + 8 * hh;
-                uint4 bh[2], bl[2];
-                bias_b(W, p, 2, n0 + 64 * wv + ln, Gd, gl, &bh[0], &bl[0]);
-                bias_b(W, p, 2, n0 + 64 * wv + 32 + ln, Gd, gl, &bh[1], &bl[1]);
+                uint4 bh[4], bl[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) bias_b(Wb, p, 2, nr + 32 * c + ln, Gd, gl, &bh[c], &bl[c]);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     const int r = mt * 32 + ln;
                     uint4 xh, xl;
                     bias_a(p.hsum + static_cast<int64_t>(pbase + (r < rows ? r : 0)) * Gd, Gd, gl, &xh, &xl);
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) {
-                        R[mt][ct] = mma<FMT>(xh, bh[ct], R[mt][ct]);
-                        R[mt][ct] = mma<FMT>(xl, bh[ct], R[mt][ct]);
-                        R[mt][ct] = mma<FMT>(xh, bl[ct], R[mt][ct]);
+                    for (int c = 0; c < 4; ++c) {
+                        R[mt][c] = mma<FMT>(xh, bh[c], R[mt][c]);
+                        R[mt][c] = mma<FMT>(xl, bh[c], R[mt][c]);
+                        R[mt][c] = mma<FMT>(xh, bl[c], R[mt][c]);
                     }
                 }
             }
         }
 
-        // combine: out[t, n] += w * y
+        // combine: out[t, n] += w * y; lane (ln, hh) holds rows rc + 4 hh of
+        // column nw + 32 c + ln, rc = 32 mt + 8 (i / 4) + i % 4
+        if (live) {
+            const int h4 = 4 * hh;
+            const int32_t* rt = rtok + h4;
+            const float* rwt = rw + h4;
+            float* obase = p.out + nw + ln;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = mt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-                if (r < rows) {
-                    const float wt = rw[r];
-                    float* orow = p.out + static_cast<int64_t>(rtok[r]) * p.H + n0 + 64 * wv + ln;
-                    unsafeAtomicAdd(orow, wt * R[mt][0][i]);
-                    unsafeAtomicAdd(orow + 32, wt * R[mt][1][i]);
+                for (int i = 0; i < 16; ++i) {
+                    const int rc = mt * 32 + 8 * (i >> 2) + (i & 3);
+                    if (rc + h4 < rows) {
+                        const float wt = rwt[rc];
+                        float* orow = obase + static_cast<int64_t>(rt[rc]) * H;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) unsafeAtomicAdd(orow + 32 * c, wt * R[mt][c][i]);
+                    }
                 }
-            }
+        }
     }
 }
 
@@ -778,6 +782,9 @@ extern "C" moe355_status moe355_expert_ffn_prefill(const moe355_layer_desc* d, c
     MOE355_REQUIRE(d->hidden <= 8192 && d->inter <= 2048, MOE355_ENOTSUP,
                    "expert_ffn_prefill: H=%d (at most 8192) or I=%d (at most 2048) too large for LDS",
                    d->hidden, d->inter);
+    // the gate/up kernel addresses x rows by 32-bit byte offsets
+    MOE355_REQUIRE(static_cast<int64_t>(T) * d->hidden * 2 <= 0xFFFFFFFFll, MOE355_ENOTSUP,
+                   "expert_ffn_prefill: T*H=%lld beyond 2^31 activations", static_cast<long long>(T) * d->hidden);
     const size_t need = prefill_ws_bytes(d, T);
     MOE355_REQUIRE(ws && ws_bytes >= need, MOE355_ECAPACITY,
                    "expert_ffn_prefill: workspace %zu < %zu bytes", ws_bytes, need);
@@ -832,8 +839,8 @@ extern "C" moe355_status moe355_expert_ffn_prefill(const moe355_layer_desc* d, c
         st = check_launch("expert_ffn_prefill x16");
         if (st) return st;
     }
-    const size_t lds_gu = PD * 16384 + BM * 4 + 4 * 64 * 4;
-    const size_t lds_dn = PD * 32768 + 2 * BM * 4;
+    const size_t lds_gu = GU_PD * GU_SLOT + BM * 4;
+    const size_t lds_dn = DN_PD * DN_SLOT + 2 * BM * 4;
     MOE355_REQUIRE(lds_gu <= 160 * 1024 && lds_dn <= 160 * 1024, MOE355_ENOTSUP,
                    "expert_ffn_prefill: LDS need %zu / %zu bytes", lds_gu, lds_dn);
     auto gu = int4 ? gate_up_mfma<MOE355_W_INT4_G64> : gate_up_mfma<MOE355_W_MXFP4>;
