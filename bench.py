@@ -27,6 +27,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# sources of the decode FFN kernels (a recorded traffic figure is void once they change)
+DECODE_SOURCES = ["moe_expert_layer_02_amd/csrc/decode.hip", "moe_expert_layer_02_amd/csrc/internal.h"]
+PREFILL_SOURCES = ["moe_expert_layer_02_amd/csrc/prefill.hip", "moe_expert_layer_02_amd/csrc/internal.h"]
 METRIC = "decode MoE-layer expert-weight GB/s (% HBM peak); prefill tokens/s (% MFMA peak)"
 
 
@@ -185,49 +188,62 @@ def bench_decode(args, w):
     n_calls = args.steps * L
     value = bytes_total / dt / 1e9
 
-    # roofline pass: the FFN kernel alone between two events, eager, same trace
+    # roofline pass: the FFN kernels alone.  Each step's bookkeeping (route,
+    # classify_evict, cache_fill) runs eagerly for all layers first; then the
+    # step's L FFN calls, one per layer (each reading its own layer's experts, as
+    # in the real step), are captured into a graph whose replay is bracketed by
+    # two events on the replay stream.  There are no host gaps inside the
+    # bracket, so the per-launch time is the kernels' own (plus the graph's
+    # inter-kernel gaps).
     rp = Step()
-    ids = torch.empty((T, w.top_k), dtype=torch.int32, device=dev)
-    wt = torch.empty((T, w.top_k), dtype=torch.float32, device=dev)
-    lst = m.DeviceClassifyOut(cap)
     stream = torch.cuda.current_stream()
-    ev = []
     rp_steps = min(args.steps, 10)
     u_rp = 0
+    ev = []
     for s in range(args.warmup + rp_steps):
         rp.stage(s)
         for l in range(L):
-            m.route(desc, rp.logits[l], ids, wt)
-            m.classify_evict(rp.cache, l, s * L + l + 1, ids, policy, lst)
-            m.cache_fill(rp.cache, pool, l, lst, K)
-            timed = s >= args.warmup
-            if timed:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-            m.expert_ffn_decode(desc, rp.x[l], ids, wt, rp.cache, pool, l, lst, rp.out[l], rp.ws)
-            if timed:
-                e1.record(stream)
-                ev.append((e0, e1))
-                u_rp += len(np.unique(trace.targets[s % n_trace, l]))
-    torch.cuda.synchronize()
-    ffn_avg_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
-    per_call_bytes = u_rp * S / len(ev)
+            m.route(desc, rp.logits[l], rp.ids[l], rp.wt[l])
+            m.classify_evict(rp.cache, l, s * L + l + 1, rp.ids[l], policy, rp.lists[l])
+            m.cache_fill(rp.cache, pool, l, rp.lists[l], K)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for l in range(L):
+                m.expert_ffn_decode(desc, rp.x[l], rp.ids[l], rp.wt[l], rp.cache, pool, l,
+                                    rp.lists[l], rp.out[l], rp.ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if s >= args.warmup:
+            ev.append(e0.elapsed_time(e1) / L)
+            u_rp += sum(len(np.unique(trace.targets[s % n_trace, l])) for l in range(L))
+        del g
+    ffn_avg_s = float(np.mean(ev)) / 1e3
+    n_launch = len(ev) * L
+    per_call_bytes = u_rp * S / n_launch
     achieved = per_call_bytes / ffn_avg_s / 1e9
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt / args.steps * 1e3, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16" if w.wfmt == 0 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "layers": L, "tokens_per_step": T, "hidden": w.hidden,
                    "inter": w.inter, "experts": w.n_experts, "top_k": w.top_k,
                    "weights": "int4_g64" if w.wfmt == 0 else "mxfp4", "cache_slots": w.n_slots,
                    "expert_bytes": S, "layer_calls_timed": n_calls, "parallelism": "single_gpu",
                    "order": order, "step": "one replay of a captured graph of the step's layer calls"},
-        "roofline": {"bound": "hbm", "kernel": "ffn_decode_kernel (expert_ffn_decode)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "expert_ffn_decode: gate_up_kernel + down_kernel (one call, two launches)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_record(f"decode_ffn_{w.name}_traffic.md", DECODE_SOURCES),
                      "bytes_per_launch": round(per_call_bytes),
-                     "avg_launch_us": round(ffn_avg_s * 1e6, 2), "launches_timed": len(ev)},
+                     "avg_launch_us": round(ffn_avg_s * 1e6, 2), "launches_timed": n_launch},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_decode(w, trace, n_calls=args.cpu_calls,
@@ -318,7 +334,8 @@ def bench_prefill(args, w):
         "metric": METRIC, "value": round(T * args.steps / dt, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(dt / args.steps * 1e3, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16-mfma/f32-acc", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16" if w.wfmt == 0 else "bf16",
+        "data": "synthetic",
         "config": {"workload": w.name, "tokens": T, "hidden": w.hidden, "inter": w.inter,
                    "experts": w.n_experts, "top_k": k,
                    "weights": "int4_g64" if w.wfmt == 0 else "mxfp4",
@@ -326,7 +343,8 @@ def bench_prefill(args, w):
         "roofline": {"bound": "mfma", "kernel": "expert_ffn_prefill",
                      "achieved": round(achieved, 1), "peak": MFMA_PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "flops_per_launch": flops,
+                     "traffic": traffic_record(f"prefill_ffn_{w.name}_traffic.md", PREFILL_SOURCES),
+                     "flops_per_launch": flops,
                      "avg_launch_us": round(ffn_s * 1e6, 1)},
     }
     if not args.no_cpu_baseline:
@@ -341,6 +359,43 @@ def C_seed(w):
     return C.seed(w.cid, 0)
 
 
+def calib_copy(mib: int, reps: int):
+    """A plain device copy of known size, for scaling the HBM byte counters.
+
+    Under ``rocprofv3 --pmc FETCH_SIZE`` (or WRITE_SIZE) each copy dispatch should
+    read (write) ``mib`` MiB; the ratio of that to the counter's reading is the
+    factor applied to the FFN kernels' readings.
+    """
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"calib_copy_bytes": n, "dispatches": reps}
+
+
+def traffic_record(name: str, sources: list[str]):
+    """HBM bytes per launch from a committed PMC summary, if it still describes
+    the current kernel sources (sha256 of the listed files), else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", " ")):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in sources:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if rec.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in rec:
+        return None
+    return float(rec["traffic_bytes_per_launch"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -353,11 +408,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-calls", type=int, default=160)
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is "
               "single-GPU by design", file=sys.stderr)
         sys.exit(2)
+    if args.calib_copy:
+        print(json.dumps(calib_copy(args.calib_copy, 5)), flush=True)
+        return
     from workloads import configs as C
     w = {"qwen_decode": C.QWEN_DECODE, "ds_decode": C.DS_DECODE, "qwen_prefill": C.QWEN_PREFILL,
          "ds_prefill": C.DS_STRESS}[args.workload]
