@@ -27,6 +27,7 @@ constexpr int CL_WAVES = CL_THREADS / WAVE;
 constexpr int MAX_SLOTS = 16384;
 constexpr int MAX_EXPERTS = 1024;
 constexpr int MAX_LIST = 1024;
+constexpr uint32_t SMALL_K = 16;   // up to this many victims: min rounds instead of radix select
 
 // Exclusive block scan over CL_THREADS threads (all threads must call it).
 __device__ uint64_t block_excl_scan(uint64_t v, uint64_t* wave_tot, uint64_t* total) {
@@ -191,6 +192,18 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
     v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
     v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
     return v;
+}
+
+// Minimum over the 64 lanes (an inclusive min-scan by the same DPP steps; lane
+// 63 ends with the minimum of all).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, v, 0x111, 0xf, 0xf, false)));
+    v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, v, 0x112, 0xf, 0xf, false)));
+    v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, v, 0x114, 0xf, 0xf, false)));
+    v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, v, 0x118, 0xf, 0xf, false)));
+    v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, v, 0x142, 0xa, 0xf, false)));
+    v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, v, 0x143, 0xc, 0xf, false)));
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Exclusive prefix sum and total over the 64 lanes.
@@ -396,6 +409,7 @@ __global__ void __launch_bounds__(CL_THREADS) classify_kernel(ClassifyParams cp)
     // registers; otherwise it reads them from LDS.
     const bool narrow = (static_cast<uint64_t>(tick) << sbits) < (1ull << 32);
     uint32_t n_elig = 0, n_vic = 0;
+    bool ranked = false;   // victims already written in rank order
     auto select = [&](auto key_zero, auto in_regs) {
         using KT = decltype(key_zero);
         constexpr bool REGS = decltype(in_regs)::value && SPL > 0;
@@ -429,6 +443,36 @@ __global__ void __launch_bounds__(CL_THREADS) classify_kernel(ClassifyParams cp)
         if (n_vic == 0) return;
         constexpr int KB = 8 * sizeof(KT);
         auto key = [&](int sl, uint32_t t) { return (static_cast<KT>(t) << sbits) | static_cast<KT>(sl); };
+        if constexpr (REGS && KB == 32) {
+            if (n_vic <= SMALL_K) {
+                // Few victims: n_vic rounds of a wave-wide minimum, each over the keys
+                // above the previous pick; the picks come out in rank order.  An
+                // ineligible slot holds the key ~0, which no round reaches (eligible
+                // keys are below tick << sbits < 2^32 and n_vic <= n_elig).
+                uint32_t kr[RL];
+#pragma unroll
+                for (int j = 0; j < RL; ++j)
+                    kr[j] = (s0 + j < N && tsr[j] < tick) ? key(s0 + j, tsr[j]) : ~0u;
+                uint32_t from = 0;   // smallest key still eligible for a pick
+                for (uint32_t r = 0; r < n_vic; ++r) {
+                    // min over kr[j] >= from of (kr[j] - from): the subtraction sends
+                    // the keys below `from` to the top of the unsigned range
+                    uint32_t lm = ~0u;
+#pragma unroll
+                    for (int j = 0; j < RL; ++j) lm = min(lm, kr[j] - from);
+                    const uint32_t m = wave_min_u32(lm) + from;
+                    if (lane == 0) {
+                        const int sl = static_cast<int>(m & ((1u << sbits) - 1));
+                        sh.victims[r] = sl;
+                        sh.vic_owner[r] = own_lds ? sh.own[sl] : owner[sl];
+                        cp.victims[r] = sl;
+                    }
+                    from = m + 1;
+                }
+                ranked = true;
+                return;
+            }
+        }
         KT thr = ~static_cast<KT>(0);
         if (n_elig > n_vic) {
             const uint64_t top = static_cast<uint64_t>(tick) << sbits;
@@ -494,7 +538,8 @@ __global__ void __launch_bounds__(CL_THREADS) classify_kernel(ClassifyParams cp)
         select(uint32_t{0}, std::true_type{});
     else
         select(uint64_t{0}, std::false_type{});
-    if (n_vic > 0) {
+    if (n_vic > 0 && ranked) wave_lds_sync();   // lane 0 wrote the victims
+    if (n_vic > 0 && !ranked) {
         wave_lds_sync();
         for (uint32_t i = lane; i < n_vic; i += WAVE) {
             const uint64_t k = sh.sel_key[i];
