@@ -177,7 +177,6 @@ struct ClassifyShared {
     int32_t plocal[MAX_LIST];    // a pair's place inside its expert's group
     int32_t miss[MAX_LIST];
     uint64_t sel_key[MAX_LIST];
-    int32_t sel_owner[MAX_LIST];
     int32_t victims[MAX_LIST];
     int32_t vic_owner[MAX_LIST];
     uint32_t hist[256];
@@ -454,6 +453,7 @@ __global__ void __launch_bounds__(CL_THREADS) classify_kernel(ClassifyParams cp)
                 for (int j = 0; j < RL; ++j)
                     kr[j] = (s0 + j < N && tsr[j] < tick) ? key(s0 + j, tsr[j]) : ~0u;
                 uint32_t from = 0;   // smallest key still eligible for a pick
+                int vic = -1;        // lane r keeps pick r
                 for (uint32_t r = 0; r < n_vic; ++r) {
                     // min over kr[j] >= from of (kr[j] - from): the subtraction sends
                     // the keys below `from` to the top of the unsigned range
@@ -461,13 +461,14 @@ __global__ void __launch_bounds__(CL_THREADS) classify_kernel(ClassifyParams cp)
 #pragma unroll
                     for (int j = 0; j < RL; ++j) lm = min(lm, kr[j] - from);
                     const uint32_t m = wave_min_u32(lm) + from;
-                    if (lane == 0) {
-                        const int sl = static_cast<int>(m & ((1u << sbits) - 1));
-                        sh.victims[r] = sl;
-                        sh.vic_owner[r] = own_lds ? sh.own[sl] : owner[sl];
-                        cp.victims[r] = sl;
-                    }
+                    if (static_cast<uint32_t>(lane) == r) vic = static_cast<int>(m & ((1u << sbits) - 1));
                     from = m + 1;
+                }
+                if (static_cast<uint32_t>(lane) < n_vic) {
+                    sh.victims[lane] = vic;
+                    cp.victims[lane] = vic;
+                    if (own_lds) sh.vic_owner[lane] = sh.own[vic];
+                    else sh.vic_owner[lane] = owner[vic];
                 }
                 ranked = true;
                 return;
@@ -527,11 +528,7 @@ __global__ void __launch_bounds__(CL_THREADS) classify_kernel(ClassifyParams cp)
         uint32_t n_sel;
         uint32_t at = wave_excl_scan(cs, &n_sel);
         for_slots([&](int sl, uint32_t t) {
-            if (sl < N && t < tick && key(sl, t) <= thr) {
-                sh.sel_key[at] = static_cast<uint64_t>(key(sl, t));
-                sh.sel_owner[at] = own_lds ? sh.own[sl] : owner[sl];
-                ++at;
-            }
+            if (sl < N && t < tick && key(sl, t) <= thr) sh.sel_key[at++] = static_cast<uint64_t>(key(sl, t));
         });
     };
     if (narrow)
@@ -547,8 +544,12 @@ __global__ void __launch_bounds__(CL_THREADS) classify_kernel(ClassifyParams cp)
             for (uint32_t j = 0; j < n_vic; ++j) r += sh.sel_key[j] < k ? 1u : 0u;
             const int sl = static_cast<int>(k & ((1ull << sbits) - 1));
             sh.victims[r] = sl;
-            sh.vic_owner[r] = sh.sel_owner[i];
             cp.victims[r] = sl;
+            // owners looked up here, off the collection loop, from LDS or from
+            // memory by a uniform branch (a generic load would wait for every
+            // store in flight)
+            if (own_lds) sh.vic_owner[r] = sh.own[sl];
+            else sh.vic_owner[r] = owner[sl];
         }
         wave_lds_sync();
     }

@@ -71,9 +71,15 @@ struct DecodeParams {
     float* out;              // [T][H]
 };
 
+// Device-memory (address space 1) byte pointers: loads and stores through them
+// compile to global instructions, which, unlike generic ones, do not count
+// against the LDS wait counter.
+typedef __attribute__((address_space(1))) const uint8_t* gbytes;
+typedef __attribute__((address_space(1))) uint8_t* gbytes_w;
+
 struct ExpertRef {
-    const uint8_t* src;
-    uint8_t* dst;  // fill-through destination slot, or null
+    gbytes src;
+    gbytes_w dst;  // fill-through destination slot, or null
 };
 
 // The per-call plan, staged in LDS by every block before any weight load.
@@ -82,23 +88,36 @@ struct PlanLds {
     int4 plan[MAX_PLAN];
     int32_t uniq[MAX_PLAN];
     int32_t pairs[MAX_PLAN];
+    int32_t tok[MAX_PLAN];   // token of pairs[i] (pairs[i] / k)
     float w[MAX_PLAN];       // routing weight of each pair
     int32_t n_uniq;
 };
 
+// A wavefront-uniform device pointer moved into scalar registers, so that loads
+// from it take a 32-bit per-lane offset instead of 64-bit per-lane arithmetic.
+__device__ __forceinline__ uint64_t uniform_addr(const void* q) {
+    const uint64_t v = reinterpret_cast<uint64_t>(q);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // Where distinct expert u's bytes are read from (and written to, with fill-through).
+// u is wavefront-uniform, so are both pointers.
 __device__ __forceinline__ ExpertRef expert_ref(const DecodeParams& p, const PlanLds& pl, int u) {
     const int4 row = pl.plan[u];
     ExpertRef r;
-    r.dst = nullptr;
-    r.src = p.pool + (static_cast<int64_t>(p.layer) * p.E + pl.uniq[u]) * p.S;
+    const uint8_t* src = p.pool + (static_cast<int64_t>(p.layer) * p.E + pl.uniq[u]) * p.S;
+    const uint8_t* dst = nullptr;
     if (p.has_cache && row.x >= 0) {
-        uint8_t* slot = const_cast<uint8_t*>(p.slots) + static_cast<int64_t>(row.x) * p.S;
+        const uint8_t* slot = p.slots + static_cast<int64_t>(row.x) * p.S;
         if (p.fill_through && row.y)
-            r.dst = slot;        // filled by this call: read the pool, write the slot
+            dst = slot;          // filled by this call: read the pool, write the slot
         else
-            r.src = slot;
+            src = slot;
     }
+    r.src = reinterpret_cast<gbytes>(uniform_addr(src));
+    r.dst = reinterpret_cast<gbytes_w>(uniform_addr(dst));
     return r;
 }
 
@@ -109,6 +128,7 @@ __device__ __forceinline__ void stage_plan(const DecodeParams& p, PlanLds& pl) {
     }
     if (threadIdx.x < p.T * p.k) {
         pl.pairs[threadIdx.x] = p.pairs[threadIdx.x];
+        pl.tok[threadIdx.x] = p.pairs[threadIdx.x] / p.k;
         pl.w[threadIdx.x] = p.w[threadIdx.x];
     }
     if (threadIdx.x == 0) pl.n_uniq = p.counts[0];
@@ -117,6 +137,20 @@ __device__ __forceinline__ void stage_plan(const DecodeParams& p, PlanLds& pl) {
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint32_t ldg4(const void* p) { return *reinterpret_cast<const uint32_t*>(p); }
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldg16(gbytes p) {
+    const u32x4_t v = *reinterpret_cast<__attribute__((address_space(1))) const u32x4_t*>(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ldg4(gbytes p) {
+    return *reinterpret_cast<__attribute__((address_space(1))) const uint32_t*>(p);
+}
+__device__ __forceinline__ void stg16(gbytes_w p, const uint4& v) {
+    *reinterpret_cast<__attribute__((address_space(1))) u32x4_t*>(p) = u32x4_t{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ void stg4(gbytes_w p, uint32_t v) {
+    *reinterpret_cast<__attribute__((address_space(1))) uint32_t*>(p) = v;
+}
 __device__ __forceinline__ uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ uint32_t as_u32(bf16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
@@ -223,7 +257,9 @@ __device__ __forceinline__ half2_t int4_scale(uint32_t sd, int gq) {
     return half2_t{sh, sh};
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z), with the hardware reciprocal (about 1 ulp) in place
+// of an IEEE division
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Loads of one slab for one matrix and RT row tiles: codes, scale dword, bias dword.
 template <int RT>
@@ -233,45 +269,45 @@ struct WSlab {
     uint32_t bi[RT];
 };
 
-// Byte offsets of row r's slab at input kb: codes, scale/exponent dword, bias dword.
+// Byte offsets of row r's slab at input kb: codes, scale/exponent dword, bias
+// dword (32-bit: an expert's blob is far below 4 GiB).  Scale rows are kdim / 32
+// bytes in both formats.
 struct SlabOff {
-    int64_t q, s;
+    uint32_t q, s;
 };
 template <int FMT>
 __device__ __forceinline__ SlabOff slab_off(int r, int kdim, int kb, int gq) {
     SlabOff o;
-    o.q = static_cast<int64_t>(r) * (kdim / 2) + kb / 2 + 16 * gq;
-    o.s = FMT == MOE355_W_INT4_G64 ? static_cast<int64_t>(r) * (kdim / 32) + kb / 32
-                                   : static_cast<int64_t>(r) * (kdim / 32) + kb / 32;
+    o.q = static_cast<uint32_t>(r) * static_cast<uint32_t>(kdim / 2) + static_cast<uint32_t>(kb / 2 + 16 * gq);
+    o.s = static_cast<uint32_t>(r) * static_cast<uint32_t>(kdim / 32) + static_cast<uint32_t>(kb / 32);
     return o;
 }
 
 template <int FMT, int RT>
-__device__ __forceinline__ void load_wslab(const DecodeParams& p, const uint8_t* src, int m,
+__device__ __forceinline__ void load_wslab(const DecodeParams& p, gbytes src, int m,
                                            int row0, int kdim, int kb, int ln, int gq,
                                            WSlab<RT>& w) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
         const SlabOff o = slab_off<FMT>(row0 + 16 * t + ln, kdim, kb, gq);
-        w.q[t] = ldg16(src + p.q_off[m] + o.q);
-        w.sc[t] = ldg4(src + p.s_off[m] + o.s);
+        w.q[t] = ldg16(src + (static_cast<uint32_t>(p.q_off[m]) + o.q));
+        w.sc[t] = ldg4(src + (static_cast<uint32_t>(p.s_off[m]) + o.s));
         // every lane loads (a broadcast within the row); only chunk-0 lanes use it
-        w.bi[t] = FMT == MOE355_W_INT4_G64 ? ldg4(src + p.b_off[m] + o.s) : 0u;
+        w.bi[t] = FMT == MOE355_W_INT4_G64 ? ldg4(src + (static_cast<uint32_t>(p.b_off[m]) + o.s)) : 0u;
     }
 }
 
 // Fill-through: write a slab's bytes (codes by every lane, scale words once per row).
 template <int FMT, int RT>
-__device__ __forceinline__ void store_wslab(const DecodeParams& p, uint8_t* dst, int m, int row0,
+__device__ __forceinline__ void store_wslab(const DecodeParams& p, gbytes_w dst, int m, int row0,
                                             int kdim, int kb, int ln, int gq, const WSlab<RT>& w) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
         const SlabOff o = slab_off<FMT>(row0 + 16 * t + ln, kdim, kb, gq);
-        *reinterpret_cast<uint4*>(dst + p.q_off[m] + o.q) = w.q[t];
+        stg16(dst + (static_cast<uint32_t>(p.q_off[m]) + o.q), w.q[t]);
         if (gq == 0) {
-            *reinterpret_cast<uint32_t*>(dst + p.s_off[m] + o.s) = w.sc[t];
-            if (FMT == MOE355_W_INT4_G64)
-                *reinterpret_cast<uint32_t*>(dst + p.b_off[m] + o.s) = w.bi[t];
+            stg4(dst + (static_cast<uint32_t>(p.s_off[m]) + o.s), w.sc[t]);
+            if (FMT == MOE355_W_INT4_G64) stg4(dst + (static_cast<uint32_t>(p.b_off[m]) + o.s), w.bi[t]);
         }
     }
 }
@@ -309,11 +345,15 @@ struct Cursor {
     bool valid;
 };
 
-template <int FMT, int KW, int RT, int D>
-__global__ void __launch_bounds__(256) gate_up_kernel(DecodeParams p) {
-    constexpr int RW = 4 / KW;
+// NW wavefronts per block (KW of them split H, NW / KW row groups); D stages in
+// flight per wavefront.  SKIP: a wavefront's loads past its last stage are
+// skipped instead of repeated (used when all of a wavefront's loads fit in the
+// ring's first D - 1 stages, so nothing is lost by the compiler's coarser wait).
+template <int FMT, int NW, int KW, int RT, int D, bool SKIP>
+__global__ void __launch_bounds__(NW * WAVE) gate_up_kernel(DecodeParams p) {
+    constexpr int RW = NW / KW;
     __shared__ PlanLds pl;
-    __shared__ f32x4 red[2][4][RT][2][WAVE];
+    __shared__ f32x4 red[2][NW][RT][2][WAVE];
     const int lane = threadIdx.x & (WAVE - 1), ln = lane & 15, gq = lane >> 4;
     const int wv = threadIdx.x / WAVE, kw = wv % KW, rw = wv / KW;
     stage_plan(p, pl);
@@ -349,8 +389,9 @@ __global__ void __launch_bounds__(256) gate_up_kernel(DecodeParams p) {
         load_wslab<FMT, RT>(p, ref.src, 1, row0, H, kb, ln, gq, st.u);
         const int4 pr = pl.plan[u];
         const int n = tg * TOK + ln;
-        const int t = pl.pairs[pr.z + (n < pr.w ? n : 0)] / p.k;
-        const uint16_t* xs = p.x + static_cast<int64_t>(t) * H + kb + 32 * gq;
+        const int t = pl.tok[pr.z + (n < pr.w ? n : 0)];
+        // 32-bit offset from the (scalar) base: x is far below 4 GiB
+        const uint16_t* xs = p.x + (static_cast<uint32_t>(t) * static_cast<uint32_t>(H) + static_cast<uint32_t>(kb + 32 * gq));
 #pragma unroll
         for (int i = 0; i < 4; ++i) st.x[i] = ldg16(xs + 8 * i);
     };
@@ -462,7 +503,7 @@ __global__ void __launch_bounds__(256) gate_up_kernel(DecodeParams p) {
     Cursor lc{i_beg, 0, 0, true}, cc = lc;
 #pragma unroll
     for (int d = 0; d < D - 1; ++d) {
-        load(st[d], lc.item, lc.tg, lc.s);
+        if (!SKIP || lc.valid) load(st[d], lc.item, lc.tg, lc.s);
         advance(lc);
     }
     bool done = false;
@@ -470,7 +511,7 @@ __global__ void __launch_bounds__(256) gate_up_kernel(DecodeParams p) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             if (!done) {
-                load(st[(d + D - 1) % D], lc.item, lc.tg, lc.s);
+                if (!SKIP || lc.valid) load(st[(d + D - 1) % D], lc.item, lc.tg, lc.s);
                 advance(lc);
                 compute(st[d], cc.item, cc.tg, cc.s);
                 if (cc.s == NS - 1) epilogue(cc.item, cc.tg);
@@ -489,15 +530,17 @@ struct DnStage {
     uint4 hh[4], hl[4];
 };
 
-template <int FMT, int RT, int D>
+// KSPLIT wavefronts share a row tile and split I (their partial sums meet in the
+// output atomics); SKIP as in the gate/up kernel.
+template <int FMT, int RT, int D, int KSPLIT, bool SKIP>
 __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
     __shared__ PlanLds pl;
     const int lane = threadIdx.x & (WAVE - 1), ln = lane & 15, gq = lane >> 4;
     stage_plan(p, pl);
-    const int I = p.I, NS = I / SLAB;
+    const int I = p.I, NS = I / SLAB / KSPLIT;
     const int tile_rows = RT * 16;
     const int tiles = p.H / tile_rows;
-    const int n_items = pl.n_uniq * tiles;
+    const int n_items = pl.n_uniq * tiles * KSPLIT;
     const int n_waves = gridDim.x * (blockDim.x / WAVE);
     const int gw = blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
     const int per = (n_items + n_waves - 1) / n_waves;
@@ -505,17 +548,22 @@ __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
     const int i_end = min(n_items, i_beg + per);
     if (i_beg >= i_end) return;
 
-    auto tokens_of = [&](int item) { return pl.plan[item / tiles].w; };
-    // unconditional loads, as in gate/up
+    // item = (distinct expert u, row tile, part ks of I)
+    const int per_u = tiles * KSPLIT;
+    auto tokens_of = [&](int item) { return pl.plan[item / per_u].w; };
+    auto kbase_of = [&](int item) { return (item % KSPLIT) * (I / KSPLIT); };
+    auto tile_of = [&](int item) { return (item % per_u) / KSPLIT; };
+    // unconditional loads (unless SKIP), as in gate/up
     auto load = [&](DnStage<FMT, RT>& st, int item, int tg, int s) {
         const int it = min(item, i_end - 1);
-        const int u = it / tiles, tile = it - u * tiles;
+        const int u = it / per_u, tile = tile_of(it);
         const ExpertRef ref = expert_ref(p, pl, u);
-        const int kb = s * SLAB;
+        const int kb = kbase_of(it) + s * SLAB;
         load_wslab<FMT, RT>(p, ref.src, 2, tile * tile_rows, I, kb, ln, gq, st.w);
         const int4 pr = pl.plan[u];
         const int n = tg * TOK + ln;
-        const int64_t o = static_cast<int64_t>(pl.pairs[pr.z + (n < pr.w ? n : 0)]) * I + kb + 32 * gq;
+        const uint32_t o = static_cast<uint32_t>(pl.pairs[pr.z + (n < pr.w ? n : 0)]) * static_cast<uint32_t>(I) +
+                           static_cast<uint32_t>(kb + 32 * gq);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             st.hh[i] = ldg16(p.h_hi + o + 8 * i);
@@ -540,21 +588,20 @@ __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
                 acc[t] = mma<FMT>(bias_a_operand(st.w.bi[t], st.w.sc[t], gq), bb, acc[t]);
         }
         if (tg == 0) {
-            const int u = item / tiles;
-            const ExpertRef ref = expert_ref(p, pl, u);
+            const ExpertRef ref = expert_ref(p, pl, item / per_u);
             if (ref.dst)
-                store_wslab<FMT, RT>(p, ref.dst, 2, (item - u * tiles) * tile_rows, I, s * SLAB, ln,
-                                     gq, st.w);
+                store_wslab<FMT, RT>(p, ref.dst, 2, tile_of(item) * tile_rows, I,
+                                     kbase_of(item) + s * SLAB, ln, gq, st.w);
         }
     };
     auto epilogue = [&](int item, int tg) {
-        const int u = item / tiles;
+        const int u = item / per_u;
         const int4 pr = pl.plan[u];
         const int n = tg * TOK + ln;
         if (n < pr.w) {
             const int pair = pl.pairs[pr.z + n];
             const float wt = pl.w[pair];
-            float* o = p.out + static_cast<int64_t>(pair / p.k) * p.H + (item - u * tiles) * tile_rows;
+            float* o = p.out + static_cast<int64_t>(pl.tok[pr.z + n]) * p.H + tile_of(item) * tile_rows;
 #pragma unroll
             for (int t = 0; t < RT; ++t)
 #pragma unroll
@@ -581,7 +628,7 @@ __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
     Cursor lc{i_beg, 0, 0, true}, cc = lc;
 #pragma unroll
     for (int d = 0; d < D - 1; ++d) {
-        load(st[d], lc.item, lc.tg, lc.s);
+        if (!SKIP || lc.valid) load(st[d], lc.item, lc.tg, lc.s);
         advance(lc);
     }
     bool done = false;
@@ -589,7 +636,7 @@ __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             if (!done) {
-                load(st[(d + D - 1) % D], lc.item, lc.tg, lc.s);
+                if (!SKIP || lc.valid) load(st[(d + D - 1) % D], lc.item, lc.tg, lc.s);
                 advance(lc);
                 compute(st[d], cc.item, cc.tg, cc.s);
                 if (cc.s == NS - 1) epilogue(cc.item, cc.tg);
@@ -626,10 +673,24 @@ moe355_status launch_gate_up(const DecodeParams& p, int max_uniq, hipStream_t st
     // two items per block slot; else one tile with four stages in flight
     const int items2 = max_uniq * (p.I / (RW * 32));
     if (items2 >= 2 * cap && p.I % (RW * 32) == 0) {
-        gate_up_kernel<FMT, KW, 2, 3><<<items2 < cap ? items2 : cap, 256, 0, stream>>>(p);
+        gate_up_kernel<FMT, 4, KW, 2, 3, false><<<items2 < cap ? items2 : cap, 256, 0, stream>>>(p);
     } else {
         const int items1 = max_uniq * (p.I / (RW * 16));
-        gate_up_kernel<FMT, KW, 1, 4><<<items1 < cap ? items1 : cap, 256, 0, stream>>>(p);
+        gate_up_kernel<FMT, 4, KW, 1, 4, false><<<items1 < cap ? items1 : cap, 256, 0, stream>>>(p);
+    }
+    return check_launch("expert_ffn_decode gate_up");
+}
+
+// Little work (a block per CU or fewer): eight wavefronts per block split H, so
+// that two wavefronts per SIMD overlap their load and dequantisation chains;
+// each wavefront's few slabs are all in flight at once.
+template <int FMT>
+moe355_status launch_gate_up_wide(const DecodeParams& p, int max_uniq, hipStream_t stream) {
+    const int blocks = max_uniq * (p.I / 16);
+    switch (p.H) {
+        case 1024: gate_up_kernel<FMT, 8, 8, 1, 2, true><<<blocks, 512, 0, stream>>>(p); break;
+        case 2048: gate_up_kernel<FMT, 8, 8, 1, 3, true><<<blocks, 512, 0, stream>>>(p); break;
+        default: gate_up_kernel<FMT, 8, 8, 1, 5, true><<<blocks, 512, 0, stream>>>(p); break;
     }
     return check_launch("expert_ffn_decode gate_up");
 }
@@ -637,20 +698,29 @@ moe355_status launch_gate_up(const DecodeParams& p, int max_uniq, hipStream_t st
 template <int FMT>
 moe355_status launch_decode(const DecodeParams& p, int max_uniq, hipStream_t stream) {
     moe355_status st;
-    // wavefronts splitting H: 4 when H >= 512
-    if (p.H >= 512) st = launch_gate_up<FMT, 4>(p, max_uniq, stream);
+    const int cus = device_cus();
+    if (p.H >= 1024 && p.H <= 4096 && max_uniq * (p.I / 16) <= cus)
+        st = launch_gate_up_wide<FMT>(p, max_uniq, stream);
+    else if (p.H >= 512)   // wavefronts splitting H: 4 when H >= 512
+        st = launch_gate_up<FMT, 4>(p, max_uniq, stream);
     else if (p.H == 256) st = launch_gate_up<FMT, 2>(p, max_uniq, stream);
     else st = launch_gate_up<FMT, 1>(p, max_uniq, stream);
     if (st) return st;
-    const int slots = device_cus() * 8;   // eight resident wavefronts per CU
+    const int slots = cus * 8;   // eight resident wavefronts per CU
     const int items2 = max_uniq * (p.H / 32);
+    const int items1 = max_uniq * (p.H / 16);
     if (items2 >= 2 * slots) {
         const int waves = items2 < slots ? items2 : slots;
-        down_kernel<FMT, 2, 3><<<(waves + 3) / 4, 256, 0, stream>>>(p);
+        down_kernel<FMT, 2, 3, 1, false><<<(waves + 3) / 4, 256, 0, stream>>>(p);
+    } else if (items1 <= cus * 4 && p.I >= 256 && p.I <= 1024) {
+        // little work: two wavefronts per row tile split I, all slabs in flight
+        const int waves = 2 * items1;
+        if (p.I == 1024) down_kernel<FMT, 1, 5, 2, true><<<(waves + 3) / 4, 256, 0, stream>>>(p);
+        else if (p.I == 512) down_kernel<FMT, 1, 3, 2, true><<<(waves + 3) / 4, 256, 0, stream>>>(p);
+        else down_kernel<FMT, 1, 2, 2, true><<<(waves + 3) / 4, 256, 0, stream>>>(p);
     } else {
-        const int items1 = max_uniq * (p.H / 16);
         const int waves = items1 < slots ? items1 : slots;
-        down_kernel<FMT, 1, 4><<<(waves + 3) / 4, 256, 0, stream>>>(p);
+        down_kernel<FMT, 1, 4, 1, false><<<(waves + 3) / 4, 256, 0, stream>>>(p);
     }
     return check_launch("expert_ffn_decode down");
 }

@@ -59,6 +59,10 @@ SMALL = [
     (2048, 1024, 40, 6, 9, C.WFMT_MXFP4),
     (4096, 2048, 16, 6, 2, C.WFMT_MXFP4),
     (4096, 256, 20, 5, 4, C.WFMT_INT4_G64),
+    # few experts per call: eight-wavefront gate/up blocks and down split over I
+    (1024, 512, 32, 4, 1, C.WFMT_INT4_G64),
+    (4096, 1024, 16, 2, 1, C.WFMT_MXFP4),
+    (1024, 256, 16, 2, 2, C.WFMT_INT4_G64),
 ]
 
 
