@@ -352,8 +352,9 @@ struct Cursor {
 template <int FMT, int NW, int KW, int RT, int D, bool SKIP>
 __global__ void __launch_bounds__(NW * WAVE) gate_up_kernel(DecodeParams p) {
     constexpr int RW = NW / KW;
+    constexpr int NB = SKIP ? 1 : 2;   // reduction buffers (one item per block when SKIP)
     __shared__ PlanLds pl;
-    __shared__ f32x4 red[2][NW][RT][2][WAVE];
+    __shared__ f32x4 red[NB][NW][RT][2][WAVE];
     const int lane = threadIdx.x & (WAVE - 1), ln = lane & 15, gq = lane >> 4;
     const int wv = threadIdx.x / WAVE, kw = wv % KW, rw = wv / KW;
     stage_plan(p, pl);
@@ -449,7 +450,7 @@ __global__ void __launch_bounds__(NW * WAVE) gate_up_kernel(DecodeParams p) {
 #pragma unroll
                         for (int t = 0; t < RT; ++t) acc[m][t] += red[ebuf][wv + o][t][m][lane];
             }
-            ebuf ^= 1;
+            if (NB == 2) ebuf ^= 1;
         }
         const int n = tg * TOK + ln;
         if (kw == 0 && n < pr.w) {
@@ -687,10 +688,10 @@ moe355_status launch_gate_up(const DecodeParams& p, int max_uniq, hipStream_t st
 template <int FMT>
 moe355_status launch_gate_up_wide(const DecodeParams& p, int max_uniq, hipStream_t stream) {
     const int blocks = max_uniq * (p.I / 16);
-    switch (p.H) {
+    switch (p.H) {   // H / KW = 128 or 256 inputs per wavefront
         case 1024: gate_up_kernel<FMT, 8, 8, 1, 2, true><<<blocks, 512, 0, stream>>>(p); break;
-        case 2048: gate_up_kernel<FMT, 8, 8, 1, 3, true><<<blocks, 512, 0, stream>>>(p); break;
-        default: gate_up_kernel<FMT, 8, 8, 1, 5, true><<<blocks, 512, 0, stream>>>(p); break;
+        case 2048: gate_up_kernel<FMT, 16, 16, 1, 2, true><<<blocks, 1024, 0, stream>>>(p); break;
+        default: gate_up_kernel<FMT, 16, 16, 1, 3, true><<<blocks, 1024, 0, stream>>>(p); break;
     }
     return check_launch("expert_ffn_decode gate_up");
 }
@@ -713,11 +714,15 @@ moe355_status launch_decode(const DecodeParams& p, int max_uniq, hipStream_t str
         const int waves = items2 < slots ? items2 : slots;
         down_kernel<FMT, 2, 3, 1, false><<<(waves + 3) / 4, 256, 0, stream>>>(p);
     } else if (items1 <= cus * 4 && p.I >= 256 && p.I <= 1024) {
-        // little work: two wavefronts per row tile split I, all slabs in flight
-        const int waves = 2 * items1;
-        if (p.I == 1024) down_kernel<FMT, 1, 5, 2, true><<<(waves + 3) / 4, 256, 0, stream>>>(p);
-        else if (p.I == 512) down_kernel<FMT, 1, 3, 2, true><<<(waves + 3) / 4, 256, 0, stream>>>(p);
-        else down_kernel<FMT, 1, 2, 2, true><<<(waves + 3) / 4, 256, 0, stream>>>(p);
+        // little work: up to four wavefronts per row tile split I (one or two
+        // slabs each), all slabs in flight
+        if (p.I == 1024) {
+            down_kernel<FMT, 1, 3, 4, true><<<items1, 256, 0, stream>>>(p);
+        } else if (p.I == 512) {
+            down_kernel<FMT, 1, 2, 4, true><<<items1, 256, 0, stream>>>(p);
+        } else {
+            down_kernel<FMT, 1, 2, 2, true><<<(2 * items1 + 3) / 4, 256, 0, stream>>>(p);
+        }
     } else {
         const int waves = items1 < slots ? items1 : slots;
         down_kernel<FMT, 1, 4, 1, false><<<(waves + 3) / 4, 256, 0, stream>>>(p);
