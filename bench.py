@@ -100,7 +100,7 @@ def bench_decode(args, w):
     L, T = w.n_layers, w.t_decode
     n_trace = w.steps
     trace = tr.DecodeTrace(w, n_trace)
-    pool = wg.make_pool(w)
+    pool = wg.make_pool(w, pack=lambda src, dst, n: m.pack_experts(desc, src, dst, n))
     K = w.victims_k
     policy = m.EvictPolicy(K, w.q_num, w.q_den)
     cap = max(K, min(T * w.top_k, w.n_experts))
@@ -295,8 +295,8 @@ def bench_prefill(args, w):
     T, k = w.t_prefill, w.top_k
     x_bits = tr.prefill_x(w)
     logits_np = tr.prefill_logits(w)
-    layer = torch.empty(w.n_experts * S, dtype=torch.uint8, device=dev)
-    wg.fill_experts(layer, 0, w.n_experts, w.wfmt, w.hidden, w.inter, C_seed(w))
+    layer = wg.make_experts(w, 0, w.n_experts, C_seed(w),
+                            pack=lambda src, dst, n: m.pack_experts(desc, src, dst, n))
     x = _x_dev(x_bits, torch)
     logits = torch.from_numpy(logits_np).to(dev)
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)

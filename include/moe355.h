@@ -75,14 +75,39 @@ typedef struct {
 } moe355_layer_desc;
 
 /*
- * Bytes of one expert, S.  One expert is a contiguous blob: for gate [I,H],
- * up [I,H] and down [H,I] in that order, int4 stores q uint8 [out, in/2]
- * (element 2c in the low nibble of byte c), s bf16 [out, in/64] and
- * b bf16 [out, in/64] (weight = s*q + b); MXFP4 stores q uint8 [out, in/2]
+ * Bytes of one expert, S.  One expert is a contiguous blob with, for gate
+ * [I,H], up [I,H] and down [H,I] in that order, a code region, a scale region
+ * and (int4 only) a bias region.  In the canonical layout ([Edge0, section 2]
+ * affine int4 in groups of 64, OCP MX for MXFP4) int4 stores q uint8
+ * [out, in/2] (element 2c in the low nibble of byte c), s bf16 [out, in/64]
+ * and b bf16 [out, in/64] (weight = s*q + b); MXFP4 stores q uint8 [out, in/2]
  * (e2m1 codes, same nibble order) and e uint8 [out, in/32] (scale 2^(e-127)).
  * Returns 0 for an invalid descriptor.
  */
 int64_t moe355_expert_bytes(const moe355_layer_desc* d);
+
+/*
+ * The device layout, read by every expert FFN call and kept in the pool, the
+ * cache slots and the prefill layer buffer: the same regions at the same
+ * offsets, each cut into blocks of 16 output rows x 128 inputs, block
+ * (rt, kc) at index rt * (in/128) + kc.
+ *   code block, 1024 bytes: the 16-byte chunk j (inputs 32j..32j+31 of the
+ *     block) of row r sits at byte (16 j + r) * 16;
+ *   scale (and bias) block, 64 bytes: row r's 4 bytes at 4 r, the canonical
+ *     bytes that cover the block's 128 inputs (two bf16 group values for
+ *     int4, four e8m0 exponents for MXFP4).
+ * A wavefront reads a block with one contiguous 1 KB load and its scales with
+ * one 64-byte load (the canonical layout needs one memory request per row).
+ * Requires hidden and inter to be multiples of 128.
+ *
+ * moe355_pack_experts: n experts from the canonical layout at src to the
+ * device layout at dst (device arrays of n * S bytes that must not overlap).
+ * Asynchronous on `stream`.  Errors: MOE355_EINVAL for a bad descriptor, null
+ * pointers or n < 0; MOE355_ENOTSUP when hidden or inter is not a multiple of
+ * 128.
+ */
+moe355_status moe355_pack_experts(const moe355_layer_desc* d, const uint8_t* src, uint8_t* dst,
+                                  int64_t n, hipStream_t stream);
 
 /*
  * The HBM expert cache [FT-zh, Core method: N slots shared by every MoE layer,

@@ -16,7 +16,7 @@ from .abi import (LayerDesc, Cache, EvictPolicy, ClassifyOut, ROUTE_SOFTMAX_TOPK
                   MODE_PERMUTE, Moe355Error, lib_path, load)
 from .ops import (router_logits, route, dedup, classify_evict, cache_fill, cache_rebuild,
                   permute, expert_ffn_decode, decode_layer, route_plan, evict_fill,
-                  expert_ffn_prefill, combine, workspace_bytes,
+                  expert_ffn_prefill, combine, workspace_bytes, pack_experts,
                   expert_bytes, version, DeviceCache, DeviceClassifyOut)
 
 __all__ = [
@@ -26,5 +26,6 @@ __all__ = [
     "cache_fill", "cache_rebuild", "permute", "expert_ffn_decode", "decode_layer", "route_plan",
     "evict_fill",
     "expert_ffn_prefill",
-    "combine", "workspace_bytes", "expert_bytes", "version", "DeviceCache", "DeviceClassifyOut",
+    "combine", "workspace_bytes", "pack_experts", "expert_bytes", "version", "DeviceCache",
+    "DeviceClassifyOut",
 ]

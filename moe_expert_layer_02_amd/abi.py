@@ -54,6 +54,7 @@ _SIGS = {
     "moe355_last_error": (ctypes.c_char_p, []),
     "moe355_version": (ctypes.c_char_p, []),
     "moe355_expert_bytes": (c_i64, [_P(LayerDesc)]),
+    "moe355_pack_experts": (c_i32, [_P(LayerDesc), c_ptr, c_ptr, c_i64, c_ptr]),
     "moe355_router_logits": (c_i32, [_P(LayerDesc), c_ptr, c_ptr, c_i32, c_ptr, c_ptr]),
     "moe355_route": (c_i32, [_P(LayerDesc), c_ptr, c_i32, c_ptr, c_ptr, c_ptr]),
     "moe355_dedup": (c_i32, [c_ptr, c_i32, c_i32, _P(ClassifyOut), c_ptr]),

@@ -269,17 +269,20 @@ struct WSlab {
     uint32_t bi[RT];
 };
 
-// Byte offsets of row r's slab at input kb: codes, scale/exponent dword, bias
-// dword (32-bit: an expert's blob is far below 4 GiB).  Scale rows are kdim / 32
-// bytes in both formats.
+// Byte offsets, within a matrix's regions, of lane (ln, gq)'s part of the slab
+// of rows r0 .. r0+15 (r0 a multiple of 16) at input kb (a multiple of 128): in
+// the device layout that slab is one block, its codes one contiguous 1 KB (the
+// lane's chunk gq of row ln at (16 gq + ln) * 16) and its scale words 64
+// contiguous bytes (row ln's at 4 ln).  32-bit: a blob is far below 4 GiB.
 struct SlabOff {
     uint32_t q, s;
 };
-template <int FMT>
-__device__ __forceinline__ SlabOff slab_off(int r, int kdim, int kb, int gq) {
+__device__ __forceinline__ SlabOff slab_off(int r0, int kdim, int kb, int ln, int gq) {
+    const uint32_t blk = static_cast<uint32_t>(r0 / 16) * static_cast<uint32_t>(kdim / 128) +
+                         static_cast<uint32_t>(kb / 128);
     SlabOff o;
-    o.q = static_cast<uint32_t>(r) * static_cast<uint32_t>(kdim / 2) + static_cast<uint32_t>(kb / 2 + 16 * gq);
-    o.s = static_cast<uint32_t>(r) * static_cast<uint32_t>(kdim / 32) + static_cast<uint32_t>(kb / 32);
+    o.q = blk * 1024u + static_cast<uint32_t>(16 * gq + ln) * 16u;
+    o.s = blk * 64u + static_cast<uint32_t>(ln) * 4u;
     return o;
 }
 
@@ -289,7 +292,7 @@ __device__ __forceinline__ void load_wslab(const DecodeParams& p, gbytes src, in
                                            WSlab<RT>& w) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-        const SlabOff o = slab_off<FMT>(row0 + 16 * t + ln, kdim, kb, gq);
+        const SlabOff o = slab_off(row0 + 16 * t, kdim, kb, ln, gq);
         w.q[t] = ldg16(src + (static_cast<uint32_t>(p.q_off[m]) + o.q));
         w.sc[t] = ldg4(src + (static_cast<uint32_t>(p.s_off[m]) + o.s));
         // every lane loads (a broadcast within the row); only chunk-0 lanes use it
@@ -303,7 +306,7 @@ __device__ __forceinline__ void store_wslab(const DecodeParams& p, gbytes_w dst,
                                             int kdim, int kb, int ln, int gq, const WSlab<RT>& w) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-        const SlabOff o = slab_off<FMT>(row0 + 16 * t + ln, kdim, kb, gq);
+        const SlabOff o = slab_off(row0 + 16 * t, kdim, kb, ln, gq);
         stg16(dst + (static_cast<uint32_t>(p.q_off[m]) + o.q), w.q[t]);
         if (gq == 0) {
             stg4(dst + (static_cast<uint32_t>(p.s_off[m]) + o.s), w.sc[t]);
@@ -390,11 +393,19 @@ __global__ void __launch_bounds__(NW * WAVE) gate_up_kernel(DecodeParams p) {
         load_wslab<FMT, RT>(p, ref.src, 1, row0, H, kb, ln, gq, st.u);
         const int4 pr = pl.plan[u];
         const int n = tg * TOK + ln;
-        const int t = pl.tok[pr.z + (n < pr.w ? n : 0)];
-        // 32-bit offset from the (scalar) base: x is far below 4 GiB
-        const uint16_t* xs = p.x + (static_cast<uint32_t>(t) * static_cast<uint32_t>(H) + static_cast<uint32_t>(kb + 32 * gq));
+        // only lanes of a token column that holds a pair load x (the address
+        // unit then sees a fraction of the lanes when an expert has few tokens);
+        // the other columns are zero and their MFMA results are never read
+        if (n < pr.w) {
+            const int t = pl.tok[pr.z + n];
+            // 32-bit offset from the (scalar) base: x is far below 4 GiB
+            const uint16_t* xs = p.x + (static_cast<uint32_t>(t) * static_cast<uint32_t>(H) + static_cast<uint32_t>(kb + 32 * gq));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st.x[i] = ldg16(xs + 8 * i);
+            for (int i = 0; i < 4; ++i) st.x[i] = ldg16(xs + 8 * i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st.x[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
     };
     f32x4 acc[2][RT];
     auto zero_acc = [&]() {
@@ -507,13 +518,17 @@ __global__ void __launch_bounds__(NW * WAVE) gate_up_kernel(DecodeParams p) {
         if (!SKIP || lc.valid) load(st[d], lc.item, lc.tg, lc.s);
         advance(lc);
     }
+    // Without SKIP every step of the unrolled ring issues its loads (a cursor
+    // past the end re-reads its last item) and only the computation is
+    // guarded: a guarded load lets the compiler's wait before a stage's MFMAs
+    // count only the loads present on every path (one stage of lookahead).
     bool done = false;
     while (!done) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
+            if (!SKIP || lc.valid) load(st[(d + D - 1) % D], lc.item, lc.tg, lc.s);
+            advance(lc);
             if (!done) {
-                if (!SKIP || lc.valid) load(st[(d + D - 1) % D], lc.item, lc.tg, lc.s);
-                advance(lc);
                 compute(st[d], cc.item, cc.tg, cc.s);
                 if (cc.s == NS - 1) epilogue(cc.item, cc.tg);
                 advance(cc);
@@ -563,12 +578,17 @@ __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
         load_wslab<FMT, RT>(p, ref.src, 2, tile * tile_rows, I, kb, ln, gq, st.w);
         const int4 pr = pl.plan[u];
         const int n = tg * TOK + ln;
-        const uint32_t o = static_cast<uint32_t>(pl.pairs[pr.z + (n < pr.w ? n : 0)]) * static_cast<uint32_t>(I) +
-                           static_cast<uint32_t>(kb + 32 * gq);
+        if (n < pr.w) {   // as in gate/up: only columns holding a pair load h
+            const uint32_t o = static_cast<uint32_t>(pl.pairs[pr.z + n]) * static_cast<uint32_t>(I) +
+                               static_cast<uint32_t>(kb + 32 * gq);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            st.hh[i] = ldg16(p.h_hi + o + 8 * i);
-            st.hl[i] = ldg16(p.h_lo + o + 8 * i);
+            for (int i = 0; i < 4; ++i) {
+                st.hh[i] = ldg16(p.h_hi + o + 8 * i);
+                st.hl[i] = ldg16(p.h_lo + o + 8 * i);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st.hh[i] = st.hl[i] = make_uint4(0u, 0u, 0u, 0u);
         }
     };
     f32x4 acc[RT];
@@ -632,13 +652,17 @@ __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
         if (!SKIP || lc.valid) load(st[d], lc.item, lc.tg, lc.s);
         advance(lc);
     }
+    // Without SKIP every step of the unrolled ring issues its loads (a cursor
+    // past the end re-reads its last item) and only the computation is
+    // guarded: a guarded load lets the compiler's wait before a stage's MFMAs
+    // count only the loads present on every path (one stage of lookahead).
     bool done = false;
     while (!done) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
+            if (!SKIP || lc.valid) load(st[(d + D - 1) % D], lc.item, lc.tg, lc.s);
+            advance(lc);
             if (!done) {
-                if (!SKIP || lc.valid) load(st[(d + D - 1) % D], lc.item, lc.tg, lc.s);
-                advance(lc);
                 compute(st[d], cc.item, cc.tg, cc.s);
                 if (cc.s == NS - 1) epilogue(cc.item, cc.tg);
                 advance(cc);

@@ -165,25 +165,21 @@ __device__ __forceinline__ float f16x8_sum(uint4 v, float s) {
 }
 
 // The bias MFMA operands for 8 groups [g0, g0+8): b' = b + 8 s of weight row n
-// as an f16 hi/lo pair (B side), and 8 group sums of one A row (A side).
+// as an f16 hi/lo pair (B side), and 8 group sums of one A row (A side).  In the
+// device layout group g of row n sits in the scale (bias) word of block
+// (n / 16, g / 2), half g % 2.
 __device__ __forceinline__ void bias_b(const uint8_t* W, const PrefillParams& p, int m, int n,
                                        int G, int g0, uint4* hi, uint4* lo) {
-    // rows of b and s are G bf16 values (G even); 8 groups from g0 (a multiple of 8)
-    const uint16_t* bp = reinterpret_cast<const uint16_t*>(W + p.b_off[m]) + static_cast<int64_t>(n) * G + g0;
-    const uint16_t* sp = reinterpret_cast<const uint16_t*>(W + p.s_off[m]) + static_cast<int64_t>(n) * G + g0;
+    const int64_t row = static_cast<int64_t>(n / 16) * (G / 2) * 64 + (n & 15) * 4;
+    const uint8_t* bp = W + p.b_off[m] + row;
+    const uint8_t* sp = W + p.s_off[m] + row;
     uint32_t bw[4] = {0u, 0u, 0u, 0u}, sw[4] = {0u, 0u, 0u, 0u};
-    if (g0 + 8 <= G) {
-        const uint4 b4 = *reinterpret_cast<const uint4*>(bp), s4 = *reinterpret_cast<const uint4*>(sp);
-        bw[0] = b4.x; bw[1] = b4.y; bw[2] = b4.z; bw[3] = b4.w;
-        sw[0] = s4.x; sw[1] = s4.y; sw[2] = s4.z; sw[3] = s4.w;
-    } else {
-        // a short row (G = 2 or 4 groups, always even): only the dwords inside it
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (g0 + 2 * j < G) {
-                bw[j] = reinterpret_cast<const uint32_t*>(bp)[j];
-                sw[j] = reinterpret_cast<const uint32_t*>(sp)[j];
-            }
+    for (int j = 0; j < 4; ++j) {
+        if (g0 + 2 * j < G) {   // a short row (G = 2 or 4 groups, always even) stops early
+            const int64_t o = static_cast<int64_t>(g0 / 2 + j) * 64;
+            bw[j] = *reinterpret_cast<const uint32_t*>(bp + o);
+            sw[j] = *reinterpret_cast<const uint32_t*>(sp + o);
         }
     }
     uint32_t h[4], l[4];
@@ -321,6 +317,22 @@ __device__ __forceinline__ uint4 a_operand(const uint4* A, int mt, int ln, int h
     return A[r * 8 + (c ^ (r & 7))];
 }
 
+// Byte offsets (from the expert's blob) of weight sources in the device
+// layout, where each region is cut into blocks of 16 rows x 128 inputs (a code
+// block of 1 KB holds chunk j of row r at (16 j + r) * 16; a scale block holds
+// row r's word at 4 r).  A 64-input stage kk is half a block: chunks
+// 2 (kk & 1) + {0, 1}, so lane half hh of row n reads chunk 2 (kk & 1) + hh of
+// block (n / 16, kk / 2), and the word that covers the stage is the block's.
+__device__ __forceinline__ uint32_t code_src(int64_t q_off, int n, int kdim, int hh) {
+    return static_cast<uint32_t>(q_off + static_cast<int64_t>(n / 16) * (kdim / 128) * 1024 +
+                                 (16 * hh + (n & 15)) * 16);
+}
+__device__ __forceinline__ uint32_t code_step(int kk) { return (kk >> 1) * 1024 + (kk & 1) * 512; }
+__device__ __forceinline__ uint32_t scale_src(int64_t s_off, int n, int kdim) {
+    return static_cast<uint32_t>(s_off + static_cast<int64_t>(n / 16) * (kdim / 128) * 64 + (n & 15) * 4);
+}
+__device__ __forceinline__ uint32_t scale_step(int kk) { return (kk >> 1) * 64; }
+
 // Stage slot layouts (bytes).  gate/up: A = 128 rows x 64 inputs; B codes
 // [wavefront][4 column tiles][64 lanes] x 16 bytes; scales [wavefront][2][64]
 // dwords, load j holding the scale dwords of the wavefront's weight rows
@@ -393,11 +405,9 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
         }
         uint32_t bq[4], bsc[2];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            bq[c] = static_cast<uint32_t>(p.q_off[c >> 1] + static_cast<int64_t>(fr + 32 * (c & 1) + ln) * (H / 2) + hh * 16);
+        for (int c = 0; c < 4; ++c) bq[c] = code_src(p.q_off[c >> 1], fr + 32 * (c & 1) + ln, H, hh);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            bsc[j] = static_cast<uint32_t>(p.s_off[j] + static_cast<int64_t>(fr + lane) * (H / 32));
+        for (int j = 0; j < 2; ++j) bsc[j] = scale_src(p.s_off[j], fr + lane, H);
 
         f32x16 R[4][4];   // [column tile][row tile]
 #pragma unroll
@@ -409,9 +419,9 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) dma16(xs, aoff[j] + kk * 128, sl + GU_A + (4 * wv + j) * 1024);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) dma16(W, bq[c] + kk * 32, sl + GU_B + (4 * wv + c) * 1024);
+            for (int c = 0; c < 4; ++c) dma16(W, bq[c] + code_step(kk), sl + GU_B + (4 * wv + c) * 1024);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) dma4(W, bsc[j] + (kk >> 1) * 4, sl + GU_S + (2 * wv + j) * 256);
+            for (int j = 0; j < 2; ++j) dma4(W, bsc[j] + scale_step(kk), sl + GU_S + (2 * wv + j) * 256);
         };
         auto compute = [&](int kk, int slot) {
             const uint8_t* sp = ring + slot * GU_SLOT;
@@ -610,11 +620,9 @@ __global__ void __launch_bounds__(256) down_mfma(PrefillParams p) {
         }
         uint32_t bq[4], bsc[2];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            bq[c] = static_cast<uint32_t>(p.q_off[2] + static_cast<int64_t>(nr + 32 * c + ln) * (I / 2) + hh * 16);
+        for (int c = 0; c < 4; ++c) bq[c] = code_src(p.q_off[2], nr + 32 * c + ln, I, hh);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            bsc[j] = static_cast<uint32_t>(p.s_off[2] + static_cast<int64_t>(nr + 64 * j + lane) * (I / 32));
+        for (int j = 0; j < 2; ++j) bsc[j] = scale_src(p.s_off[2], nr + 64 * j + lane, I);
 
         f32x16 R[4][4];   // [row tile][column tile]
 #pragma unroll
@@ -629,9 +637,9 @@ __global__ void __launch_bounds__(256) down_mfma(PrefillParams p) {
                 dma16(lb, aoff[j] + kk * 128, sl + DN_AL + (4 * wv + j) * 1024);
             }
 #pragma unroll
-            for (int c = 0; c < 4; ++c) dma16(W, bq[c] + kk * 32, sl + DN_B + (4 * wv + c) * 1024);
+            for (int c = 0; c < 4; ++c) dma16(W, bq[c] + code_step(kk), sl + DN_B + (4 * wv + c) * 1024);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) dma4(W, bsc[j] + (kk >> 1) * 4, sl + DN_S + (2 * wv + j) * 256);
+            for (int j = 0; j < 2; ++j) dma4(W, bsc[j] + scale_step(kk), sl + DN_S + (2 * wv + j) * 256);
         };
         auto compute = [&](int kk, int slot) {
             const uint8_t* sp = ring + slot * DN_SLOT;

@@ -42,6 +42,17 @@ def expert_bytes(desc: LayerDesc) -> int:
     return int(load().moe355_expert_bytes(ctypes.byref(desc)))
 
 
+def pack_experts(desc: LayerDesc, src, dst, n: int, stream=None):
+    """n expert blobs from the canonical layout (src) to the device layout (dst)."""
+    _need(src, torch.uint8, "src")
+    _need(dst, torch.uint8, "dst")
+    S = expert_bytes(desc)
+    if src.numel() < n * S or dst.numel() < n * S:
+        raise ValueError(f"pack_experts: buffers hold fewer than {n} experts of {S} bytes")
+    check(load().moe355_pack_experts(ctypes.byref(desc), _ptr(src), _ptr(dst), n, _stream(stream)),
+          "moe355_pack_experts")
+
+
 def workspace_bytes(desc: LayerDesc, T: int, mode: int) -> int:
     return int(load().moe355_workspace_bytes(ctypes.byref(desc), T, mode))
 

@@ -24,6 +24,12 @@ def desc_of(w: C.Workload):
                        w.topk_group, w.route_scale, w.wfmt)
 
 
+def packer(desc):
+    """The library's canonical -> device layout conversion, as a pack(src, dst, n) callable."""
+    import moe_expert_layer_02_amd as m
+    return lambda src, dst, n: m.pack_experts(desc, src, dst, n)
+
+
 def check_close(got, want, what=""):
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)

@@ -12,7 +12,7 @@ from workloads import configs as C
 from workloads import experts as wx
 from workloads import traces as tr
 
-from gpu_common import BlobSource, check_close, desc_of, say
+from gpu_common import BlobSource, check_close, desc_of, packer, say
 
 pytestmark = pytest.mark.gpu
 
@@ -29,10 +29,9 @@ def _decode_whole_layer(w, x_bits, ids_np, wt_np, seed=None):
     from workloads import gpu as wg
     seed = C.seed(w.cid, 0) if seed is None else seed
     S = wx.expert_bytes(w.wfmt, w.hidden, w.inter)
-    layer = torch.empty(w.n_experts * S, dtype=torch.uint8, device="cuda")
-    wg.fill_experts(layer, 0, w.n_experts, w.wfmt, w.hidden, w.inter, seed)
-    T = x_bits.shape[0]
     desc = desc_of(w)
+    layer = wg.make_experts(w, 0, w.n_experts, seed, pack=packer(desc))
+    T = x_bits.shape[0]
     ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).cuda()
     wt = torch.from_numpy(np.ascontiguousarray(wt_np, dtype=np.float32)).cuda()
     exp = m.DeviceClassifyOut(max(1, min(T * w.top_k, w.n_experts)))
@@ -151,7 +150,7 @@ def test_decode_full_size_sampled_calls(cid, steps, sample):
     say(f"decode full size {w.name}: {steps} steps, sampled {sample}")
     desc = desc_of(w)
     trace = tr.DecodeTrace(w, steps)
-    pool = wg.make_pool(w)
+    pool = wg.make_pool(w, pack=packer(desc_of(w)))
     S = wx.expert_bytes(w.wfmt, w.hidden, w.inter)
     cache = m.DeviceCache(w.n_slots, w.n_layers, w.n_experts, S)
     K = w.victims_k

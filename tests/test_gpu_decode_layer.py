@@ -16,7 +16,7 @@ from workloads import configs as C
 from workloads import experts as wx
 from workloads import traces as tr
 
-from gpu_common import BlobSource, check_close, desc_of, say
+from gpu_common import BlobSource, check_close, desc_of, packer, say
 
 pytestmark = pytest.mark.gpu
 
@@ -94,7 +94,7 @@ def test_decode_layer_trace(cid, steps, sample, mode):
     w = C.ALL[cid]
     say(f"decode_layer trace {w.name} ({mode}): {steps} steps")
     trace = tr.DecodeTrace(w, steps)
-    pool = wg.make_pool(w)
+    pool = wg.make_pool(w, pack=packer(desc_of(w)))
     run = LayerRunner(w, w.n_slots, pool, mode)
     sim = ocache.CacheSim(w.n_slots, w.n_layers, w.n_experts)
     src = BlobSource(w)
@@ -138,7 +138,7 @@ def test_decode_step_graph_replay_matches_eager(mode):
     w = C.QWEN_DECODE
     steps = 6
     trace = tr.DecodeTrace(w, steps)
-    pool = wg.make_pool(w)
+    pool = wg.make_pool(w, pack=packer(desc_of(w)))
     # one eager step on a throwaway cache, so no kernel is launched for the
     # first time (occupancy query) while the graph is being captured
     warm = LayerRunner(w, w.n_slots, pool, mode)

@@ -12,7 +12,7 @@ from workloads import configs as C
 from workloads import experts as wx
 from workloads import traces as tr
 
-from gpu_common import BlobSource, check_close, desc_of, say
+from gpu_common import BlobSource, check_close, desc_of, packer, say
 
 pytestmark = pytest.mark.gpu
 
@@ -55,8 +55,7 @@ def _prefill(w, x_bits, ids_np, wt_np, layer_seed):
     desc = desc_of(w)
     T = x_bits.shape[0]
     S = wx.expert_bytes(w.wfmt, w.hidden, w.inter)
-    layer = torch.empty(w.n_experts * S, dtype=torch.uint8, device="cuda")
-    wg.fill_experts(layer, 0, w.n_experts, w.wfmt, w.hidden, w.inter, layer_seed)
+    layer = wg.make_experts(w, 0, w.n_experts, layer_seed, pack=packer(desc))
     ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).cuda()
     wt = torch.from_numpy(np.ascontiguousarray(wt_np, dtype=np.float32)).cuda()
     x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).cuda().view(torch.bfloat16)

@@ -42,10 +42,37 @@ def fill_experts(dst: torch.Tensor, g0: int, count: int, wfmt: int, H: int, I: i
         raise RuntimeError(f"synth_fill_experts failed: hip error {rc}")
 
 
-def make_pool(w: Workload, n_layers: int | None = None, device="cuda") -> torch.Tensor:
-    """All experts of ``n_layers`` layers (default: every layer), [L * E * S] uint8."""
+def make_pool(w: Workload, n_layers: int | None = None, device="cuda", pack=None) -> torch.Tensor:
+    """All experts of ``n_layers`` layers (default: every layer), [L * E * S] uint8.
+
+    The bytes are generated in the canonical layout; with ``pack(src, dst, n)``
+    (the caller's layout conversion) each layer is generated into a scratch
+    buffer and converted into the pool.
+    """
     L = w.n_layers if n_layers is None else n_layers
+    E = w.n_experts
     S = expert_bytes(w.wfmt, w.hidden, w.inter)
-    pool = torch.empty(L * w.n_experts * S, dtype=torch.uint8, device=device)
-    fill_experts(pool, 0, L * w.n_experts, w.wfmt, w.hidden, w.inter, seed(w.cid, 0))
+    pool = torch.empty(L * E * S, dtype=torch.uint8, device=device)
+    if pack is None:
+        fill_experts(pool, 0, L * E, w.wfmt, w.hidden, w.inter, seed(w.cid, 0))
+        return pool
+    scratch = torch.empty(E * S, dtype=torch.uint8, device=device)
+    for l in range(L):
+        fill_experts(scratch, l * E, E, w.wfmt, w.hidden, w.inter, seed(w.cid, 0))
+        pack(scratch, pool[l * E * S:(l + 1) * E * S], E)
+    del scratch
     return pool
+
+
+def make_experts(w: Workload, g0: int, count: int, seed_value: int, pack=None,
+                 device="cuda") -> torch.Tensor:
+    """``count`` experts from global expert index ``g0``, canonical bytes converted
+    by ``pack(src, dst, n)`` when given."""
+    S = expert_bytes(w.wfmt, w.hidden, w.inter)
+    raw = torch.empty(count * S, dtype=torch.uint8, device=device)
+    fill_experts(raw, g0, count, w.wfmt, w.hidden, w.inter, seed_value)
+    if pack is None:
+        return raw
+    out = torch.empty_like(raw)
+    pack(raw, out, count)
+    return out
