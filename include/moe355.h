@@ -266,8 +266,16 @@ moe355_status moe355_permute(const moe355_layer_desc* d, const int32_t* topk_ids
  * else from pool + (layer*E + e) * S (pool = one layer's buffer with layer = 0
  * for a whole-layer call).  x: device bf16 [T, H]; out: device fp32 [T, H];
  * ws: device scratch of moe355_workspace_bytes(d, T, MOE355_MODE_DECODE) bytes
- * (calls sharing one workspace must not overlap).  exp->plan and exp->pairs
- * (written by moe355_classify_evict or moe355_dedup) are required.  Two
+ * (calls sharing one workspace must not overlap).  Its first 8192 bytes hold
+ * the call's synchronisation counters: zero them once when the workspace is
+ * allocated; every call leaves them zero.  The 32-bit word at byte offset 4608
+ * is a sticky error word: nonzero means a bounded in-kernel wait gave up and
+ * that call's output is not valid.  exp->plan and exp->pairs (written by moe355_classify_evict or
+ * moe355_dedup) are required.
+ * Kernels: a small call (T <= 16, H in {1024, 2048, 4096}, distinct experts x
+ * I/16 <= the device's compute units, T*k*I*4 <= 32 KiB) runs as one launch in
+ * which the down blocks wait for the gate/up blocks and each owns 16 output
+ * rows of all experts (plain stores, a fixed summation order).  Otherwise two
  * kernels: gate/up (which also zeroes out), then down with the combine as fp32
  * atomic additions, so the order of a token's k additions is not fixed.
  * Limits: T*k <= 256; H and I in {128, 256, 512, 1024, 2048, 4096}.

@@ -352,28 +352,25 @@ struct Cursor {
 // flight per wavefront.  SKIP: a wavefront's loads past its last stage are
 // skipped instead of repeated (used when all of a wavefront's loads fit in the
 // ring's first D - 1 stages, so nothing is lost by the compiler's coarser wait).
-template <int FMT, int NW, int KW, int RT, int D, bool SKIP>
-__global__ void __launch_bounds__(NW * WAVE) gate_up_kernel(DecodeParams p) {
+// The gate/up work of block `bid` of `nblk`.  WH: h leaves multiplied by its
+// pair's routing weight (the fused small-call kernel sums experts in its down
+// products) and written through to the device coherence point; otherwise the
+// down pass applies the weight.
+template <int FMT, int NW, int KW, int RT, int D, bool SKIP, bool WH>
+__device__ __forceinline__ void gate_up_body(const DecodeParams& p, const PlanLds& pl,
+                                             f32x4 (&red)[SKIP ? 1 : 2][NW][RT][2][WAVE],
+                                             int bid, int nblk) {
     constexpr int RW = NW / KW;
     constexpr int NB = SKIP ? 1 : 2;   // reduction buffers (one item per block when SKIP)
-    __shared__ PlanLds pl;
-    __shared__ f32x4 red[NB][NW][RT][2][WAVE];
     const int lane = threadIdx.x & (WAVE - 1), ln = lane & 15, gq = lane >> 4;
     const int wv = threadIdx.x / WAVE, kw = wv % KW, rw = wv / KW;
-    stage_plan(p, pl);
-    {   // zero the layer output for the down launch's atomics
-        const int64_t n = static_cast<int64_t>(p.T) * p.H;
-        for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-             i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-            p.out[i] = 0.0f;
-    }
     const int H = p.H;
     const int kpart = H / KW, NS = kpart / SLAB, kbase = kw * kpart;
     const int tile_rows = RW * RT * 16;
     const int tiles = p.I / tile_rows;
     const int n_items = pl.n_uniq * tiles;
-    const int per = (n_items + gridDim.x - 1) / gridDim.x;
-    const int i_beg = blockIdx.x * per;
+    const int per = (n_items + nblk - 1) / nblk;
+    const int i_beg = bid * per;
     const int i_end = min(n_items, i_beg + per);
     if (i_beg >= i_end) return;
 
@@ -464,7 +461,40 @@ __global__ void __launch_bounds__(NW * WAVE) gate_up_kernel(DecodeParams p) {
             if (NB == 2) ebuf ^= 1;
         }
         const int n = tg * TOK + ln;
-        if (kw == 0 && n < pr.w) {
+        if (WH && kw == 0 && n < pr.w) {
+            // w * h of rows row0 + 16 t + 4 gq + 0..3 as one 16-byte piece (four hi
+            // halves, then four lo halves, rows in natural order) per lane: the
+            // four lanes of a token write 64 contiguous bytes, through to the
+            // device coherence point
+            const int pair = pl.pairs[pr.z + n];
+            const float wt = pl.w[pair];
+            const int row0 = (item - u * tiles) * tile_rows + rw * RT * 16;
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float hv = silu(acc[0][t][r]) * acc[1][t][r] * wt;
+                    if (FMT == MOE355_W_INT4_G64) {
+                        const _Float16 a = static_cast<_Float16>(hv);
+                        const _Float16 b = static_cast<_Float16>(hv - static_cast<float>(a));
+                        hi[r] = __builtin_bit_cast(uint16_t, a);
+                        lo[r] = __builtin_bit_cast(uint16_t, b);
+                    } else {
+                        const __bf16 a = static_cast<__bf16>(hv);
+                        const __bf16 b = static_cast<__bf16>(hv - static_cast<float>(a));
+                        hi[r] = __builtin_bit_cast(uint16_t, a);
+                        lo[r] = __builtin_bit_cast(uint16_t, b);
+                    }
+                }
+                const u32x4_t v = {hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                                   lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+                uint4* dst = reinterpret_cast<uint4*>(p.h_hi) +
+                             (static_cast<int64_t>(pair) * p.I + row0 + 16 * t + 4 * gq) / 4;
+                asm volatile("global_store_dwordx4 %0, %1, off sc1" :: "v"(dst), "v"(v) : "memory");
+            }
+        }
+        if (!WH && kw == 0 && n < pr.w) {
             const int pair = pl.pairs[pr.z + n];
             const int row0 = (item - u * tiles) * tile_rows + rw * RT * 16;
 #pragma unroll
@@ -536,6 +566,20 @@ __global__ void __launch_bounds__(NW * WAVE) gate_up_kernel(DecodeParams p) {
             }
         }
     }
+}
+
+template <int FMT, int NW, int KW, int RT, int D, bool SKIP>
+__global__ void __launch_bounds__(NW * WAVE) gate_up_kernel(DecodeParams p) {
+    __shared__ PlanLds pl;
+    __shared__ f32x4 red[SKIP ? 1 : 2][NW][RT][2][WAVE];
+    stage_plan(p, pl);
+    {   // zero the layer output for the down launch's atomics
+        const int64_t n = static_cast<int64_t>(p.T) * p.H;
+        for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+             i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+            p.out[i] = 0.0f;
+    }
+    gate_up_body<FMT, NW, KW, RT, D, SKIP, false>(p, pl, red, blockIdx.x, gridDim.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -672,6 +716,281 @@ __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fused small-call FFN: one launch in which blocks [0, G) run the gate/up work
+// (h leaves multiplied by the routing weight; they also zero the output) and
+// blocks [G, G + 2 H/16) come in pairs that own 16 output rows of every token:
+// each sums the down products of half of the distinct experts' slabs and adds
+// its result onto the output.  A down block loads and dequantises its weights at
+// once (they do not depend on h), then waits until all G gate/up blocks have
+// counted themselves done, stages the call's h in LDS and runs its products.
+//
+// Waits only ever point at lower block indices and a gate/up block never waits,
+// so the call finishes whatever the number of resident blocks: every XCD
+// dispatches its blocks in index order.  Every wait is also bounded (it gives
+// up, flags the error word and goes on) so that a block always exits.
+//
+// Synchronisation words, 256 bytes apart (so that no two share a cache line),
+// in the first SYNC_BYTES of the decode workspace; zero before a call and left
+// zero by it.  Word w sits at byte 256 w:
+//   0..7   gate/up blocks of group g = block % 8 done
+//   8      groups whose gate/up blocks are all done (what the down blocks poll)
+//   9..16  blocks of group g = block % 8 exited
+//   17     groups whose blocks have all exited; the last block to exit clears
+//          every counter
+//   18     error word, sticky: bit 0 = a bounded wait gave up
+// Counting in groups keeps each counter to about 1/8 of the blocks: atomic
+// operations on one address are serialised at the memory side, and 256 of
+// them cost about as much as the whole gate/up pass.
+//
+// h crosses between blocks without whole-cache maintenance: the gate/up blocks
+// store it with device-scope (write-through) stores and wait for their
+// completion before counting themselves done; the down blocks read it with
+// device-scope loads after seeing the count.  (A release or acquire fence at
+// device scope would write back or invalidate the XCD's whole L2, once per
+// block.)
+constexpr uint32_t SPIN_LIMIT = 1u << 18;   // polls of >= 128 cycles: tens of ms at most
+constexpr int SYNC_BYTES = 8192;
+__device__ __forceinline__ uint32_t* sync_word(uint32_t* sync, int w) { return sync + 64 * w; }
+constexpr int SW_DONE = 0, SW_DONE_TOP = 8, SW_EXIT = 9, SW_EXIT_TOP = 17, SW_ERR = 18;
+
+__device__ __forceinline__ uint32_t atomic_add_dev(uint32_t* a, uint32_t v) {
+    return __hip_atomic_fetch_add(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev(uint32_t* a, uint32_t v) {
+    __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// blocks b < n with b % 8 == g
+__device__ __forceinline__ uint32_t group_size(uint32_t n, uint32_t g) { return g < n ? (n - g + 7) / 8 : 0; }
+
+// A gate/up block (index < n_gu) counts itself done once its h stores are complete.
+__device__ __forceinline__ void signal_done(uint32_t* sync, uint32_t n_gu) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's h stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t g = blockIdx.x & 7;
+        if (atomic_add_dev(sync_word(sync, SW_DONE + g), 1u) == group_size(n_gu, g) - 1)
+            atomic_add_dev(sync_word(sync, SW_DONE_TOP), 1u);
+    }
+}
+
+__device__ __forceinline__ void wait_done(uint32_t* sync, uint32_t n_gu) {
+    if (threadIdx.x == 0) {
+        const uint32_t target = n_gu < 8 ? n_gu : 8;
+        const uint32_t* top = sync_word(sync, SW_DONE_TOP);
+        uint32_t n = 0;
+        while (__hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++n == SPIN_LIMIT) {
+                __hip_atomic_fetch_or(sync_word(sync, SW_ERR), 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void block_exit(uint32_t* sync) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t nblk = gridDim.x, g = blockIdx.x & 7;
+        if (atomic_add_dev(sync_word(sync, SW_EXIT + g), 1u) == group_size(nblk, g) - 1) {
+            store_dev(sync_word(sync, SW_EXIT + g), 0u);   // the whole group has exited
+            const uint32_t groups = nblk < 8 ? nblk : 8;
+            if (atomic_add_dev(sync_word(sync, SW_EXIT_TOP), 1u) == groups - 1) {
+                // every block is past its waits
+                for (int w = 0; w < 8; ++w) store_dev(sync_word(sync, SW_DONE + w), 0u);
+                store_dev(sync_word(sync, SW_DONE_TOP), 0u);
+                store_dev(sync_word(sync, SW_EXIT_TOP), 0u);
+            }
+        }
+    }
+}
+
+// 16 bytes by two device-scope 8-byte loads.
+__device__ __forceinline__ uint4 ld_dev16(const void* q) {
+    const uint64_t* w = reinterpret_cast<const uint64_t*>(q);
+    const uint64_t a = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t b = __hip_atomic_load(w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_uint4(static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32),
+                      static_cast<uint32_t>(b), static_cast<uint32_t>(b >> 32));
+}
+
+constexpr int SMALL_DB = 2;            // (expert, slab) items per down wavefront
+constexpr int SMALL_H_LDS = 32768;     // bytes of h (hi and lo halves of T*k*I values) in LDS
+
+// One slab's weights as MFMA A operands (and, for int4, the bias operand).
+struct ASlab {
+    uint4 a[4];
+    uint4 bias;
+};
+template <int FMT>
+__device__ __forceinline__ ASlab prep_a(const WSlab<1>& w, int gq) {
+    ASlab r;
+    const uint32_t d4[4] = {w.q[0].x, w.q[0].y, w.q[0].z, w.q[0].w};
+    if (FMT == MOE355_W_INT4_G64) {
+        const half2_t s2 = int4_scale(w.sc[0], gq);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r.a[j] = a_int4(d4[j], s2);
+        r.bias = bias_a_operand(w.bi[0], w.sc[0], gq);
+    } else {
+        const float scale = e8m0_to_f32((w.sc[0] >> (8 * gq)) & 0xFFu);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r.a[j] = a_fp4(d4[j], scale);
+        r.bias = make_uint4(0u, 0u, 0u, 0u);
+    }
+    return r;
+}
+
+// Down rows r0 .. r0+15 of every token, half `half` of the (distinct expert u,
+// 128-input slab) items: item 2 (wv + NW i) + half for i < SMALL_DB.  The B
+// operand's column n is token n (T <= 16), holding that token's weighted h for
+// u, or zero when the token is not routed to u.  The weights are loaded and
+// dequantised before the wait; the wavefronts' partial sums meet through LDS
+// and the two halves meet in fp32 atomic additions onto the zeroed output
+// (0 + a + b in either order gives the same sum).
+template <int FMT, int NW>
+__device__ __forceinline__ void down_rows_body(const DecodeParams& p, const PlanLds& pl,
+                                               uint4* hs, f32x4 (&red)[NW][WAVE], int r0,
+                                               int half, uint32_t* sync, uint32_t n_gu) {
+    const int lane = threadIdx.x & (WAVE - 1), ln = lane & 15, gq = lane >> 4;
+    const int wv = threadIdx.x / WAVE;
+    const int I = p.I, nsl = I / SLAB;
+    const int n_items = pl.n_uniq * nsl;
+    auto item_of = [&](int i) { return 2 * (wv + i * NW) + half; };
+    // weights first (unconditional: an item past the end re-reads the last one)
+    WSlab<1> w[SMALL_DB];
+    if (n_items > 0) {
+#pragma unroll
+        for (int i = 0; i < SMALL_DB; ++i) {
+            const int j = min(item_of(i), n_items - 1);
+            const int u = j / nsl, sl = j - u * nsl;
+            load_wslab<FMT, 1>(p, expert_ref(p, pl, u).src, 2, r0, I, sl * SLAB, ln, gq, w[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < SMALL_DB; ++i) {   // fill-through of this block's down bytes
+        const int j = item_of(i);
+        if (j < n_items) {
+            const int u = j / nsl;
+            const ExpertRef ref = expert_ref(p, pl, u);
+            if (ref.dst) store_wslab<FMT, 1>(p, ref.dst, 2, r0, I, (j - u * nsl) * SLAB, ln, gq, w[i]);
+        }
+    }
+    ASlab A[SMALL_DB];
+    int hoff[SMALL_DB];   // LDS piece of the lane's h for each item, or -1 (token not routed)
+#pragma unroll
+    for (int i = 0; i < SMALL_DB; ++i) {
+        A[i] = prep_a<FMT>(w[i], gq);
+        const int j = item_of(i);
+        hoff[i] = -1;
+        if (j < n_items) {
+            const int u = j / nsl, sl = j - u * nsl;
+            const int4 pr = pl.plan[u];
+            for (int n = 0; n < pr.w; ++n)
+                if (pl.tok[pr.z + n] == ln) hoff[i] = (pl.pairs[pr.z + n] * I + sl * SLAB + 32 * gq) / 4;
+        }
+    }
+    wait_done(sync, n_gu);
+    // h pieces: [pair][I / 4] x 16 bytes (four hi halves, then four lo halves)
+    const int nc = p.T * p.k * I / 4;
+    {   // stage every pair's h in LDS: at most four pieces per thread
+        static_assert(SMALL_H_LDS / 16 <= 4 * NW * WAVE, "h staging covers four pieces per thread");
+        constexpr int NT = NW * WAVE;
+        const int t0 = threadIdx.x;
+        uint4 a0, a1, a2, a3;
+        if (t0 < nc) a0 = ld_dev16(reinterpret_cast<const uint4*>(p.h_hi) + t0);
+        if (t0 + NT < nc) a1 = ld_dev16(reinterpret_cast<const uint4*>(p.h_hi) + t0 + NT);
+        if (t0 + 2 * NT < nc) a2 = ld_dev16(reinterpret_cast<const uint4*>(p.h_hi) + t0 + 2 * NT);
+        if (t0 + 3 * NT < nc) a3 = ld_dev16(reinterpret_cast<const uint4*>(p.h_hi) + t0 + 3 * NT);
+        if (t0 < nc) hs[t0] = a0;
+        if (t0 + NT < nc) hs[t0 + NT] = a1;
+        if (t0 + 2 * NT < nc) hs[t0 + 2 * NT] = a2;
+        if (t0 + 3 * NT < nc) hs[t0 + 3 * NT] = a3;
+        __syncthreads();
+    }
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f}, acc_lo = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < SMALL_DB; ++i) {
+        if (item_of(i) >= n_items) break;
+        // B operands of the lane's 32 inputs sl * 128 + 32 gq + 8 q + (0..7): hi and
+        // lo halves, in the int4 A order (0,4,1,5,2,6,3,7) or, for MXFP4, natural
+        uint4 hh[4], hl[4];
+        if (hoff[i] >= 0) {
+            const uint4* src = hs + hoff[i];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint4 a = src[2 * q], b = src[2 * q + 1];   // inputs 0..3, 4..7
+                if (FMT == MOE355_W_INT4_G64) {
+                    hh[q] = make_uint4(__builtin_amdgcn_perm(b.x, a.x, 0x05040100u), __builtin_amdgcn_perm(b.x, a.x, 0x07060302u),
+                                       __builtin_amdgcn_perm(b.y, a.y, 0x05040100u), __builtin_amdgcn_perm(b.y, a.y, 0x07060302u));
+                    hl[q] = make_uint4(__builtin_amdgcn_perm(b.z, a.z, 0x05040100u), __builtin_amdgcn_perm(b.z, a.z, 0x07060302u),
+                                       __builtin_amdgcn_perm(b.w, a.w, 0x05040100u), __builtin_amdgcn_perm(b.w, a.w, 0x07060302u));
+                } else {
+                    hh[q] = make_uint4(a.x, a.y, b.x, b.y);
+                    hl[q] = make_uint4(a.z, a.w, b.z, b.w);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) hh[q] = hl[q] = make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc = mma<FMT>(A[i].a[q], hh[q], acc);
+            acc_lo = mma<FMT>(A[i].a[q], hl[q], acc_lo);
+        }
+        if (FMT == MOE355_W_INT4_G64) {
+            float part[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) part[q] = sum_f16x8(hl[q], sum_f16x8(hh[q], 0.0f));
+            acc = mma<FMT>(A[i].bias, bias_b_operand((part[0] + part[1]) + (part[2] + part[3]), gq), acc);
+        }
+    }
+    acc += acc_lo;
+    red[wv][lane] = acc;
+    __syncthreads();
+    if (wv == 0) {
+#pragma unroll
+        for (int o = 1; o < NW; ++o) acc += red[o][lane];
+        if (ln < p.T) {
+            float* o = p.out + static_cast<int64_t>(ln) * p.H + r0 + 4 * gq;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) unsafeAtomicAdd(o + r, acc[r]);
+        }
+    }
+}
+
+template <int FMT, int NW, int D>
+__global__ void __launch_bounds__(NW * WAVE, 4) ffn_small_kernel(DecodeParams p, uint32_t n_gu,
+                                                              uint32_t* sync) {
+    __shared__ PlanLds pl;
+    // the gate/up reduction buffers, or the staged h and the down reduction
+    constexpr int GU_BYTES = NW * 2 * WAVE * 16;
+    constexpr int DN_BYTES = SMALL_H_LDS + NW * WAVE * 16;
+    __shared__ uint4 raw[(GU_BYTES > DN_BYTES ? GU_BYTES : DN_BYTES) / 16];
+    stage_plan(p, pl);
+    if (blockIdx.x < n_gu) {
+        {   // zero the output for the down blocks' additions (written through, and
+            // complete before this block counts itself done)
+            const int n = p.T * p.H;
+            uint32_t* o = reinterpret_cast<uint32_t*>(p.out);
+            for (int i = blockIdx.x * (NW * WAVE) + threadIdx.x; i < n; i += n_gu * (NW * WAVE))
+                store_dev(o + i, 0u);
+        }
+        gate_up_body<FMT, NW, NW, 1, D, true, true>(
+            p, pl, *reinterpret_cast<f32x4 (*)[1][NW][1][2][WAVE]>(raw), blockIdx.x, n_gu);
+        signal_done(sync, n_gu);
+    } else {
+        const int b = blockIdx.x - n_gu;   // two blocks per 16-row tile
+        down_rows_body<FMT, NW>(p, pl, raw,
+                                *reinterpret_cast<f32x4 (*)[NW][WAVE]>(raw + SMALL_H_LDS / 16),
+                                (b >> 1) * 16, b & 1, sync, n_gu);
+    }
+    block_exit(sync);
+}
+
 bool valid_row_len(int L) {
     return L == 128 || L == 256 || L == 512 || L == 1024 || L == 2048 || L == 4096;
 }
@@ -720,10 +1039,31 @@ moe355_status launch_gate_up_wide(const DecodeParams& p, int max_uniq, hipStream
     return check_launch("expert_ffn_decode gate_up");
 }
 
+// The fused small-call kernel when the call fits it: at most 16 tokens, gate/up
+// items for at most one block per CU, down items for eight wavefronts of
+// SMALL_DB each, and h small enough for LDS.
 template <int FMT>
-moe355_status launch_decode(const DecodeParams& p, int max_uniq, hipStream_t stream) {
+bool launch_small(const DecodeParams& p, int max_uniq, uint32_t* sync, hipStream_t stream) {
+    if (p.T > TOK || !(p.H == 1024 || p.H == 2048 || p.H == 4096)) return false;
+    if (max_uniq * (p.I / 16) > device_cus() || max_uniq * (p.I / SLAB) > 2 * 8 * SMALL_DB) return false;
+    if (static_cast<int64_t>(p.T) * p.k * p.I * 4 > SMALL_H_LDS) return false;
+    const uint32_t n_gu = static_cast<uint32_t>(max_uniq * (p.I / 16));
+    const int blocks = static_cast<int>(n_gu) + 2 * (p.H / 16);
+    // H / 8 inputs per gate/up wavefront: one or two slabs of each matrix, all
+    // in flight at once; four slabs (H = 4096) go through a three-stage ring
+    if (p.H <= 2048)
+        ffn_small_kernel<FMT, 8, 2><<<blocks, 8 * WAVE, 0, stream>>>(p, n_gu, sync);
+    else
+        ffn_small_kernel<FMT, 8, 3><<<blocks, 8 * WAVE, 0, stream>>>(p, n_gu, sync);
+    return true;
+}
+
+template <int FMT>
+moe355_status launch_decode(const DecodeParams& p, int max_uniq, uint32_t* sync,
+                            hipStream_t stream) {
     moe355_status st;
     const int cus = device_cus();
+    if (launch_small<FMT>(p, max_uniq, sync, stream)) return check_launch("expert_ffn_decode");
     if (p.H >= 1024 && p.H <= 4096 && max_uniq * (p.I / 16) <= cus)
         st = launch_gate_up_wide<FMT>(p, max_uniq, stream);
     else if (p.H >= 512)   // wavefronts splitting H: 4 when H >= 512
@@ -770,7 +1110,7 @@ __global__ void combine_kernel(int T, int H, int k, const float* __restrict__ y,
 
 size_t decode_ws_bytes(const moe355_layer_desc* d, int T) {
     const size_t tk = static_cast<size_t>(T) * d->top_k;
-    return 256 + 2 * tk * d->inter * sizeof(uint16_t);   // h as hi and lo halves
+    return SYNC_BYTES + 2 * tk * d->inter * sizeof(uint16_t);   // h as hi and lo halves
 }
 
 // Shared by the public decode call and the fused decode-layer call.
@@ -812,7 +1152,7 @@ moe355_status decode_ffn(const moe355_layer_desc* d, const void* x_bf16, int32_t
         p.b_off[m] = L.b_off[m];
     }
     const size_t tkI = static_cast<size_t>(T) * d->top_k * d->inter;
-    p.h_hi = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + 256);
+    p.h_hi = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + SYNC_BYTES);
     p.h_lo = p.h_hi + tkI;
     p.out = out;
     if (cache) {
@@ -832,8 +1172,9 @@ moe355_status decode_ffn(const moe355_layer_desc* d, const void* x_bf16, int32_t
     p.plan = exp->plan;
     p.pairs = exp->pairs;
     p.n_plan = max_uniq;
-    if (d->wfmt == MOE355_W_INT4_G64) return launch_decode<MOE355_W_INT4_G64>(p, max_uniq, stream);
-    return launch_decode<MOE355_W_MXFP4>(p, max_uniq, stream);
+    uint32_t* sync = static_cast<uint32_t*>(ws);   // the workspace's first SYNC_BYTES
+    if (d->wfmt == MOE355_W_INT4_G64) return launch_decode<MOE355_W_INT4_G64>(p, max_uniq, sync, stream);
+    return launch_decode<MOE355_W_MXFP4>(p, max_uniq, sync, stream);
 }
 
 }  // namespace moe355

@@ -65,6 +65,43 @@ SMALL = [
 ]
 
 
+def test_decode_small_call_sync_words_left_zero():
+    """The one-launch small-call FFN (gate/up and down blocks counting through
+    the workspace's first 8192 bytes) leaves those bytes zero after every call,
+    the error word (byte 4608) included, and gives the same output on repeated
+    calls: the down blocks sum the experts in a fixed order, and the two halves
+    of each tile add onto zero in either order to the same value."""
+    import torch
+    import moe_expert_layer_02_amd as m
+    from workloads import gpu as wg
+    H, I, E, k, T = 2048, 512, 64, 8, 1
+    w = C.Workload(cid=177, name="small-sync", hidden=H, inter=I, n_experts=E, top_k=k,
+                   route=0, wfmt=C.WFMT_INT4_G64)
+    say("decode small-call sync words")
+    desc = desc_of(w)
+    layer = wg.make_experts(w, 0, E, C.seed(w.cid, 0), pack=packer(desc))
+    rng = np.random.default_rng(7)
+    ws = torch.zeros(m.workspace_bytes(desc, T, m.MODE_DECODE), dtype=torch.uint8, device="cuda")
+    outs = []
+    for call in range(6):
+        # three calls with fresh inputs, then the same inputs three times in a row
+        r = rng if call < 3 else np.random.default_rng(11)
+        x_bits = tr.bf16_normal(r, (T, H))
+        ids_np, wt_np = oroute.softmax_topk(r.standard_normal((T, E)).astype(np.float32), k)
+        ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).cuda()
+        wt = torch.from_numpy(np.ascontiguousarray(wt_np, dtype=np.float32)).cuda()
+        exp = m.DeviceClassifyOut(min(T * k, E))
+        m.dedup(ids, E, exp)
+        out = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+        m.expert_ffn_decode(desc, _x_dev(x_bits), ids, wt, None, layer, 0, exp, out, ws)
+        torch.cuda.synchronize()
+        assert int(ws[:8192].count_nonzero()) == 0, f"call {call}: sync words not cleared"
+        outs.append(out.cpu().numpy())
+        if call == 0:
+            check_close(outs[0], _oracle_layer(w, x_bits, ids_np, wt_np), "small-call decode")
+    assert np.array_equal(outs[3], outs[4]) and np.array_equal(outs[4], outs[5])
+
+
 @pytest.mark.parametrize("H,I,E,k,T,wfmt", SMALL)
 def test_decode_small_shapes(H, I, E, k, T, wfmt):
     w = C.Workload(cid=100 + H // 256 + I // 64 + E, name="small", hidden=H, inter=I,
