@@ -266,9 +266,9 @@ moe355_status moe355_permute(const moe355_layer_desc* d, const int32_t* topk_ids
  * else from pool + (layer*E + e) * S (pool = one layer's buffer with layer = 0
  * for a whole-layer call).  x: device bf16 [T, H]; out: device fp32 [T, H];
  * ws: device scratch of moe355_workspace_bytes(d, T, MOE355_MODE_DECODE) bytes
- * (calls sharing one workspace must not overlap).  Its first 8192 bytes hold
- * the call's synchronisation counters: zero them once when the workspace is
- * allocated; every call leaves them zero.  The 32-bit word at byte offset 4608
+ * (calls sharing one workspace must not overlap).  Its first 65536 bytes hold
+ * the call's synchronisation counters and flags: zero them once when the
+ * workspace is allocated; every call leaves them zero.  The 32-bit word at byte offset 4608
  * is a sticky error word: nonzero means a bounded in-kernel wait gave up and
  * that call's output is not valid.  exp->plan and exp->pairs (written by moe355_classify_evict or
  * moe355_dedup) are required.

@@ -15,19 +15,13 @@
 // (ts, slot) keys among slots with ts < tick are found by an 8-bit-digit radix
 // select over LDS histograms, then ranked by counting.  Owning the whole call
 // in one workgroup keeps the table updates free of cross-workgroup atomics.
-#include <type_traits>
-
-#include "route_dev.h"
+#include "classify_dev.h"
 
 namespace moe355 {
 namespace {
 
 constexpr int CL_THREADS = 1024;
 constexpr int CL_WAVES = CL_THREADS / WAVE;
-constexpr int MAX_SLOTS = 16384;
-constexpr int MAX_EXPERTS = 1024;
-constexpr int MAX_LIST = 1024;
-constexpr uint32_t SMALL_K = 16;   // up to this many victims: min rounds instead of radix select
 
 // Exclusive block scan over CL_THREADS threads (all threads must call it).
 __device__ uint64_t block_excl_scan(uint64_t v, uint64_t* wave_tot, uint64_t* total) {
@@ -139,465 +133,17 @@ __device__ uint64_t radix_select(int n, uint32_t rank, int bits, KeyFn key_of, S
 
 }  // namespace
 
-struct ClassifyParams {
-    int mode;                  // ClassifyMode (internal.h)
-    int32_t* table;
-    int table_len;
-    int32_t* owner;
-    int64_t* slot_ts;
-    int N, E, layer;
-    const int64_t* tick_dev;   // tick = *tick_dev + tick_add when set, else tick_add
-    int64_t tick_add;
-    const int32_t* ids;
-    int n_ids;
-    int K, q_num, q_den;
-    // optional routing of the call's tokens before the bookkeeping
-    const float* logits;
-    int T, k, route_kind, n_group, topk_group;
-    float route_scale;
-    int32_t* ids_out;
-    float* w_out;
-    int32_t *uniq, *hit_e, *hit_s, *miss, *fill_e, *fill_s, *inplace, *victims, *counts;
-    int32_t *plan, *pairs;     // optional: the FFN's per-expert plan and grouped pairs
-};
-
 namespace {
 
-constexpr int OWN_SLOTS = 4096;   // owners staged in LDS for caches up to this size
+using ClassifyShared = ClassifySharedT<MAX_SLOTS, OWN_SLOTS, MAX_EXPERTS, MAX_LIST>;
 
-struct ClassifyShared {
-    uint32_t ts[MAX_SLOTS];
-    int32_t own[OWN_SLOTS];
-    int32_t tab[MAX_EXPERTS];    // this layer's row of the slot table
-    int32_t mark[MAX_EXPERTS];
-    int32_t upos[MAX_EXPERTS];   // expert -> its index u in uniq
-    int32_t pcnt[MAX_EXPERTS];   // routed pairs per u
-    int32_t pbeg[MAX_EXPERTS];   // first index of u's pairs
-    int32_t ids[MAX_LIST];       // the call's routed ids
-    int32_t plocal[MAX_LIST];    // a pair's place inside its expert's group
-    int32_t miss[MAX_LIST];
-    uint64_t sel_key[MAX_LIST];
-    int32_t victims[MAX_LIST];
-    int32_t vic_owner[MAX_LIST];
-    uint32_t hist[256];
-};
-
-// Inclusive prefix sum over the 64 lanes (DPP row shifts and row broadcasts).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-    v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false);  // row_shr:1
-    v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false);  // row_shr:2
-    v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false);  // row_shr:4
-    v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false);  // row_shr:8
-    v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
-    v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
-    return v;
-}
-
-// Minimum over the 64 lanes (an inclusive min-scan by the same DPP steps; lane
-// 63 ends with the minimum of all).
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-    v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, v, 0x111, 0xf, 0xf, false)));
-    v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, v, 0x112, 0xf, 0xf, false)));
-    v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, v, 0x114, 0xf, 0xf, false)));
-    v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, v, 0x118, 0xf, 0xf, false)));
-    v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, v, 0x142, 0xa, 0xf, false)));
-    v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, v, 0x143, 0xc, 0xf, false)));
-    return __builtin_amdgcn_readlane(v, 63);
-}
-
-// Exclusive prefix sum and total over the 64 lanes.
-__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t* total) {
-    const uint32_t inc = wave_incl_scan(v);
-    *total = __builtin_amdgcn_readlane(inc, 63);
-    return inc - v;
-}
-
-// Orders this wavefront's LDS accesses before the ones that follow: a compiler
-// barrier plus a wait for outstanding LDS operations only (global stores stay
-// in flight).
-__device__ __forceinline__ void wave_lds_sync() {
-    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+template <int SPL>
+__global__ void __launch_bounds__(CL_THREADS) classify_kernel(ClassifyParams cp) {
+    __shared__ ClassifyShared sh;
+    classify_body<SPL, CL_THREADS>(cp, sh, nullptr, nullptr);
 }
 
 }  // namespace
-
-// One layer call.  All 16 wavefronts request the slot timestamps, owners and
-// this layer's table row at once and route the call's tokens (one wavefront
-// per token); then a single wavefront does the bookkeeping with DPP scans and
-// LDS histograms, so no step after routing waits on a workgroup barrier.
-// SPT = slots per thread held in registers while routing runs (caches up to
-// SPT * CL_THREADS slots); SPT = 0 stores the timestamps before routing.
-// SPL = slots per lane the bookkeeping wavefront holds in registers (caches up
-// to 64 * SPL slots); SPL = 0 reads them from LDS.
-template <int SPT, int SPL>
-__global__ void __launch_bounds__(CL_THREADS) classify_kernel(ClassifyParams cp) {
-    __shared__ ClassifyShared sh;
-    const int tid = threadIdx.x;
-    int32_t* __restrict__ table = cp.table;
-    int32_t* __restrict__ owner = cp.owner;
-    int64_t* __restrict__ slot_ts = cp.slot_ts;
-    const int N = cp.N, E = cp.E, layer = cp.layer, K = cp.K, table_len = cp.table_len;
-    const int mode = cp.mode;
-    const bool dedup_only = mode == CLASSIFY_DEDUP;
-    const bool plan_only = mode == CLASSIFY_PLAN;     // no cache state changes
-    const bool evict_only = mode == CLASSIFY_EVICT;   // the plan is another call's
-    const bool need_slots = mode == CLASSIFY_FULL || evict_only;
-    const bool own_lds = N <= OWN_SLOTS;
-    const int n_ids = cp.logits ? cp.T * cp.k : cp.n_ids;
-
-    // ---- every wavefront: requests, routing, clears ---------------------------
-    constexpr int R = SPT > 0 ? SPT : 1;
-    int64_t ts_r[R];
-    int32_t own_r[R];
-#pragma unroll
-    for (int j = 0; j < SPT; ++j) {
-        const int sl = tid + j * CL_THREADS;
-        ts_r[j] = 0;
-        own_r[j] = -1;
-        if (need_slots && sl < N) {
-            ts_r[j] = slot_ts[sl];
-            if (own_lds) own_r[j] = owner[sl];
-        }
-    }
-    if (SPT == 0 && need_slots) {
-        for (int sl = tid; sl < N; sl += CL_THREADS) {
-            sh.ts[sl] = static_cast<uint32_t>(slot_ts[sl]);
-            if (own_lds) sh.own[sl] = owner[sl];
-        }
-    }
-    for (int e = tid; e < E; e += CL_THREADS) {
-        sh.tab[e] = dedup_only ? -1 : table[layer * E + e];
-        sh.mark[e] = 0;
-        sh.pcnt[e] = 0;
-    }
-    if (cp.logits) {
-        for (int t = tid / WAVE; t < cp.T; t += CL_WAVES) {
-            float w;
-            const int e = route_token(cp.logits + static_cast<int64_t>(t) * E, E, cp.k,
-                                      cp.route_kind, cp.n_group, cp.topk_group, cp.route_scale, &w);
-            const int lane = tid & (WAVE - 1);
-            if (lane < cp.k) {
-                cp.ids_out[t * cp.k + lane] = e;
-                cp.w_out[t * cp.k + lane] = w;
-                sh.ids[t * cp.k + lane] = e;
-            }
-        }
-    } else {
-        for (int i = tid; i < n_ids; i += CL_THREADS) sh.ids[i] = cp.ids[i];
-    }
-#pragma unroll
-    for (int j = 0; j < SPT; ++j) {
-        const int sl = tid + j * CL_THREADS;
-        if (need_slots && sl < N) {
-            sh.ts[sl] = static_cast<uint32_t>(ts_r[j]);
-            if (own_lds) sh.own[sl] = own_r[j];
-        }
-    }
-    const uint32_t tick = cp.tick_dev ? static_cast<uint32_t>(*cp.tick_dev + cp.tick_add)
-                                      : static_cast<uint32_t>(cp.tick_add);
-    __syncthreads();
-    if (tid >= WAVE) return;
-
-    // ---- one wavefront from here on ------------------------------------------
-    const int lane = tid;
-    const bool with_plan = cp.plan != nullptr && cp.pairs != nullptr && !evict_only;
-    for (int i = lane; i < n_ids; i += WAVE) {
-        const int e = sh.ids[i];
-        if (e >= 0 && e < E) sh.mark[e] = 1;  // ids out of range are ignored
-    }
-    wave_lds_sync();
-
-    // distinct experts, hits and misses; lane owns experts [e0, e0 + epl)
-    const int epl = (E + WAVE - 1) / WAVE;
-    const int e0 = lane * epl, e1 = min(E, e0 + epl);
-    auto slot_of = [&](int e) {
-        const int sl = sh.tab[e];
-        return (sl >= 0 && sl < N) ? sl : -1;  // an entry outside the cache counts as absent
-    };
-    uint32_t cu = 0, ch = 0, cm = 0;
-    for (int e = e0; e < e1; ++e) {
-        if (!sh.mark[e]) continue;
-        ++cu;
-        if (slot_of(e) >= 0) ++ch;
-        else ++cm;
-    }
-    uint32_t n_uniq, n_hit, n_miss;
-    const uint32_t bu = wave_excl_scan(cu, &n_uniq);
-    const uint32_t bh = wave_excl_scan(ch, &n_hit);
-    const uint32_t bm = wave_excl_scan(cm, &n_miss);
-    {
-        uint32_t u = bu, h = bh, mi = bm;
-        for (int e = e0; e < e1; ++e) {
-            if (!sh.mark[e]) continue;
-            if (!evict_only) cp.uniq[u] = e;
-            sh.upos[e] = static_cast<int32_t>(u++);
-            const int sl = slot_of(e);
-            if (dedup_only) continue;
-            if (sl >= 0) {
-                if (!evict_only) {
-                    cp.hit_e[h] = e;
-                    cp.hit_s[h] = sl;
-                }
-                ++h;
-                if (!plan_only) {
-                    sh.ts[sl] = tick;  // recency moves on a router selection
-                    slot_ts[sl] = tick;
-                }
-            } else {
-                if (!evict_only) cp.miss[mi] = e;
-                sh.miss[mi++] = e;
-            }
-        }
-    }
-    wave_lds_sync();
-
-    // the routed pairs of each distinct expert, grouped by u
-    if (with_plan) {
-        for (int i = lane; i < n_ids; i += WAVE) {
-            const int e = sh.ids[i];
-            sh.plocal[i] = (e >= 0 && e < E) ? atomicAdd(&sh.pcnt[sh.upos[e]], 1) : -1;
-        }
-        wave_lds_sync();
-        const int upl = (static_cast<int>(n_uniq) + WAVE - 1) / WAVE;
-        const int u0 = lane * upl, u1 = min(static_cast<int>(n_uniq), u0 + upl);
-        uint32_t c = 0, tot;
-        for (int u = u0; u < u1; ++u) c += sh.pcnt[u];
-        uint32_t b = wave_excl_scan(c, &tot);
-        for (int u = u0; u < u1; ++u) {
-            sh.pbeg[u] = static_cast<int32_t>(b);
-            b += sh.pcnt[u];
-        }
-        wave_lds_sync();
-        for (int i = lane; i < n_ids; i += WAVE) {
-            const int e = sh.ids[i];
-            if (e >= 0 && e < E) cp.pairs[sh.pbeg[sh.upos[e]] + sh.plocal[i]] = i;
-        }
-    }
-
-    if (dedup_only) {
-        if (lane < 6) cp.counts[lane] = lane == 0 ? static_cast<int32_t>(n_uniq) : 0;
-        if (with_plan)
-            for (int u = lane; u < static_cast<int>(n_uniq); u += WAVE)
-                reinterpret_cast<int4*>(cp.plan)[u] = make_int4(-1, 0, sh.pbeg[u], sh.pcnt[u]);
-        return;
-    }
-    if (plan_only) {
-        // hits are read from their slots, misses from the pool; the cache is
-        // updated later by the evict-only call
-        if (with_plan) {
-            for (int e = e0; e < e1; ++e) {
-                if (!sh.mark[e]) continue;
-                const int u = sh.upos[e];
-                reinterpret_cast<int4*>(cp.plan)[u] = make_int4(slot_of(e), 0, sh.pbeg[u], sh.pcnt[u]);
-            }
-        }
-        if (lane < 6) {
-            const uint32_t c3[3] = {n_uniq, n_hit, n_miss};
-            cp.counts[lane] = lane < 3 ? static_cast<int32_t>(c3[lane]) : 0;
-        }
-        return;
-    }
-
-    // ---- one scan of every slot's timestamp: the K oldest eligible slots -----
-    wave_lds_sync();   // hit stamps are in LDS
-    const int sbits = N > 1 ? 32 - __clz(N - 1) : 1;
-    const int spl = SPL > 0 ? SPL : (N + WAVE - 1) / WAVE;
-    const int s0 = lane * spl, s1 = min(N, s0 + spl);
-    // Victims: the n_vic smallest (ts << sbits | slot) keys among eligible slots.
-    // With 32-bit keys (tick << sbits fits) each lane holds its timestamps in
-    // registers; otherwise it reads them from LDS.
-    const bool narrow = (static_cast<uint64_t>(tick) << sbits) < (1ull << 32);
-    uint32_t n_elig = 0, n_vic = 0;
-    bool ranked = false;   // victims already written in rank order
-    auto select = [&](auto key_zero, auto in_regs) {
-        using KT = decltype(key_zero);
-        constexpr bool REGS = decltype(in_regs)::value && SPL > 0;
-        constexpr int RL = REGS ? SPL : 1;
-        uint32_t tsr[RL];
-        if constexpr (REGS) {
-#pragma unroll
-            for (int j = 0; j < SPL; j += 4) {
-                if (s0 + j + 3 < N) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(&sh.ts[s0 + j]);
-                    tsr[j] = v.x; tsr[j + 1] = v.y; tsr[j + 2] = v.z; tsr[j + 3] = v.w;
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) tsr[j + i] = s0 + j + i < N ? sh.ts[s0 + j + i] : ~0u;
-                }
-            }
-        }
-        // calls f(slot, ts) for each of this lane's slots
-        auto for_slots = [&](auto f) {
-            if constexpr (REGS) {
-#pragma unroll
-                for (int j = 0; j < SPL; ++j) f(s0 + j, tsr[j]);
-            } else {
-                for (int sl = s0; sl < s1; ++sl) f(sl, sh.ts[sl]);
-            }
-        };
-        uint32_t ce = 0;
-        for_slots([&](int sl, uint32_t t) { ce += (sl < N && t < tick) ? 1u : 0u; });
-        wave_excl_scan(ce, &n_elig);
-        n_vic = n_elig < static_cast<uint32_t>(K) ? n_elig : static_cast<uint32_t>(K);
-        if (n_vic == 0) return;
-        constexpr int KB = 8 * sizeof(KT);
-        auto key = [&](int sl, uint32_t t) { return (static_cast<KT>(t) << sbits) | static_cast<KT>(sl); };
-        if constexpr (REGS && KB == 32) {
-            if (n_vic <= SMALL_K) {
-                // Few victims: n_vic rounds of a wave-wide minimum, each over the keys
-                // above the previous pick; the picks come out in rank order.  An
-                // ineligible slot holds the key ~0, which no round reaches (eligible
-                // keys are below tick << sbits < 2^32 and n_vic <= n_elig).
-                uint32_t kr[RL];
-#pragma unroll
-                for (int j = 0; j < RL; ++j)
-                    kr[j] = (s0 + j < N && tsr[j] < tick) ? key(s0 + j, tsr[j]) : ~0u;
-                uint32_t from = 0;   // smallest key still eligible for a pick
-                int vic = -1;        // lane r keeps pick r
-                for (uint32_t r = 0; r < n_vic; ++r) {
-                    // min over kr[j] >= from of (kr[j] - from): the subtraction sends
-                    // the keys below `from` to the top of the unsigned range
-                    uint32_t lm = ~0u;
-#pragma unroll
-                    for (int j = 0; j < RL; ++j) lm = min(lm, kr[j] - from);
-                    const uint32_t m = wave_min_u32(lm) + from;
-                    if (static_cast<uint32_t>(lane) == r) vic = static_cast<int>(m & ((1u << sbits) - 1));
-                    from = m + 1;
-                }
-                if (static_cast<uint32_t>(lane) < n_vic) {
-                    sh.victims[lane] = vic;
-                    cp.victims[lane] = vic;
-                    if (own_lds) sh.vic_owner[lane] = sh.own[vic];
-                    else sh.vic_owner[lane] = owner[vic];
-                }
-                ranked = true;
-                return;
-            }
-        }
-        KT thr = ~static_cast<KT>(0);
-        if (n_elig > n_vic) {
-            const uint64_t top = static_cast<uint64_t>(tick) << sbits;
-            const int bits = 64 - __clzll(static_cast<long long>(top));
-            KT prefix = 0, pmask = 0;
-            uint32_t remaining = n_vic;
-            for (int shift = ((bits - 1) / 8) * 8; shift >= 0; shift -= 8) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sh.hist[lane * 4 + i] = 0;
-                wave_lds_sync();
-                for_slots([&](int sl, uint32_t t) {
-                    const KT k = key(sl, t);
-                    if (sl < N && t < tick && (k & pmask) == prefix)
-                        atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
-                });
-                wave_lds_sync();
-                uint32_t c4[4], local = 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    c4[i] = sh.hist[lane * 4 + i];
-                    local += c4[i];
-                }
-                uint32_t tot;
-                const uint32_t before = wave_excl_scan(local, &tot);
-                // the lane whose range of the histogram crosses `remaining`
-                const bool mine = before < remaining && remaining <= before + local;
-                uint32_t digit = 0, rem = 0;
-                if (mine) {
-                    uint32_t acc = before;
-                    for (int i = 0; i < 4; ++i) {
-                        if (acc + c4[i] >= remaining) {
-                            digit = lane * 4 + i;
-                            rem = remaining - acc;
-                            break;
-                        }
-                        acc += c4[i];
-                    }
-                }
-                const int src = __builtin_ctzll(__ballot(mine));
-                digit = __builtin_amdgcn_readlane(digit, src);
-                rem = __builtin_amdgcn_readlane(rem, src);
-                prefix |= static_cast<KT>(digit) << shift;
-                pmask |= static_cast<KT>(255) << shift;
-                remaining = rem;
-            }
-            thr = prefix;
-        }
-        static_assert(KB == 32 || KB == 64, "key width");
-        // collect the selected keys in slot order, then rank them by key
-        uint32_t cs = 0;
-        for_slots([&](int sl, uint32_t t) { cs += (sl < N && t < tick && key(sl, t) <= thr) ? 1u : 0u; });
-        uint32_t n_sel;
-        uint32_t at = wave_excl_scan(cs, &n_sel);
-        for_slots([&](int sl, uint32_t t) {
-            if (sl < N && t < tick && key(sl, t) <= thr) sh.sel_key[at++] = static_cast<uint64_t>(key(sl, t));
-        });
-    };
-    if (narrow)
-        select(uint32_t{0}, std::true_type{});
-    else
-        select(uint64_t{0}, std::false_type{});
-    if (n_vic > 0 && ranked) wave_lds_sync();   // lane 0 wrote the victims
-    if (n_vic > 0 && !ranked) {
-        wave_lds_sync();
-        for (uint32_t i = lane; i < n_vic; i += WAVE) {
-            const uint64_t k = sh.sel_key[i];
-            uint32_t r = 0;
-            for (uint32_t j = 0; j < n_vic; ++j) r += sh.sel_key[j] < k ? 1u : 0u;
-            const int sl = static_cast<int>(k & ((1ull << sbits) - 1));
-            sh.victims[r] = sl;
-            cp.victims[r] = sl;
-            // owners looked up here, off the collection loop, from LDS or from
-            // memory by a uniform branch (a generic load would wait for every
-            // store in flight)
-            if (own_lds) sh.vic_owner[r] = sh.own[sl];
-            else sh.vic_owner[r] = owner[sl];
-        }
-        wave_lds_sync();
-    }
-
-    // ---- q split and slot update -------------------------------------------
-    const int64_t q_raw = (2ll * cp.q_num * n_miss + cp.q_den) / (2ll * cp.q_den);
-    const uint32_t q = static_cast<uint32_t>(q_raw < n_miss ? q_raw : n_miss);
-    const uint32_t q_eff = q < n_vic ? q : n_vic;
-    for (uint32_t i = lane; i < q_eff; i += WAVE) {
-        const int v = sh.victims[i];
-        const int ex = sh.miss[i];
-        const int old = sh.vic_owner[i];
-        // evict; `old` is never one of this call's misses
-        if (old >= 0 && old < table_len) table[old] = -1;
-        table[layer * E + ex] = v;
-        owner[v] = layer * E + ex;
-        slot_ts[v] = tick;
-        cp.fill_e[i] = ex;
-        cp.fill_s[i] = v;
-    }
-    for (uint32_t i = q_eff + lane; i < n_miss; i += WAVE) cp.inplace[i - q_eff] = sh.miss[i];
-    if (with_plan) {
-        // where the FFN reads each expert from after the call, and whether it is filled now
-        uint32_t mi = bm;
-        for (int e = e0; e < e1; ++e) {
-            if (!sh.mark[e]) continue;
-            const int u = sh.upos[e];
-            const int sl = slot_of(e);
-            int final_slot = sl, filled = 0;
-            if (sl < 0) {
-                filled = mi < q_eff ? 1 : 0;
-                final_slot = filled ? sh.victims[mi] : -1;
-                ++mi;
-            }
-            reinterpret_cast<int4*>(cp.plan)[u] = make_int4(final_slot, filled, sh.pbeg[u], sh.pcnt[u]);
-        }
-    }
-    if (lane == 0) {
-        if (!evict_only) {
-            cp.counts[0] = static_cast<int32_t>(n_uniq);
-            cp.counts[1] = static_cast<int32_t>(n_hit);
-            cp.counts[2] = static_cast<int32_t>(n_miss);
-        }
-        cp.counts[3] = static_cast<int32_t>(q_eff);
-        cp.counts[4] = static_cast<int32_t>(n_miss - q_eff);
-        cp.counts[5] = static_cast<int32_t>(n_vic);
-    }
-}
 
 namespace {
 
@@ -737,10 +283,10 @@ moe355_status check_cache(const moe355_cache* c) {
 
 // classify_evict with an optional route phase (route != null: ids are produced
 // from route->logits) and an optional device-resident tick base.
-moe355_status classify_call(const moe355_cache* c, int32_t layer, const int64_t* tick_dev,
-                            int64_t tick, const int32_t* ids, int32_t n_ids,
-                            const moe355_evict_policy* p, moe355_classify_out* out,
-                            const RouteArgs* route, ClassifyMode mode, hipStream_t stream) {
+moe355_status classify_setup(const moe355_cache* c, int32_t layer, const int64_t* tick_dev,
+                             int64_t tick, const int32_t* ids, int32_t n_ids,
+                             const moe355_evict_policy* p, moe355_classify_out* out,
+                             const RouteArgs* route, ClassifyMode mode, ClassifyParams* cpp) {
     moe355_status st = check_cache(c);
     if (st) return st;
     st = check_out(out, true, n_ids);
@@ -761,7 +307,8 @@ moe355_status classify_call(const moe355_cache* c, int32_t layer, const int64_t*
     const int need = need_u > p->K ? need_u : p->K;
     MOE355_REQUIRE(out->capacity >= need, MOE355_ECAPACITY,
                    "classify_evict: list capacity %d < %d", out->capacity, need);
-    ClassifyParams cp{};
+    ClassifyParams& cp = *cpp;
+    cp = ClassifyParams{};
     cp.mode = mode;
     cp.table = c->slot_table;
     cp.table_len = c->n_layers * c->n_experts;
@@ -799,18 +346,28 @@ moe355_status classify_call(const moe355_cache* c, int32_t layer, const int64_t*
     cp.counts = out->counts;
     cp.plan = out->plan;
     cp.pairs = out->pairs;
+    return ok();
+}
+
+moe355_status classify_launch(const ClassifyParams& cp, hipStream_t stream) {
     const int N = cp.N;
-    if (N <= 512) classify_kernel<1, 8><<<1, CL_THREADS, 0, stream>>>(cp);
-    else if (N <= 1024) classify_kernel<1, 16><<<1, CL_THREADS, 0, stream>>>(cp);
-    else if (N <= 2048) classify_kernel<2, 32><<<1, CL_THREADS, 0, stream>>>(cp);
-    else if (N <= 4096) classify_kernel<4, 0><<<1, CL_THREADS, 0, stream>>>(cp);
-    else if (N <= 8192) classify_kernel<8, 0><<<1, CL_THREADS, 0, stream>>>(cp);
-    else classify_kernel<0, 0><<<1, CL_THREADS, 0, stream>>>(cp);
+    if (N <= 512) classify_kernel<8><<<1, CL_THREADS, 0, stream>>>(cp);
+    else if (N <= 1024) classify_kernel<16><<<1, CL_THREADS, 0, stream>>>(cp);
+    else if (N <= 2048) classify_kernel<32><<<1, CL_THREADS, 0, stream>>>(cp);
+    else classify_kernel<0><<<1, CL_THREADS, 0, stream>>>(cp);
     return check_launch("classify_evict");
 }
 
-namespace {
-}  // namespace
+moe355_status classify_call(const moe355_cache* c, int32_t layer, const int64_t* tick_dev,
+                            int64_t tick, const int32_t* ids, int32_t n_ids,
+                            const moe355_evict_policy* p, moe355_classify_out* out,
+                            const RouteArgs* route, ClassifyMode mode, hipStream_t stream) {
+    ClassifyParams cp;
+    const moe355_status st = classify_setup(c, layer, tick_dev, tick, ids, n_ids, p, out, route, mode, &cp);
+    if (st) return st;
+    return classify_launch(cp, stream);
+}
+
 }  // namespace moe355
 
 using namespace moe355;
@@ -836,7 +393,7 @@ extern "C" moe355_status moe355_dedup(const int32_t* ids, int32_t n_ids, int32_t
     cp.counts = out->counts;
     cp.plan = out->plan;
     cp.pairs = out->pairs;
-    classify_kernel<1, 8><<<1, CL_THREADS, 0, stream>>>(cp);
+    classify_kernel<8><<<1, CL_THREADS, 0, stream>>>(cp);
     return check_launch("dedup");
 }
 

@@ -38,6 +38,7 @@
 // fill-through on, an expert that this call fills into a cache slot is read
 // from the pool and the lanes that read its bytes also write them to the slot.
 #include "internal.h"
+#include "classify_dev.h"
 
 namespace moe355 {
 namespace {
@@ -334,6 +335,153 @@ __device__ __forceinline__ void mma_slab(const WSlab<RT>& w, const uint4 b[4], i
     }
 }
 
+// Synchronisation words, 256 bytes apart (so that no two share a cache line),
+// in the first SYNC_BYTES of the decode workspace; zero before a call and left
+// zero by it.  Word w sits at byte 256 w:
+//   0..7     gate/up blocks of group g = block % 8 done
+//   8        groups whose gate/up blocks are all done
+//   9..16    blocks of group g = block % 8 exited
+//   17       groups whose blocks have all exited; the last block to exit clears
+//            every word
+//   18       error word, sticky: bit 0 = a bounded wait gave up
+//   32..95   flag "all gate/up blocks done", one copy per line
+//   96..159  whole-layer launch: flag "plan published", one copy per line
+//   160..223 whole-layer launch: flag "fills' victim slots published"
+// Counting in groups keeps each counter to about 1/8 of the blocks, and a flag
+// is raised in 64 copies (one store by each lane of a wavefront) of which a
+// block polls copy block % 64: requests to one address are served one after
+// another at the memory side, so 256 atomic additions on one counter cost
+// about as much as the whole gate/up pass, and a few hundred blocks polling
+// one word slow down every other access that falls on that channel.
+//
+// h crosses between blocks without whole-cache maintenance: the gate/up blocks
+// store it with device-scope (write-through) stores and wait for their
+// completion before counting themselves done; the down blocks read it with
+// device-scope loads after seeing the flag.  (A release or acquire fence at
+// device scope would write back or invalidate the XCD's whole L2, once per
+// block.)
+constexpr uint32_t SPIN_LIMIT = 1u << 18;   // polls of >= 128 cycles: tens of ms at most
+constexpr int SYNC_BYTES = 65536;
+__device__ __forceinline__ uint32_t* sync_word(uint32_t* sync, int w) { return sync + 64 * w; }
+constexpr int SW_DONE = 0, SW_DONE_TOP = 8, SW_EXIT = 9, SW_EXIT_TOP = 17, SW_ERR = 18;
+constexpr int FL_DONE = 32, FL_PLAN = 96, FL_VICT = 160;   // 64 copies each
+
+__device__ __forceinline__ uint32_t atomic_add_dev(uint32_t* a, uint32_t v) {
+    return __hip_atomic_fetch_add(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev(uint32_t* a, uint32_t v) {
+    __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// blocks b < n with b % 8 == g
+__device__ __forceinline__ uint32_t group_size(uint32_t n, uint32_t g) { return g < n ? (n - g + 7) / 8 : 0; }
+
+// Gate/up block `a` (of n_gu) counts itself done once its h stores are complete;
+// the block that completes the count raises the flag.
+__device__ __forceinline__ void signal_done(uint32_t* sync, uint32_t n_gu, uint32_t a) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's h stores are complete
+    __syncthreads();
+    if (threadIdx.x < WAVE) {
+        uint32_t last = 0;
+        if (threadIdx.x == 0) {
+            const uint32_t g = a & 7;
+            if (atomic_add_dev(sync_word(sync, SW_DONE + g), 1u) == group_size(n_gu, g) - 1)
+                last = atomic_add_dev(sync_word(sync, SW_DONE_TOP), 1u) == (n_gu < 8 ? n_gu : 8) - 1;
+        }
+        if (__shfl(last, 0, WAVE)) store_dev(sync_word(sync, FL_DONE + threadIdx.x), 1u);
+    }
+}
+
+// Until copy `b % 64` of flag f is up (bounded; thread 0 polls, the block then meets).
+__device__ __forceinline__ void wait_flag(uint32_t* sync, int f, uint32_t b) {
+    if (threadIdx.x == 0) {
+        const uint32_t* word = sync_word(sync, f + static_cast<int>(b & 63));
+        uint32_t n = 0;
+        while (__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++n == SPIN_LIMIT) {
+                __hip_atomic_fetch_or(sync_word(sync, SW_ERR), 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void block_exit(uint32_t* sync) {
+    __syncthreads();
+    if (threadIdx.x < WAVE) {
+        uint32_t last = 0;
+        if (threadIdx.x == 0) {
+            const uint32_t nblk = gridDim.x, g = blockIdx.x & 7;
+            if (atomic_add_dev(sync_word(sync, SW_EXIT + g), 1u) == group_size(nblk, g) - 1) {
+                store_dev(sync_word(sync, SW_EXIT + g), 0u);   // the whole group has exited
+                const uint32_t groups = nblk < 8 ? nblk : 8;
+                last = atomic_add_dev(sync_word(sync, SW_EXIT_TOP), 1u) == groups - 1;
+            }
+        }
+        if (__shfl(last, 0, WAVE)) {   // every block is past its waits: clear the rest
+            const int l = threadIdx.x;
+            store_dev(sync_word(sync, FL_DONE + l), 0u);
+            store_dev(sync_word(sync, FL_PLAN + l), 0u);
+            store_dev(sync_word(sync, FL_VICT + l), 0u);
+            if (l < 8) store_dev(sync_word(sync, SW_DONE + l), 0u);
+            if (l == 0) {
+                store_dev(sync_word(sync, SW_DONE_TOP), 0u);
+                store_dev(sync_word(sync, SW_EXIT_TOP), 0u);
+            }
+        }
+    }
+}
+
+// 16 bytes by two device-scope 8-byte loads.
+__device__ __forceinline__ uint4 ld_dev16(const void* q) {
+    const uint64_t* w = reinterpret_cast<const uint64_t*>(q);
+    const uint64_t a = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t b = __hip_atomic_load(w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_uint4(static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32),
+                      static_cast<uint32_t>(b), static_cast<uint32_t>(b >> 32));
+}
+
+__device__ __forceinline__ int32_t ld_dev32(const int32_t* q) {
+    return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Whole-layer launch: the plan comes from the bookkeeping workgroup of the same
+// launch, so it is read with device-scope loads once its flag is up.
+__device__ __forceinline__ void stage_plan_dev(const DecodeParams& p, PlanLds& pl) {
+    const int t = threadIdx.x;
+    if (t < p.n_plan) {
+        const uint4 r = ld_dev16(p.plan + 4 * t);
+        pl.plan[t] = make_int4(static_cast<int>(r.x), static_cast<int>(r.y), static_cast<int>(r.z),
+                               static_cast<int>(r.w));
+        pl.uniq[t] = ld_dev32(p.uniq + t);
+    }
+    if (t < p.T * p.k) {
+        const int32_t pr = ld_dev32(p.pairs + t);
+        pl.pairs[t] = pr;
+        pl.tok[t] = pr / p.k;
+        pl.w[t] = __int_as_float(ld_dev32(reinterpret_cast<const int32_t*>(p.w) + t));
+    }
+    if (t == 0) pl.n_uniq = ld_dev32(p.counts);
+    __syncthreads();
+}
+
+// Whole-layer launch, a block that reads a missed expert (block-uniform `need`):
+// wait until the fills' victim slots are published, then re-read the plan rows,
+// which now name the slot each filled expert is written to.
+__device__ __forceinline__ void refresh_for_fills(const DecodeParams& p, PlanLds& pl,
+                                                  uint32_t* sync, bool need) {
+    if (!need) return;
+    wait_flag(sync, FL_VICT, blockIdx.x);
+    if (threadIdx.x < p.n_plan) {
+        const uint4 r = ld_dev16(p.plan + 4 * threadIdx.x);
+        pl.plan[threadIdx.x] = make_int4(static_cast<int>(r.x), static_cast<int>(r.y),
+                                         static_cast<int>(r.z), static_cast<int>(r.w));
+    }
+    __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // gate/up.  KW wavefronts share a row tile and split H; RT tiles of 16 rows each.
 template <int FMT, int KW, int RT>
@@ -357,9 +505,9 @@ struct Cursor {
 // products) and written through to the device coherence point; otherwise the
 // down pass applies the weight.
 template <int FMT, int NW, int KW, int RT, int D, bool SKIP, bool WH>
-__device__ __forceinline__ void gate_up_body(const DecodeParams& p, const PlanLds& pl,
+__device__ __forceinline__ void gate_up_body(const DecodeParams& p, PlanLds& pl,
                                              f32x4 (&red)[SKIP ? 1 : 2][NW][RT][2][WAVE],
-                                             int bid, int nblk) {
+                                             int bid, int nblk, uint32_t* fill_sync = nullptr) {
     constexpr int RW = NW / KW;
     constexpr int NB = SKIP ? 1 : 2;   // reduction buffers (one item per block when SKIP)
     const int lane = threadIdx.x & (WAVE - 1), ln = lane & 15, gq = lane >> 4;
@@ -552,6 +700,12 @@ __device__ __forceinline__ void gate_up_body(const DecodeParams& p, const PlanLd
     // past the end re-reads its last item) and only the computation is
     // guarded: a guarded load lets the compiler's wait before a stage's MFMAs
     // count only the loads present on every path (one stage of lookahead).
+    // whole-layer launch: a block reading a missed expert learns where to write
+    // it (the fills' victim slots) before its first fill-through store
+    bool fresh = fill_sync == nullptr;
+    bool need = false;
+    if (!fresh)
+        for (int it = i_beg; it < i_end; ++it) need |= pl.plan[it / tiles].x < 0;
     bool done = false;
     while (!done) {
 #pragma unroll
@@ -559,6 +713,10 @@ __device__ __forceinline__ void gate_up_body(const DecodeParams& p, const PlanLd
             if (!SKIP || lc.valid) load(st[(d + D - 1) % D], lc.item, lc.tg, lc.s);
             advance(lc);
             if (!done) {
+                if (!fresh) {
+                    refresh_for_fills(p, pl, fill_sync, need);
+                    fresh = true;
+                }
                 compute(st[d], cc.item, cc.tg, cc.s);
                 if (cc.s == NS - 1) epilogue(cc.item, cc.tg);
                 advance(cc);
@@ -730,92 +888,6 @@ __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
 // dispatches its blocks in index order.  Every wait is also bounded (it gives
 // up, flags the error word and goes on) so that a block always exits.
 //
-// Synchronisation words, 256 bytes apart (so that no two share a cache line),
-// in the first SYNC_BYTES of the decode workspace; zero before a call and left
-// zero by it.  Word w sits at byte 256 w:
-//   0..7   gate/up blocks of group g = block % 8 done
-//   8      groups whose gate/up blocks are all done (what the down blocks poll)
-//   9..16  blocks of group g = block % 8 exited
-//   17     groups whose blocks have all exited; the last block to exit clears
-//          every counter
-//   18     error word, sticky: bit 0 = a bounded wait gave up
-// Counting in groups keeps each counter to about 1/8 of the blocks: atomic
-// operations on one address are serialised at the memory side, and 256 of
-// them cost about as much as the whole gate/up pass.
-//
-// h crosses between blocks without whole-cache maintenance: the gate/up blocks
-// store it with device-scope (write-through) stores and wait for their
-// completion before counting themselves done; the down blocks read it with
-// device-scope loads after seeing the count.  (A release or acquire fence at
-// device scope would write back or invalidate the XCD's whole L2, once per
-// block.)
-constexpr uint32_t SPIN_LIMIT = 1u << 18;   // polls of >= 128 cycles: tens of ms at most
-constexpr int SYNC_BYTES = 8192;
-__device__ __forceinline__ uint32_t* sync_word(uint32_t* sync, int w) { return sync + 64 * w; }
-constexpr int SW_DONE = 0, SW_DONE_TOP = 8, SW_EXIT = 9, SW_EXIT_TOP = 17, SW_ERR = 18;
-
-__device__ __forceinline__ uint32_t atomic_add_dev(uint32_t* a, uint32_t v) {
-    return __hip_atomic_fetch_add(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_dev(uint32_t* a, uint32_t v) {
-    __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// blocks b < n with b % 8 == g
-__device__ __forceinline__ uint32_t group_size(uint32_t n, uint32_t g) { return g < n ? (n - g + 7) / 8 : 0; }
-
-// A gate/up block (index < n_gu) counts itself done once its h stores are complete.
-__device__ __forceinline__ void signal_done(uint32_t* sync, uint32_t n_gu) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's h stores are complete
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t g = blockIdx.x & 7;
-        if (atomic_add_dev(sync_word(sync, SW_DONE + g), 1u) == group_size(n_gu, g) - 1)
-            atomic_add_dev(sync_word(sync, SW_DONE_TOP), 1u);
-    }
-}
-
-__device__ __forceinline__ void wait_done(uint32_t* sync, uint32_t n_gu) {
-    if (threadIdx.x == 0) {
-        const uint32_t target = n_gu < 8 ? n_gu : 8;
-        const uint32_t* top = sync_word(sync, SW_DONE_TOP);
-        uint32_t n = 0;
-        while (__hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(2);
-            if (++n == SPIN_LIMIT) {
-                __hip_atomic_fetch_or(sync_word(sync, SW_ERR), 1u, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-        }
-    }
-    __syncthreads();
-}
-
-__device__ __forceinline__ void block_exit(uint32_t* sync) {
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t nblk = gridDim.x, g = blockIdx.x & 7;
-        if (atomic_add_dev(sync_word(sync, SW_EXIT + g), 1u) == group_size(nblk, g) - 1) {
-            store_dev(sync_word(sync, SW_EXIT + g), 0u);   // the whole group has exited
-            const uint32_t groups = nblk < 8 ? nblk : 8;
-            if (atomic_add_dev(sync_word(sync, SW_EXIT_TOP), 1u) == groups - 1) {
-                // every block is past its waits
-                for (int w = 0; w < 8; ++w) store_dev(sync_word(sync, SW_DONE + w), 0u);
-                store_dev(sync_word(sync, SW_DONE_TOP), 0u);
-                store_dev(sync_word(sync, SW_EXIT_TOP), 0u);
-            }
-        }
-    }
-}
-
-// 16 bytes by two device-scope 8-byte loads.
-__device__ __forceinline__ uint4 ld_dev16(const void* q) {
-    const uint64_t* w = reinterpret_cast<const uint64_t*>(q);
-    const uint64_t a = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t b = __hip_atomic_load(w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return make_uint4(static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32),
-                      static_cast<uint32_t>(b), static_cast<uint32_t>(b >> 32));
-}
 
 constexpr int SMALL_DB = 2;            // (expert, slab) items per down wavefront
 constexpr int SMALL_H_LDS = 32768;     // bytes of h (hi and lo halves of T*k*I values) in LDS
@@ -851,9 +923,10 @@ __device__ __forceinline__ ASlab prep_a(const WSlab<1>& w, int gq) {
 // and the two halves meet in fp32 atomic additions onto the zeroed output
 // (0 + a + b in either order gives the same sum).
 template <int FMT, int NW>
-__device__ __forceinline__ void down_rows_body(const DecodeParams& p, const PlanLds& pl,
+__device__ __forceinline__ void down_rows_body(const DecodeParams& p, PlanLds& pl,
                                                uint4* hs, f32x4 (&red)[NW][WAVE], int r0,
-                                               int half, uint32_t* sync, uint32_t n_gu) {
+                                               int half, uint32_t* sync, uint32_t n_gu,
+                                               bool layer_fills = false) {
     const int lane = threadIdx.x & (WAVE - 1), ln = lane & 15, gq = lane >> 4;
     const int wv = threadIdx.x / WAVE;
     const int I = p.I, nsl = I / SLAB;
@@ -869,15 +942,18 @@ __device__ __forceinline__ void down_rows_body(const DecodeParams& p, const Plan
             load_wslab<FMT, 1>(p, expert_ref(p, pl, u).src, 2, r0, I, sl * SLAB, ln, gq, w[i]);
         }
     }
+    auto fill_stores = [&]() {   // fill-through of this block's down bytes
 #pragma unroll
-    for (int i = 0; i < SMALL_DB; ++i) {   // fill-through of this block's down bytes
-        const int j = item_of(i);
-        if (j < n_items) {
-            const int u = j / nsl;
-            const ExpertRef ref = expert_ref(p, pl, u);
-            if (ref.dst) store_wslab<FMT, 1>(p, ref.dst, 2, r0, I, (j - u * nsl) * SLAB, ln, gq, w[i]);
+        for (int i = 0; i < SMALL_DB; ++i) {
+            const int j = item_of(i);
+            if (j < n_items) {
+                const int u = j / nsl;
+                const ExpertRef ref = expert_ref(p, pl, u);
+                if (ref.dst) store_wslab<FMT, 1>(p, ref.dst, 2, r0, I, (j - u * nsl) * SLAB, ln, gq, w[i]);
+            }
         }
-    }
+    };
+    if (!layer_fills) fill_stores();
     ASlab A[SMALL_DB];
     int hoff[SMALL_DB];   // LDS piece of the lane's h for each item, or -1 (token not routed)
 #pragma unroll
@@ -892,7 +968,19 @@ __device__ __forceinline__ void down_rows_body(const DecodeParams& p, const Plan
                 if (pl.tok[pr.z + n] == ln) hoff[i] = (pl.pairs[pr.z + n] * I + sl * SLAB + 32 * gq) / 4;
         }
     }
-    wait_done(sync, n_gu);
+    if (layer_fills) {
+        // whole-layer launch: the fills' victim slots are published (in practice
+        // well before the gate/up blocks finish), then the down bytes of the
+        // filled experts go to their slots while the gate/up work goes on
+        bool need = false;   // block-uniform: over every wavefront's items
+        for (int m = 0; m < NW * SMALL_DB; ++m) {
+            const int j = 2 * m + half;
+            if (j < n_items) need |= pl.plan[j / nsl].x < 0;
+        }
+        refresh_for_fills(p, pl, sync, need);
+        fill_stores();
+    }
+    wait_flag(sync, FL_DONE, blockIdx.x);
     // h pieces: [pair][I / 4] x 16 bytes (four hi halves, then four lo halves)
     const int nc = p.T * p.k * I / 4;
     {   // stage every pair's h in LDS: at most four pieces per thread
@@ -981,7 +1069,7 @@ __global__ void __launch_bounds__(NW * WAVE, 4) ffn_small_kernel(DecodeParams p,
         }
         gate_up_body<FMT, NW, NW, 1, D, true, true>(
             p, pl, *reinterpret_cast<f32x4 (*)[1][NW][1][2][WAVE]>(raw), blockIdx.x, n_gu);
-        signal_done(sync, n_gu);
+        signal_done(sync, n_gu, blockIdx.x);
     } else {
         const int b = blockIdx.x - n_gu;   // two blocks per 16-row tile
         down_rows_body<FMT, NW>(p, pl, raw,
@@ -1039,14 +1127,107 @@ moe355_status launch_gate_up_wide(const DecodeParams& p, int max_uniq, hipStream
     return check_launch("expert_ffn_decode gate_up");
 }
 
+// Whole-layer launch, after a gate/up block has counted itself done: once the
+// fills' victim slots are published, the block copies its share of each filled
+// expert's gate and up matrices (its 16-row tiles: contiguous code, scale and
+// bias ranges in the device layout) from the pool to the slot.  The bytes were
+// read moments ago, so the copy mostly hits the caches; it is off the path to
+// the output.
+template <int FMT>
+__device__ __forceinline__ void copy_gate_up_fills(const DecodeParams& p, PlanLds& pl,
+                                                   uint32_t* sync, int b, int n_gu) {
+    const int tiles = p.I / 16;
+    const int n_items = pl.n_uniq * tiles;
+    const int per = (n_items + n_gu - 1) / n_gu;
+    const int i_beg = b * per, i_end = min(n_items, i_beg + per);
+    bool need = false;   // block-uniform
+    for (int it = i_beg; it < i_end; ++it) need |= pl.plan[it / tiles].x < 0;
+    if (!need) return;
+    refresh_for_fills(p, pl, sync, true);
+    const uint32_t kb = static_cast<uint32_t>(p.H / 128);   // 128-input blocks per row tile
+    for (int it = i_beg; it < i_end; ++it) {
+        const int u = it / tiles, tile = it - u * tiles;
+        const int4 row = pl.plan[u];
+        if (!(row.x >= 0 && row.y)) continue;   // block-uniform
+        const uint8_t* src = p.pool + (static_cast<int64_t>(p.layer) * p.E + pl.uniq[u]) * p.S;
+        uint8_t* dst = const_cast<uint8_t*>(p.slots) + static_cast<int64_t>(row.x) * p.S;
+        for (int m = 0; m < 2; ++m) {
+            // (offset, bytes) of the tile's codes, scale words and bias words
+            const uint32_t q0 = static_cast<uint32_t>(p.q_off[m]) + tile * kb * 1024u, qn = kb * 1024u;
+            const uint32_t s0 = static_cast<uint32_t>(p.s_off[m]) + tile * kb * 64u, sn = kb * 64u;
+            const uint32_t b0 = static_cast<uint32_t>(p.b_off[m]) + tile * kb * 64u;
+            const uint32_t bn = FMT == MOE355_W_INT4_G64 ? kb * 64u : 0u;
+            const uint32_t n16 = (qn + sn + bn) / 16;
+            for (uint32_t c = threadIdx.x; c < n16; c += blockDim.x) {
+                const uint32_t o = 16 * c;
+                const uint32_t at = o < qn ? q0 + o : (o < qn + sn ? s0 + (o - qn) : b0 + (o - qn - sn));
+                *reinterpret_cast<uint4*>(dst + at) = *reinterpret_cast<const uint4*>(src + at);
+            }
+        }
+    }
+}
+
+// Whole decode layer call in one launch: workgroup 0 runs the bookkeeping
+// (routing, dedup, hit/miss, victims, slot update; classify_dev.h) and
+// publishes the plan as soon as hits and misses are known; the other
+// workgroups are the small-call FFN's gate/up and down blocks, which wait for
+// that plan, stage it, and start streaming weights while workgroup 0 is still
+// picking victims.  A block that reads a missed expert also waits for the
+// fills' victim slots before its fill-through stores.  Waits point only at
+// lower workgroup indices (workgroup 0 first), as in the FFN alone.
+using ClassifySmall = ClassifySharedT<2048, 2048, 256, 128>;
+
+template <int FMT, int NW, int D, int SPL>
+__global__ void __launch_bounds__(NW * WAVE, 4) layer_small_kernel(DecodeParams p, ClassifyParams cp,
+                                                                   uint32_t n_gu, uint32_t* sync) {
+    __shared__ PlanLds pl;
+    constexpr int GU_BYTES = NW * 2 * WAVE * 16;
+    constexpr int DN_BYTES = SMALL_H_LDS + NW * WAVE * 16;
+    constexpr int CL_BYTES = static_cast<int>(sizeof(ClassifySmall));
+    constexpr int RAW = GU_BYTES > DN_BYTES ? (GU_BYTES > CL_BYTES ? GU_BYTES : CL_BYTES)
+                                            : (DN_BYTES > CL_BYTES ? DN_BYTES : CL_BYTES);
+    __shared__ uint4 raw[(RAW + 15) / 16];
+    if (blockIdx.x == 0) {
+        classify_body<SPL, NW * WAVE>(cp, *reinterpret_cast<ClassifySmall*>(raw),
+                                           sync_word(sync, FL_PLAN), sync_word(sync, FL_VICT));
+    } else {
+        wait_flag(sync, FL_PLAN, blockIdx.x);
+        stage_plan_dev(p, pl);
+        const bool fills = p.has_cache && p.fill_through;
+        const uint32_t b = blockIdx.x - 1;
+        if (b < n_gu) {
+            {   // zero the output for the down blocks' additions
+                const int n = p.T * p.H;
+                uint32_t* o = reinterpret_cast<uint32_t*>(p.out);
+                for (int i = b * (NW * WAVE) + threadIdx.x; i < n; i += n_gu * (NW * WAVE))
+                    store_dev(o + i, 0u);
+            }
+            gate_up_body<FMT, NW, NW, 1, D, true, true>(
+                p, pl, *reinterpret_cast<f32x4 (*)[1][NW][1][2][WAVE]>(raw), b, n_gu);
+            signal_done(sync, n_gu, b);
+            if (fills) copy_gate_up_fills<FMT>(p, pl, sync, b, n_gu);
+        } else {
+            const int c = b - n_gu;   // two blocks per 16-row tile
+            down_rows_body<FMT, NW>(p, pl, raw,
+                                    *reinterpret_cast<f32x4 (*)[NW][WAVE]>(raw + SMALL_H_LDS / 16),
+                                    (c >> 1) * 16, c & 1, sync, n_gu, fills);
+        }
+    }
+    block_exit(sync);
+}
+
 // The fused small-call kernel when the call fits it: at most 16 tokens, gate/up
 // items for at most one block per CU, down items for eight wavefronts of
 // SMALL_DB each, and h small enough for LDS.
-template <int FMT>
-bool launch_small(const DecodeParams& p, int max_uniq, uint32_t* sync, hipStream_t stream) {
+bool small_fits(const DecodeParams& p, int max_uniq) {
     if (p.T > TOK || !(p.H == 1024 || p.H == 2048 || p.H == 4096)) return false;
     if (max_uniq * (p.I / 16) > device_cus() || max_uniq * (p.I / SLAB) > 2 * 8 * SMALL_DB) return false;
-    if (static_cast<int64_t>(p.T) * p.k * p.I * 4 > SMALL_H_LDS) return false;
+    return static_cast<int64_t>(p.T) * p.k * p.I * 4 <= SMALL_H_LDS;
+}
+
+template <int FMT>
+bool launch_small(const DecodeParams& p, int max_uniq, uint32_t* sync, hipStream_t stream) {
+    if (!small_fits(p, max_uniq)) return false;
     const uint32_t n_gu = static_cast<uint32_t>(max_uniq * (p.I / 16));
     const int blocks = static_cast<int>(n_gu) + 2 * (p.H / 16);
     // H / 8 inputs per gate/up wavefront: one or two slabs of each matrix, all
@@ -1113,17 +1294,18 @@ size_t decode_ws_bytes(const moe355_layer_desc* d, int T) {
     return SYNC_BYTES + 2 * tk * d->inter * sizeof(uint16_t);   // h as hi and lo halves
 }
 
-// Shared by the public decode call and the fused decode-layer call.
-moe355_status decode_ffn(const moe355_layer_desc* d, const void* x_bf16, int32_t T,
-                         const int32_t* topk_ids, const float* topk_w, const moe355_cache* cache,
-                         const uint8_t* pool, int32_t layer, const moe355_classify_out* exp,
-                         bool fill_through, float* out, void* ws, size_t ws_bytes,
-                         hipStream_t stream) {
+namespace {
+
+// Checks a decode FFN call and fills its parameter block.
+moe355_status decode_params(const moe355_layer_desc* d, const void* x_bf16, int32_t T,
+                            const int32_t* topk_ids, const float* topk_w,
+                            const moe355_cache* cache, const uint8_t* pool, int32_t layer,
+                            const moe355_classify_out* exp, bool fill_through, float* out,
+                            void* ws, size_t ws_bytes, DecodeParams* pp, int* max_uniq_out) {
     MOE355_REQUIRE(T >= 0 && T * d->top_k <= 256, MOE355_ENOTSUP,
                    "expert_ffn_decode: T*k=%d outside [0, 256]", T * d->top_k);
     MOE355_REQUIRE(valid_row_len(d->hidden) && valid_row_len(d->inter), MOE355_ENOTSUP,
                    "expert_ffn_decode: H=%d I=%d unsupported", d->hidden, d->inter);
-    if (T == 0) return ok();
     MOE355_REQUIRE(x_bf16 && topk_ids && topk_w && pool && exp && exp->uniq && exp->counts && out,
                    MOE355_EINVAL, "expert_ffn_decode: null pointer");
     MOE355_REQUIRE(exp->plan && exp->pairs && exp->pair_capacity >= T * d->top_k, MOE355_EINVAL,
@@ -1133,7 +1315,8 @@ moe355_status decode_ffn(const moe355_layer_desc* d, const void* x_bf16, int32_t
                    "expert_ffn_decode: workspace %zu < %zu bytes", ws_bytes, need);
     ExpertLayout L;
     expert_layout(d, &L);
-    DecodeParams p{};
+    DecodeParams& p = *pp;
+    p = DecodeParams{};
     p.x = static_cast<const uint16_t*>(x_bf16);
     p.w = topk_w;
     p.uniq = exp->uniq;
@@ -1172,6 +1355,69 @@ moe355_status decode_ffn(const moe355_layer_desc* d, const void* x_bf16, int32_t
     p.plan = exp->plan;
     p.pairs = exp->pairs;
     p.n_plan = max_uniq;
+    *max_uniq_out = max_uniq;
+    return ok();
+}
+
+template <int FMT>
+void launch_layer_small(const DecodeParams& p, const ClassifyParams& cp, int max_uniq,
+                        uint32_t* sync, hipStream_t stream) {
+    const uint32_t n_gu = static_cast<uint32_t>(max_uniq * (p.I / 16));
+    const int blocks = 1 + static_cast<int>(n_gu) + 2 * (p.H / 16);
+    // bookkeeping: N / 64 slots per lane in registers for the victim scan
+    if (cp.N <= 512) {
+        if (p.H <= 2048) layer_small_kernel<FMT, 8, 2, 8><<<blocks, 8 * WAVE, 0, stream>>>(p, cp, n_gu, sync);
+        else layer_small_kernel<FMT, 8, 3, 8><<<blocks, 8 * WAVE, 0, stream>>>(p, cp, n_gu, sync);
+    } else if (cp.N <= 1024) {
+        if (p.H <= 2048) layer_small_kernel<FMT, 8, 2, 16><<<blocks, 8 * WAVE, 0, stream>>>(p, cp, n_gu, sync);
+        else layer_small_kernel<FMT, 8, 3, 16><<<blocks, 8 * WAVE, 0, stream>>>(p, cp, n_gu, sync);
+    } else {
+        if (p.H <= 2048) layer_small_kernel<FMT, 8, 2, 32><<<blocks, 8 * WAVE, 0, stream>>>(p, cp, n_gu, sync);
+        else layer_small_kernel<FMT, 8, 3, 32><<<blocks, 8 * WAVE, 0, stream>>>(p, cp, n_gu, sync);
+    }
+}
+
+}  // namespace
+
+moe355_status decode_layer_small(const moe355_layer_desc* d, const moe355_cache* c,
+                                 const uint8_t* pool, int32_t layer, const ClassifyParams& cp,
+                                 const void* x_bf16, int32_t T, const int32_t* topk_ids,
+                                 const float* topk_w, const moe355_classify_out* lists,
+                                 const moe355_evict_policy* pol, float* out, void* ws,
+                                 size_t ws_bytes, hipStream_t stream, bool* launched) {
+    *launched = false;
+    DecodeParams p;
+    int max_uniq = 0;
+    const moe355_status st = decode_params(d, x_bf16, T, topk_ids, topk_w, c, pool, layer, lists,
+                                           true, out, ws, ws_bytes, &p, &max_uniq);
+    if (st) return st;
+    // the bookkeeping workgroup's LDS limits (ClassifySmall) and the FFN's
+    if (!small_fits(p, max_uniq) || cp.N > 2048 || cp.E > 256 || T * d->top_k > 128 || pol->K > 128)
+        return ok();
+    uint32_t* sync = static_cast<uint32_t*>(ws);
+    if (d->wfmt == MOE355_W_INT4_G64) launch_layer_small<MOE355_W_INT4_G64>(p, cp, max_uniq, sync, stream);
+    else launch_layer_small<MOE355_W_MXFP4>(p, cp, max_uniq, sync, stream);
+    *launched = true;
+    return check_launch("decode_layer");
+}
+
+// Shared by the public decode call and the fused decode-layer call.
+moe355_status decode_ffn(const moe355_layer_desc* d, const void* x_bf16, int32_t T,
+                         const int32_t* topk_ids, const float* topk_w, const moe355_cache* cache,
+                         const uint8_t* pool, int32_t layer, const moe355_classify_out* exp,
+                         bool fill_through, float* out, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+    if (T == 0) {
+        MOE355_REQUIRE(T * d->top_k <= 256 && valid_row_len(d->hidden) && valid_row_len(d->inter),
+                       MOE355_ENOTSUP, "expert_ffn_decode: H=%d I=%d unsupported", d->hidden,
+                       d->inter);
+        return ok();
+    }
+    DecodeParams p;
+    int max_uniq = 0;
+    const moe355_status st = decode_params(d, x_bf16, T, topk_ids, topk_w, cache, pool, layer, exp,
+                                           fill_through, out, ws, ws_bytes, &p, &max_uniq);
+    if (st) return st;
     uint32_t* sync = static_cast<uint32_t*>(ws);   // the workspace's first SYNC_BYTES
     if (d->wfmt == MOE355_W_INT4_G64) return launch_decode<MOE355_W_INT4_G64>(p, max_uniq, sync, stream);
     return launch_decode<MOE355_W_MXFP4>(p, max_uniq, sync, stream);

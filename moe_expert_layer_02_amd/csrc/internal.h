@@ -44,12 +44,28 @@ enum ClassifyMode {
     CLASSIFY_PLAN = 2,    // route?, dedup, hit/miss and a plan reading misses from the pool
     CLASSIFY_EVICT = 3,   // hit stamps, victims, slot update and fill lists for a planned call
 };
+// The bookkeeping call's parameter block (classify_dev.h), checked and filled,
+// and its launch as one workgroup.
+struct ClassifyParams;
+moe355_status classify_setup(const moe355_cache* c, int32_t layer, const int64_t* tick_dev,
+                             int64_t tick, const int32_t* ids, int32_t n_ids,
+                             const moe355_evict_policy* p, moe355_classify_out* out,
+                             const RouteArgs* route, ClassifyMode mode, ClassifyParams* cp);
+moe355_status classify_launch(const ClassifyParams& cp, hipStream_t stream);
 moe355_status classify_call(const moe355_cache* c, int32_t layer, const int64_t* tick_dev,
                             int64_t tick, const int32_t* ids, int32_t n_ids,
                             const moe355_evict_policy* p, moe355_classify_out* out,
                             const RouteArgs* route, ClassifyMode mode, hipStream_t stream);
 moe355_status fill_call(const moe355_cache* c, const uint8_t* pool, int32_t layer,
                         const moe355_classify_out* out, int32_t max_fill, hipStream_t stream);
+// The whole decode layer call (bookkeeping and FFN with fill-through) as one
+// launch when the call is small enough; *launched tells whether it was.
+moe355_status decode_layer_small(const moe355_layer_desc* d, const moe355_cache* c,
+                                 const uint8_t* pool, int32_t layer, const ClassifyParams& cp,
+                                 const void* x_bf16, int32_t T, const int32_t* topk_ids,
+                                 const float* topk_w, const moe355_classify_out* lists,
+                                 const moe355_evict_policy* pol, float* out, void* ws,
+                                 size_t ws_bytes, hipStream_t stream, bool* launched);
 moe355_status decode_ffn(const moe355_layer_desc* d, const void* x_bf16, int32_t T,
                          const int32_t* topk_ids, const float* topk_w, const moe355_cache* cache,
                          const uint8_t* pool, int32_t layer, const moe355_classify_out* exp,
@@ -87,6 +103,27 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);
     return v;
+}
+
+// Minimum / maximum over the 64 lanes by DPP row shifts and row broadcasts (an
+// inclusive scan; lane 63 ends with the result), without the LDS crossbar.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, v, 0x111, 0xf, 0xf, false)));  // row_shr:1
+    v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, v, 0x112, 0xf, 0xf, false)));  // row_shr:2
+    v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, v, 0x114, 0xf, 0xf, false)));  // row_shr:4
+    v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, v, 0x118, 0xf, 0xf, false)));  // row_shr:8
+    v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, v, 0x142, 0xa, 0xf, false)));  // row_bcast:15
+    v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, v, 0x143, 0xc, 0xf, false)));  // row_bcast:31
+    return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false)));
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Sum over aligned segments of `width` lanes (width a power of two <= 64).

@@ -1,5 +1,7 @@
-// One decode layer call as two kernels: route + cache bookkeeping in one
-// workgroup, then the expert FFN with fill-through and the combine.  Or, split
+// One decode layer call: route + cache bookkeeping in one workgroup, then the
+// expert FFN with fill-through and the combine -- as one launch for a small
+// call (the bookkeeping workgroup publishes the plan to the FFN's workgroups
+// mid-way), else as two kernels.  Or, split
 // so that the bookkeeping leaves the critical path: route + plan, then the FFN
 // (hits from slots, misses from the pool) on the caller's stream, while the
 // LRU update and the fill copy run on a second stream.
@@ -10,7 +12,7 @@
 // the partial sums merge exactly -- all inside one captured graph with no host
 // involvement.  The tick may live in device memory so a whole decode step can be
 // captured once and replayed.
-#include "route_dev.h"
+#include "classify_dev.h"
 
 using namespace moe355;
 
@@ -35,8 +37,16 @@ extern "C" moe355_status moe355_decode_layer(const moe355_layer_desc* d, const m
                    d->n_experts);
     RouteArgs ra{logits, T, d->top_k, d->route, d->n_group, d->topk_group, d->route_scale,
                  topk_ids, topk_w};
-    st = classify_call(c, layer, tick_base, tick_add, nullptr, T * d->top_k, p, lists, &ra,
-                       CLASSIFY_FULL, stream);
+    ClassifyParams cp;
+    st = classify_setup(c, layer, tick_base, tick_add, nullptr, T * d->top_k, p, lists, &ra,
+                        CLASSIFY_FULL, &cp);
+    if (st) return st;
+    // a small call runs as one launch: the FFN starts once hits and misses are known
+    bool launched = false;
+    st = decode_layer_small(d, c, pool, layer, cp, x_bf16, T, topk_ids, topk_w, lists, p, out, ws,
+                            ws_bytes, stream, &launched);
+    if (st || launched) return st;
+    st = classify_launch(cp, stream);
     if (st) return st;
     return decode_ffn(d, x_bf16, T, topk_ids, topk_w, c, pool, layer, lists, true, out, ws,
                       ws_bytes, stream);

@@ -67,7 +67,7 @@ SMALL = [
 
 def test_decode_small_call_sync_words_left_zero():
     """The one-launch small-call FFN (gate/up and down blocks counting through
-    the workspace's first 8192 bytes) leaves those bytes zero after every call,
+    the workspace's first 65536 bytes) leaves those bytes zero after every call,
     the error word (byte 4608) included, and gives the same output on repeated
     calls: the down blocks sum the experts in a fixed order, and the two halves
     of each tile add onto zero in either order to the same value."""
@@ -95,7 +95,7 @@ def test_decode_small_call_sync_words_left_zero():
         out = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
         m.expert_ffn_decode(desc, _x_dev(x_bits), ids, wt, None, layer, 0, exp, out, ws)
         torch.cuda.synchronize()
-        assert int(ws[:8192].count_nonzero()) == 0, f"call {call}: sync words not cleared"
+        assert int(ws[:65536].count_nonzero()) == 0, f"call {call}: sync words not cleared"
         outs.append(out.cpu().numpy())
         if call == 0:
             check_close(outs[0], _oracle_layer(w, x_bits, ids_np, wt_np), "small-call decode")
