@@ -237,8 +237,7 @@ def bench_decode(args, w):
                    "weights": "int4_g64" if w.wfmt == 0 else "mxfp4", "cache_slots": w.n_slots,
                    "expert_bytes": S, "layer_calls_timed": n_calls, "parallelism": "single_gpu",
                    "order": order, "step": "one replay of a captured graph of the step's layer calls"},
-        "roofline": {"bound": "hbm",
-                     "kernel": "expert_ffn_decode: gate_up_kernel + down_kernel (one call, two launches)",
+        "roofline": {"bound": "hbm", "kernel": ffn_kernel_label(w, T),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_record(f"decode_ffn_{w.name}_traffic.md", DECODE_SOURCES),
@@ -249,6 +248,20 @@ def bench_decode(args, w):
         res["cpu_baseline"] = cpu_baseline_decode(w, trace, n_calls=args.cpu_calls,
                                                   budget_s=args.cpu_budget)
     return res
+
+
+def ffn_kernel_label(w, T):
+    """Which kernels one expert_ffn_decode call launches for this workload (the
+    library's small-call rule)."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    u = min(T * w.top_k, w.n_experts)
+    small = (T <= 16 and w.hidden in (1024, 2048, 4096) and u * (w.inter // 16) <= cus
+             and u * (w.inter // 128) <= 32 and T * w.top_k * w.inter * 4 <= 32768)
+    if small:
+        return ("expert_ffn_decode: ffn_small_kernel (one launch; inside a decode step the "
+                "same work runs in layer_small_kernel together with the bookkeeping)")
+    return "expert_ffn_decode: gate_up_kernel + down_kernel (one call, two launches)"
 
 
 MFMA_PEAK_BF16_TFLOPS = 2500.0

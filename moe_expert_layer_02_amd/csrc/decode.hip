@@ -975,7 +975,7 @@ __device__ __forceinline__ void down_rows_body(const DecodeParams& p, PlanLds& p
         bool need = false;   // block-uniform: over every wavefront's items
         for (int m = 0; m < NW * SMALL_DB; ++m) {
             const int j = 2 * m + half;
-            if (j < n_items) need |= pl.plan[j / nsl].x < 0;
+            if (j < n_items) need |= pl.plan[j / nsl].x < 0 || pl.plan[j / nsl].y != 0;
         }
         refresh_for_fills(p, pl, sync, need);
         fill_stores();
@@ -1140,8 +1140,13 @@ __device__ __forceinline__ void copy_gate_up_fills(const DecodeParams& p, PlanLd
     const int n_items = pl.n_uniq * tiles;
     const int per = (n_items + n_gu - 1) / n_gu;
     const int i_beg = b * per, i_end = min(n_items, i_beg + per);
-    bool need = false;   // block-uniform
-    for (int it = i_beg; it < i_end; ++it) need |= pl.plan[it / tiles].x < 0;
+    // block-uniform: a miss in the first plan, or a row already refreshed to a
+    // fill (this block may have refreshed its plan in an earlier step)
+    bool need = false;
+    for (int it = i_beg; it < i_end; ++it) {
+        const int4 row = pl.plan[it / tiles];
+        need |= row.x < 0 || row.y != 0;
+    }
     if (!need) return;
     refresh_for_fills(p, pl, sync, true);
     const uint32_t kb = static_cast<uint32_t>(p.H / 128);   // 128-input blocks per row tile
@@ -1174,7 +1179,9 @@ __device__ __forceinline__ void copy_gate_up_fills(const DecodeParams& p, PlanLd
 // that plan, stage it, and start streaming weights while workgroup 0 is still
 // picking victims.  A block that reads a missed expert also waits for the
 // fills' victim slots before its fill-through stores.  Waits point only at
-// lower workgroup indices (workgroup 0 first), as in the FFN alone.
+// lower workgroup indices (workgroup 0 first), as in the FFN alone.  (A
+// Qwen-like call is 513 workgroups at two per CU: the last down block starts
+// when workgroup 0 is done, about when the others start waiting for h.)
 using ClassifySmall = ClassifySharedT<2048, 2048, 256, 128>;
 
 template <int FMT, int NW, int D, int SPL>
