@@ -92,6 +92,7 @@ struct PlanLds {
     int32_t tok[MAX_PLAN];   // token of pairs[i] (pairs[i] / k)
     float w[MAX_PLAN];       // routing weight of each pair
     int32_t n_uniq;
+    int32_t fills_known;     // whole-layer launch: the staged plan already names the fills
 };
 
 // A wavefront-uniform device pointer moved into scalar registers, so that loads
@@ -404,6 +405,29 @@ __device__ __forceinline__ void wait_flag(uint32_t* sync, int f, uint32_t b) {
                 break;
             }
         }
+    }
+    __syncthreads();
+}
+
+// Whole-layer launch: until the plan flag (copy b % 64) is up, also noting
+// whether the victims flag already was (then the plan about to be staged is
+// final and names every fill).
+__device__ __forceinline__ void wait_plan(uint32_t* sync, uint32_t b, PlanLds& pl) {
+    if (threadIdx.x == 0) {
+        const uint32_t* pw = sync_word(sync, FL_PLAN + static_cast<int>(b & 63));
+        const uint32_t* vw = sync_word(sync, FL_VICT + static_cast<int>(b & 63));
+        uint32_t n = 0, v = 0;
+        while (true) {
+            v = __hip_atomic_load(vw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (__hip_atomic_load(pw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
+            __builtin_amdgcn_s_sleep(2);
+            if (++n == SPIN_LIMIT) {
+                __hip_atomic_fetch_or(sync_word(sync, SW_ERR), 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
+        pl.fills_known = v != 0u;
     }
     __syncthreads();
 }
@@ -932,16 +956,22 @@ __device__ __forceinline__ void down_rows_body(const DecodeParams& p, PlanLds& p
     const int I = p.I, nsl = I / SLAB;
     const int n_items = pl.n_uniq * nsl;
     auto item_of = [&](int i) { return 2 * (wv + i * NW) + half; };
-    // weights first (unconditional: an item past the end re-reads the last one)
+    // weights (unconditional: an item past the end re-reads the last one)
     WSlab<1> w[SMALL_DB];
-    if (n_items > 0) {
+    auto load_weights = [&]() {
+        if (n_items > 0) {
 #pragma unroll
-        for (int i = 0; i < SMALL_DB; ++i) {
-            const int j = min(item_of(i), n_items - 1);
-            const int u = j / nsl, sl = j - u * nsl;
-            load_wslab<FMT, 1>(p, expert_ref(p, pl, u).src, 2, r0, I, sl * SLAB, ln, gq, w[i]);
+            for (int i = 0; i < SMALL_DB; ++i) {
+                const int j = min(item_of(i), n_items - 1);
+                const int u = j / nsl, sl = j - u * nsl;
+                load_wslab<FMT, 1>(p, expert_ref(p, pl, u).src, 2, r0, I, sl * SLAB, ln, gq, w[i]);
+            }
         }
-    }
+    };
+    // alone, the down weights load at once (they do not depend on h); in the
+    // whole-layer launch they load once the fills are known, which leaves the
+    // memory system to the gate/up blocks' weights first
+    if (!layer_fills) load_weights();
     auto fill_stores = [&]() {   // fill-through of this block's down bytes
 #pragma unroll
         for (int i = 0; i < SMALL_DB; ++i) {
@@ -954,6 +984,19 @@ __device__ __forceinline__ void down_rows_body(const DecodeParams& p, PlanLds& p
         }
     };
     if (!layer_fills) fill_stores();
+    if (layer_fills) {
+        // whole-layer launch: once the fills' victim slots are published (well
+        // before the gate/up blocks finish), load, and write the filled
+        // experts' down bytes to their slots
+        bool need = false;   // block-uniform: over every wavefront's items
+        for (int m = 0; m < NW * SMALL_DB; ++m) {
+            const int j = 2 * m + half;
+            if (j < n_items) need |= pl.plan[j / nsl].x < 0 || pl.plan[j / nsl].y != 0;
+        }
+        refresh_for_fills(p, pl, sync, need);
+        load_weights();
+        fill_stores();
+    }
     ASlab A[SMALL_DB];
     int hoff[SMALL_DB];   // LDS piece of the lane's h for each item, or -1 (token not routed)
 #pragma unroll
@@ -967,18 +1010,6 @@ __device__ __forceinline__ void down_rows_body(const DecodeParams& p, PlanLds& p
             for (int n = 0; n < pr.w; ++n)
                 if (pl.tok[pr.z + n] == ln) hoff[i] = (pl.pairs[pr.z + n] * I + sl * SLAB + 32 * gq) / 4;
         }
-    }
-    if (layer_fills) {
-        // whole-layer launch: the fills' victim slots are published (in practice
-        // well before the gate/up blocks finish), then the down bytes of the
-        // filled experts go to their slots while the gate/up work goes on
-        bool need = false;   // block-uniform: over every wavefront's items
-        for (int m = 0; m < NW * SMALL_DB; ++m) {
-            const int j = 2 * m + half;
-            if (j < n_items) need |= pl.plan[j / nsl].x < 0 || pl.plan[j / nsl].y != 0;
-        }
-        refresh_for_fills(p, pl, sync, need);
-        fill_stores();
     }
     wait_flag(sync, FL_DONE, blockIdx.x);
     // h pieces: [pair][I / 4] x 16 bytes (four hi halves, then four lo halves)
@@ -1198,9 +1229,11 @@ __global__ void __launch_bounds__(NW * WAVE, 4) layer_small_kernel(DecodeParams 
         classify_body<SPL, NW * WAVE>(cp, *reinterpret_cast<ClassifySmall*>(raw),
                                            sync_word(sync, FL_PLAN), sync_word(sync, FL_VICT));
     } else {
-        wait_flag(sync, FL_PLAN, blockIdx.x);
+        wait_plan(sync, blockIdx.x, pl);
         stage_plan_dev(p, pl);
-        const bool fills = p.has_cache && p.fill_through;
+        // with the fills already in the staged plan, the FFN writes them the
+        // plain way (gate/up from registers, down stores without a refresh)
+        const bool fills = p.has_cache && p.fill_through && !pl.fills_known;
         const uint32_t b = blockIdx.x - 1;
         if (b < n_gu) {
             {   // zero the output for the down blocks' additions
