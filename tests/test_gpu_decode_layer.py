@@ -85,13 +85,28 @@ def _xs(w, s):
     return torch.stack([_x_dev(tr.decode_x(w, s, l)) for l in range(w.n_layers)])
 
 
+# Small multi-token calls that take the one-launch whole-layer path (several
+# routing wavefronts, several token columns in the down products), with caches
+# small enough to evict every step: int4 + softmax-top-k, MXFP4 + sigmoid-group.
+EXTRA = {
+    6: C.Workload(cid=6, name="small_int4_t3", hidden=1024, inter=256, n_experts=32, top_k=4,
+                  route=C.ROUTE_SOFTMAX_TOPK, wfmt=C.WFMT_INT4_G64, n_layers=4, n_slots=64,
+                  t_decode=3, steps=40, zipf_alpha=1.1, keep_prob=0.5, q_num=2, q_den=3),
+    7: C.Workload(cid=7, name="small_mxfp4_t2", hidden=2048, inter=256, n_experts=64, top_k=4,
+                  route=C.ROUTE_SIGMOID_GROUP, n_group=8, topk_group=2, route_scale=2.5,
+                  wfmt=C.WFMT_MXFP4, n_layers=4, n_slots=96, t_decode=2, steps=40,
+                  zipf_alpha=1.0, keep_prob=0.6),
+}
+
+
 @pytest.mark.parametrize("mode", ["fused", "split"])
 @pytest.mark.parametrize("cid,steps,sample", [(2, 64, [(0, 3), (63, 39)]), (4, 24, [(5, 7)]),
-                                              (5, 24, [(23, 0)])])
+                                              (5, 24, [(23, 0)]), (6, 40, [(0, 1), (39, 3)]),
+                                              (7, 40, [(1, 0), (39, 2)])])
 def test_decode_layer_trace(cid, steps, sample, mode):
     import torch
     from workloads import gpu as wg
-    w = C.ALL[cid]
+    w = C.ALL[cid] if cid in C.ALL else EXTRA[cid]
     say(f"decode_layer trace {w.name} ({mode}): {steps} steps")
     trace = tr.DecodeTrace(w, steps)
     pool = wg.make_pool(w, pack=packer(desc_of(w)))
