@@ -197,6 +197,33 @@ __device__ __forceinline__ void classify_body(const ClassifyParams& cp, SH& sh, 
     // ---- one wavefront from here on ------------------------------------------
     const int lane = tid;
     const bool with_plan = cp.plan != nullptr && cp.pairs != nullptr && !evict_only;
+    auto slot_of = [&](int e) {
+        const int sl = sh.tab[e];
+        return (sl >= 0 && sl < N) ? sl : -1;  // an entry outside the cache counts as absent
+    };
+
+    // One token, published at once: its k routed experts are distinct, so the
+    // plan is those ids in ascending order, each with its slot and one pair (the
+    // pair's place is its selection rank).  The bookkeeping below writes the same
+    // values again, then the fills.
+    bool published = false;
+    if (pub_plan && mode == CLASSIFY_FULL && with_plan && cp.logits && cp.T == 1 && cp.k <= WAVE) {
+        const int k = cp.k;
+        const int ej = lane < k ? sh.ids[lane] : 0;
+        if (__ballot(lane < k && (ej < 0 || ej >= E)) == 0) {
+            int rank = 0;
+            for (int j = 0; j < k; ++j) rank += __shfl(ej, j, WAVE) < ej ? 1 : 0;
+            if (lane < k) {
+                cp.uniq[rank] = ej;
+                cp.pairs[rank] = lane;
+                reinterpret_cast<int4*>(cp.plan)[rank] = make_int4(slot_of(ej), 0, rank, 1);
+            }
+            if (lane == 0) cp.counts[0] = k;
+            publish(pub_plan);
+            published = true;
+        }
+    }
+
     for (int i = lane; i < n_ids; i += WAVE) {
         const int e = sh.ids[i];
         if (e >= 0 && e < E) sh.mark[e] = 1;  // ids out of range are ignored
@@ -206,10 +233,6 @@ __device__ __forceinline__ void classify_body(const ClassifyParams& cp, SH& sh, 
     // distinct experts, hits and misses; lane owns experts [e0, e0 + epl)
     const int epl = (E + WAVE - 1) / WAVE;
     const int e0 = lane * epl, e1 = min(E, e0 + epl);
-    auto slot_of = [&](int e) {
-        const int sl = sh.tab[e];
-        return (sl >= 0 && sl < N) ? sl : -1;  // an entry outside the cache counts as absent
-    };
     uint32_t cu = 0, ch = 0, cm = 0;
     for (int e = e0; e < e1; ++e) {
         if (!sh.mark[e]) continue;
@@ -267,7 +290,7 @@ __device__ __forceinline__ void classify_body(const ClassifyParams& cp, SH& sh, 
         }
     }
 
-    if (pub_plan && mode == CLASSIFY_FULL && with_plan) {
+    if (pub_plan && !published && mode == CLASSIFY_FULL && with_plan) {
         // first publication: where each distinct expert is read from (hits from
         // their slots, misses from the pool) and its pairs; the fills follow
         for (int e = e0; e < e1; ++e) {
