@@ -64,6 +64,9 @@ struct ClassifySharedT {
     uint64_t sel_key[NL];
     int32_t victims[NL];
     int32_t vic_owner[NL];
+    int32_t uexp[NL];      // distinct expert u's id (lane-parallel classification)
+    int32_t hslot[NL];     // the hits' slots
+    int32_t n_hit;
     uint32_t hist[256];
 };
 
@@ -158,6 +161,51 @@ __device__ __forceinline__ void classify_body(const ClassifyParams& cp, SH& sh, 
     }
     const uint32_t tick = cp.tick_dev ? static_cast<uint32_t>(*cp.tick_dev + cp.tick_add)
                                       : static_cast<uint32_t>(cp.tick_add);
+    // Victim keys (ts << sbits | slot): 32 bits when tick << sbits fits.  With
+    // 32-bit keys, slots in registers and few victims, every wavefront picks the
+    // K smallest keys of its own range of slots and wavefront 0 merges those.
+    const int sbits = N > 1 ? 32 - __clz(N - 1) : 1;
+    const bool narrow = (static_cast<uint64_t>(tick) << sbits) < (1ull << 32);
+    const bool wave_sel = need_slots && SPL > 0 && narrow && K >= 1 &&
+                          static_cast<uint32_t>(K) <= SMALL_K;
+    static_assert(2 * SH::LIST >= NWV * static_cast<int>(SMALL_K), "candidate keys fit sel_key");
+    uint32_t* const cand = reinterpret_cast<uint32_t*>(sh.sel_key);
+    // Wavefront wv over slots [wv * 64 * SPW, (wv + 1) * 64 * SPW), SPW per
+    // lane (consecutive, so the lanes read consecutive LDS words): the hits
+    // among them take the current stamp, then K rounds of a wavefront minimum
+    // over the keys above the previous pick; cand[wv * K + r] = pick r, or ~0
+    // past the last eligible key.  An ineligible slot holds the key ~0, which
+    // no round reaches (eligible keys are below tick << sbits < 2^32).
+    auto wave_pick = [&](int wv, int ln) {
+        constexpr int SPW = SPL > 0 ? (SPL + NWV - 1) / NWV : 1;
+        const int wb = wv * (WAVE * SPW), we = wb + WAVE * SPW;
+        for (int i = ln; i < sh.n_hit; i += WAVE) {
+            const int hs = sh.hslot[i];
+            if (hs >= wb && hs < we) sh.ts[hs] = tick;
+        }
+        wave_lds_sync();
+        const int s0 = wb + ln * SPW;
+        uint32_t kr[SPW];
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+            const int sl = s0 + j;
+            const uint32_t t = sl < N ? sh.ts[sl] : ~0u;
+            kr[j] = (sl < N && t < tick) ? (t << sbits) | static_cast<uint32_t>(sl) : ~0u;
+        }
+        uint32_t from = 0, mine = ~0u;   // lane r keeps pick r
+        for (int r = 0; r < K; ++r) {
+            // min over kr[j] >= from of (kr[j] - from): the subtraction sends the
+            // keys below `from` above every other
+            uint32_t lm = ~0u;
+#pragma unroll
+            for (int j = 0; j < SPW; ++j) lm = min(lm, kr[j] - from);
+            const uint32_t m = wave_min_u32(lm) + from;
+            if (m == ~0u) break;
+            if (ln == r) mine = m;
+            from = m + 1;
+        }
+        if (ln < K) cand[wv * K + ln] = mine;
+    };
     // with publication, the routing outputs must be complete before wavefront 0's release
     if (pub_plan) __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -189,7 +237,11 @@ __device__ __forceinline__ void classify_body(const ClassifyParams& cp, SH& sh, 
                     }
                 }
             }
-            __syncthreads();
+            __syncthreads();   // meet wavefront 0 (timestamps staged, hits known)
+            if (wave_sel) {
+                wave_pick(tid / WAVE, tid & (WAVE - 1));
+                __syncthreads();
+            }
         }
         return;
     }
@@ -202,21 +254,35 @@ __device__ __forceinline__ void classify_body(const ClassifyParams& cp, SH& sh, 
         return (sl >= 0 && sl < N) ? sl : -1;  // an entry outside the cache counts as absent
     };
 
+    // distinct experts (ascending ids), hits and misses, each expert's pairs
+    uint32_t n_uniq = 0, n_hit = 0, n_miss = 0;
+    const int epl = (E + WAVE - 1) / WAVE;   // general form: lane owns experts [e0, e1)
+    const int e0 = lane * epl, e1 = min(E, e0 + epl);
+    uint32_t bm = 0;                          // general form: the lane's first miss index
+    // Lane-parallel form, for a full or evict-only call of at most 64 routed
+    // ids: lane i holds id i; broadcasts of the ids give each its earlier and
+    // total occurrences and the number of distinct ids below it (its u).  Lane
+    // u then holds distinct expert u: id, slot, first pair, pair count and, for
+    // a miss, its index among the misses.
+    const bool small = n_ids <= WAVE && (mode == CLASSIFY_FULL || evict_only);
+    int su_e = -1, su_slot = -1;
+    uint32_t su_pbeg = 0, su_pcnt = 0, su_mi = 0;
+
     // One token, published at once: its k routed experts are distinct, so the
     // plan is those ids in ascending order, each with its slot and one pair (the
-    // pair's place is its selection rank).  The bookkeeping below writes the same
-    // values again, then the fills.
+    // pair's place is its selection rank).  The bookkeeping below writes the
+    // same values again, then the fills.
     bool published = false;
     if (pub_plan && mode == CLASSIFY_FULL && with_plan && cp.logits && cp.T == 1 && cp.k <= WAVE) {
         const int k = cp.k;
         const int ej = lane < k ? sh.ids[lane] : 0;
         if (__ballot(lane < k && (ej < 0 || ej >= E)) == 0) {
-            int rank = 0;
-            for (int j = 0; j < k; ++j) rank += __shfl(ej, j, WAVE) < ej ? 1 : 0;
+            uint32_t rank = 0;
+            for (int j = 0; j < k; ++j) rank += __builtin_amdgcn_readlane(ej, j) < ej ? 1u : 0u;
             if (lane < k) {
                 cp.uniq[rank] = ej;
                 cp.pairs[rank] = lane;
-                reinterpret_cast<int4*>(cp.plan)[rank] = make_int4(slot_of(ej), 0, rank, 1);
+                reinterpret_cast<int4*>(cp.plan)[rank] = make_int4(slot_of(ej), 0, static_cast<int>(rank), 1);
             }
             if (lane == 0) cp.counts[0] = k;
             publish(pub_plan);
@@ -224,82 +290,141 @@ __device__ __forceinline__ void classify_body(const ClassifyParams& cp, SH& sh, 
         }
     }
 
-    for (int i = lane; i < n_ids; i += WAVE) {
-        const int e = sh.ids[i];
-        if (e >= 0 && e < E) sh.mark[e] = 1;  // ids out of range are ignored
-    }
-    wave_lds_sync();
+    if (small) {
+        const int e = lane < n_ids ? sh.ids[lane] : -1;
+        const bool valid = lane < n_ids && e >= 0 && e < E;   // ids out of range are ignored
+        uint32_t before = 0, cnt = 0;
+        for (int j = 0; j < n_ids; ++j) {
+            const int o = __builtin_amdgcn_readlane(e, j);
+            before += (o == e && j < lane) ? 1u : 0u;
+            cnt += o == e ? 1u : 0u;
+        }
+        const uint64_t fm = __ballot(valid && before == 0);   // first occurrences
+        n_uniq = static_cast<uint32_t>(__popcll(fm));
+        uint32_t u = 0;
+        for (uint64_t m = fm; m; m &= m - 1) u += __builtin_amdgcn_readlane(e, __builtin_ctzll(m)) < e ? 1u : 0u;
+        if (valid && before == 0) {
+            sh.uexp[u] = e;
+            sh.pcnt[u] = static_cast<int32_t>(cnt);
+        }
+        wave_lds_sync();
+        const bool has_u = static_cast<uint32_t>(lane) < n_uniq;
+        su_e = has_u ? sh.uexp[lane] : -1;
+        su_pcnt = has_u ? static_cast<uint32_t>(sh.pcnt[lane]) : 0u;
+        su_slot = has_u ? slot_of(su_e) : -1;
+        uint32_t n_pairs;
+        su_pbeg = wave_excl_scan(su_pcnt, &n_pairs);
+        const bool hit = has_u && su_slot >= 0, miss = has_u && su_slot < 0;
+        const uint64_t hm = __ballot(hit), mm = __ballot(miss);
+        n_hit = static_cast<uint32_t>(__popcll(hm));
+        n_miss = static_cast<uint32_t>(__popcll(mm));
+        const uint32_t hi = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(hm >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(hm), 0u));
+        su_mi = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mm >> 32),
+                                          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mm), 0u));
+        if (has_u) {
+            if (!evict_only) cp.uniq[lane] = su_e;
+            sh.pbeg[lane] = static_cast<int32_t>(su_pbeg);
+        }
+        if (hit) {
+            if (!evict_only) {
+                cp.hit_e[hi] = su_e;
+                cp.hit_s[hi] = su_slot;
+            }
+            sh.hslot[hi] = su_slot;
+            slot_ts[su_slot] = tick;   // recency moves on a router selection
+        }
+        if (miss) {
+            if (!evict_only) cp.miss[su_mi] = su_e;
+            sh.miss[su_mi] = su_e;
+        }
+        if (lane == 0) sh.n_hit = static_cast<int32_t>(n_hit);
+        wave_lds_sync();
+        if (with_plan && valid) cp.pairs[sh.pbeg[u] + static_cast<int32_t>(before)] = lane;
+        if (pub_plan && !published && mode == CLASSIFY_FULL && with_plan) {
+            // first publication: where each distinct expert is read from (hits
+            // from their slots, misses from the pool) and its pairs
+            if (has_u)
+                reinterpret_cast<int4*>(cp.plan)[lane] =
+                    make_int4(su_slot, 0, static_cast<int>(su_pbeg), static_cast<int>(su_pcnt));
+            if (lane == 0) cp.counts[0] = static_cast<int32_t>(n_uniq);
+            publish(pub_plan);
+        }
+    } else {
+        for (int i = lane; i < n_ids; i += WAVE) {
+            const int e = sh.ids[i];
+            if (e >= 0 && e < E) sh.mark[e] = 1;  // ids out of range are ignored
+        }
+        wave_lds_sync();
 
-    // distinct experts, hits and misses; lane owns experts [e0, e0 + epl)
-    const int epl = (E + WAVE - 1) / WAVE;
-    const int e0 = lane * epl, e1 = min(E, e0 + epl);
-    uint32_t cu = 0, ch = 0, cm = 0;
-    for (int e = e0; e < e1; ++e) {
-        if (!sh.mark[e]) continue;
-        ++cu;
-        if (slot_of(e) >= 0) ++ch;
-        else ++cm;
-    }
-    uint32_t n_uniq, n_hit, n_miss;
-    const uint32_t bu = wave_excl_scan(cu, &n_uniq);
-    const uint32_t bh = wave_excl_scan(ch, &n_hit);
-    const uint32_t bm = wave_excl_scan(cm, &n_miss);
-    {
-        uint32_t u = bu, h = bh, mi = bm;
+        uint32_t cu = 0, ch = 0, cm = 0;
         for (int e = e0; e < e1; ++e) {
             if (!sh.mark[e]) continue;
-            if (!evict_only) cp.uniq[u] = e;
-            sh.upos[e] = static_cast<int32_t>(u++);
-            const int sl = slot_of(e);
-            if (dedup_only) continue;
-            if (sl >= 0) {
-                if (!evict_only) {
-                    cp.hit_e[h] = e;
-                    cp.hit_s[h] = sl;
+            ++cu;
+            if (slot_of(e) >= 0) ++ch;
+            else ++cm;
+        }
+        const uint32_t bu = wave_excl_scan(cu, &n_uniq);
+        const uint32_t bh = wave_excl_scan(ch, &n_hit);
+        bm = wave_excl_scan(cm, &n_miss);
+        if (lane == 0) sh.n_hit = static_cast<int32_t>(n_hit);
+        {
+            uint32_t u = bu, h = bh, mi = bm;
+            for (int e = e0; e < e1; ++e) {
+                if (!sh.mark[e]) continue;
+                if (!evict_only) cp.uniq[u] = e;
+                sh.upos[e] = static_cast<int32_t>(u++);
+                const int sl = slot_of(e);
+                if (dedup_only) continue;
+                if (sl >= 0) {
+                    if (!evict_only) {
+                        cp.hit_e[h] = e;
+                        cp.hit_s[h] = sl;
+                    }
+                    sh.hslot[h++] = sl;
+                    if (!plan_only) slot_ts[sl] = tick;  // recency moves on a router selection
+                } else {
+                    if (!evict_only) cp.miss[mi] = e;
+                    sh.miss[mi++] = e;
                 }
-                ++h;
-                if (!plan_only) slot_ts[sl] = tick;  // recency moves on a router selection
-            } else {
-                if (!evict_only) cp.miss[mi] = e;
-                sh.miss[mi++] = e;
             }
         }
-    }
-    wave_lds_sync();
-
-    // the routed pairs of each distinct expert, grouped by u
-    if (with_plan) {
-        for (int i = lane; i < n_ids; i += WAVE) {
-            const int e = sh.ids[i];
-            sh.plocal[i] = (e >= 0 && e < E) ? atomicAdd(&sh.pcnt[sh.upos[e]], 1) : -1;
-        }
         wave_lds_sync();
-        const int upl = (static_cast<int>(n_uniq) + WAVE - 1) / WAVE;
-        const int u0 = lane * upl, u1 = min(static_cast<int>(n_uniq), u0 + upl);
-        uint32_t c = 0, tot;
-        for (int u = u0; u < u1; ++u) c += sh.pcnt[u];
-        uint32_t b = wave_excl_scan(c, &tot);
-        for (int u = u0; u < u1; ++u) {
-            sh.pbeg[u] = static_cast<int32_t>(b);
-            b += sh.pcnt[u];
-        }
-        wave_lds_sync();
-        for (int i = lane; i < n_ids; i += WAVE) {
-            const int e = sh.ids[i];
-            if (e >= 0 && e < E) cp.pairs[sh.pbeg[sh.upos[e]] + sh.plocal[i]] = i;
-        }
-    }
 
-    if (pub_plan && !published && mode == CLASSIFY_FULL && with_plan) {
-        // first publication: where each distinct expert is read from (hits from
-        // their slots, misses from the pool) and its pairs; the fills follow
-        for (int e = e0; e < e1; ++e) {
-            if (!sh.mark[e]) continue;
-            const int u = sh.upos[e];
-            reinterpret_cast<int4*>(cp.plan)[u] = make_int4(slot_of(e), 0, sh.pbeg[u], sh.pcnt[u]);
+        // the routed pairs of each distinct expert, grouped by u
+        if (with_plan) {
+            for (int i = lane; i < n_ids; i += WAVE) {
+                const int e = sh.ids[i];
+                sh.plocal[i] = (e >= 0 && e < E) ? atomicAdd(&sh.pcnt[sh.upos[e]], 1) : -1;
+            }
+            wave_lds_sync();
+            const int upl = (static_cast<int>(n_uniq) + WAVE - 1) / WAVE;
+            const int u0 = lane * upl, u1 = min(static_cast<int>(n_uniq), u0 + upl);
+            uint32_t c = 0, tot;
+            for (int u = u0; u < u1; ++u) c += sh.pcnt[u];
+            uint32_t b = wave_excl_scan(c, &tot);
+            for (int u = u0; u < u1; ++u) {
+                sh.pbeg[u] = static_cast<int32_t>(b);
+                b += sh.pcnt[u];
+            }
+            wave_lds_sync();
+            for (int i = lane; i < n_ids; i += WAVE) {
+                const int e = sh.ids[i];
+                if (e >= 0 && e < E) cp.pairs[sh.pbeg[sh.upos[e]] + sh.plocal[i]] = i;
+            }
         }
-        if (lane == 0) cp.counts[0] = static_cast<int32_t>(n_uniq);
-        publish(pub_plan);
+
+        if (pub_plan && !published && mode == CLASSIFY_FULL && with_plan) {
+            // first publication: where each distinct expert is read from (hits from
+            // their slots, misses from the pool) and its pairs; the fills follow
+            for (int e = e0; e < e1; ++e) {
+                if (!sh.mark[e]) continue;
+                const int u = sh.upos[e];
+                reinterpret_cast<int4*>(cp.plan)[u] = make_int4(slot_of(e), 0, sh.pbeg[u], sh.pcnt[u]);
+            }
+            if (lane == 0) cp.counts[0] = static_cast<int32_t>(n_uniq);
+            publish(pub_plan);
+        }
     }
 
     if (dedup_only) {
@@ -328,161 +453,190 @@ __device__ __forceinline__ void classify_body(const ClassifyParams& cp, SH& sh, 
 
     // ---- one scan of every slot's timestamp: the K oldest eligible slots -----
     __syncthreads();   // the other wavefronts have staged the timestamps and owners
-    for (int e = e0; e < e1; ++e)   // the hits' new stamps, over the staged ones
-        if (sh.mark[e] && slot_of(e) >= 0) sh.ts[slot_of(e)] = tick;
-    wave_lds_sync();
-    const int sbits = N > 1 ? 32 - __clz(N - 1) : 1;
-    const int spl = SPL > 0 ? SPL : (N + WAVE - 1) / WAVE;
-    const int s0 = lane * spl, s1 = min(N, s0 + spl);
-    // Victims: the n_vic smallest (ts << sbits | slot) keys among eligible slots.
-    // With 32-bit keys (tick << sbits fits) each lane holds its timestamps in
-    // registers; otherwise it reads them from LDS.
-    const bool narrow = (static_cast<uint64_t>(tick) << sbits) < (1ull << 32);
-    uint32_t n_elig = 0, n_vic = 0;
-    bool ranked = false;   // victims already written in rank order
-    auto select = [&](auto key_zero, auto in_regs) {
-        using KT = decltype(key_zero);
-        constexpr bool REGS = decltype(in_regs)::value && SPL > 0;
-        constexpr int RL = REGS ? SPL : 1;
-        uint32_t tsr[RL];
-        if constexpr (REGS) {
+    uint32_t n_vic = 0;
+    if (wave_sel) {
+        wave_pick(0, lane);
+        __syncthreads();   // every wavefront's picks
+        // the K smallest of the NWV * K candidates, in rank order (lane r keeps pick r)
+        constexpr int CPL = (NWV * static_cast<int>(SMALL_K) + WAVE - 1) / WAVE;
+        const int C = NWV * K;
+        uint32_t c[CPL];
 #pragma unroll
-            for (int j = 0; j < SPL; j += 4) {
-                if (s0 + j + 3 < N) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(&sh.ts[s0 + j]);
-                    tsr[j] = v.x; tsr[j + 1] = v.y; tsr[j + 2] = v.z; tsr[j + 3] = v.w;
-                } else {
+        for (int j = 0; j < CPL; ++j) c[j] = lane + j * WAVE < C ? cand[lane + j * WAVE] : ~0u;
+        uint32_t from = 0;
+        int vic = -1;
+        for (int r = 0; r < K; ++r) {
+            uint32_t lm = ~0u;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) tsr[j + i] = s0 + j + i < N ? sh.ts[s0 + j + i] : ~0u;
-                }
-            }
+            for (int j = 0; j < CPL; ++j) lm = min(lm, c[j] - from);
+            const uint32_t m = wave_min_u32(lm) + from;
+            if (m == ~0u) break;
+            if (lane == r) vic = static_cast<int>(m & ((1u << sbits) - 1));
+            from = m + 1;
+            ++n_vic;
         }
-        // calls f(slot, ts) for each of this lane's slots
-        auto for_slots = [&](auto f) {
+        if (static_cast<uint32_t>(lane) < n_vic) {
+            sh.victims[lane] = vic;
+            cp.victims[lane] = vic;
+            if (own_lds) sh.vic_owner[lane] = sh.own[vic];
+            else sh.vic_owner[lane] = owner[vic];
+        }
+        wave_lds_sync();
+    } else {
+        for (int i = lane; i < static_cast<int>(n_hit); i += WAVE)   // the hits' new stamps, over the staged ones
+            sh.ts[sh.hslot[i]] = tick;
+        wave_lds_sync();
+        const int spl = SPL > 0 ? SPL : (N + WAVE - 1) / WAVE;
+        const int s0 = lane * spl, s1 = min(N, s0 + spl);
+        // Victims: the n_vic smallest (ts << sbits | slot) keys among eligible slots.
+        // With 32-bit keys (tick << sbits fits) wavefront 0 holds every timestamp in
+        // registers; otherwise it reads them from LDS.
+        uint32_t n_elig = 0;
+        bool ranked = false;   // victims already written in rank order
+        auto select = [&](auto key_zero, auto in_regs) {
+            using KT = decltype(key_zero);
+            constexpr bool REGS = decltype(in_regs)::value && SPL > 0;
+            constexpr int RL = REGS ? SPL : 1;
+            uint32_t tsr[RL];
             if constexpr (REGS) {
 #pragma unroll
-                for (int j = 0; j < SPL; ++j) f(s0 + j, tsr[j]);
-            } else {
-                for (int sl = s0; sl < s1; ++sl) f(sl, sh.ts[sl]);
-            }
-        };
-        uint32_t ce = 0;
-        for_slots([&](int sl, uint32_t t) { ce += (sl < N && t < tick) ? 1u : 0u; });
-        wave_excl_scan(ce, &n_elig);
-        n_vic = n_elig < static_cast<uint32_t>(K) ? n_elig : static_cast<uint32_t>(K);
-        if (n_vic == 0) return;
-        constexpr int KB = 8 * sizeof(KT);
-        auto key = [&](int sl, uint32_t t) { return (static_cast<KT>(t) << sbits) | static_cast<KT>(sl); };
-        if constexpr (REGS && KB == 32) {
-            if (n_vic <= SMALL_K) {
-                // Few victims: n_vic rounds of a wave-wide minimum, each over the keys
-                // above the previous pick; the picks come out in rank order.  An
-                // ineligible slot holds the key ~0, which no round reaches (eligible
-                // keys are below tick << sbits < 2^32 and n_vic <= n_elig).
-                uint32_t kr[RL];
+                for (int j = 0; j < SPL; j += 4) {
+                    if (s0 + j + 3 < N) {
+                        const uint4 v = *reinterpret_cast<const uint4*>(&sh.ts[s0 + j]);
+                        tsr[j] = v.x; tsr[j + 1] = v.y; tsr[j + 2] = v.z; tsr[j + 3] = v.w;
+                    } else {
 #pragma unroll
-                for (int j = 0; j < RL; ++j)
-                    kr[j] = (s0 + j < N && tsr[j] < tick) ? key(s0 + j, tsr[j]) : ~0u;
-                uint32_t from = 0;   // smallest key still eligible for a pick
-                int vic = -1;        // lane r keeps pick r
-                for (uint32_t r = 0; r < n_vic; ++r) {
-                    // min over kr[j] >= from of (kr[j] - from): the subtraction sends
-                    // the keys below `from` to the top of the unsigned range
-                    uint32_t lm = ~0u;
-#pragma unroll
-                    for (int j = 0; j < RL; ++j) lm = min(lm, kr[j] - from);
-                    const uint32_t m = wave_min_u32(lm) + from;
-                    if (static_cast<uint32_t>(lane) == r) vic = static_cast<int>(m & ((1u << sbits) - 1));
-                    from = m + 1;
-                }
-                if (static_cast<uint32_t>(lane) < n_vic) {
-                    sh.victims[lane] = vic;
-                    cp.victims[lane] = vic;
-                    if (own_lds) sh.vic_owner[lane] = sh.own[vic];
-                    else sh.vic_owner[lane] = owner[vic];
-                }
-                ranked = true;
-                return;
-            }
-        }
-        KT thr = ~static_cast<KT>(0);
-        if (n_elig > n_vic) {
-            const uint64_t top = static_cast<uint64_t>(tick) << sbits;
-            const int bits = 64 - __clzll(static_cast<long long>(top));
-            KT prefix = 0, pmask = 0;
-            uint32_t remaining = n_vic;
-            for (int shift = ((bits - 1) / 8) * 8; shift >= 0; shift -= 8) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sh.hist[lane * 4 + i] = 0;
-                wave_lds_sync();
-                for_slots([&](int sl, uint32_t t) {
-                    const KT k = key(sl, t);
-                    if (sl < N && t < tick && (k & pmask) == prefix)
-                        atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
-                });
-                wave_lds_sync();
-                uint32_t c4[4], local = 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    c4[i] = sh.hist[lane * 4 + i];
-                    local += c4[i];
-                }
-                uint32_t tot;
-                const uint32_t before = wave_excl_scan(local, &tot);
-                // the lane whose range of the histogram crosses `remaining`
-                const bool mine = before < remaining && remaining <= before + local;
-                uint32_t digit = 0, rem = 0;
-                if (mine) {
-                    uint32_t acc = before;
-                    for (int i = 0; i < 4; ++i) {
-                        if (acc + c4[i] >= remaining) {
-                            digit = lane * 4 + i;
-                            rem = remaining - acc;
-                            break;
-                        }
-                        acc += c4[i];
+                        for (int i = 0; i < 4; ++i) tsr[j + i] = s0 + j + i < N ? sh.ts[s0 + j + i] : ~0u;
                     }
                 }
-                const int src = __builtin_ctzll(__ballot(mine));
-                digit = __builtin_amdgcn_readlane(digit, src);
-                rem = __builtin_amdgcn_readlane(rem, src);
-                prefix |= static_cast<KT>(digit) << shift;
-                pmask |= static_cast<KT>(255) << shift;
-                remaining = rem;
             }
-            thr = prefix;
+            // calls f(slot, ts) for each of this lane's slots
+            auto for_slots = [&](auto f) {
+                if constexpr (REGS) {
+#pragma unroll
+                    for (int j = 0; j < SPL; ++j) f(s0 + j, tsr[j]);
+                } else {
+                    for (int sl = s0; sl < s1; ++sl) f(sl, sh.ts[sl]);
+                }
+            };
+            uint32_t ce = 0;
+            for_slots([&](int sl, uint32_t t) { ce += (sl < N && t < tick) ? 1u : 0u; });
+            wave_excl_scan(ce, &n_elig);
+            n_vic = n_elig < static_cast<uint32_t>(K) ? n_elig : static_cast<uint32_t>(K);
+            if (n_vic == 0) return;
+            constexpr int KB = 8 * sizeof(KT);
+            auto key = [&](int sl, uint32_t t) { return (static_cast<KT>(t) << sbits) | static_cast<KT>(sl); };
+            if constexpr (REGS && KB == 32) {
+                if (n_vic <= SMALL_K) {
+                    // Few victims: n_vic rounds of a wave-wide minimum, each over the keys
+                    // above the previous pick; the picks come out in rank order.  An
+                    // ineligible slot holds the key ~0, which no round reaches (eligible
+                    // keys are below tick << sbits < 2^32 and n_vic <= n_elig).
+                    uint32_t kr[RL];
+#pragma unroll
+                    for (int j = 0; j < RL; ++j)
+                        kr[j] = (s0 + j < N && tsr[j] < tick) ? key(s0 + j, tsr[j]) : ~0u;
+                    uint32_t from = 0;   // smallest key still eligible for a pick
+                    int vic = -1;        // lane r keeps pick r
+                    for (uint32_t r = 0; r < n_vic; ++r) {
+                        // min over kr[j] >= from of (kr[j] - from): the subtraction sends
+                        // the keys below `from` to the top of the unsigned range
+                        uint32_t lm = ~0u;
+#pragma unroll
+                        for (int j = 0; j < RL; ++j) lm = min(lm, kr[j] - from);
+                        const uint32_t m = wave_min_u32(lm) + from;
+                        if (static_cast<uint32_t>(lane) == r) vic = static_cast<int>(m & ((1u << sbits) - 1));
+                        from = m + 1;
+                    }
+                    if (static_cast<uint32_t>(lane) < n_vic) {
+                        sh.victims[lane] = vic;
+                        cp.victims[lane] = vic;
+                        if (own_lds) sh.vic_owner[lane] = sh.own[vic];
+                        else sh.vic_owner[lane] = owner[vic];
+                    }
+                    ranked = true;
+                    return;
+                }
+            }
+            KT thr = ~static_cast<KT>(0);
+            if (n_elig > n_vic) {
+                const uint64_t top = static_cast<uint64_t>(tick) << sbits;
+                const int bits = 64 - __clzll(static_cast<long long>(top));
+                KT prefix = 0, pmask = 0;
+                uint32_t remaining = n_vic;
+                for (int shift = ((bits - 1) / 8) * 8; shift >= 0; shift -= 8) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sh.hist[lane * 4 + i] = 0;
+                    wave_lds_sync();
+                    for_slots([&](int sl, uint32_t t) {
+                        const KT k = key(sl, t);
+                        if (sl < N && t < tick && (k & pmask) == prefix)
+                            atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
+                    });
+                    wave_lds_sync();
+                    uint32_t c4[4], local = 0;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        c4[i] = sh.hist[lane * 4 + i];
+                        local += c4[i];
+                    }
+                    uint32_t tot;
+                    const uint32_t before = wave_excl_scan(local, &tot);
+                    // the lane whose range of the histogram crosses `remaining`
+                    const bool mine = before < remaining && remaining <= before + local;
+                    uint32_t digit = 0, rem = 0;
+                    if (mine) {
+                        uint32_t acc = before;
+                        for (int i = 0; i < 4; ++i) {
+                            if (acc + c4[i] >= remaining) {
+                                digit = lane * 4 + i;
+                                rem = remaining - acc;
+                                break;
+                            }
+                            acc += c4[i];
+                        }
+                    }
+                    const int src = __builtin_ctzll(__ballot(mine));
+                    digit = __builtin_amdgcn_readlane(digit, src);
+                    rem = __builtin_amdgcn_readlane(rem, src);
+                    prefix |= static_cast<KT>(digit) << shift;
+                    pmask |= static_cast<KT>(255) << shift;
+                    remaining = rem;
+                }
+                thr = prefix;
+            }
+            static_assert(KB == 32 || KB == 64, "key width");
+            // collect the selected keys in slot order, then rank them by key
+            uint32_t cs = 0;
+            for_slots([&](int sl, uint32_t t) { cs += (sl < N && t < tick && key(sl, t) <= thr) ? 1u : 0u; });
+            uint32_t n_sel;
+            uint32_t at = wave_excl_scan(cs, &n_sel);
+            for_slots([&](int sl, uint32_t t) {
+                if (sl < N && t < tick && key(sl, t) <= thr) sh.sel_key[at++] = static_cast<uint64_t>(key(sl, t));
+            });
+        };
+        if (narrow)
+            select(uint32_t{0}, std::true_type{});
+        else
+            select(uint64_t{0}, std::false_type{});
+        if (n_vic > 0 && ranked) wave_lds_sync();   // lane 0 wrote the victims
+        if (n_vic > 0 && !ranked) {
+            wave_lds_sync();
+            for (uint32_t i = lane; i < n_vic; i += WAVE) {
+                const uint64_t k = sh.sel_key[i];
+                uint32_t r = 0;
+                for (uint32_t j = 0; j < n_vic; ++j) r += sh.sel_key[j] < k ? 1u : 0u;
+                const int sl = static_cast<int>(k & ((1ull << sbits) - 1));
+                sh.victims[r] = sl;
+                cp.victims[r] = sl;
+                // owners looked up here, off the collection loop, from LDS or from
+                // memory by a uniform branch (a generic load would wait for every
+                // store in flight)
+                if (own_lds) sh.vic_owner[r] = sh.own[sl];
+                else sh.vic_owner[r] = owner[sl];
+            }
+            wave_lds_sync();
         }
-        static_assert(KB == 32 || KB == 64, "key width");
-        // collect the selected keys in slot order, then rank them by key
-        uint32_t cs = 0;
-        for_slots([&](int sl, uint32_t t) { cs += (sl < N && t < tick && key(sl, t) <= thr) ? 1u : 0u; });
-        uint32_t n_sel;
-        uint32_t at = wave_excl_scan(cs, &n_sel);
-        for_slots([&](int sl, uint32_t t) {
-            if (sl < N && t < tick && key(sl, t) <= thr) sh.sel_key[at++] = static_cast<uint64_t>(key(sl, t));
-        });
-    };
-    if (narrow)
-        select(uint32_t{0}, std::true_type{});
-    else
-        select(uint64_t{0}, std::false_type{});
-    if (n_vic > 0 && ranked) wave_lds_sync();   // lane 0 wrote the victims
-    if (n_vic > 0 && !ranked) {
-        wave_lds_sync();
-        for (uint32_t i = lane; i < n_vic; i += WAVE) {
-            const uint64_t k = sh.sel_key[i];
-            uint32_t r = 0;
-            for (uint32_t j = 0; j < n_vic; ++j) r += sh.sel_key[j] < k ? 1u : 0u;
-            const int sl = static_cast<int>(k & ((1ull << sbits) - 1));
-            sh.victims[r] = sl;
-            cp.victims[r] = sl;
-            // owners looked up here, off the collection loop, from LDS or from
-            // memory by a uniform branch (a generic load would wait for every
-            // store in flight)
-            if (own_lds) sh.vic_owner[r] = sh.own[sl];
-            else sh.vic_owner[r] = owner[sl];
-        }
-        wave_lds_sync();
     }
 
     // ---- q split and slot update -------------------------------------------
@@ -502,8 +656,18 @@ __device__ __forceinline__ void classify_body(const ClassifyParams& cp, SH& sh, 
         cp.fill_s[i] = v;
     }
     for (uint32_t i = q_eff + lane; i < n_miss; i += WAVE) cp.inplace[i - q_eff] = sh.miss[i];
-    if (with_plan) {
+    if (with_plan && small) {
         // where the FFN reads each expert from after the call, and whether it is filled now
+        if (static_cast<uint32_t>(lane) < n_uniq) {
+            int final_slot = su_slot, filled = 0;
+            if (su_slot < 0) {
+                filled = su_mi < q_eff ? 1 : 0;
+                final_slot = filled ? sh.victims[su_mi] : -1;
+            }
+            reinterpret_cast<int4*>(cp.plan)[lane] =
+                make_int4(final_slot, filled, static_cast<int>(su_pbeg), static_cast<int>(su_pcnt));
+        }
+    } else if (with_plan) {
         uint32_t mi = bm;
         for (int e = e0; e < e1; ++e) {
             if (!sh.mark[e]) continue;
