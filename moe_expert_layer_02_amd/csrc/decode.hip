@@ -968,8 +968,10 @@ __device__ __forceinline__ void down_rows_body(const DecodeParams& p, PlanLds& p
             }
         }
     };
-    // the down weights load at once (they depend neither on h nor on the fills)
-    load_weights();
+    // alone, the down weights load at once (they do not depend on h); in the
+    // whole-layer launch they load once the fills are known, which leaves the
+    // memory system to the gate/up blocks' weights first
+    if (!layer_fills) load_weights();
     auto fill_stores = [&]() {   // fill-through of this block's down bytes
 #pragma unroll
         for (int i = 0; i < SMALL_DB; ++i) {
@@ -983,15 +985,16 @@ __device__ __forceinline__ void down_rows_body(const DecodeParams& p, PlanLds& p
     };
     if (!layer_fills) fill_stores();
     if (layer_fills) {
-        // whole-layer launch: once the fills' victim slots are published (about
-        // when the gate/up blocks finish), write the filled experts' down bytes
-        // to their slots
+        // whole-layer launch: once the fills' victim slots are published (while
+        // the gate/up blocks compute), load, and write the filled experts' down
+        // bytes to their slots
         bool need = false;   // block-uniform: over every wavefront's items
         for (int m = 0; m < NW * SMALL_DB; ++m) {
             const int j = 2 * m + half;
             if (j < n_items) need |= pl.plan[j / nsl].x < 0 || pl.plan[j / nsl].y != 0;
         }
         refresh_for_fills(p, pl, sync, need);
+        load_weights();
         fill_stores();
     }
     ASlab A[SMALL_DB];
