@@ -43,6 +43,23 @@ struct ClassifyParams {
     int32_t *plan, *pairs;     // optional: the FFN's per-expert plan and grouped pairs
 };
 
+// One-token plan record.  In the whole-layer launch a one-token call with at
+// most REC_K routed experts and non-negative routing weights carries its whole
+// plan in the plan flag: each of the flag's 64 copies is 16 words, written
+// through to the device coherence point by one lane, each word with bit 31 set
+// so that a reader can tell a complete copy from a cleared one (a word is
+// written whole).  Word u, for the u-th smallest routed id (u < k): miss << 30
+// | slot << 16 (14 bits) | id << 6 (10 bits) | the pair, i.e. the id's
+// selection rank (6 bits); word 8 + u: that pair's routing weight.  Words of
+// u >= k hold bit 31 alone.
+constexpr int REC_K = 8;
+constexpr uint32_t REC_BIT = 0x80000000u;
+__host__ __device__ inline bool plan_record(const ClassifyParams& cp) {
+    return cp.mode == CLASSIFY_FULL && cp.plan != nullptr && cp.pairs != nullptr &&
+           cp.logits != nullptr && cp.T == 1 && cp.k >= 1 && cp.k <= REC_K && cp.N <= 16384 &&
+           cp.E <= 1024 && (cp.route_kind == MOE355_ROUTE_SOFTMAX_TOPK || cp.route_scale > 0.0f);
+}
+
 
 namespace {
 
@@ -139,11 +156,13 @@ __device__ __forceinline__ void classify_body(const ClassifyParams& cp, SH& sh, 
     // The table entry is requested before the logits, so the two loads are in
     // flight together (a wavefront's loads complete in order).
     const int32_t tab_v = (tid < E && !dedup_only) ? table[layer * E + tid] : -1;
+    float w_tok0 = 0.0f;   // wavefront 0: token 0's routing weight of the lane's pick
     if (cp.logits) {
         for (int t = tid / WAVE; t < cp.T; t += NWV) {
             float w;
             const int e = route_token(cp.logits + static_cast<int64_t>(t) * E, E, cp.k,
                                       cp.route_kind, cp.n_group, cp.topk_group, cp.route_scale, &w);
+            if (t == 0) w_tok0 = w;
             const int lane = tid & (WAVE - 1);
             if (lane < cp.k) {
                 cp.ids_out[t * cp.k + lane] = e;
@@ -279,13 +298,31 @@ __device__ __forceinline__ void classify_body(const ClassifyParams& cp, SH& sh, 
         if (__ballot(lane < k && (ej < 0 || ej >= E)) == 0) {
             uint32_t rank = 0;
             for (int j = 0; j < k; ++j) rank += __builtin_amdgcn_readlane(ej, j) < ej ? 1u : 0u;
-            if (lane < k) {
-                cp.uniq[rank] = ej;
-                cp.pairs[rank] = lane;
-                reinterpret_cast<int4*>(cp.plan)[rank] = make_int4(slot_of(ej), 0, static_cast<int>(rank), 1);
+            if (plan_record(cp)) {
+                // the record in LDS (hist is free until the victim scan), then
+                // lane l writes copy l
+                if (lane < 2 * REC_K) sh.hist[lane] = REC_BIT;
+                wave_lds_sync();
+                if (lane < k) {
+                    const int sl = slot_of(ej);
+                    sh.hist[rank] = REC_BIT | (sl < 0 ? 1u << 30 : static_cast<uint32_t>(sl) << 16) |
+                                    static_cast<uint32_t>(ej) << 6 | static_cast<uint32_t>(lane);
+                    sh.hist[REC_K + rank] = __float_as_uint(w_tok0) | REC_BIT;
+                }
+                wave_lds_sync();
+                uint32_t* dst = pub_plan + 64 * lane;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    st_dev16(dst + 4 * q, sh.hist[4 * q], sh.hist[4 * q + 1], sh.hist[4 * q + 2], sh.hist[4 * q + 3]);
+            } else {
+                if (lane < k) {
+                    cp.uniq[rank] = ej;
+                    cp.pairs[rank] = lane;
+                    reinterpret_cast<int4*>(cp.plan)[rank] = make_int4(slot_of(ej), 0, static_cast<int>(rank), 1);
+                }
+                if (lane == 0) cp.counts[0] = k;
+                publish(pub_plan);
             }
-            if (lane == 0) cp.counts[0] = k;
-            publish(pub_plan);
             published = true;
         }
     }

@@ -93,6 +93,7 @@ struct PlanLds {
     float w[MAX_PLAN];       // routing weight of each pair
     int32_t n_uniq;
     int32_t fills_known;     // whole-layer launch: the staged plan already names the fills
+    uint32_t rec[2 * REC_K]; // whole-layer launch: the one-token plan record
 };
 
 // A wavefront-uniform device pointer moved into scalar registers, so that loads
@@ -447,7 +448,9 @@ __device__ __forceinline__ void block_exit(uint32_t* sync) {
         if (__shfl(last, 0, WAVE)) {   // every block is past its waits: clear the rest
             const int l = threadIdx.x;
             store_dev(sync_word(sync, FL_DONE + l), 0u);
-            store_dev(sync_word(sync, FL_PLAN + l), 0u);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)   // the plan flag copy, record words included
+                st_dev16(sync_word(sync, FL_PLAN + l) + 4 * q, 0u, 0u, 0u, 0u);
             store_dev(sync_word(sync, FL_VICT + l), 0u);
             if (l < 8) store_dev(sync_word(sync, SW_DONE + l), 0u);
             if (l == 0) {
@@ -469,6 +472,62 @@ __device__ __forceinline__ uint4 ld_dev16(const void* q) {
 
 __device__ __forceinline__ int32_t ld_dev32(const int32_t* q) {
     return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Whole-layer launch, one-token plan record: until every word of copy b % 64 of
+// the plan flag carries REC_BIT (lanes 0..3 poll 16 bytes each); the record
+// then fills the staged plan (pair u of expert u, token 0).  The record is the
+// first plan and never names the fills: a block that finds the victims flag
+// already up (a block that starts late) stages the final plan from memory
+// instead.  A wait that gives up stages no experts.
+__device__ __forceinline__ void stage_plan_dev(const DecodeParams& p, PlanLds& pl);
+__device__ __forceinline__ void wait_plan_record(uint32_t* sync, uint32_t b, const DecodeParams& p,
+                                                 PlanLds& pl) {
+    const int t = threadIdx.x;
+    if (t < 4) {
+        const uint32_t* rec = sync_word(sync, FL_PLAN + static_cast<int>(b & 63));
+        const uint32_t* vw = sync_word(sync, FL_VICT + static_cast<int>(b & 63));
+        uint32_t n = 0, v = 0;
+        bool whole = false;
+        uint4 r;
+        while (true) {
+            if (t == 0) v = __hip_atomic_load(vw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            r = ld_dev16(rec + 4 * t);
+            if (__shfl(v, 0, 4) != 0u) break;
+            whole = (__ballot((r.x & r.y & r.z & r.w & REC_BIT) != 0u) & 0xFull) == 0xFull;
+            if (whole) break;
+            __builtin_amdgcn_s_sleep(2);
+            if (++n == SPIN_LIMIT) {
+                if (t == 0)
+                    __hip_atomic_fetch_or(sync_word(sync, SW_ERR), 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
+        pl.rec[4 * t] = r.x;
+        pl.rec[4 * t + 1] = r.y;
+        pl.rec[4 * t + 2] = r.z;
+        pl.rec[4 * t + 3] = r.w;
+        if (t == 0) {
+            pl.fills_known = v != 0u;
+            pl.n_uniq = whole ? p.k : 0;
+        }
+    }
+    __syncthreads();
+    if (pl.fills_known) {   // block-uniform
+        stage_plan_dev(p, pl);
+        return;
+    }
+    if (t < p.k && pl.n_uniq > 0) {
+        const uint32_t a = pl.rec[t];
+        const int pair = static_cast<int>(a & 63u);
+        pl.plan[t] = make_int4((a >> 30) & 1u ? -1 : static_cast<int>((a >> 16) & 0x3FFFu), 0, t, 1);
+        pl.uniq[t] = static_cast<int>((a >> 6) & 0x3FFu);
+        pl.pairs[t] = pair;
+        pl.tok[t] = 0;
+        pl.w[pair] = __uint_as_float(pl.rec[REC_K + t] & ~REC_BIT);
+    }
+    __syncthreads();
 }
 
 // Whole-layer launch: the plan comes from the bookkeeping workgroup of the same
@@ -659,11 +718,10 @@ __device__ __forceinline__ void gate_up_body(const DecodeParams& p, PlanLds& pl,
                         lo[r] = __builtin_bit_cast(uint16_t, b);
                     }
                 }
-                const u32x4_t v = {hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
-                                   lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
                 uint4* dst = reinterpret_cast<uint4*>(p.h_hi) +
                              (static_cast<int64_t>(pair) * p.I + row0 + 16 * t + 4 * gq) / 4;
-                asm volatile("global_store_dwordx4 %0, %1, off sc1" :: "v"(dst), "v"(v) : "memory");
+                st_dev16(dst, hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), lo[0] | (lo[1] << 16),
+                         lo[2] | (lo[3] << 16));
             }
         }
         if (!WH && kw == 0 && n < pr.w) {
@@ -1229,8 +1287,12 @@ __global__ void __launch_bounds__(NW * WAVE, 4) layer_small_kernel(DecodeParams 
         classify_body<SPL, NW * WAVE>(cp, *reinterpret_cast<ClassifySmall*>(raw),
                                            sync_word(sync, FL_PLAN), sync_word(sync, FL_VICT));
     } else {
-        wait_plan(sync, blockIdx.x, pl);
-        stage_plan_dev(p, pl);
+        if (plan_record(cp)) {
+            wait_plan_record(sync, blockIdx.x, p, pl);
+        } else {
+            wait_plan(sync, blockIdx.x, pl);
+            stage_plan_dev(p, pl);
+        }
         // with the fills already in the staged plan, the FFN writes them the
         // plain way (gate/up from registers, down stores without a refresh)
         const bool fills = p.has_cache && p.fill_through && !pl.fills_known;

@@ -105,6 +105,17 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
     return v;
 }
 
+// 16 bytes written through to the device coherence point by two device-scope
+// 8-byte stores (compiler-visible stores, so the hazard that a store's data
+// registers must not be overwritten right after issue is handled for them).
+__device__ __forceinline__ void st_dev16(void* q, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    uint64_t* w = static_cast<uint64_t*>(q);
+    __hip_atomic_store(w, static_cast<uint64_t>(a) | static_cast<uint64_t>(b) << 32, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(w + 1, static_cast<uint64_t>(c) | static_cast<uint64_t>(d) << 32, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Minimum / maximum over the 64 lanes by DPP row shifts and row broadcasts (an
 // inclusive scan; lane 63 ends with the result), without the LDS crossbar.
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
