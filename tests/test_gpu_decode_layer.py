@@ -96,13 +96,22 @@ EXTRA = {
                   route=C.ROUTE_SIGMOID_GROUP, n_group=8, topk_group=2, route_scale=2.5,
                   wfmt=C.WFMT_MXFP4, n_layers=4, n_slots=96, t_decode=2, steps=40,
                   zipf_alpha=1.0, keep_prob=0.6),
+    # one token per call: the whole-layer launch publishes the plan as a record
+    8: C.Workload(cid=8, name="small_mxfp4_sig_t1", hidden=2048, inter=256, n_experts=64, top_k=6,
+                  route=C.ROUTE_SIGMOID_GROUP, n_group=8, topk_group=4, route_scale=2.5,
+                  wfmt=C.WFMT_MXFP4, n_layers=4, n_slots=48, t_decode=1, steps=40,
+                  zipf_alpha=1.0, keep_prob=0.6),
+    9: C.Workload(cid=9, name="small_int4_t1_split", hidden=1024, inter=256, n_experts=32, top_k=8,
+                  route=C.ROUTE_SOFTMAX_TOPK, wfmt=C.WFMT_INT4_G64, n_layers=4, n_slots=40,
+                  t_decode=1, steps=40, zipf_alpha=1.1, keep_prob=0.5, q_num=1, q_den=2),
 }
 
 
 @pytest.mark.parametrize("mode", ["fused", "split"])
 @pytest.mark.parametrize("cid,steps,sample", [(2, 64, [(0, 3), (63, 39)]), (4, 24, [(5, 7)]),
                                               (5, 24, [(23, 0)]), (6, 40, [(0, 1), (39, 3)]),
-                                              (7, 40, [(1, 0), (39, 2)])])
+                                              (7, 40, [(1, 0), (39, 2)]), (8, 40, [(0, 2), (39, 1)]),
+                                              (9, 40, [(0, 0), (39, 3)])])
 def test_decode_layer_trace(cid, steps, sample, mode):
     import torch
     from workloads import gpu as wg
