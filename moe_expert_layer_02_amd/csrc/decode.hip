@@ -337,6 +337,34 @@ __device__ __forceinline__ void mma_slab(const WSlab<RT>& w, const uint4 b[4], i
     }
 }
 
+// acc[t] += W_slab(row tile t) . (Bh + Bl): the hi and lo halves of the B
+// operand against weights dequantised once.
+template <int FMT, int RT>
+__device__ __forceinline__ void mma_slab2(const WSlab<RT>& w, const uint4 bh[4], const uint4 bl[4],
+                                          int gq, f32x4 acc[RT]) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const uint32_t d4[4] = {w.q[t].x, w.q[t].y, w.q[t].z, w.q[t].w};
+        if (FMT == MOE355_W_INT4_G64) {
+            const half2_t s2 = int4_scale(w.sc[t], gq);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint4 a = a_int4(d4[j], s2);
+                acc[t] = mma<FMT>(a, bh[j], acc[t]);
+                acc[t] = mma<FMT>(a, bl[j], acc[t]);
+            }
+        } else {
+            const float scale = e8m0_to_f32((w.sc[t] >> (8 * gq)) & 0xFFu);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint4 a = a_fp4(d4[j], scale);
+                acc[t] = mma<FMT>(a, bh[j], acc[t]);
+                acc[t] = mma<FMT>(a, bl[j], acc[t]);
+            }
+        }
+    }
+}
+
 // Synchronisation words, 256 bytes apart (so that no two share a cache line),
 // in the first SYNC_BYTES of the decode workspace; zero before a call and left
 // zero by it.  Word w sits at byte 256 w:
@@ -881,8 +909,7 @@ __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
         for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     };
     auto compute = [&](const DnStage<FMT, RT>& st, int item, int tg, int s) {
-        mma_slab<FMT, RT>(st.w, st.hh, gq, acc);
-        mma_slab<FMT, RT>(st.w, st.hl, gq, acc);
+        mma_slab2<FMT, RT>(st.w, st.hh, st.hl, gq, acc);
         if (FMT == MOE355_W_INT4_G64) {
             float part = 0.0f;
 #pragma unroll
@@ -951,6 +978,184 @@ __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
                 if (cc.s == NS - 1) epilogue(cc.item, cc.tg);
                 advance(cc);
                 done = !cc.valid;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// down + combine with h in LDS (many distinct experts, e.g. the DS-like decode).
+// A block of NW wavefronts takes items (distinct expert u, token group tg of up
+// to 16 of its pairs, NW * 32 consecutive output rows); wavefront w computes
+// rows r0 + 32 w (two 16-row tiles) over all of I.  The block keeps the h rows
+// (hi and lo halves) of a window of consecutive pair positions in LDS, staged
+// before the first item and again only when an item's pairs leave the window
+// (the positions of consecutive items rise), so a wavefront's register ring
+// holds weights alone and runs D - 1 slabs ahead.  (With h in the ring, each
+// stage also held 32 registers of h and two stages ahead filled the register
+// budget at two wavefronts per SIMD: half the bytes in flight of gate/up.)
+constexpr int DNL_LDS = 135168;   // bytes of staged h: 16 rows of I = 2048 with padding
+constexpr int DNL_NW = 8;         // wavefronts per block (one block per CU)
+
+template <int FMT, int D>
+__global__ void __launch_bounds__(DNL_NW * WAVE) down_lds_kernel(DecodeParams p) {
+    constexpr int NW = DNL_NW;
+    __shared__ PlanLds pl;
+    __shared__ int32_t tgb[MAX_PLAN + 1];   // item base of each distinct expert, in token groups
+    __shared__ int32_t win[2];              // staged pair positions [win[0], win[1])
+    __shared__ uint4 hsm[DNL_LDS / 16];
+    stage_plan(p, pl);
+    const int lane = threadIdx.x & (WAVE - 1), ln = lane & 15, gq = lane >> 4;
+    const int wv = threadIdx.x / WAVE;
+    const int I = p.I, NS = I / SLAB, CH = p.H / (NW * 32);
+    // row r of the window: hi halves (I / 8 uint4), lo halves, one uint4 of padding
+    // (consecutive rows then start 4 banks apart, so 16 token rows do not collide)
+    const int RSq = I / 4 + 1;
+    const int nwin = min(DNL_LDS / 16 / RSq, 64);
+    const int nu = pl.n_uniq;
+    if (nu <= 0) return;
+    if (threadIdx.x == 0) {
+        int acc = 0;
+        for (int u = 0; u < nu; ++u) {
+            tgb[u] = acc;
+            acc += max(1, (pl.plan[u].w + TOK - 1) / TOK);
+        }
+        tgb[nu] = acc;
+    }
+    __syncthreads();
+    const int n_items = tgb[nu] * CH;
+    const int per = (n_items + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x);
+    const int i_beg = static_cast<int>(blockIdx.x) * per, i_end = min(n_items, i_beg + per);
+    if (i_beg >= i_end) return;   // block-uniform
+    const int n_pos = pl.plan[nu - 1].z + pl.plan[nu - 1].w;   // pair positions in use
+
+    // cursor over (item, slab); an item past the block's end re-reads its last one
+    struct Cur {
+        int it, s, u, tg, c;
+    };
+    auto set_item = [&](Cur& k, int it) {
+        k.it = it;
+        k.s = 0;
+        const int q = min(it, i_end - 1) / CH;
+        k.c = min(it, i_end - 1) - q * CH;
+        int lo = 0, hi = nu - 1;   // the last u with tgb[u] <= q
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tgb[mid] <= q) lo = mid;
+            else hi = mid - 1;
+        }
+        k.u = lo;
+        k.tg = q - tgb[lo];
+    };
+    auto adv = [&](Cur& k) {
+        if (++k.s == NS) set_item(k, k.it + 1);
+    };
+    // the window from pair position p0 on (all threads; ends with a barrier)
+    auto stage_h = [&](int p0) {
+        const int nr = min(nwin, n_pos - p0);
+        const int rq = I / 4;   // uint4 of h per row
+        for (int i = threadIdx.x; i < nr * rq; i += NW * WAVE) {
+            const int r = i / rq, c = i - r * rq;
+            const int64_t pair = pl.pairs[p0 + r];
+            const uint4* src = c < I / 8 ? reinterpret_cast<const uint4*>(p.h_hi + pair * I) + c
+                                         : reinterpret_cast<const uint4*>(p.h_lo + pair * I) + (c - I / 8);
+            hsm[r * RSq + c] = *src;
+        }
+        if (threadIdx.x == 0) {
+            win[0] = p0;
+            win[1] = p0 + nr;
+        }
+        __syncthreads();
+    };
+    auto group_of = [&](const Cur& k, int& a, int& nt) {
+        const int4 pr = pl.plan[k.u];
+        a = pr.z + TOK * k.tg;
+        nt = min(TOK, pr.w - TOK * k.tg);
+    };
+
+    f32x4 acc[2];
+    acc[0] = acc[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    auto load_stage = [&](WSlab<2>& w, const Cur& k) {
+        const ExpertRef ref = expert_ref(p, pl, k.u);
+        load_wslab<FMT, 2>(p, ref.src, 2, k.c * (NW * 32) + 32 * wv, I, k.s * SLAB, ln, gq, w);
+    };
+    auto compute = [&](const WSlab<2>& w, const Cur& k) {
+        int a, nt;
+        group_of(k, a, nt);
+        uint4 hh[4], hl[4];
+        if (ln < nt) {
+            const uint4* row = hsm + (a + ln - win[0]) * RSq + k.s * (SLAB / 8) + 4 * gq;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                hh[i] = row[i];
+                hl[i] = row[I / 8 + i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hh[i] = hl[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        mma_slab2<FMT, 2>(w, hh, hl, gq, acc);
+        if (FMT == MOE355_W_INT4_G64) {
+            float part = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part = sum_f16x8(hl[i], sum_f16x8(hh[i], part));
+            const uint4 bb = bias_b_operand(part, gq);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) acc[t] = mma<FMT>(bias_a_operand(w.bi[t], w.sc[t], gq), bb, acc[t]);
+        }
+        if (k.tg == 0) {   // fill-through of the expert's down bytes
+            const ExpertRef ref = expert_ref(p, pl, k.u);
+            if (ref.dst) store_wslab<FMT, 2>(p, ref.dst, 2, k.c * (NW * 32) + 32 * wv, I, k.s * SLAB, ln, gq, w);
+        }
+    };
+    auto epilogue = [&](const Cur& k) {
+        int a, nt;
+        group_of(k, a, nt);
+        if (ln < nt) {
+            const int pair = pl.pairs[a + ln];
+            const float wt = pl.w[pair];
+            float* o = p.out + static_cast<int64_t>(pl.tok[a + ln]) * p.H + k.c * (NW * 32) + 32 * wv;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) unsafeAtomicAdd(o + 16 * t + 4 * gq + r, wt * acc[t][r]);
+        }
+        acc[0] = acc[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    };
+
+    Cur lc, cc;
+    set_item(lc, i_beg);
+    cc = lc;
+    {
+        int a, nt;
+        group_of(cc, a, nt);
+        stage_h(a);
+    }
+    WSlab<2> ring[D];
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) {
+        load_stage(ring[d], lc);
+        adv(lc);
+    }
+    bool done = false;
+    while (!done) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            load_stage(ring[(d + D - 1) % D], lc);
+            adv(lc);
+            if (!done) {
+                if (cc.s == 0) {   // block-uniform: every wavefront walks the same items
+                    int a, nt;
+                    group_of(cc, a, nt);
+                    if (a < win[0] || a + nt > win[1]) {
+                        __syncthreads();   // every wavefront is done with the old window
+                        stage_h(a);
+                    }
+                }
+                compute(ring[d], cc);
+                if (cc.s == NS - 1) epilogue(cc);
+                adv(cc);
+                done = cc.it >= i_end;
             }
         }
     }
@@ -1357,7 +1562,11 @@ moe355_status launch_decode(const DecodeParams& p, int max_uniq, uint32_t* sync,
     const int slots = cus * 8;   // eight resident wavefronts per CU
     const int items2 = max_uniq * (p.H / 32);
     const int items1 = max_uniq * (p.H / 16);
-    if (items2 >= 2 * slots) {
+    if (items2 >= 2 * slots && p.H % (DNL_NW * 32) == 0 && 16 * (p.I / 4 + 1) * 16 <= DNL_LDS) {
+        // many distinct experts: h in LDS, one block per CU (a window holds a
+        // full token group of any expert)
+        down_lds_kernel<FMT, 8><<<cus, DNL_NW * WAVE, 0, stream>>>(p);
+    } else if (items2 >= 2 * slots) {
         const int waves = items2 < slots ? items2 : slots;
         down_kernel<FMT, 2, 3, 1, false><<<(waves + 3) / 4, 256, 0, stream>>>(p);
     } else if (items1 <= cus * 4 && p.I >= 256 && p.I <= 1024) {
