@@ -160,6 +160,25 @@ def test_decode_largest_pair_count():
     check_close(got, _oracle_layer(w, x_bits, ids, wt), "T*k=256")
 
 
+@pytest.mark.parametrize("wfmt", [C.WFMT_MXFP4, C.WFMT_INT4_G64])
+def test_decode_many_experts_window_restage(wfmt):
+    """Many distinct experts (the h-in-LDS down pass): expert 0 takes all 32 tokens
+    (two token groups of 16) and 224 other experts one pair each, so a block's
+    items run past the 16-row h window and it restages; two tokens checked."""
+    w = C.Workload(cid=122 + wfmt, name="window", hidden=4096, inter=2048, n_experts=256,
+                   top_k=8, route=0, wfmt=wfmt)
+    T = 32
+    rng = np.random.default_rng(5 + wfmt)
+    x_bits = tr.bf16_normal(rng, (T, w.hidden))
+    others = rng.permutation(np.arange(1, 256))[:T * 7].reshape(T, 7)
+    ids = np.concatenate([np.zeros((T, 1), dtype=np.int64), others], axis=1).astype(np.int32)
+    wt = (0.05 + rng.random((T, 8))).astype(np.float32)
+    got = _decode_whole_layer(w, x_bits, ids, wt)
+    toks = [0, T - 1]
+    want = _oracle_layer(w, x_bits, ids, wt, tokens=toks)
+    check_close(got[toks], want, f"many experts, window restage (fmt {wfmt})")
+
+
 def test_decode_empty_batch_is_noop():
     import torch
     import moe_expert_layer_02_amd as m
