@@ -461,13 +461,22 @@ __device__ __forceinline__ void wait_plan(uint32_t* sync, uint32_t b, PlanLds& p
     __syncthreads();
 }
 
-__device__ __forceinline__ void block_exit(uint32_t* sync) {
-    __syncthreads();
+// The exit count in two halves.  exit_begin, once every thread of the block is
+// past its last wait: thread 0 adds the block to its group's count (a down block
+// calls it right after its last wait, so the round trip overlaps its products).
+// exit_end: the block that completed its group adds the group to the top count,
+// and the block that completes that clears every word.
+__device__ __forceinline__ uint32_t exit_begin(uint32_t* sync) {
+    uint32_t old = 0;
+    if (threadIdx.x == 0) old = atomic_add_dev(sync_word(sync, SW_EXIT + (blockIdx.x & 7)), 1u);
+    return old;
+}
+__device__ __forceinline__ void exit_end(uint32_t* sync, uint32_t old) {
     if (threadIdx.x < WAVE) {
         uint32_t last = 0;
         if (threadIdx.x == 0) {
             const uint32_t nblk = gridDim.x, g = blockIdx.x & 7;
-            if (atomic_add_dev(sync_word(sync, SW_EXIT + g), 1u) == group_size(nblk, g) - 1) {
+            if (old == group_size(nblk, g) - 1) {
                 store_dev(sync_word(sync, SW_EXIT + g), 0u);   // the whole group has exited
                 const uint32_t groups = nblk < 8 ? nblk : 8;
                 last = atomic_add_dev(sync_word(sync, SW_EXIT_TOP), 1u) == groups - 1;
@@ -487,6 +496,10 @@ __device__ __forceinline__ void block_exit(uint32_t* sync) {
             }
         }
     }
+}
+__device__ __forceinline__ void block_exit(uint32_t* sync) {
+    __syncthreads();
+    exit_end(sync, exit_begin(sync));
 }
 
 // 16 bytes by two device-scope 8-byte loads.
@@ -1213,7 +1226,7 @@ template <int FMT, int NW>
 __device__ __forceinline__ void down_rows_body(const DecodeParams& p, PlanLds& pl,
                                                uint4* hs, f32x4 (&red)[NW][WAVE], int r0,
                                                int half, uint32_t* sync, uint32_t n_gu,
-                                               bool layer_fills = false) {
+                                               bool layer_fills, uint32_t& exit_old) {
     const int lane = threadIdx.x & (WAVE - 1), ln = lane & 15, gq = lane >> 4;
     const int wv = threadIdx.x / WAVE;
     const int I = p.I, nsl = I / SLAB;
@@ -1275,6 +1288,7 @@ __device__ __forceinline__ void down_rows_body(const DecodeParams& p, PlanLds& p
         }
     }
     wait_flag(sync, FL_DONE, blockIdx.x);
+    exit_old = exit_begin(sync);   // no sync word is read after this wait
     // h pieces: [pair][I / 4] x 16 bytes (four hi halves, then four lo halves)
     const int nc = p.T * p.k * I / 4;
     {   // stage every pair's h in LDS: at most four pieces per thread
@@ -1366,9 +1380,12 @@ __global__ void __launch_bounds__(NW * WAVE, 4) ffn_small_kernel(DecodeParams p,
         signal_done(sync, n_gu, blockIdx.x);
     } else {
         const int b = blockIdx.x - n_gu;   // two blocks per 16-row tile
+        uint32_t old;
         down_rows_body<FMT, NW>(p, pl, raw,
                                 *reinterpret_cast<f32x4 (*)[NW][WAVE]>(raw + SMALL_H_LDS / 16),
-                                (b >> 1) * 16, b & 1, sync, n_gu);
+                                (b >> 1) * 16, b & 1, sync, n_gu, false, old);
+        exit_end(sync, old);
+        return;
     }
     block_exit(sync);
 }
@@ -1515,9 +1532,12 @@ __global__ void __launch_bounds__(NW * WAVE, 4) layer_small_kernel(DecodeParams 
             if (fills) copy_gate_up_fills<FMT>(p, pl, sync, b, n_gu);
         } else {
             const int c = b - n_gu;   // two blocks per 16-row tile
+            uint32_t old;
             down_rows_body<FMT, NW>(p, pl, raw,
                                     *reinterpret_cast<f32x4 (*)[NW][WAVE]>(raw + SMALL_H_LDS / 16),
-                                    (c >> 1) * 16, c & 1, sync, n_gu, fills);
+                                    (c >> 1) * 16, c & 1, sync, n_gu, fills, old);
+            exit_end(sync, old);
+            return;
         }
     }
     block_exit(sync);
