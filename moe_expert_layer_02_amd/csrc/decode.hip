@@ -461,27 +461,33 @@ __device__ __forceinline__ void wait_plan(uint32_t* sync, uint32_t b, PlanLds& p
     __syncthreads();
 }
 
-// The exit count in two halves.  exit_begin, once every thread of the block is
-// past its last wait: thread 0 adds the block to its group's count (a down block
-// calls it right after its last wait, so the round trip overlaps its products).
-// exit_end: the block that completed its group adds the group to the top count,
-// and the block that completes that clears every word.
+// The exit count in three steps.  exit_begin, once every thread of the block is
+// past its last wait: thread 0 adds the block to its group's count.  exit_mid,
+// once that count's old value has come back: the block that completed its
+// group adds the group to the top count.  exit_final: the block that completed
+// the top count clears every word.  A down block runs the first two in the
+// middle of its work (right after its last wait and after staging h), so the
+// round trips overlap its products.
 __device__ __forceinline__ uint32_t exit_begin(uint32_t* sync) {
     uint32_t old = 0;
     if (threadIdx.x == 0) old = atomic_add_dev(sync_word(sync, SW_EXIT + (blockIdx.x & 7)), 1u);
     return old;
 }
-__device__ __forceinline__ void exit_end(uint32_t* sync, uint32_t old) {
-    if (threadIdx.x < WAVE) {
-        uint32_t last = 0;
-        if (threadIdx.x == 0) {
-            const uint32_t nblk = gridDim.x, g = blockIdx.x & 7;
-            if (old == group_size(nblk, g) - 1) {
-                store_dev(sync_word(sync, SW_EXIT + g), 0u);   // the whole group has exited
-                const uint32_t groups = nblk < 8 ? nblk : 8;
-                last = atomic_add_dev(sync_word(sync, SW_EXIT_TOP), 1u) == groups - 1;
-            }
+__device__ __forceinline__ uint32_t exit_mid(uint32_t* sync, uint32_t old) {
+    uint32_t top = ~0u;
+    if (threadIdx.x == 0) {
+        const uint32_t g = blockIdx.x & 7;
+        if (old == group_size(gridDim.x, g) - 1) {
+            store_dev(sync_word(sync, SW_EXIT + g), 0u);   // the whole group has exited
+            top = atomic_add_dev(sync_word(sync, SW_EXIT_TOP), 1u);
         }
+    }
+    return top;
+}
+__device__ __forceinline__ void exit_final(uint32_t* sync, uint32_t top) {
+    if (threadIdx.x < WAVE) {
+        const uint32_t groups = gridDim.x < 8 ? gridDim.x : 8;
+        const uint32_t last = threadIdx.x == 0 && top == groups - 1;
         if (__shfl(last, 0, WAVE)) {   // every block is past its waits: clear the rest
             const int l = threadIdx.x;
             store_dev(sync_word(sync, FL_DONE + l), 0u);
@@ -499,7 +505,7 @@ __device__ __forceinline__ void exit_end(uint32_t* sync, uint32_t old) {
 }
 __device__ __forceinline__ void block_exit(uint32_t* sync) {
     __syncthreads();
-    exit_end(sync, exit_begin(sync));
+    exit_final(sync, exit_mid(sync, exit_begin(sync)));
 }
 
 // 16 bytes by two device-scope 8-byte loads.
@@ -1226,7 +1232,7 @@ template <int FMT, int NW>
 __device__ __forceinline__ void down_rows_body(const DecodeParams& p, PlanLds& pl,
                                                uint4* hs, f32x4 (&red)[NW][WAVE], int r0,
                                                int half, uint32_t* sync, uint32_t n_gu,
-                                               bool layer_fills, uint32_t& exit_old) {
+                                               bool layer_fills, uint32_t& exit_top) {
     const int lane = threadIdx.x & (WAVE - 1), ln = lane & 15, gq = lane >> 4;
     const int wv = threadIdx.x / WAVE;
     const int I = p.I, nsl = I / SLAB;
@@ -1288,7 +1294,7 @@ __device__ __forceinline__ void down_rows_body(const DecodeParams& p, PlanLds& p
         }
     }
     wait_flag(sync, FL_DONE, blockIdx.x);
-    exit_old = exit_begin(sync);   // no sync word is read after this wait
+    const uint32_t exit_old = exit_begin(sync);   // no sync word is read after this wait
     // h pieces: [pair][I / 4] x 16 bytes (four hi halves, then four lo halves)
     const int nc = p.T * p.k * I / 4;
     {   // stage every pair's h in LDS: at most four pieces per thread
@@ -1306,6 +1312,7 @@ __device__ __forceinline__ void down_rows_body(const DecodeParams& p, PlanLds& p
         if (t0 + 3 * NT < nc) hs[t0 + 3 * NT] = a3;
         __syncthreads();
     }
+    exit_top = exit_mid(sync, exit_old);
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f}, acc_lo = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < SMALL_DB; ++i) {
@@ -1384,7 +1391,7 @@ __global__ void __launch_bounds__(NW * WAVE, 4) ffn_small_kernel(DecodeParams p,
         down_rows_body<FMT, NW>(p, pl, raw,
                                 *reinterpret_cast<f32x4 (*)[NW][WAVE]>(raw + SMALL_H_LDS / 16),
                                 (b >> 1) * 16, b & 1, sync, n_gu, false, old);
-        exit_end(sync, old);
+        exit_final(sync, old);
         return;
     }
     block_exit(sync);
@@ -1536,7 +1543,7 @@ __global__ void __launch_bounds__(NW * WAVE, 4) layer_small_kernel(DecodeParams 
             down_rows_body<FMT, NW>(p, pl, raw,
                                     *reinterpret_cast<f32x4 (*)[NW][WAVE]>(raw + SMALL_H_LDS / 16),
                                     (c >> 1) * 16, c & 1, sync, n_gu, fills, old);
-            exit_end(sync, old);
+            exit_final(sync, old);
             return;
         }
     }
