@@ -521,13 +521,32 @@ __device__ __forceinline__ int32_t ld_dev32(const int32_t* q) {
     return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Whole-layer launch: the plan comes from the bookkeeping workgroup of the same
+// launch, so it is read with device-scope loads once its flag is up.
+__device__ __forceinline__ void stage_plan_dev(const DecodeParams& p, PlanLds& pl) {
+    const int t = threadIdx.x;
+    if (t < p.n_plan) {
+        const uint4 r = ld_dev16(p.plan + 4 * t);
+        pl.plan[t] = make_int4(static_cast<int>(r.x), static_cast<int>(r.y), static_cast<int>(r.z),
+                               static_cast<int>(r.w));
+        pl.uniq[t] = ld_dev32(p.uniq + t);
+    }
+    if (t < p.T * p.k) {
+        const int32_t pr = ld_dev32(p.pairs + t);
+        pl.pairs[t] = pr;
+        pl.tok[t] = pr / p.k;
+        pl.w[t] = __int_as_float(ld_dev32(reinterpret_cast<const int32_t*>(p.w) + t));
+    }
+    if (t == 0) pl.n_uniq = ld_dev32(p.counts);
+    __syncthreads();
+}
+
 // Whole-layer launch, one-token plan record: until every word of copy b % 64 of
 // the plan flag carries REC_BIT (lanes 0..3 poll 16 bytes each); the record
 // then fills the staged plan (pair u of expert u, token 0).  The record is the
 // first plan and never names the fills: a block that finds the victims flag
 // already up (a block that starts late) stages the final plan from memory
 // instead.  A wait that gives up stages no experts.
-__device__ __forceinline__ void stage_plan_dev(const DecodeParams& p, PlanLds& pl);
 __device__ __forceinline__ void wait_plan_record(uint32_t* sync, uint32_t b, const DecodeParams& p,
                                                  PlanLds& pl) {
     const int t = threadIdx.x;
@@ -574,26 +593,6 @@ __device__ __forceinline__ void wait_plan_record(uint32_t* sync, uint32_t b, con
         pl.tok[t] = 0;
         pl.w[pair] = __uint_as_float(pl.rec[REC_K + t] & ~REC_BIT);
     }
-    __syncthreads();
-}
-
-// Whole-layer launch: the plan comes from the bookkeeping workgroup of the same
-// launch, so it is read with device-scope loads once its flag is up.
-__device__ __forceinline__ void stage_plan_dev(const DecodeParams& p, PlanLds& pl) {
-    const int t = threadIdx.x;
-    if (t < p.n_plan) {
-        const uint4 r = ld_dev16(p.plan + 4 * t);
-        pl.plan[t] = make_int4(static_cast<int>(r.x), static_cast<int>(r.y), static_cast<int>(r.z),
-                               static_cast<int>(r.w));
-        pl.uniq[t] = ld_dev32(p.uniq + t);
-    }
-    if (t < p.T * p.k) {
-        const int32_t pr = ld_dev32(p.pairs + t);
-        pl.pairs[t] = pr;
-        pl.tok[t] = pr / p.k;
-        pl.w[t] = __int_as_float(ld_dev32(reinterpret_cast<const int32_t*>(p.w) + t));
-    }
-    if (t == 0) pl.n_uniq = ld_dev32(p.counts);
     __syncthreads();
 }
 
