@@ -155,6 +155,40 @@ def test_decode_layer_trace(cid, steps, sample, mode):
     say(f"{w.name}: {steps * w.n_layers} calls bit-exact, {len(occ)} slots hold their pool bytes")
 
 
+def test_decode_layer_workspace_header_left_zero():
+    """Whole-layer calls of two shapes share one workspace, steps alternating: a
+    one-token call (its plan travels as a 64-byte record in every plan-flag
+    copy) and a three-token call (plain flags).  After every step the first
+    65536 bytes, error word included, are zero again, and the outputs match
+    the oracle on sampled calls."""
+    import torch
+    from workloads import gpu as wg
+    ws_ = None
+    runs = []
+    for cid in (9, 6):
+        w = EXTRA[cid]
+        run = LayerRunner(w, w.n_slots, wg.make_pool(w, pack=packer(desc_of(w))), "fused")
+        ws_ = run.ws if ws_ is None or run.ws.numel() > ws_.numel() else ws_
+        runs.append((w, run, tr.DecodeTrace(w, 6), BlobSource(w)))
+    for _, run, _, _ in runs:
+        run.ws = ws_
+    for s in range(6):
+        for w, run, trace, src in runs:
+            xs = _xs(w, s)
+            run.stage(s, trace.logits[s], xs)
+            run.step()
+            torch.cuda.synchronize()
+            assert int(ws_[:65536].count_nonzero()) == 0, (w.name, s)
+            if s in (0, 5):
+                l = s % w.n_layers
+                rid, rw = oroute.route(trace.logits[s, l], w.top_k, w.route, w.n_group,
+                                       w.topk_group, w.route_scale)
+                want = offn.moe_layer(tr.x_as_f32(tr.decode_x(w, s, l)), rid, rw,
+                                      lambda e: src(l, e), w.wfmt, w.hidden, w.inter)
+                check_close(run.out[l].cpu().numpy(), want, f"{w.name} shared workspace ({s},{l})")
+    say("workspace header zero after every step, two shapes sharing it")
+
+
 @pytest.mark.parametrize("mode", ["fused", "split"])
 def test_decode_step_graph_replay_matches_eager(mode):
     import torch
