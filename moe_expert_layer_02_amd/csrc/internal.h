@@ -137,6 +137,23 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return __builtin_amdgcn_readlane(v, 63);
 }
 
+// Sum over the 64 lanes by DPP row shifts and row broadcasts (an inclusive
+// scan; lane 63 ends with the total), without the LDS crossbar.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                                 ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum_dpp_f32(float v) {
+    v += dpp_f32<0x111, 0xf>(v);   // row_shr:1
+    v += dpp_f32<0x112, 0xf>(v);   // row_shr:2
+    v += dpp_f32<0x114, 0xf>(v);   // row_shr:4
+    v += dpp_f32<0x118, 0xf>(v);   // row_shr:8
+    v += dpp_f32<0x142, 0xa>(v);   // row_bcast:15
+    v += dpp_f32<0x143, 0xc>(v);   // row_bcast:31
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 // Sum over aligned segments of `width` lanes (width a power of two <= 64).
 __device__ __forceinline__ float segment_sum_f32(float v, int width) {
     for (int m = width >> 1; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);

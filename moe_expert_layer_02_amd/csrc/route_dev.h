@@ -121,7 +121,7 @@ __device__ __forceinline__ int route_token_n(const float* __restrict__ lg, int E
 
     if (kind == MOE355_ROUTE_SOFTMAX_TOPK) {
         const float p = lane < k ? expf(my_v - vmax) : 0.0f;
-        const float sum = wave_sum_f32(p);
+        const float sum = wave_sum_dpp_f32(p);
         *w_out = p / sum;
     } else {
         const double s = lane < k ? 1.0 / (1.0 + exp(-static_cast<double>(my_v))) : 0.0;
