@@ -274,8 +274,10 @@ moe355_status moe355_permute(const moe355_layer_desc* d, const int32_t* topk_ids
  * moe355_dedup) are required.
  * Kernels: a small call (T <= 16, H in {1024, 2048, 4096}, distinct experts x
  * I/16 <= the device's compute units, T*k*I*4 <= 32 KiB) runs as one launch in
- * which the down blocks wait for the gate/up blocks and each owns 16 output
- * rows of all experts (plain stores, a fixed summation order).  Otherwise two
+ * which the down blocks wait for the gate/up blocks and each pair of them owns
+ * 16 output rows of all experts (two fp32 additions per element onto zero,
+ * which give the same sum in either order: the output is deterministic).
+ * Otherwise two
  * kernels: gate/up (which also zeroes out), then down with the combine as fp32
  * atomic additions, so the order of a token's k additions is not fixed.
  * Limits: T*k <= 256; H and I in {128, 256, 512, 1024, 2048, 4096}.

@@ -375,7 +375,9 @@ __device__ __forceinline__ void mma_slab2(const WSlab<RT>& w, const uint4 bh[4],
 //            every word
 //   18       error word, sticky: bit 0 = a bounded wait gave up
 //   32..95   flag "all gate/up blocks done", one copy per line
-//   96..159  whole-layer launch: flag "plan published", one copy per line
+//   96..159  whole-layer launch: flag "plan published", one copy per line (a
+//            one-token call writes the whole plan as a 16-word record in each
+//            copy, see plan_record)
 //   160..223 whole-layer launch: flag "fills' victim slots published"
 // Counting in groups keeps each counter to about 1/8 of the blocks, and a flag
 // is raised in 64 copies (one store by each lane of a wavefront) of which a
@@ -1494,11 +1496,13 @@ __device__ __forceinline__ void copy_gate_up_fills(const DecodeParams& p, PlanLd
 // publishes the plan as soon as hits and misses are known; the other
 // workgroups are the small-call FFN's gate/up and down blocks, which wait for
 // that plan, stage it, and start streaming weights while workgroup 0 is still
-// picking victims.  A block that reads a missed expert also waits for the
-// fills' victim slots before its fill-through stores.  Waits point only at
-// lower workgroup indices (workgroup 0 first), as in the FFN alone.  (A
-// Qwen-like call is 513 workgroups at two per CU: the last down block starts
-// when workgroup 0 is done, about when the others start waiting for h.)
+// picking victims (a one-token call's plan travels as a record in the flag
+// itself).  A block that reads a missed expert also waits for the fills'
+// victim slots before its fill-through stores (a down block before loading its
+// weights).  Waits point only at lower workgroup indices (workgroup 0 first),
+// as in the FFN alone.  (A Qwen-like call is 513 workgroups at two per CU: the
+// last one starts when another exits, after the victims are out, and stages
+// the final plan.)
 using ClassifySmall = ClassifySharedT<2048, 2048, 256, 128>;
 
 template <int FMT, int NW, int D, int SPL>
