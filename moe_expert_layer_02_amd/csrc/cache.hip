@@ -147,6 +147,26 @@ __global__ void __launch_bounds__(CL_THREADS) classify_kernel(ClassifyParams cp)
 
 namespace {
 
+// Copy 16-byte units [b, e) of src to dst by a 256-thread block: eight loads in
+// flight per thread, then non-temporal stores (the copied bytes are not read
+// again by this launch).
+__device__ __forceinline__ void copy_units(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                           int64_t b, int64_t e) {
+    typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+    constexpr int U = 8;
+    for (int64_t base = b + threadIdx.x; base < e; base += 256 * U) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (base + 256 * u < e) v[u] = src[base + 256 * u];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (base + 256 * u < e)
+                __builtin_nontemporal_store(u32x4v{v[u].x, v[u].y, v[u].z, v[u].w},
+                                            reinterpret_cast<u32x4v*>(dst + base + 256 * u));
+    }
+}
+
 // Copy the filled experts' bytes from the pool into their slots.
 __global__ void __launch_bounds__(256)
 fill_kernel(const uint8_t* __restrict__ pool, uint8_t* __restrict__ slots, int64_t S, int E,
@@ -158,9 +178,8 @@ fill_kernel(const uint8_t* __restrict__ pool, uint8_t* __restrict__ slots, int64
     const int64_t dst_off = static_cast<int64_t>(fill_s[i]) * S;
     const int64_t beg = static_cast<int64_t>(blockIdx.x) * chunk;
     const int64_t end = beg + chunk < S ? beg + chunk : S;
-    const uint4* src = reinterpret_cast<const uint4*>(pool + src_off);
-    uint4* dst = reinterpret_cast<uint4*>(slots + dst_off);
-    for (int64_t o = beg / 16 + threadIdx.x; o < end / 16; o += blockDim.x) dst[o] = src[o];
+    copy_units(reinterpret_cast<const uint4*>(pool + src_off), reinterpret_cast<uint4*>(slots + dst_off),
+               beg / 16, end / 16);
 }
 
 struct RebuildShared {
@@ -244,9 +263,8 @@ rebuild_copy_kernel(const int32_t* __restrict__ f_table, int table_len, int f_n,
     if (s_old < 0 || s_old >= f_n) return;
     const int64_t beg = static_cast<int64_t>(blockIdx.x) * chunk;
     const int64_t end = beg + chunk < S ? beg + chunk : S;
-    const uint4* src = reinterpret_cast<const uint4*>(f_data + static_cast<int64_t>(s_old) * S);
-    uint4* dst = reinterpret_cast<uint4*>(t_data + static_cast<int64_t>(n) * S);
-    for (int64_t o = beg / 16 + threadIdx.x; o < end / 16; o += blockDim.x) dst[o] = src[o];
+    copy_units(reinterpret_cast<const uint4*>(f_data + static_cast<int64_t>(s_old) * S),
+               reinterpret_cast<uint4*>(t_data + static_cast<int64_t>(n) * S), beg / 16, end / 16);
 }
 
 constexpr int64_t COPY_CHUNK = 64 * 1024;
