@@ -294,7 +294,7 @@ def ffn_kernel_label(w, T):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     u = min(T * w.top_k, w.n_experts)
     # the library's rule for the down pass with h in LDS (many distinct experts)
-    if (u * (w.hidden // 32) >= 2 * cus * 8 and w.hidden % 256 == 0
+    if (u * (w.hidden // 32) >= 2 * cus * 8 and w.hidden % 512 == 0
             and 16 * (w.inter // 4 + 1) * 16 <= 135168):
         return "expert_ffn_decode: gate_up_kernel + down_lds_kernel (one call, two launches)"
     return "expert_ffn_decode: gate_up_kernel + down_kernel (one call, two launches)"

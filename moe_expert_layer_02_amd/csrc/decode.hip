@@ -1010,8 +1010,8 @@ __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // down + combine with h in LDS (many distinct experts, e.g. the DS-like decode).
 // A block of NW wavefronts takes items (distinct expert u, token group tg of up
-// to 16 of its pairs, NW * 32 consecutive output rows); wavefront w computes
-// rows r0 + 32 w (two 16-row tiles) over all of I.  The block keeps the h rows
+// to 16 of its pairs, NW * 16 RT consecutive output rows); wavefront w computes
+// rows r0 + 16 RT w (RT 16-row tiles) over all of I.  The block keeps the h rows
 // (hi and lo halves) of a window of consecutive pair positions in LDS, staged
 // before the first item and again only when an item's pairs leave the window
 // (the positions of consecutive items rise), so a wavefront's register ring
@@ -1021,7 +1021,7 @@ __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
 constexpr int DNL_LDS = 135168;   // bytes of staged h: 16 rows of I = 2048 with padding
 constexpr int DNL_NW = 8;         // wavefronts per block (one block per CU)
 
-template <int FMT, int D>
+template <int FMT, int RT, int D>
 __global__ void __launch_bounds__(DNL_NW * WAVE) down_lds_kernel(DecodeParams p) {
     constexpr int NW = DNL_NW;
     __shared__ PlanLds pl;
@@ -1031,7 +1031,8 @@ __global__ void __launch_bounds__(DNL_NW * WAVE) down_lds_kernel(DecodeParams p)
     stage_plan(p, pl);
     const int lane = threadIdx.x & (WAVE - 1), ln = lane & 15, gq = lane >> 4;
     const int wv = threadIdx.x / WAVE;
-    const int I = p.I, NS = I / SLAB, CH = p.H / (NW * 32);
+    constexpr int WR = 16 * RT;   // output rows per wavefront
+    const int I = p.I, NS = I / SLAB, CH = p.H / (NW * WR);
     // row r of the window: hi halves (I / 8 uint4), lo halves, one uint4 of padding
     // (consecutive rows then start 4 banks apart, so 16 token rows do not collide)
     const int RSq = I / 4 + 1;
@@ -1097,13 +1098,14 @@ __global__ void __launch_bounds__(DNL_NW * WAVE) down_lds_kernel(DecodeParams p)
         nt = min(TOK, pr.w - TOK * k.tg);
     };
 
-    f32x4 acc[2];
-    acc[0] = acc[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    auto load_stage = [&](WSlab<2>& w, const Cur& k) {
+    f32x4 acc[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    auto load_stage = [&](WSlab<RT>& w, const Cur& k) {
         const ExpertRef ref = expert_ref(p, pl, k.u);
-        load_wslab<FMT, 2>(p, ref.src, 2, k.c * (NW * 32) + 32 * wv, I, k.s * SLAB, ln, gq, w);
+        load_wslab<FMT, RT>(p, ref.src, 2, k.c * (NW * WR) + WR * wv, I, k.s * SLAB, ln, gq, w);
     };
-    auto compute = [&](const WSlab<2>& w, const Cur& k) {
+    auto compute = [&](const WSlab<RT>& w, const Cur& k) {
         int a, nt;
         group_of(k, a, nt);
         uint4 hh[4], hl[4];
@@ -1118,18 +1120,18 @@ __global__ void __launch_bounds__(DNL_NW * WAVE) down_lds_kernel(DecodeParams p)
 #pragma unroll
             for (int i = 0; i < 4; ++i) hh[i] = hl[i] = make_uint4(0u, 0u, 0u, 0u);
         }
-        mma_slab2<FMT, 2>(w, hh, hl, gq, acc);
+        mma_slab2<FMT, RT>(w, hh, hl, gq, acc);
         if (FMT == MOE355_W_INT4_G64) {
             float part = 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) part = sum_f16x8(hl[i], sum_f16x8(hh[i], part));
             const uint4 bb = bias_b_operand(part, gq);
 #pragma unroll
-            for (int t = 0; t < 2; ++t) acc[t] = mma<FMT>(bias_a_operand(w.bi[t], w.sc[t], gq), bb, acc[t]);
+            for (int t = 0; t < RT; ++t) acc[t] = mma<FMT>(bias_a_operand(w.bi[t], w.sc[t], gq), bb, acc[t]);
         }
         if (k.tg == 0) {   // fill-through of the expert's down bytes
             const ExpertRef ref = expert_ref(p, pl, k.u);
-            if (ref.dst) store_wslab<FMT, 2>(p, ref.dst, 2, k.c * (NW * 32) + 32 * wv, I, k.s * SLAB, ln, gq, w);
+            if (ref.dst) store_wslab<FMT, RT>(p, ref.dst, 2, k.c * (NW * WR) + WR * wv, I, k.s * SLAB, ln, gq, w);
         }
     };
     auto epilogue = [&](const Cur& k) {
@@ -1138,13 +1140,14 @@ __global__ void __launch_bounds__(DNL_NW * WAVE) down_lds_kernel(DecodeParams p)
         if (ln < nt) {
             const int pair = pl.pairs[a + ln];
             const float wt = pl.w[pair];
-            float* o = p.out + static_cast<int64_t>(pl.tok[a + ln]) * p.H + k.c * (NW * 32) + 32 * wv;
+            float* o = p.out + static_cast<int64_t>(pl.tok[a + ln]) * p.H + k.c * (NW * WR) + WR * wv;
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < RT; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) unsafeAtomicAdd(o + 16 * t + 4 * gq + r, wt * acc[t][r]);
         }
-        acc[0] = acc[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     };
 
     Cur lc, cc;
@@ -1155,7 +1158,7 @@ __global__ void __launch_bounds__(DNL_NW * WAVE) down_lds_kernel(DecodeParams p)
         group_of(cc, a, nt);
         stage_h(a);
     }
-    WSlab<2> ring[D];
+    WSlab<RT> ring[D];
 #pragma unroll
     for (int d = 0; d < D - 1; ++d) {
         load_stage(ring[d], lc);
@@ -1597,10 +1600,12 @@ moe355_status launch_decode(const DecodeParams& p, int max_uniq, uint32_t* sync,
     const int slots = cus * 8;   // eight resident wavefronts per CU
     const int items2 = max_uniq * (p.H / 32);
     const int items1 = max_uniq * (p.H / 16);
-    if (items2 >= 2 * slots && p.H % (DNL_NW * 32) == 0 && 16 * (p.I / 4 + 1) * 16 <= DNL_LDS) {
+    if (items2 >= 2 * slots && p.H % (DNL_NW * 64) == 0 && 16 * (p.I / 4 + 1) * 16 <= DNL_LDS) {
         // many distinct experts: h in LDS, one block per CU (a window holds a
-        // full token group of any expert)
-        down_lds_kernel<FMT, 8><<<cus, DNL_NW * WAVE, 0, stream>>>(p);
+        // full token group of any expert); four row tiles per wavefront, one
+        // slab ahead (DS-like: 157.8 us per FFN call, against 168-172 us with
+        // two row tiles at any depth and 159-164 us with four tiles 3-6 deep)
+        down_lds_kernel<FMT, 4, 2><<<cus, DNL_NW * WAVE, 0, stream>>>(p);
     } else if (items2 >= 2 * slots) {
         const int waves = items2 < slots ? items2 : slots;
         down_kernel<FMT, 2, 3, 1, false><<<(waves + 3) / 4, 256, 0, stream>>>(p);
