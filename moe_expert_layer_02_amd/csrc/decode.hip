@@ -1019,11 +1019,10 @@ __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
 // stage also held 32 registers of h and two stages ahead filled the register
 // budget at two wavefronts per SIMD: half the bytes in flight of gate/up.)
 constexpr int DNL_LDS = 135168;   // bytes of staged h: 16 rows of I = 2048 with padding
-constexpr int DNL_NW = 8;         // wavefronts per block (one block per CU)
 
-template <int FMT, int RT, int D>
-__global__ void __launch_bounds__(DNL_NW * WAVE) down_lds_kernel(DecodeParams p) {
-    constexpr int NW = DNL_NW;
+// NW wavefronts per block, one block per CU
+template <int FMT, int RT, int D, int NW>
+__global__ void __launch_bounds__(NW * WAVE) down_lds_kernel(DecodeParams p) {
     __shared__ PlanLds pl;
     __shared__ int32_t tgb[MAX_PLAN + 1];   // item base of each distinct expert, in token groups
     __shared__ int32_t win[2];              // staged pair positions [win[0], win[1])
@@ -1604,12 +1603,17 @@ moe355_status launch_decode(const DecodeParams& p, int max_uniq, uint32_t* sync,
     const int slots = cus * 8;   // eight resident wavefronts per CU
     const int items2 = max_uniq * (p.H / 32);
     const int items1 = max_uniq * (p.H / 16);
-    if (items2 >= 2 * slots && p.H % (DNL_NW * 64) == 0 && 16 * (p.I / 4 + 1) * 16 <= DNL_LDS) {
+    if (items2 >= 2 * slots && p.H % 512 == 0 && 16 * (p.I / 4 + 1) * 16 <= DNL_LDS) {
         // many distinct experts: h in LDS, one block per CU (a window holds a
         // full token group of any expert); four row tiles per wavefront, one
-        // slab ahead (DS-like: 157.8 us per FFN call, against 168-172 us with
-        // two row tiles at any depth and 159-164 us with four tiles 3-6 deep)
-        down_lds_kernel<FMT, 4, 2><<<cus, DNL_NW * WAVE, 0, stream>>>(p);
+        // slab ahead, sixteen wavefronts (four per SIMD) where H allows items of
+        // 1024 rows, else eight (DS-like: 154 us per FFN call with sixteen,
+        // 156 us with eight, against 168-172 us with two row tiles at any depth
+        // and 159-164 us with four tiles 3-6 deep)
+        if (p.H % 1024 == 0)
+            down_lds_kernel<FMT, 4, 2, 16><<<cus, 16 * WAVE, 0, stream>>>(p);
+        else
+            down_lds_kernel<FMT, 4, 2, 8><<<cus, 8 * WAVE, 0, stream>>>(p);
     } else if (items2 >= 2 * slots) {
         const int waves = items2 < slots ? items2 : slots;
         down_kernel<FMT, 2, 3, 1, false><<<(waves + 3) / 4, 256, 0, stream>>>(p);
