@@ -1428,10 +1428,14 @@ moe355_status launch_gate_up(const DecodeParams& p, int max_uniq, hipStream_t st
     const int cap = device_cus() * 2;   // two resident blocks per CU
     // the widest tile that still leaves two items per block slot: four row tiles
     // per wavefront with two stages in flight (8 KB of gate and up codes per
-    // stage), else two tiles with three stages, else one tile with four
+    // stage; three when the call also writes fill-through bytes, which then run
+    // at one wavefront per SIMD but keep more reads in flight beside the
+    // stores), else two tiles with three stages, else one tile with four
     const int items2 = max_uniq * (p.I / (RW * 32));
     const int items4 = max_uniq * (p.I / (RW * 64));
-    if (items4 >= 2 * cap && p.I % (RW * 64) == 0) {
+    if (items4 >= 2 * cap && p.I % (RW * 64) == 0 && p.has_cache && p.fill_through) {
+        gate_up_kernel<FMT, 4, KW, 4, 3, false><<<items4 < cap ? items4 : cap, 256, 0, stream>>>(p);
+    } else if (items4 >= 2 * cap && p.I % (RW * 64) == 0) {
         gate_up_kernel<FMT, 4, KW, 4, 2, false><<<items4 < cap ? items4 : cap, 256, 0, stream>>>(p);
     } else if (items2 >= 2 * cap && p.I % (RW * 32) == 0) {
         gate_up_kernel<FMT, 4, KW, 2, 3, false><<<items2 < cap ? items2 : cap, 256, 0, stream>>>(p);
