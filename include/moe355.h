@@ -46,8 +46,36 @@ typedef int32_t moe355_status;
 const char* moe355_status_string(moe355_status s);
 /* Description of the latest failure on this host thread ("" if none). */
 const char* moe355_last_error(void);
-/* Library version string. */
+/* Library version string: "libmoe355 <version> gfx950 src:<hash>", where <hash>
+ * is the first 16 hex digits of the sha256 of the sources the library was
+ * built from (so a loaded binary can be matched to its source tree). */
 const char* moe355_version(void);
+
+/*
+ * Error words.  Some failures can only be seen on the device while a call runs;
+ * they are recorded in a 32-bit word of the call's workspace, which the caller
+ * reads after the call has completed:
+ *   decode (moe355_expert_ffn_decode, moe355_decode_layer): the word at byte
+ *     MOE355_DECODE_ERR_BYTE of the workspace, sticky (never cleared by the
+ *     library: clear it with the rest of the workspace's first 65536 bytes);
+ *   prefill (moe355_expert_ffn_prefill): the word at byte MOE355_PREFILL_ERR_BYTE,
+ *     cleared by each call with T > 0 before its kernels run.
+ * A set bit means the outputs of the call that set it are not valid:
+ *   MOE355_ERR_WAIT      a bounded in-kernel wait gave up (one-launch decode calls);
+ *   MOE355_ERR_F16_RANGE int4 weights only: an activation x (|x| > 65504 as a bf16
+ *                        value, inf or NaN) or an intermediate h = silu(gate x) * (up x)
+ *                        (times the routing weight inside the one-launch decode
+ *                        calls; |h| >= 65520) lies outside f16's finite range.  The
+ *                        int4 path runs its products on f16 operands; inside that
+ *                        range they are exact, except that |x| < 2^-14 keeps only
+ *                        the multiples of 2^-24 (an absolute error below 2^-24 per
+ *                        element).  MXFP4 weights run on bf16 operands and have no
+ *                        such limit.
+ */
+#define MOE355_DECODE_ERR_BYTE   4608
+#define MOE355_PREFILL_ERR_BYTE  0
+#define MOE355_ERR_WAIT          1u
+#define MOE355_ERR_F16_RANGE     2u
 
 /* Routing families [Edge0, section 2 "MoE routing"]. */
 #define MOE355_ROUTE_SOFTMAX_TOPK   0
@@ -175,8 +203,12 @@ typedef struct {
 } moe355_classify_out;
 
 /*
- * logits[t, e] = sum_h x[t, h] * w_router[e, h], fp32 accumulation.
+ * Router projection: logits[t, e] = sum_h x[t, h] * w_router[e, h], fp32
+ * accumulation.  The routing families of [Edge0, section 2 "MoE routing"] score
+ * per-expert logits of each token; no page spells out how the logits are formed,
+ * and this call forms them with the plain linear router x . W_r^T.
  * x: device bf16 [T, H]; w_router: device fp32 [E, H]; logits: device fp32 [T, E].
+ * Errors: MOE355_EINVAL for a bad descriptor, null pointers or T < 0.
  */
 moe355_status moe355_router_logits(const moe355_layer_desc* d, const void* x_bf16,
                                    const float* w_router, int32_t T, float* logits,
@@ -217,7 +249,9 @@ moe355_status moe355_dedup(const int32_t* ids, int32_t n_ids, int32_t n_experts,
  * miss i to victim i, set owner and ts = tick.  Remaining misses go to `inplace`.
  * The caller must use a tick larger than every earlier one (e.g. step*L + l + 1).
  * Limits: n_slots <= 16384, n_experts <= 1024, n_ids <= 1024, 0 < tick < 2^31,
- * out->capacity >= max(min(n_ids, E), K).
+ * out->capacity >= max(min(n_ids, E), K).  (The device keeps timestamps as 32-bit
+ * values: calls that take the tick from device memory, tick_base below, must keep
+ * it under 2^32, which the host cannot check.)
  */
 moe355_status moe355_classify_evict(const moe355_cache* c, int32_t layer, int64_t tick,
                                     const int32_t* ids, int32_t n_ids,
@@ -241,16 +275,23 @@ moe355_status moe355_cache_fill(const moe355_cache* c, const uint8_t* pool, int3
  * receives the to->n_slots occupied slots of `from` that are last in
  * (ts, slot) order, packed into slots 0.. in ascending old-slot order with
  * their timestamps and bytes; remaining slots of `to` are empty.  `from` is
- * read only.  The two caches must not share memory.
+ * read only.  No byte of `to`'s four arrays may overlap any byte of `from`'s
+ * (table n_layers*n_experts*4, owner n_slots*4, ts n_slots*8, data
+ * n_slots*slot_bytes bytes): MOE355_EINVAL otherwise.
  */
 moe355_status moe355_cache_rebuild(const moe355_cache* from, moe355_cache* to,
                                    hipStream_t stream);
 
 /*
- * Prefill bucketing: a stable sort of the T*k pairs p = t*k + j by expert id.
+ * Prefill bucketing.  No page defines this call: it groups a prefill batch's
+ * routed pairs by expert so that the whole-layer path of [Edge0, section 3.1
+ * "Executor paths"] runs each expert once over its token bucket.  It is a stable
+ * sort of the T*k pairs p = t*k + j by expert id.
  * perm: device int32 [T*k]; offsets: device int32 [E+1] (offsets[e] = first
  * position of expert e, offsets[E] = T*k).  ws: device scratch of
- * moe355_workspace_bytes(d, T, MOE355_MODE_PERMUTE) bytes.
+ * moe355_workspace_bytes(d, T, MOE355_MODE_PERMUTE) bytes.  Errors: MOE355_EINVAL
+ * for a bad descriptor, null pointers or ids; MOE355_ECAPACITY for a short
+ * workspace.
  */
 moe355_status moe355_permute(const moe355_layer_desc* d, const int32_t* topk_ids, int32_t T,
                              int32_t* perm, int32_t* offsets, void* ws, size_t ws_bytes,
@@ -268,10 +309,9 @@ moe355_status moe355_permute(const moe355_layer_desc* d, const int32_t* topk_ids
  * ws: device scratch of moe355_workspace_bytes(d, T, MOE355_MODE_DECODE) bytes
  * (calls sharing one workspace must not overlap).  Its first 65536 bytes hold
  * the call's synchronisation counters and flags: zero them once when the
- * workspace is allocated; every call leaves them zero.  The 32-bit word at byte offset 4608
- * is a sticky error word: nonzero means a bounded in-kernel wait gave up and
- * that call's output is not valid.  exp->plan and exp->pairs (written by moe355_classify_evict or
- * moe355_dedup) are required.
+ * workspace is allocated; every call leaves them zero, except the sticky error
+ * word at byte MOE355_DECODE_ERR_BYTE (see "Error words" above).  exp->plan and
+ * exp->pairs (written by moe355_classify_evict or moe355_dedup) are required.
  * Kernels: a small call (T <= 16, H in {1024, 2048, 4096}, distinct experts x
  * I/16 <= the device's compute units, T*k*I*4 <= 32 KiB) runs as one launch in
  * which the down blocks wait for the gate/up blocks and each pair of them owns
@@ -290,7 +330,7 @@ moe355_status moe355_expert_ffn_decode(const moe355_layer_desc* d, const void* x
                                        hipStream_t stream);
 
 /*
- * One whole decode layer call in two kernels [FT-zh, Method steps: per layer a
+ * One whole decode layer call [FT-zh, Method steps: per layer a
  * single device kernel routes, deduplicates, classifies, splits the misses and
  * picks the LRU victims; the GPU computes G = H u F while F is copied into its
  * slots; everything replays inside one captured graph with no host
@@ -304,7 +344,12 @@ moe355_status moe355_expert_ffn_decode(const moe355_layer_desc* d, const void* x
  * logits: device fp32 [T, E]; x: device bf16 [T, H]; topk_ids / topk_w: device
  * [T, k] outputs; lists: the call's classify lists (capacity >= max(min(T*k, E),
  * K)); out: device fp32 [T, H]; ws as for moe355_expert_ffn_decode.
- * Limits: 1 <= T*k <= 256, plus those of the two calls.
+ * Kernels: a small call (the small-call rule of moe355_expert_ffn_decode, plus a
+ * cache of at most 2048 slots, E <= 256, T*k <= 128 and K <= 128; every
+ * one-token Qwen-like call) runs as ONE launch whose first workgroup does the
+ * routing and bookkeeping and publishes the plan to the FFN workgroups;
+ * otherwise the bookkeeping kernel runs first and the expert FFN after it.
+ * Limits: 1 <= T*k <= 256, plus those of the two calls; tick < 2^32.
  */
 moe355_status moe355_decode_layer(const moe355_layer_desc* d, const moe355_cache* c,
                                   const uint8_t* pool, int32_t layer, const int64_t* tick_base,
@@ -349,7 +394,10 @@ moe355_status moe355_evict_fill(const moe355_layer_desc* d, const moe355_cache* 
  * [Edge0, section 3.1 "Executor paths": the whole-layer path loads all experts
  * of a layer for prefill; FT-zh, Method steps].  Same result as the decode
  * call.  layer_w: device [E * S].  out: device fp32 [T, H].
- * ws: moe355_workspace_bytes(d, T, MOE355_MODE_PREFILL) bytes.
+ * ws: moe355_workspace_bytes(d, T, MOE355_MODE_PREFILL) bytes, whose word at
+ * MOE355_PREFILL_ERR_BYTE is the call's error word (see "Error words").
+ * Limits: H a multiple of 256 up to 8192, I a multiple of 128 up to 2048,
+ * E <= 1024, T*H < 2^31.
  */
 moe355_status moe355_expert_ffn_prefill(const moe355_layer_desc* d, const void* x_bf16,
                                         int32_t T, const int32_t* topk_ids, const float* topk_w,
@@ -358,8 +406,14 @@ moe355_status moe355_expert_ffn_prefill(const moe355_layer_desc* d, const void* 
                                         size_t ws_bytes, hipStream_t stream);
 
 /*
- * Unfused combine: out[t, n] = sum_j topk_w[t, j] * y[t*k + j, n], j ascending.
- * y: device fp32 [T*k, H]; out: device fp32 [T, H].
+ * Unfused combine [FT-zh, Core method: the partial sums of a token's experts
+ * merge into its output exactly; Edge0, section 2 "MoE routing": the output is
+ * the routing-weighted sum over the selected experts]:
+ * out[t, n] = sum_j topk_w[t, j] * y[t*k + j, n], j ascending, fp32 fused
+ * multiply-adds.  The expert FFN calls fuse this step; this call serves callers
+ * that hold per-pair outputs.  y: device fp32 [T*k, H]; topk_w: device fp32
+ * [T, k]; out: device fp32 [T, H].  Errors: MOE355_EINVAL for null pointers,
+ * T < 0, H < 1 or k < 1.
  */
 moe355_status moe355_combine(int32_t T, int32_t H, int32_t k, const float* y,
                              const float* topk_w, float* out, hipStream_t stream);
@@ -367,7 +421,9 @@ moe355_status moe355_combine(int32_t T, int32_t H, int32_t k, const float* y,
 #define MOE355_MODE_DECODE   0
 #define MOE355_MODE_PREFILL  1
 #define MOE355_MODE_PERMUTE  2
-/* Scratch bytes a call of the given mode needs for T tokens. */
+/* Scratch bytes a call of the given mode needs for T tokens.  No page defines
+ * this call; it sizes the caller-owned workspaces above.  Returns 0 for an
+ * invalid descriptor, T < 0 or an unknown mode. */
 size_t moe355_workspace_bytes(const moe355_layer_desc* d, int32_t T, int32_t mode);
 
 #ifdef __cplusplus

@@ -17,7 +17,8 @@ from .abi import (LayerDesc, Cache, EvictPolicy, ClassifyOut, ROUTE_SOFTMAX_TOPK
 from .ops import (router_logits, route, dedup, classify_evict, cache_fill, cache_rebuild,
                   permute, expert_ffn_decode, decode_layer, route_plan, evict_fill,
                   expert_ffn_prefill, combine, workspace_bytes, pack_experts,
-                  expert_bytes, version, DeviceCache, DeviceClassifyOut)
+                  expert_bytes, version, check_build, error_word, check_error, ERR_WAIT,
+                  ERR_F16_RANGE, DeviceCache, DeviceClassifyOut)
 
 __all__ = [
     "LayerDesc", "Cache", "EvictPolicy", "ClassifyOut", "ROUTE_SOFTMAX_TOPK",
@@ -26,6 +27,6 @@ __all__ = [
     "cache_fill", "cache_rebuild", "permute", "expert_ffn_decode", "decode_layer", "route_plan",
     "evict_fill",
     "expert_ffn_prefill",
-    "combine", "workspace_bytes", "pack_experts", "expert_bytes", "version", "DeviceCache",
-    "DeviceClassifyOut",
+    "combine", "workspace_bytes", "pack_experts", "expert_bytes", "version", "check_build",
+    "error_word", "check_error", "ERR_WAIT", "ERR_F16_RANGE", "DeviceCache", "DeviceClassifyOut",
 ]

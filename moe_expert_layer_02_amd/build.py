@@ -6,6 +6,7 @@ from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
+import hashlib
 import os
 import subprocess
 import sys
@@ -27,9 +28,25 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
+HEADER = os.path.join(os.path.dirname(HERE), "include", "moe355.h")
+
+
+def source_hash() -> str:
+    """First 16 hex digits of the sha256 over every kernel source, internal
+    header and the public header, in name order; the built library reports it
+    in moe355_version(), so a loaded binary can be matched to the tree."""
+    h = hashlib.sha256()
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
+    for f in files:
+        h.update(f.encode())
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    h.update(open(HEADER, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _compile(src: str, digest: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, f'-DMOE355_SRC_SHA="{digest}"', "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
@@ -43,8 +60,9 @@ def _compile(src: str) -> str:
 def build(jobs: int = 8, verbose: bool = True) -> str:
     os.makedirs(OBJ, exist_ok=True)
     srcs = sources()
+    digest = source_hash()
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda f: _compile(f, digest), srcs))
     tmp = OUT + ".tmp"
     cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -93,7 +93,11 @@ extern "C" const char* moe355_status_string(moe355_status s) {
 
 extern "C" const char* moe355_last_error(void) { return g_last_error; }
 
-extern "C" const char* moe355_version(void) { return "libmoe355 0.1 gfx950"; }
+#ifndef MOE355_SRC_SHA
+#define MOE355_SRC_SHA "unknown"
+#endif
+// "libmoe355 <version> gfx950 src:<first 16 hex digits of the sources' sha256>"
+extern "C" const char* moe355_version(void) { return "libmoe355 0.2 gfx950 src:" MOE355_SRC_SHA; }
 
 extern "C" int64_t moe355_expert_bytes(const moe355_layer_desc* d) {
     ExpertLayout L;

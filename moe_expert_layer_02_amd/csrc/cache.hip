@@ -15,6 +15,8 @@
 // (ts, slot) keys among slots with ts < tick are found by an 8-bit-digit radix
 // select over LDS histograms, then ranked by counting.  Owning the whole call
 // in one workgroup keeps the table updates free of cross-workgroup atomics.
+#include <utility>
+
 #include "classify_dev.h"
 
 namespace moe355 {
@@ -461,9 +463,27 @@ extern "C" moe355_status moe355_cache_rebuild(const moe355_cache* from, moe355_c
     MOE355_REQUIRE(from->n_layers == to->n_layers && from->n_experts == to->n_experts &&
                        from->slot_bytes == to->slot_bytes,
                    MOE355_EINVAL, "cache_rebuild: caches of different shape");
-    MOE355_REQUIRE(from->slot_data && to->slot_data && from->slot_data != to->slot_data &&
-                       from->slot_table != to->slot_table,
-                   MOE355_EINVAL, "cache_rebuild: caches must be separate buffers");
+    MOE355_REQUIRE(from->slot_data && to->slot_data, MOE355_EINVAL, "cache_rebuild: null slot data");
+    {   // `to` is written while `from` is read: no byte of the one may be a byte of the other
+        const int64_t tl = static_cast<int64_t>(from->n_layers) * from->n_experts;
+        auto span = [](const void* p, int64_t n) {
+            const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+            return std::pair<uintptr_t, uintptr_t>(b, b + static_cast<uintptr_t>(n));
+        };
+        const std::pair<uintptr_t, uintptr_t> f[4] = {
+            span(from->slot_table, tl * 4), span(from->slot_owner, int64_t{from->n_slots} * 4),
+            span(from->slot_ts, int64_t{from->n_slots} * 8),
+            span(from->slot_data, int64_t{from->n_slots} * from->slot_bytes)};
+        const std::pair<uintptr_t, uintptr_t> t[4] = {
+            span(to->slot_table, tl * 4), span(to->slot_owner, int64_t{to->n_slots} * 4),
+            span(to->slot_ts, int64_t{to->n_slots} * 8),
+            span(to->slot_data, int64_t{to->n_slots} * to->slot_bytes)};
+        for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 4; ++j)
+                MOE355_REQUIRE(t[i].second <= f[j].first || f[j].second <= t[i].first, MOE355_EINVAL,
+                               "cache_rebuild: array %d of the new cache overlaps array %d of the old",
+                               i, j);
+    }
     MOE355_REQUIRE(to->slot_bytes % 16 == 0 && to->n_slots <= 65535, MOE355_ENOTSUP,
                    "cache_rebuild: slot_bytes or n_slots unsupported");
     rebuild_select_kernel<<<1, CL_THREADS, 0, stream>>>(

@@ -70,6 +70,7 @@ struct DecodeParams {
     uint16_t* h_hi;          // [T*k][I] high half of h (f16 for int4, bf16 for MXFP4)
     uint16_t* h_lo;          // [T*k][I] remainder h - h_hi
     float* out;              // [T][H]
+    uint32_t* err;           // the workspace's sticky error word
 };
 
 // Device-memory (address space 1) byte pointers: loads and stores through them
@@ -377,7 +378,8 @@ __device__ __forceinline__ void mma_slab2(const WSlab<RT>& w, const uint4 bh[4],
 //   9..16    blocks of group g = block % 8 exited
 //   17       groups whose blocks have all exited; the last block to exit clears
 //            every word
-//   18       error word, sticky: bit 0 = a bounded wait gave up
+//   18       error word, sticky: bit 0 = a bounded wait gave up, bit 1 = an
+//            int4 activation or h value outside f16's finite range
 //   32..95   flag "all gate/up blocks done", one copy per line
 //   96..159  whole-layer launch: flag "plan published", one copy per line (a
 //            one-token call writes the whole plan as a 16-word record in each
@@ -435,7 +437,7 @@ __device__ __forceinline__ void wait_flag(uint32_t* sync, int f, uint32_t b) {
         while (__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
             __builtin_amdgcn_s_sleep(2);
             if (++n == SPIN_LIMIT) {
-                __hip_atomic_fetch_or(sync_word(sync, SW_ERR), 1u, __ATOMIC_RELAXED,
+                __hip_atomic_fetch_or(sync_word(sync, SW_ERR), ERR_WAIT, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
@@ -457,7 +459,7 @@ __device__ __forceinline__ void wait_plan(uint32_t* sync, uint32_t b, PlanLds& p
             if (__hip_atomic_load(pw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
             __builtin_amdgcn_s_sleep(2);
             if (++n == SPIN_LIMIT) {
-                __hip_atomic_fetch_or(sync_word(sync, SW_ERR), 1u, __ATOMIC_RELAXED,
+                __hip_atomic_fetch_or(sync_word(sync, SW_ERR), ERR_WAIT, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
@@ -571,7 +573,7 @@ __device__ __forceinline__ void wait_plan_record(uint32_t* sync, uint32_t b, con
             __builtin_amdgcn_s_sleep(2);
             if (++n == SPIN_LIMIT) {
                 if (t == 0)
-                    __hip_atomic_fetch_or(sync_word(sync, SW_ERR), 1u, __ATOMIC_RELAXED,
+                    __hip_atomic_fetch_or(sync_word(sync, SW_ERR), ERR_WAIT, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
@@ -688,6 +690,10 @@ __device__ __forceinline__ void gate_up_body(const DecodeParams& p, PlanLds& pl,
         }
     };
     f32x4 acc[2][RT];
+    // int4: largest bf16 magnitude of x seen and whether an h value left f16's
+    // range (either makes the f16 operands inexact: flagged in the error word)
+    u16x2_t xmag = {0, 0};
+    bool hbad = false;
     auto zero_acc = [&]() {
 #pragma unroll
         for (int m = 0; m < 2; ++m)
@@ -698,8 +704,10 @@ __device__ __forceinline__ void gate_up_body(const DecodeParams& p, PlanLds& pl,
         uint4 b[4];
         float part = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
             b[j] = FMT == MOE355_W_INT4_G64 ? b_x_f16(st.x[j], &part) : st.x[j];
+            if (FMT == MOE355_W_INT4_G64) xmag = bf16_mag_max(st.x[j], xmag);
+        }
         mma_slab<FMT, RT>(st.g, b, gq, acc[0]);
         mma_slab<FMT, RT>(st.u, b, gq, acc[1]);
         if (FMT == MOE355_W_INT4_G64) {
@@ -759,6 +767,7 @@ __device__ __forceinline__ void gate_up_body(const DecodeParams& p, PlanLds& pl,
                 for (int r = 0; r < 4; ++r) {
                     const float hv = silu(acc[0][t][r]) * acc[1][t][r] * wt;
                     if (FMT == MOE355_W_INT4_G64) {
+                        hbad |= beyond_f16(hv);
                         const _Float16 a = static_cast<_Float16>(hv);
                         const _Float16 b = static_cast<_Float16>(hv - static_cast<float>(a));
                         hi[r] = __builtin_bit_cast(uint16_t, a);
@@ -788,6 +797,7 @@ __device__ __forceinline__ void gate_up_body(const DecodeParams& p, PlanLds& pl,
                     uint16_t hi, lo;
                     int64_t at;
                     if (FMT == MOE355_W_INT4_G64) {
+                        hbad |= beyond_f16(hv);
                         const _Float16 a = static_cast<_Float16>(hv);
                         const _Float16 b = static_cast<_Float16>(hv - static_cast<float>(a));
                         hi = __builtin_bit_cast(uint16_t, a);
@@ -858,6 +868,8 @@ __device__ __forceinline__ void gate_up_body(const DecodeParams& p, PlanLds& pl,
             }
         }
     }
+    if (FMT == MOE355_W_INT4_G64 && (hbad || bf16_mag_beyond_f16(xmag)))
+        __hip_atomic_fetch_or(p.err, ERR_F16_RANGE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int FMT, int NW, int KW, int RT, int D, bool SKIP>
@@ -1701,6 +1713,7 @@ moe355_status decode_params(const moe355_layer_desc* d, const void* x_bf16, int3
     p.h_hi = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + SYNC_BYTES);
     p.h_lo = p.h_hi + tkI;
     p.out = out;
+    p.err = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + 256 * SW_ERR);
     if (cache) {
         MOE355_REQUIRE(cache->slot_table && cache->slot_data && cache->slot_bytes == L.bytes &&
                            cache->n_experts == d->n_experts && layer >= 0 &&

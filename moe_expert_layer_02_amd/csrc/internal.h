@@ -154,6 +154,29 @@ __device__ __forceinline__ float wave_sum_dpp_f32(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Error-word bits (include/moe355.h): a bounded wait gave up; an int4-path
+// activation or intermediate fell outside f16's finite range.
+constexpr uint32_t ERR_WAIT = 1u;
+constexpr uint32_t ERR_F16_RANGE = 2u;
+
+// Largest bf16 magnitude (as packed 16-bit pairs) of the 8 bf16 values in v,
+// folded into acc: one mask and one packed 16-bit maximum per dword.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2_t bf16_mag_max(uint4 v, u16x2_t acc) {
+    auto mag = [](uint32_t w) { return __builtin_bit_cast(u16x2_t, w & 0x7FFF7FFFu); };
+    const u16x2_t a = __builtin_elementwise_max(mag(v.x), mag(v.y));
+    const u16x2_t b = __builtin_elementwise_max(mag(v.z), mag(v.w));
+    return __builtin_elementwise_max(acc, __builtin_elementwise_max(a, b));
+}
+// Whether a bf16 magnitude from bf16_mag_max lies beyond f16's finite range
+// (|x| >= 65536 once in bf16; 0x4780 is 65536, 0x477F = 65280 still fits), or is
+// inf or NaN.
+__device__ __forceinline__ bool bf16_mag_beyond_f16(u16x2_t m) {
+    return m.x >= 0x4780u || m.y >= 0x4780u;
+}
+// f16 rounding to nearest overflows from 65520 on.
+__device__ __forceinline__ bool beyond_f16(float v) { return !(__builtin_fabsf(v) < 65520.0f); }
+
 // Sum over aligned segments of `width` lanes (width a power of two <= 64).
 __device__ __forceinline__ float segment_sum_f32(float v, int width) {
     for (int m = width >> 1; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);

@@ -58,6 +58,7 @@ struct PrefillParams {
     uint16_t* h_lo;          // [T*k][I] remainder
     float* hsum;             // int4: [T*k][I / 64] group sums of h
     float* out;
+    uint32_t* err;           // the call's error word (cleared by the plan kernel)
 };
 
 // Persistent tile loop: the work of a call split into NXCD contiguous ranges.
@@ -79,7 +80,8 @@ __device__ __forceinline__ TileRange tile_range(int total) {
 __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ offsets, int E,
                                                     int32_t* __restrict__ tile_e,
                                                     int32_t* __restrict__ tile_m0,
-                                                    int32_t* __restrict__ n_tiles) {
+                                                    int32_t* __restrict__ n_tiles,
+                                                    uint32_t* __restrict__ err) {
     __shared__ int32_t wave_tot[16];
     const int e = threadIdx.x, lane = e & (WAVE - 1), w = e / WAVE;
     const int me = e < E ? offsets[e + 1] - offsets[e] : 0;
@@ -102,7 +104,10 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
         tile_e[base + i] = e;
         tile_m0[base + i] = i * BM;
     }
-    if (e == 0) *n_tiles = all;
+    if (e == 0) {
+        *n_tiles = all;
+        *err = 0u;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -216,12 +221,16 @@ __device__ __forceinline__ void bias_a(const float* sums, int G, int g0, uint4* 
 // range) and its sums over each 64-wide group, once per call instead of once
 // per tile.  A thread converts 8 values; 8 neighbouring threads form a group.
 __global__ void __launch_bounds__(256) x16_kernel(const uint16_t* __restrict__ x, int64_t n8, int G,
-                                                  uint16_t* __restrict__ xf, float* __restrict__ xsum) {
+                                                  uint16_t* __restrict__ xf, float* __restrict__ xsum,
+                                                  uint32_t* __restrict__ err) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // chunk of 8
     float s = 0.0f;
     if (i < n8) {
         const uint4 v = reinterpret_cast<const uint4*>(x)[i];
         reinterpret_cast<uint4*>(xf)[i] = x8_f16(v, &s);
+        // a value beyond f16's range would not convert exactly: flag the call
+        if (bf16_mag_beyond_f16(bf16_mag_max(v, u16x2_t{0, 0})))
+            __hip_atomic_fetch_or(err, ERR_F16_RANGE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     s += __shfl_xor(s, 1, WAVE);
     s += __shfl_xor(s, 2, WAVE);
@@ -556,7 +565,10 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
             }
             if (FMT == MOE355_W_INT4_G64) {
                 // the row's sum over the wavefront's 64 features: one int4 group of h
+                // (not finite when an h value left f16's range: flag the call)
                 gsum += __shfl_xor(gsum, 32, WAVE);
+                if (keep && !(__builtin_fabsf(gsum) <= 3.0e38f))
+                    __hip_atomic_fetch_or(p.err, ERR_F16_RANGE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (keep && hh == 0) p.hsum[static_cast<int64_t>(pbase + r) * (I / 64) + fw / 64] = gsum;
             }
         }
@@ -761,7 +773,8 @@ size_t prefill_ws_bytes(const moe355_layer_desc* d, int T) {
                                 align256(static_cast<size_t>(T) * (d->hidden / 64) * 4) +
                                 align256(tk * (d->inter / 64) * 4)
                           : 0;
-    return align256(tk * d->inter * sizeof(float)) +
+    // the error word's 256 bytes, h, the tile plan, the tile count, int4's x copy and sums
+    return 256 + align256(tk * d->inter * sizeof(float)) +
            align256(2 * static_cast<size_t>(max_tiles(T, d->top_k, d->n_experts)) * sizeof(int32_t)) +
            256 + xb;
 }
@@ -799,8 +812,9 @@ extern "C" moe355_status moe355_expert_ffn_prefill(const moe355_layer_desc* d, c
     ExpertLayout L;
     expert_layout(d, &L);
     const size_t tk = static_cast<size_t>(T) * d->top_k;
-    uint8_t* wsb = static_cast<uint8_t*>(ws);
     PrefillParams p{};
+    p.err = static_cast<uint32_t*>(ws);            // first 256 bytes: the error word
+    uint8_t* wsb = static_cast<uint8_t*>(ws) + 256;
     p.x = static_cast<const uint16_t*>(x_bf16);
     p.perm = perm;
     p.offsets = offsets;
@@ -835,7 +849,7 @@ extern "C" moe355_status moe355_expert_ffn_prefill(const moe355_layer_desc* d, c
                                       align256(static_cast<size_t>(T) * (d->hidden / 64) * 4));
 
     plan_kernel<<<1, 1024, 0, stream>>>(offsets, d->n_experts, tiles, tiles + mt,
-                                        const_cast<int32_t*>(p.n_tiles));
+                                        const_cast<int32_t*>(p.n_tiles), p.err);
     st = check_launch("expert_ffn_prefill plan");
     if (st) return st;
     const int blocks = prefill_blocks();
@@ -843,7 +857,7 @@ extern "C" moe355_status moe355_expert_ffn_prefill(const moe355_layer_desc* d, c
     if (int4) {
         const int64_t n8 = static_cast<int64_t>(T) * d->hidden / 8;
         x16_kernel<<<static_cast<unsigned>((n8 + 255) / 256), 256, 0, stream>>>(
-            p.x, n8, d->hidden / 64, xf, xsum);
+            p.x, n8, d->hidden / 64, xf, xsum, p.err);
         st = check_launch("expert_ffn_prefill x16");
         if (st) return st;
     }

@@ -11,7 +11,7 @@ import ctypes
 import torch
 
 from .abi import (Cache, ClassifyOut, EvictPolicy, LayerDesc, MODE_DECODE, MODE_PERMUTE,
-                  MODE_PREFILL, check, load)
+                  MODE_PREFILL, Moe355Error, check, load)
 
 
 def _ptr(t) -> int | None:
@@ -36,6 +36,42 @@ def _need(t, dtype, name):
 
 def version() -> str:
     return load().moe355_version().decode()
+
+
+def check_build() -> str:
+    """The loaded library's source hash must be the tree's: raises otherwise."""
+    from .build import source_hash
+    v = version()
+    want = source_hash()
+    if not v.endswith("src:" + want):
+        raise Moe355Error(-1, "check_build",
+                          f"the loaded library ({v}) was not built from these sources (src:{want}); "
+                          "rebuild with python -m moe_expert_layer_02_amd.build")
+    return v
+
+
+DECODE_ERR_BYTE = 4608     # MOE355_DECODE_ERR_BYTE
+PREFILL_ERR_BYTE = 0       # MOE355_PREFILL_ERR_BYTE
+ERR_WAIT = 1
+ERR_F16_RANGE = 2
+
+
+def error_word(ws, mode: int = MODE_DECODE) -> int:
+    """The error word of a decode or prefill workspace (synchronises)."""
+    at = DECODE_ERR_BYTE if mode == MODE_DECODE else PREFILL_ERR_BYTE
+    return int(ws[at:at + 4].view(torch.int32).item()) & 0xFFFFFFFF
+
+
+def check_error(ws, mode: int = MODE_DECODE, what: str = "") -> None:
+    """Raise if the workspace's error word records an invalid call (synchronises)."""
+    e = error_word(ws, mode)
+    if e:
+        why = []
+        if e & ERR_WAIT:
+            why.append("a bounded in-kernel wait gave up")
+        if e & ERR_F16_RANGE:
+            why.append("an int4-path activation or intermediate left f16's range")
+        raise Moe355Error(-2, what or "check_error", f"error word {e:#x}: " + "; ".join(why))
 
 
 def expert_bytes(desc: LayerDesc) -> int:

@@ -115,8 +115,7 @@ class CacheSim:
         return new
 
     def moves_of_rebuild(self, n_new: int):
-        """(old slot, new slot) pairs whose bytes a rebuild copies."""
-        occ = [(int(self.ts[s]), s) for s in range(self.N) if self.owner[s] >= 0]
-        occ.sort()
-        kept = sorted(s for _, s in occ[max(0, len(occ) - n_new):])
-        return list(zip(kept, range(len(kept))))
+        """(old slot, new slot) pairs whose bytes a rebuild copies, read off the
+        rebuilt cache: new slot n holds owner g, which sat in slot table[g] here."""
+        new = self.rebuild(n_new)
+        return [(int(self.table[g]), n) for n, g in enumerate(new.owner.tolist()) if g >= 0]

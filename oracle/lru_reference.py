@@ -53,6 +53,7 @@ class OrderedLRU:
         keep = set(occupied[max(0, len(occupied) - n_new):])
         renumber = {old: new for new, old in enumerate(sorted(keep))}
         out = OrderedLRU(n_new, self.E)
+        out.moved = sorted(renumber.items())     # (old slot, new slot) of every kept entry
         out.order = OrderedDict((s, None) for s in range(len(keep), n_new))
         for old in occupied:
             if old in keep:

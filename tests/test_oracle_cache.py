@@ -146,3 +146,35 @@ def test_rebuild_keeps_most_recent_and_packs_in_slot_order():
     assert new.table[2] == 0 and new.table[3] == 1 and new.table[4] == 2 and new.table[0] == -1
     grow = sim.rebuild(8)
     assert grow.owner.tolist() == [0, 2, 3, 4, 5, -1, -1, -1]
+
+
+def test_moves_of_rebuild_hand_example():
+    """Occupied (ts, slot): (3,5) (5,0) (7,3) (9,2) (9,4); keeping three moves the
+    bytes of old slots 2, 3, 4 to new slots 0, 1, 2; keeping all moves every
+    occupied slot down to its rank in slot order."""
+    sim = CacheSim(6, 1, 16)
+    for s, (t, o) in enumerate(zip([5, 0, 9, 7, 9, 3], [0, -1, 2, 3, 4, 5])):
+        sim.ts[s], sim.owner[s] = t, o
+        if o >= 0:
+            sim.table[o] = s
+    assert sim.moves_of_rebuild(3) == [(2, 0), (3, 1), (4, 2)]
+    assert sim.moves_of_rebuild(8) == [(0, 0), (2, 1), (3, 2), (4, 3), (5, 4)]
+    assert sim.moves_of_rebuild(1) == [(4, 0)]      # ts tie (9, 2) < (9, 4): slot 4 is newest
+
+
+@pytest.mark.parametrize("n_new", [1, 7, 12, 30, 45])
+def test_moves_of_rebuild_match_ordered_dict_shrink(n_new):
+    """The bytes a rebuild moves are the renumbering the textbook LRU's shrink
+    applies to its kept entries, on a cache shaped by a random trace."""
+    N, L, E, T, k = 30, 3, 32, 2, 4
+    rng = np.random.default_rng(n_new)
+    sim, ref = CacheSim(N, L, E), OrderedLRU(N, E)
+    K = min(T * k, E, N)
+    for step, l, ids in _random_trace(rng, L, E, T, k, 12, hot=None):
+        out = sim.classify_evict(l, step * L + l + 1, ids, K)
+        ref.call(l, ids.ravel(), K, out["counts"][2])
+    moves = sim.moves_of_rebuild(n_new)
+    assert moves == ref.shrink(n_new).moved
+    # every move carries an occupied slot to a distinct new slot, in slot order
+    assert [n for _, n in moves] == list(range(len(moves)))
+    assert all(sim.owner[o] >= 0 for o, _ in moves)

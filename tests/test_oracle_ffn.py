@@ -33,7 +33,10 @@ def _int4_matrix(nibble, s, b, out, inn):
 
 
 def _silu(z):
-    return z / (1.0 + math.exp(-z))
+    if z >= 0:
+        return z / (1.0 + math.exp(-z))
+    e = math.exp(z)             # no overflow for large negative z
+    return z * e / (1.0 + e)
 
 
 def test_zero_input_gives_zero_output():
@@ -46,7 +49,21 @@ def test_zero_input_gives_zero_output():
     assert np.all(out == 0.0)
 
 
-def test_closed_form_expert():
+def _extreme_x(H):
+    """Activations far outside N(0, 1): bf16 values of +-3e4 and +-7e4 (beyond
+    f16's largest finite value) and +-1e-6 (below f16's normal range), mixed
+    with ordinary ones."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((2, H))
+    x[0, :6] = [3e4, -3e4, 7e4, -7e4, 1e-6, -1e-6]
+    x[1, ::5] = 1e-6
+    x[1, 1] = -7e4
+    bits = (x.astype(np.float32).view(np.uint32) + 0x8000) >> 16      # bf16, nearest
+    return formats.bf16_to_float(bits.astype(np.uint16))
+
+
+@pytest.mark.parametrize("xkind", ["normal", "extreme"])
+def test_closed_form_expert(xkind):
     H, I = 128, 64
     s0, b0, s1, b1, s2, b2 = 0.0078125, -0.03125, 0.015625, -0.0625, 0.00390625, -0.015625
     parts = (_int4_matrix(lambda o, i: o % 16, s0, b0, I, H)           # gate depends on the row
@@ -54,7 +71,7 @@ def test_closed_form_expert():
              + _int4_matrix(lambda o, i: (o + 2 * i) % 16, s2, b2, H, I))
     blob = np.concatenate(parts)
     rng = np.random.default_rng(0)
-    x = rng.standard_normal((2, H))
+    x = rng.standard_normal((2, H)) if xkind == "normal" else _extreme_x(H)
     out = ffn.moe_layer(x, np.array([[0], [0]]), np.array([[1.0], [0.75]]),
                         lambda e: blob, formats.INT4_G64, H, I)
     for t, wt in ((0, 1.0), (1, 0.75)):
