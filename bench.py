@@ -181,6 +181,7 @@ def bench_decode(args, w):
         step_ev.append((e0, e1))
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    m.check_error(st.ws, what="timed decode steps")   # no bounded wait gave up, no range flag
     replay_s = sum(a.elapsed_time(b) for a, b in step_ev) / 1e3   # the layer calls alone
     # distinct experts per call, from the trace's target sets (the routed top-k sets;
     # checked below against the device counts of the last step)
@@ -229,6 +230,7 @@ def bench_decode(args, w):
             ev.append(e0.elapsed_time(e1) / L)
             u_rp += sum(len(np.unique(trace.targets[s % n_trace, l])) for l in range(L))
         del g
+    m.check_error(rp.ws, what="roofline FFN calls")
     ffn_avg_s = float(np.mean(ev)) / 1e3
     n_launch = len(ev) * L
     per_call_bytes = u_rp * S / n_launch
@@ -376,6 +378,7 @@ def bench_prefill(args, w):
         step(ev[i])
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    m.check_error(ws, m.MODE_PREFILL, what="timed prefill calls")
     ffn_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
     flops = 6.0 * w.hidden * w.inter * T * k          # algorithmic: gate, up, down
     achieved = flops / ffn_s / 1e12
@@ -467,6 +470,8 @@ def main():
     if args.calib_copy:
         print(json.dumps(calib_copy(args.calib_copy, 5)), flush=True)
         return
+    import moe_expert_layer_02_amd as m
+    m.check_build()         # the library under test was built from these sources
     from workloads import configs as C
     w = {"qwen_decode": C.QWEN_DECODE, "ds_decode": C.DS_DECODE, "qwen_prefill": C.QWEN_PREFILL,
          "ds_prefill": C.DS_STRESS}[args.workload]

@@ -412,8 +412,8 @@ moe355_status moe355_expert_ffn_prefill(const moe355_layer_desc* d, const void* 
  * out[t, n] = sum_j topk_w[t, j] * y[t*k + j, n], j ascending, fp32 fused
  * multiply-adds.  The expert FFN calls fuse this step; this call serves callers
  * that hold per-pair outputs.  y: device fp32 [T*k, H]; topk_w: device fp32
- * [T, k]; out: device fp32 [T, H].  Errors: MOE355_EINVAL for null pointers,
- * T < 0, H < 1 or k < 1.
+ * [T, k]; out: device fp32 [T, H].  T = 0 enqueues nothing (the pointers may
+ * then be null).  Errors: MOE355_EINVAL for null pointers, T < 0, H < 1 or k < 1.
  */
 moe355_status moe355_combine(int32_t T, int32_t H, int32_t k, const float* y,
                              const float* topk_w, float* out, hipStream_t stream);

@@ -1818,8 +1818,8 @@ extern "C" moe355_status moe355_expert_ffn_decode(const moe355_layer_desc* d, co
 extern "C" moe355_status moe355_combine(int32_t T, int32_t H, int32_t k, const float* y,
                                         const float* topk_w, float* out, hipStream_t stream) {
     MOE355_REQUIRE(T >= 0 && H >= 1 && k >= 1, MOE355_EINVAL, "combine: T=%d H=%d k=%d", T, H, k);
+    if (T == 0) return ok();      // an empty batch: nothing to read or write
     MOE355_REQUIRE(y && topk_w && out, MOE355_EINVAL, "combine: null pointer");
-    if (T == 0) return ok();
     const int64_t n = static_cast<int64_t>(T) * H;
     const int64_t blocks64 = (n + 255) / 256;
     const int blocks = blocks64 < 65536 ? static_cast<int>(blocks64) : 65536;

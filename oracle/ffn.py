@@ -55,8 +55,19 @@ def moe_layer(x: np.ndarray, ids: np.ndarray, w: np.ndarray, expert_blob, wfmt: 
         ye = swiglu_expert(x[rows], wg, wu, wd)
         for (t, j), yrow in zip(pairs, ye):
             y[row_of[int(t)], j] = yrow
-    for j in range(k):                        # combine, slots in ascending order
-        out += w[tokens, j][:, None] * y[:, j]
+    return combine(y, w[tokens]).astype(dtype, copy=False)
+
+
+def combine(y: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """out[t] = sum_j w[t, j] * y[t, j], slots j in ascending order.
+
+    y [T, k, H] per-pair expert outputs, w [T, k] routing weights.
+    """
+    y = np.asarray(y)
+    w = np.asarray(w)
+    out = np.zeros((y.shape[0], y.shape[2]), dtype=np.result_type(y, w))
+    for j in range(y.shape[1]):
+        out += w[:, j][:, None] * y[:, j]
     return out
 
 

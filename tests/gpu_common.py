@@ -57,3 +57,51 @@ class BlobSource:
         if g not in self.cache:
             self.cache[g] = wx.expert_blob(self.seed, g, self.w.wfmt, self.w.hidden, self.w.inter)
         return self.cache[g]
+
+
+def oracle_layer(x, ids, w, blob, wfmt, H, I, tokens=None, workers=8):
+    """``ffn.moe_layer`` for the given tokens, its distinct experts split into
+    disjoint groups evaluated in parallel threads.
+
+    A token's output is the sum over its routed slots of w * y, so it equals
+    the sum of the groups' partial outputs, each of which keeps the slots routed
+    to its own experts (the others get weight 0 and point at one of the group's
+    experts, so no other expert is dequantised).  NumPy releases the GIL in the
+    dequantisation and the products, so the groups run concurrently.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle import ffn as offn
+    ids = np.asarray(ids)
+    w = np.asarray(w, dtype=np.float64)
+    x = np.asarray(x)
+    toks = np.arange(ids.shape[0]) if tokens is None else np.asarray(tokens)
+    sid, sw, sx = ids[toks], w[toks], x[toks]
+    experts = sorted({int(e) for e in sid.ravel()})
+    n = max(1, min(workers, len(experts)))
+    groups = [experts[i::n] for i in range(n)]
+
+    def part(g):
+        inside = np.isin(sid, g)
+        return offn.moe_layer(sx, np.where(inside, sid, g[0]), np.where(inside, sw, 0.0),
+                              blob, wfmt, H, I)
+
+    if n == 1:
+        return part(groups[0])
+    with ThreadPoolExecutor(n) as ex:
+        return sum(ex.map(part, groups))
+
+
+class ParityLog:
+    """Collects float parity checks and reports the worst of them."""
+
+    def __init__(self, what):
+        self.what, self.worst_rel, self.worst_abs, self.n = what, 0.0, 0.0, 0
+
+    def check(self, got, want, label):
+        rel, mx = check_close(got, want, f"{self.what} {label}")
+        self.worst_rel, self.worst_abs = max(self.worst_rel, rel), max(self.worst_abs, mx)
+        self.n += 1
+
+    def report(self):
+        say(f"{self.what}: {self.n} float checks, worst rel_l2={self.worst_rel:.3e} "
+            f"max_abs={self.worst_abs:.3e}")

@@ -71,11 +71,12 @@ class TraceRunner:
         return {k: lists[call_idx, i, :n[k]].tolist() for i, k in enumerate(KEYS)}, c
 
 
-def _run_trace(w, steps, with_pool, shrink_step=-1, shrink_slots=0):
+def _run_trace(w, steps, with_pool, shrink_step=-1, shrink_slots=0, tick0=0):
     import torch
     import moe_expert_layer_02_amd as m
     from workloads import gpu as wg
-    say(f"cache trace {w.name}: steps={steps} L={w.n_layers} N={w.n_slots} pool={with_pool}")
+    say(f"cache trace {w.name}: steps={steps} L={w.n_layers} N={w.n_slots} pool={with_pool} "
+        f"tick base {tick0}")
     trace = tr.DecodeTrace(w, steps)
     pool = wg.make_pool(w) if with_pool else None
     runner = TraceRunner(w, w.n_slots, pool, steps)
@@ -102,7 +103,7 @@ def _run_trace(w, steps, with_pool, shrink_step=-1, shrink_slots=0):
             say(f"{w.name}: step {s}/{steps}")
         for l in range(w.n_layers):
             call = s * w.n_layers + l
-            tick = call + 1
+            tick = tick0 + call + 1
             runner.call(call, l, tick, trace.logits[s, l], policy)
             ids, _ = oroute.route(trace.logits[s, l], w.top_k, w.route, w.n_group, w.topk_group,
                                   w.route_scale)
@@ -182,6 +183,26 @@ def test_cache_trace_stress_with_rebuild():
     w = C.DS_STRESS
     runner, pool = _run_trace(w, w.steps, with_pool=True, shrink_step=w.shrink_step,
                               shrink_slots=w.shrink_slots)
+
+
+# Ticks near 2^30: (tick << log2 N) no longer fits 32 bits, so the victim scan
+# ranks 64-bit keys (few victims: the Qwen-like K = 8 over 2048 slots; many:
+# the DS-like K = 96 radix select over 1024 slots, and the stress run's rebuild).
+WIDE_TICK = 1 << 30
+
+
+def test_cache_trace_qwen_decode_wide_keys():
+    _run_trace(C.QWEN_DECODE, 48, with_pool=False, tick0=WIDE_TICK)
+
+
+def test_cache_trace_ds_decode_wide_keys():
+    _run_trace(C.DS_DECODE, 32, with_pool=False, tick0=WIDE_TICK)
+
+
+def test_cache_trace_stress_wide_keys_with_rebuild():
+    w = C.DS_STRESS
+    _run_trace(w, 40, with_pool=True, shrink_step=20, shrink_slots=w.shrink_slots,
+               tick0=WIDE_TICK)
 
 
 def test_classify_small_cache_every_path():

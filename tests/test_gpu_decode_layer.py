@@ -1,24 +1,32 @@
 """The decode-layer calls on the GPU, in both orders the library offers:
-"fused" (route + classify_evict in one kernel, then the expert FFN with
-fill-through) and "split" (route + plan, the FFN reading misses from the pool,
-and the LRU update + fill copy on a second stream that the next layer waits
-for).  Every call of decode traces bit-exact against the oracle's simulator on
-the integer outputs, sampled layer outputs against the oracle, every cache slot
-holding its owner's pool bytes afterwards, and a whole decode step captured as
-a graph and replayed, each replay checked against eager execution."""
+"fused" (route + classify_evict in one kernel, or the whole call in one launch
+for small calls, then the expert FFN with fill-through) and "split" (route +
+plan, the FFN reading misses from the pool, and the LRU update + fill copy on a
+second stream that the next layer waits for).
+
+Every call of decode traces is checked bit-exact against the oracle's
+simulator on the integer outputs; layer outputs are checked against the oracle
+on whole steps (every layer) for the Qwen-like trace and on every token of
+several calls for the DS-like ones (calls with in-place experts, the cold
+start, and the calls right after the stress workload's budget shrink); every
+cache slot holds its owner's pool bytes afterwards; the workspace's error word
+stays clear after every step.  A run with the tick near 2^30 takes the victim
+scan's 64-bit key path.  A whole decode step captured as a graph and replayed
+is checked the same way against the oracle."""
 import numpy as np
 import pytest
 
 from oracle import cache as ocache
-from oracle import ffn as offn
 from oracle import route as oroute
 from workloads import configs as C
 from workloads import experts as wx
 from workloads import traces as tr
 
-from gpu_common import BlobSource, check_close, desc_of, packer, say
+from gpu_common import BlobSource, ParityLog, desc_of, oracle_layer, packer, say
 
 pytestmark = pytest.mark.gpu
+
+WIDE_TICK = 1 << 30     # tick << log2(N) no longer fits 32 bits: 64-bit victim keys
 
 
 def _x_dev(bits):
@@ -27,10 +35,10 @@ def _x_dev(bits):
 
 
 class LayerRunner:
-    def __init__(self, w, n_slots, pool, mode="fused"):
+    def __init__(self, w, n_slots, pool, mode="fused", tick0=0):
         import torch
         import moe_expert_layer_02_amd as m
-        self.m, self.torch, self.w, self.mode = m, torch, w, mode
+        self.m, self.torch, self.w, self.mode, self.tick0 = m, torch, w, mode, tick0
         self.side = torch.cuda.Stream()
         self.planned = [torch.cuda.Event() for _ in range(w.n_layers)]
         self.desc = desc_of(w)
@@ -51,10 +59,23 @@ class LayerRunner:
         self.logits = torch.empty((L, T, w.n_experts), dtype=torch.float32, device="cuda")
         self.x = torch.empty((L, T, w.hidden), dtype=torch.bfloat16, device="cuda")
 
+    def tick_of(self, step, layer):
+        return self.tick0 + step * self.w.n_layers + layer + 1
+
     def stage(self, step, logits_np, xs):
         self.logits.copy_(self.torch.from_numpy(logits_np))
         self.x.copy_(xs)
-        self.tick.fill_(step * self.w.n_layers)
+        self.tick.fill_(self.tick0 + step * self.w.n_layers)
+
+    def rebuild(self, n_new):
+        """Elastic budget change at a step boundary: a new cache of n_new slots."""
+        m = self.m
+        new = m.DeviceCache(n_new, self.w.n_layers, self.w.n_experts, self.S)
+        m.cache_rebuild(self.cache, new)
+        self.cache = new
+        self.K = min(self.w.t_decode * self.w.top_k, self.w.n_experts, n_new)
+        self.policy = m.EvictPolicy(self.K, self.w.q_num, self.w.q_den)
+        assert self.K <= self.cap
 
     def step(self):
         m = self.m
@@ -85,6 +106,82 @@ def _xs(w, s):
     return torch.stack([_x_dev(tr.decode_x(w, s, l)) for l in range(w.n_layers)])
 
 
+def _check_ints(run, sim, s, w, logits):
+    """Every layer call of step s bit-exact against the simulator; returns the
+    oracle's (ids, weights, call dict) per layer."""
+    routed = []
+    for l in range(w.n_layers):
+        rid, rw = oroute.route(logits[l], w.top_k, w.route, w.n_group, w.topk_group,
+                               w.route_scale)
+        exp = sim.classify_evict(l, run.tick_of(s, l), rid, run.K, w.q_num, w.q_den)
+        got = run.lists[l].host()
+        assert got["counts"] == exp["counts"], (s, l, got["counts"], exp["counts"])
+        for key in ("uniq", "hit_expert", "hit_slot", "miss", "fill_expert", "fill_slot",
+                    "inplace", "victims"):
+            assert got[key] == exp[key], (s, l, key)
+        assert np.array_equal(run.ids[l].cpu().numpy(), rid), (s, l)
+        routed.append((rid, rw, exp))
+    return routed
+
+
+def _check_cache_state(run, sim, pool):
+    import torch
+    assert np.array_equal(run.cache.table.cpu().numpy(), sim.table)
+    assert np.array_equal(run.cache.owner.cpu().numpy(), sim.owner)
+    assert np.array_equal(run.cache.ts.cpu().numpy(), sim.ts)
+    S = run.S
+    owner = run.cache.owner.cpu().numpy()
+    data, pv = run.cache.data.view(-1, S), pool.view(-1, S)
+    occ = np.nonzero(owner >= 0)[0]
+    for i in range(0, len(occ), 64):
+        sl = torch.from_numpy(occ[i:i + 64]).cuda()
+        ow = torch.from_numpy(owner[occ[i:i + 64]].astype(np.int64)).cuda()
+        assert torch.equal(data.index_select(0, sl), pv.index_select(0, ow)), "slot bytes differ"
+    return len(occ)
+
+
+class Sampler:
+    """Which calls' outputs to check against the oracle, decided while the
+    trace runs (the outputs are overwritten by the next step)."""
+
+    def __init__(self, steps_all_layers=(), calls=(), first_inplace=0, after_rebuild=(),
+                 tokens=None):
+        self.steps_all = set(steps_all_layers)
+        self.calls = set(calls)
+        self.first_inplace = first_inplace      # how many of the first in-place calls
+        self.after_rebuild = set(after_rebuild)
+        self.tokens = tokens
+        self.jobs = []
+
+    def pick(self, s, l, exp):
+        if s in self.steps_all or (s, l) in self.calls or (s, l) in self.after_rebuild:
+            return True
+        if self.first_inplace and exp["counts"][4] > 0:
+            self.first_inplace -= 1
+            return True
+        return False
+
+    def take(self, run, s, routed):
+        w = run.w
+        toks = list(range(w.t_decode)) if self.tokens is None else self.tokens
+        out = None
+        for l, (rid, rw, exp) in enumerate(routed):
+            if self.pick(s, l, exp):
+                out = run.out.cpu().numpy() if out is None else out
+                tag = f"call ({s},{l}) hits {exp['counts'][1]} fills {exp['counts'][3]} " \
+                      f"in-place {exp['counts'][4]}"
+                self.jobs.append((tag, l, tr.decode_x(w, s, l), rid, rw, toks, out[l][toks].copy()))
+
+    def verify(self, w, src, what):
+        log = ParityLog(what)
+        for tag, l, xb, rid, rw, toks, got in self.jobs:
+            want = oracle_layer(tr.x_as_f32(xb), rid, rw, lambda e, l=l: src(l, e), w.wfmt,
+                                w.hidden, w.inter, tokens=toks)
+            log.check(got, want, tag)
+        log.report()
+        assert log.n == len(self.jobs) and log.n > 0
+
+
 # Small multi-token calls that take the one-launch whole-layer path (several
 # routing wavefronts, several token columns in the down products), with caches
 # small enough to evict every step: int4 + softmax-top-k, MXFP4 + sigmoid-group.
@@ -107,52 +204,80 @@ EXTRA = {
 }
 
 
-@pytest.mark.parametrize("mode", ["fused", "split"])
-@pytest.mark.parametrize("cid,steps,sample", [(2, 64, [(0, 3), (63, 39)]), (4, 24, [(5, 7)]),
-                                              (5, 24, [(23, 0)]), (6, 40, [(0, 1), (39, 3)]),
-                                              (7, 40, [(1, 0), (39, 2)]), (8, 40, [(0, 2), (39, 1)]),
-                                              (9, 40, [(0, 0), (39, 3)])])
-def test_decode_layer_trace(cid, steps, sample, mode):
+def _workload(cid):
+    return C.ALL[cid] if cid in C.ALL else EXTRA[cid]
+
+
+def _sampler(cid, steps, mode):
+    w = _workload(cid)
+    if cid == 2:      # every layer of a middle and the last step
+        return Sampler(steps_all_layers=(steps // 2 - 1, steps - 1))
+    if cid == 4:      # the cold start, the last call, two in between, the first in-place calls
+        calls = [(0, 0), (steps - 1, w.n_layers - 1)]
+        if mode == "fused":
+            calls += [(5, 7), (steps // 2, 11)]
+        return Sampler(calls=calls, first_inplace=1 if mode == "fused" else 0)
+    if cid == 5:      # in-place calls, and the calls around the budget shrink when crossed
+        after = ()
+        if steps > w.shrink_step:
+            s0 = w.shrink_step
+            after = [(s0 - 1, w.n_layers - 1), (s0, 0), (s0, w.n_layers // 2), (steps - 1, w.n_layers - 1)]
+        return Sampler(calls=[(steps - 1, w.n_layers - 1)], first_inplace=2, after_rebuild=after)
+    return Sampler(calls=[(0, 0), (0, 1), (steps // 2, 2), (steps - 1, w.n_layers - 1)],
+                   first_inplace=2)
+
+
+CASES = [
+    # (workload, steps, tick base)
+    (2, 64, 0), (4, 24, 0), (5, 24, 0), (6, 40, 0), (7, 40, 0), (8, 40, 0), (9, 40, 0),
+    (2, 16, WIDE_TICK), (9, 40, WIDE_TICK), (4, 8, WIDE_TICK),
+]
+
+
+def _run_decode_trace(cid, steps, mode, tick0):
     import torch
+    import moe_expert_layer_02_amd as m
     from workloads import gpu as wg
-    w = C.ALL[cid] if cid in C.ALL else EXTRA[cid]
-    say(f"decode_layer trace {w.name} ({mode}): {steps} steps")
+    w = _workload(cid)
+    say(f"decode_layer trace {w.name} ({mode}): {steps} steps, tick base {tick0}")
     trace = tr.DecodeTrace(w, steps)
     pool = wg.make_pool(w, pack=packer(desc_of(w)))
-    run = LayerRunner(w, w.n_slots, pool, mode)
+    run = LayerRunner(w, w.n_slots, pool, mode, tick0=tick0)
     sim = ocache.CacheSim(w.n_slots, w.n_layers, w.n_experts)
-    src = BlobSource(w)
+    sampler = _sampler(cid, steps, mode)
     for s in range(steps):
+        if s == w.shrink_step:
+            torch.cuda.synchronize()
+            run.rebuild(w.shrink_slots)
+            sim = sim.rebuild(w.shrink_slots)
+            say(f"{w.name}: budget shrunk to {w.shrink_slots} slots at step {s}")
         xs = _xs(w, s)
         run.stage(s, trace.logits[s], xs)
         run.step()
         torch.cuda.synchronize()
-        for l in range(w.n_layers):
-            rid, rw = oroute.route(trace.logits[s, l], w.top_k, w.route, w.n_group, w.topk_group,
-                                   w.route_scale)
-            exp = sim.classify_evict(l, s * w.n_layers + l + 1, rid, run.K, w.q_num, w.q_den)
-            got = run.lists[l].host()
-            assert got["counts"] == exp["counts"], (s, l, got["counts"], exp["counts"])
-            for key in ("uniq", "hit_expert", "hit_slot", "miss", "fill_expert", "fill_slot",
-                        "inplace", "victims"):
-                assert got[key] == exp[key], (s, l, key)
-            assert np.array_equal(run.ids[l].cpu().numpy(), rid)
-            if (s, l) in sample:
-                toks = list(range(min(2, w.t_decode)))
-                want = offn.moe_layer(tr.x_as_f32(tr.decode_x(w, s, l)), rid, rw,
-                                      lambda e: src(l, e), w.wfmt, w.hidden, w.inter, tokens=toks)
-                check_close(run.out[l].cpu().numpy()[toks], want, f"{w.name} call ({s},{l})")
-    assert np.array_equal(run.cache.table.cpu().numpy(), sim.table)
-    assert np.array_equal(run.cache.ts.cpu().numpy(), sim.ts)
-    S = run.S
-    owner = run.cache.owner.cpu().numpy()
-    data, pv = run.cache.data.view(-1, S), pool.view(-1, S)
-    occ = np.nonzero(owner >= 0)[0]
-    for i in range(0, len(occ), 64):
-        sl = torch.from_numpy(occ[i:i + 64]).cuda()
-        ow = torch.from_numpy(owner[occ[i:i + 64]].astype(np.int64)).cuda()
-        assert torch.equal(data.index_select(0, sl), pv.index_select(0, ow)), "slot bytes differ"
-    say(f"{w.name}: {steps * w.n_layers} calls bit-exact, {len(occ)} slots hold their pool bytes")
+        m.check_error(run.ws, what=f"{w.name} step {s}")
+        routed = _check_ints(run, sim, s, w, trace.logits[s])
+        sampler.take(run, s, routed)
+        if s % 64 == 63:
+            say(f"{w.name}: step {s + 1}/{steps}")
+    n_occ = _check_cache_state(run, sim, pool)
+    say(f"{w.name}: {steps * w.n_layers} calls bit-exact, {n_occ} slots hold their pool bytes")
+    sampler.verify(w, BlobSource(w), f"{w.name} ({mode})")
+
+
+@pytest.mark.parametrize("mode", ["fused", "split"])
+@pytest.mark.parametrize("cid,steps,tick0", CASES)
+def test_decode_layer_trace(cid, steps, tick0, mode):
+    _run_decode_trace(cid, steps, mode, tick0)
+
+
+@pytest.mark.timeout(900)
+def test_decode_layer_stress_across_budget_shrink():
+    """The stress workload's decode trace through its budget shrink (1024 -> 384
+    slots at step 256) with the fused layer calls: every call bit-exact, the
+    calls right before and after the shrink checked on every token."""
+    w = C.DS_STRESS
+    _run_decode_trace(5, w.shrink_step + 6, "fused", 0)
 
 
 def test_decode_layer_workspace_header_left_zero():
@@ -172,6 +297,7 @@ def test_decode_layer_workspace_header_left_zero():
         runs.append((w, run, tr.DecodeTrace(w, 6), BlobSource(w)))
     for _, run, _, _ in runs:
         run.ws = ws_
+    log = ParityLog("shared workspace")
     for s in range(6):
         for w, run, trace, src in runs:
             xs = _xs(w, s)
@@ -179,19 +305,25 @@ def test_decode_layer_workspace_header_left_zero():
             run.step()
             torch.cuda.synchronize()
             assert int(ws_[:65536].count_nonzero()) == 0, (w.name, s)
-            if s in (0, 5):
-                l = s % w.n_layers
-                rid, rw = oroute.route(trace.logits[s, l], w.top_k, w.route, w.n_group,
-                                       w.topk_group, w.route_scale)
-                want = offn.moe_layer(tr.x_as_f32(tr.decode_x(w, s, l)), rid, rw,
-                                      lambda e: src(l, e), w.wfmt, w.hidden, w.inter)
-                check_close(run.out[l].cpu().numpy(), want, f"{w.name} shared workspace ({s},{l})")
+            l = s % w.n_layers
+            rid, rw = oroute.route(trace.logits[s, l], w.top_k, w.route, w.n_group,
+                                   w.topk_group, w.route_scale)
+            want = oracle_layer(tr.x_as_f32(tr.decode_x(w, s, l)), rid, rw,
+                                lambda e: src(l, e), w.wfmt, w.hidden, w.inter)
+            log.check(run.out[l].cpu().numpy(), want, f"{w.name} ({s},{l})")
+    log.report()
     say("workspace header zero after every step, two shapes sharing it")
 
 
 @pytest.mark.parametrize("mode", ["fused", "split"])
-def test_decode_step_graph_replay_matches_eager(mode):
+def test_decode_step_graph_replay_matches_oracle(mode):
+    """A whole Qwen-like decode step (40 layer calls, a device-resident tick)
+    captured once and replayed over six steps of the trace, with the inputs
+    staged eagerly between replays: every replay's lists bit-exact against the
+    simulator, ids against the oracle's routing, four layers' outputs per step
+    against the oracle, and the final cache state and slot bytes."""
     import torch
+    import moe_expert_layer_02_amd as m
     from workloads import gpu as wg
     w = C.QWEN_DECODE
     steps = 6
@@ -204,7 +336,6 @@ def test_decode_step_graph_replay_matches_eager(mode):
     warm.step()
     torch.cuda.synchronize()
     del warm
-    eager = LayerRunner(w, w.n_slots, pool, mode)
     graphed = LayerRunner(w, w.n_slots, pool, mode)
     graphed.stage(0, trace.logits[0], _xs(w, 0))
     torch.cuda.synchronize()
@@ -216,17 +347,15 @@ def test_decode_step_graph_replay_matches_eager(mode):
     # capturing records the launches without running them
     for a, b in zip(snap, (graphed.cache.table, graphed.cache.owner, graphed.cache.ts)):
         assert torch.equal(a, b)
+    sim = ocache.CacheSim(w.n_slots, w.n_layers, w.n_experts)
+    sampler = Sampler(calls=[(s, l) for s in range(steps) for l in (0, 13, 26, 39)])
     for s in range(steps):
-        xs = _xs(w, s)
-        eager.stage(s, trace.logits[s], xs)
-        eager.step()
-        torch.cuda.synchronize()
-        graphed.stage(s, trace.logits[s], xs)
+        graphed.stage(s, trace.logits[s], _xs(w, s))
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(eager.ids, graphed.ids), s
-        # the combine adds a token's k contributions with atomics in no fixed order
-        torch.testing.assert_close(graphed.out, eager.out, rtol=1e-6, atol=1e-5)
-        assert torch.equal(eager.cache.table, graphed.cache.table), s
-        assert torch.equal(eager.cache.ts, graphed.cache.ts), s
-        say(f"graph replay {s} ({mode}) matches eager")
+        m.check_error(graphed.ws, what=f"replay {s}")
+        routed = _check_ints(graphed, sim, s, w, trace.logits[s])
+        sampler.take(graphed, s, routed)
+        say(f"graph replay {s} ({mode}): {w.n_layers} calls bit-exact against the simulator")
+    _check_cache_state(graphed, sim, pool)
+    sampler.verify(w, BlobSource(w), f"graph replay ({mode})")

@@ -12,7 +12,7 @@ from workloads import configs as C
 from workloads import experts as wx
 from workloads import traces as tr
 
-from gpu_common import BlobSource, check_close, desc_of, packer, say
+from gpu_common import BlobSource, check_close, desc_of, oracle_layer, packer, say
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +48,7 @@ def test_permute_matches_oracle(E, k, T):
     assert np.array_equal(perm, rperm)
 
 
-def _prefill(w, x_bits, ids_np, wt_np, layer_seed):
+def _prefill(w, x_bits, ids_np, wt_np, layer_seed, with_err=False):
     import torch
     import moe_expert_layer_02_amd as m
     from workloads import gpu as wg
@@ -67,6 +67,9 @@ def _prefill(w, x_bits, ids_np, wt_np, layer_seed):
     ws = torch.empty(m.workspace_bytes(desc, T, m.MODE_PREFILL), dtype=torch.uint8, device="cuda")
     m.expert_ffn_prefill(desc, x, ids, wt, layer, perm, offsets, out, ws)
     torch.cuda.synchronize()
+    if with_err:
+        return out, m.error_word(ws, m.MODE_PREFILL)
+    assert m.error_word(ws, m.MODE_PREFILL) == 0
     return out
 
 
@@ -97,8 +100,27 @@ def test_prefill_small_shapes(H, I, E, k, T, wfmt):
     check_close(out, want, f"prefill H={H} I={I} fmt={wfmt}")
 
 
-@pytest.mark.parametrize("cid,n_tokens", [(3, 24), (5, 8)])
-def test_prefill_full_size_sampled(cid, n_tokens):
+def _tile_row_tokens(ids_np, E, k, experts, rows_in_tile):
+    """Tokens whose pairs sit at the given rows of 128-row tiles of each listed
+    expert's bucket (plus the bucket's last row), from the oracle's permutation."""
+    perm, offsets = offn.permute(ids_np, E)
+    toks = set()
+    for e in experts:
+        b, n = int(offsets[e]), int(offsets[e + 1] - offsets[e])
+        for r in sorted({t0 + r for t0 in range(0, n, 128) for r in rows_in_tile} | {n - 1}):
+            if 0 <= r < n:
+                toks.add(int(perm[b + r]) // k)
+    return np.array(sorted(toks))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cid", [3, 5])
+def test_prefill_full_size_sampled(cid):
+    """The full-size prefill layers, every output checked for finiteness and the
+    error word clear, and many tokens checked against the oracle: for the
+    Qwen-like layer the tokens at the first, middle and last row of every
+    128-row tile of every expert's bucket (and each bucket's last row); for the
+    DS-like layer the first and last row of every tile of every eighth expert."""
     import torch
     import moe_expert_layer_02_amd as m
     w = C.ALL[cid]
@@ -117,15 +139,22 @@ def test_prefill_full_size_sampled(cid, n_tokens):
     counts = np.bincount(ids_np.ravel(), minlength=w.n_experts)
     say(f"tokens per expert: min {counts.min()} max {counts.max()}")
     assert counts.min() > 0
-    out = _prefill(w, x_bits, ids_np, wt_np, C.seed(w.cid, 0))
+    out, err = _prefill(w, x_bits, ids_np, wt_np, C.seed(w.cid, 0), with_err=True)
+    assert err == 0, f"error word {err:#x}"
     got = out.cpu().numpy()
     assert np.all(np.isfinite(got))
-    rng = np.random.default_rng(cid)
-    toks = np.sort(rng.choice(T, size=n_tokens, replace=False))
-    toks[0], toks[-1] = 0, T - 1
+    experts = range(w.n_experts) if cid == 3 else range(0, w.n_experts, 8)
+    rows = (0, 63, 64, 127) if cid == 3 else (0, 127)
+    toks = _tile_row_tokens(ids_np, w.n_experts, w.top_k, experts, rows)
+    toks = np.union1d(toks, [0, T - 1])
+    hit = np.unique(ids_np[toks])
+    say(f"{len(toks)} tokens checked, covering {len(hit)} experts")
+    assert len(toks) >= (512 if cid == 3 else 64)
+    if cid == 3:
+        assert len(hit) == w.n_experts
     src = BlobSource(w)
     rid, rw = oroute.route(logits[toks], w.top_k, w.route, w.n_group, w.topk_group, w.route_scale)
     assert np.array_equal(rid, ids_np[toks])
-    want = offn.moe_layer(tr.x_as_f32(x_bits[toks]), rid, rw, lambda e: src(0, e), w.wfmt,
-                          w.hidden, w.inter)
-    check_close(got[toks], want, f"{w.name} sampled tokens")
+    want = oracle_layer(tr.x_as_f32(x_bits[toks]), rid, rw, lambda e: src(0, e), w.wfmt,
+                        w.hidden, w.inter)
+    check_close(got[toks], want, f"{w.name} {len(toks)} tokens")

@@ -183,3 +183,17 @@ def test_permute_brute_force():
     assert offsets[0] == 0 and offsets[-1] == T * k
     for e in range(E):
         assert offsets[e + 1] - offsets[e] == int((ids == e).sum())
+
+
+def test_combine_hand_example():
+    """Two tokens, three slots, small integers: every product and sum is exact."""
+    y = np.array([[[1.0, 2.0], [10.0, 20.0], [100.0, 200.0]],
+                  [[-1.0, 0.5], [4.0, -8.0], [0.0, 3.0]]])
+    w = np.array([[0.5, 0.25, 0.125], [2.0, 0.0, 1.0]])
+    out = ffn.combine(y, w)
+    assert out.tolist() == [[0.5 + 2.5 + 12.5, 1.0 + 5.0 + 25.0], [-2.0, 1.0 + 3.0]]
+    # one slot with weight 1 is the identity; a zero weight drops its slot
+    assert np.array_equal(ffn.combine(y[:, :1], np.ones((2, 1))), y[:, 0])
+    w2 = w.copy()
+    w2[:, 1] = 0.0
+    assert np.array_equal(ffn.combine(y, w2), ffn.combine(y[:, [0, 2]], w[:, [0, 2]]))
