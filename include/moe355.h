@@ -359,6 +359,31 @@ moe355_status moe355_decode_layer(const moe355_layer_desc* d, const moe355_cache
                                   size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe355_decode_layer without a workspace, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments and results as moe355_decode_layer, minus
+ * ws / ws_bytes: the call's synchronisation words and h live in a fixed scratch
+ * array inside the library, one per GPU, held until the process ends
+ * (64 KiB + 4 MiB: T*k*I <= 2^20, which every shape the decode kernels take
+ * meets -- T*k <= 256, I <= 4096; else MOE355_ECAPACITY before anything is
+ * enqueued).  Nothing is allocated: the first call on a device looks the
+ * array's address up and clears its synchronisation words with a kernel on
+ * `stream`; every call leaves them zero again.
+ * err_word: device uint32 owned by the caller, which the call ORs its error
+ * bits into (see "Error words"; the same bits the workspace's error word
+ * would get).  Every call on one GPU shares that GPU's scratch: calls that
+ * overlap on one GPU (other streams, other host threads) race and must be
+ * ordered by the caller.
+ */
+moe355_status moe355_decode_layer_static(const moe355_layer_desc* d, const moe355_cache* c,
+                                         const uint8_t* pool, int32_t layer,
+                                         const int64_t* tick_base, int64_t tick_add,
+                                         const float* logits, const void* x_bf16, int32_t T,
+                                         const moe355_evict_policy* p, int32_t* topk_ids,
+                                         float* topk_w, moe355_classify_out* lists, float* out,
+                                         uint32_t* err_word, hipStream_t stream);
+
+/*
  * The same layer call with the cache bookkeeping off the critical path
  * [FT-zh, Core method: VRAM only changes speed, never results; FT-zh, Method
  * steps: the filled experts are batch-copied into their victim slots].  Three

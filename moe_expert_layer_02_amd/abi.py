@@ -70,6 +70,9 @@ _SIGS = {
     "moe355_decode_layer": (c_i32, [_P(LayerDesc), _P(Cache), c_ptr, c_i32, c_ptr, c_i64, c_ptr,
                                     c_ptr, c_i32, _P(EvictPolicy), c_ptr, c_ptr, _P(ClassifyOut),
                                     c_ptr, c_ptr, ctypes.c_size_t, c_ptr]),
+    "moe355_decode_layer_static": (c_i32, [_P(LayerDesc), _P(Cache), c_ptr, c_i32, c_ptr, c_i64,
+                                           c_ptr, c_ptr, c_i32, _P(EvictPolicy), c_ptr, c_ptr,
+                                           _P(ClassifyOut), c_ptr, c_ptr, c_ptr]),
     "moe355_route_plan": (c_i32, [_P(LayerDesc), _P(Cache), c_i32, c_ptr, c_i32, c_ptr, c_ptr,
                                   _P(ClassifyOut), c_ptr]),
     "moe355_evict_fill": (c_i32, [_P(LayerDesc), _P(Cache), c_ptr, c_i32, c_ptr, c_i64, c_ptr, c_i32,

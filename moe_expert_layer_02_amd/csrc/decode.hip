@@ -430,15 +430,14 @@ __device__ __forceinline__ void signal_done(uint32_t* sync, uint32_t n_gu, uint3
 }
 
 // Until copy `b % 64` of flag f is up (bounded; thread 0 polls, the block then meets).
-__device__ __forceinline__ void wait_flag(uint32_t* sync, int f, uint32_t b) {
+__device__ __forceinline__ void wait_flag(uint32_t* sync, int f, uint32_t b, uint32_t* err) {
     if (threadIdx.x == 0) {
         const uint32_t* word = sync_word(sync, f + static_cast<int>(b & 63));
         uint32_t n = 0;
         while (__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
             __builtin_amdgcn_s_sleep(2);
             if (++n == SPIN_LIMIT) {
-                __hip_atomic_fetch_or(sync_word(sync, SW_ERR), ERR_WAIT, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_or(err, ERR_WAIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
         }
@@ -449,7 +448,7 @@ __device__ __forceinline__ void wait_flag(uint32_t* sync, int f, uint32_t b) {
 // Whole-layer launch: until the plan flag (copy b % 64) is up, also noting
 // whether the victims flag already was (then the plan about to be staged is
 // final and names every fill).
-__device__ __forceinline__ void wait_plan(uint32_t* sync, uint32_t b, PlanLds& pl) {
+__device__ __forceinline__ void wait_plan(uint32_t* sync, uint32_t b, PlanLds& pl, uint32_t* err) {
     if (threadIdx.x == 0) {
         const uint32_t* pw = sync_word(sync, FL_PLAN + static_cast<int>(b & 63));
         const uint32_t* vw = sync_word(sync, FL_VICT + static_cast<int>(b & 63));
@@ -459,8 +458,7 @@ __device__ __forceinline__ void wait_plan(uint32_t* sync, uint32_t b, PlanLds& p
             if (__hip_atomic_load(pw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
             __builtin_amdgcn_s_sleep(2);
             if (++n == SPIN_LIMIT) {
-                __hip_atomic_fetch_or(sync_word(sync, SW_ERR), ERR_WAIT, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_or(err, ERR_WAIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
         }
@@ -573,8 +571,7 @@ __device__ __forceinline__ void wait_plan_record(uint32_t* sync, uint32_t b, con
             __builtin_amdgcn_s_sleep(2);
             if (++n == SPIN_LIMIT) {
                 if (t == 0)
-                    __hip_atomic_fetch_or(sync_word(sync, SW_ERR), ERR_WAIT, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_fetch_or(p.err, ERR_WAIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
         }
@@ -610,7 +607,7 @@ __device__ __forceinline__ void wait_plan_record(uint32_t* sync, uint32_t b, con
 __device__ __forceinline__ void refresh_for_fills(const DecodeParams& p, PlanLds& pl,
                                                   uint32_t* sync, bool need) {
     if (!need) return;
-    wait_flag(sync, FL_VICT, blockIdx.x);
+    wait_flag(sync, FL_VICT, blockIdx.x, p.err);
     if (threadIdx.x < p.n_plan) {
         const uint4 r = ld_dev16(p.plan + 4 * threadIdx.x);
         pl.plan[threadIdx.x] = make_int4(static_cast<int>(r.x), static_cast<int>(r.y),
@@ -1312,7 +1309,7 @@ __device__ __forceinline__ void down_rows_body(const DecodeParams& p, PlanLds& p
                 if (pl.tok[pr.z + n] == ln) hoff[i] = (pl.pairs[pr.z + n] * I + sl * SLAB + 32 * gq) / 4;
         }
     }
-    wait_flag(sync, FL_DONE, blockIdx.x);
+    wait_flag(sync, FL_DONE, blockIdx.x, p.err);
     const uint32_t exit_old = exit_begin(sync);   // no sync word is read after this wait
     // h pieces: [pair][I / 4] x 16 bytes (four hi halves, then four lo halves)
     const int nc = p.T * p.k * I / 4;
@@ -1549,7 +1546,7 @@ __global__ void __launch_bounds__(NW * WAVE, 4) layer_small_kernel(DecodeParams 
         if (plan_record(cp)) {
             wait_plan_record(sync, blockIdx.x, p, pl);
         } else {
-            wait_plan(sync, blockIdx.x, pl);
+            wait_plan(sync, blockIdx.x, pl, p.err);
             stage_plan_dev(p, pl);
         }
         // with the fills already in the staged plan, the FFN writes them the
@@ -1676,7 +1673,8 @@ moe355_status decode_params(const moe355_layer_desc* d, const void* x_bf16, int3
                             const int32_t* topk_ids, const float* topk_w,
                             const moe355_cache* cache, const uint8_t* pool, int32_t layer,
                             const moe355_classify_out* exp, bool fill_through, float* out,
-                            void* ws, size_t ws_bytes, DecodeParams* pp, int* max_uniq_out) {
+                            void* ws, size_t ws_bytes, DecodeParams* pp, int* max_uniq_out,
+                            uint32_t* err) {
     MOE355_REQUIRE(T >= 0 && T * d->top_k <= 256, MOE355_ENOTSUP,
                    "expert_ffn_decode: T*k=%d outside [0, 256]", T * d->top_k);
     MOE355_REQUIRE(valid_row_len(d->hidden) && valid_row_len(d->inter), MOE355_ENOTSUP,
@@ -1713,7 +1711,7 @@ moe355_status decode_params(const moe355_layer_desc* d, const void* x_bf16, int3
     p.h_hi = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + SYNC_BYTES);
     p.h_lo = p.h_hi + tkI;
     p.out = out;
-    p.err = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + 256 * SW_ERR);
+    p.err = err ? err : reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + 256 * SW_ERR);
     if (cache) {
         MOE355_REQUIRE(cache->slot_table && cache->slot_data && cache->slot_bytes == L.bytes &&
                            cache->n_experts == d->n_experts && layer >= 0 &&
@@ -1760,12 +1758,13 @@ moe355_status decode_layer_small(const moe355_layer_desc* d, const moe355_cache*
                                  const void* x_bf16, int32_t T, const int32_t* topk_ids,
                                  const float* topk_w, const moe355_classify_out* lists,
                                  const moe355_evict_policy* pol, float* out, void* ws,
-                                 size_t ws_bytes, hipStream_t stream, bool* launched) {
+                                 size_t ws_bytes, hipStream_t stream, bool* launched,
+                                 uint32_t* err) {
     *launched = false;
     DecodeParams p;
     int max_uniq = 0;
     const moe355_status st = decode_params(d, x_bf16, T, topk_ids, topk_w, c, pool, layer, lists,
-                                           true, out, ws, ws_bytes, &p, &max_uniq);
+                                           true, out, ws, ws_bytes, &p, &max_uniq, err);
     if (st) return st;
     // the bookkeeping workgroup's LDS limits (ClassifySmall) and the FFN's
     if (!small_fits(p, max_uniq) || cp.N > 2048 || cp.E > 256 || T * d->top_k > 128 || pol->K > 128)
@@ -1782,7 +1781,7 @@ moe355_status decode_ffn(const moe355_layer_desc* d, const void* x_bf16, int32_t
                          const int32_t* topk_ids, const float* topk_w, const moe355_cache* cache,
                          const uint8_t* pool, int32_t layer, const moe355_classify_out* exp,
                          bool fill_through, float* out, void* ws, size_t ws_bytes,
-                         hipStream_t stream) {
+                         hipStream_t stream, uint32_t* err) {
     if (T == 0) {
         MOE355_REQUIRE(T * d->top_k <= 256 && valid_row_len(d->hidden) && valid_row_len(d->inter),
                        MOE355_ENOTSUP, "expert_ffn_decode: H=%d I=%d unsupported", d->hidden,
@@ -1792,7 +1791,7 @@ moe355_status decode_ffn(const moe355_layer_desc* d, const void* x_bf16, int32_t
     DecodeParams p;
     int max_uniq = 0;
     const moe355_status st = decode_params(d, x_bf16, T, topk_ids, topk_w, cache, pool, layer, exp,
-                                           fill_through, out, ws, ws_bytes, &p, &max_uniq);
+                                           fill_through, out, ws, ws_bytes, &p, &max_uniq, err);
     if (st) return st;
     uint32_t* sync = static_cast<uint32_t*>(ws);   // the workspace's first SYNC_BYTES
     if (d->wfmt == MOE355_W_INT4_G64) return launch_decode<MOE355_W_INT4_G64>(p, max_uniq, sync, stream);

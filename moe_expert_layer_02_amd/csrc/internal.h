@@ -65,12 +65,16 @@ moe355_status decode_layer_small(const moe355_layer_desc* d, const moe355_cache*
                                  const void* x_bf16, int32_t T, const int32_t* topk_ids,
                                  const float* topk_w, const moe355_classify_out* lists,
                                  const moe355_evict_policy* pol, float* out, void* ws,
-                                 size_t ws_bytes, hipStream_t stream, bool* launched);
+                                 size_t ws_bytes, hipStream_t stream, bool* launched,
+                                 uint32_t* err = nullptr);
+// err: where the kernels record device-side failures (default: the workspace's
+// error word at MOE355_DECODE_ERR_BYTE).
 moe355_status decode_ffn(const moe355_layer_desc* d, const void* x_bf16, int32_t T,
                          const int32_t* topk_ids, const float* topk_w, const moe355_cache* cache,
                          const uint8_t* pool, int32_t layer, const moe355_classify_out* exp,
                          bool fill_through, float* out, void* ws, size_t ws_bytes,
-                         hipStream_t stream);
+                         hipStream_t stream, uint32_t* err = nullptr);
+size_t decode_ws_bytes(const moe355_layer_desc* d, int T);
 
 // ---- device helpers ---------------------------------------------------------
 constexpr int WAVE = 64;

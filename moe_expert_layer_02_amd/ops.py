@@ -229,6 +229,25 @@ def decode_layer(desc, cache: DeviceCache, pool, layer: int, tick_base, tick_add
           "moe355_decode_layer")
 
 
+def decode_layer_static(desc, cache: DeviceCache, pool, layer: int, tick_base, tick_add: int,
+                        logits, x_bf16, policy: EvictPolicy, topk_ids, topk_w,
+                        lists: DeviceClassifyOut, out, err_word, stream=None):
+    """decode_layer with the library's fixed per-GPU scratch instead of a workspace;
+    err_word: a device int32 [1] the call ORs its error bits into."""
+    _need(logits, torch.float32, "logits")
+    _need(x_bf16, torch.bfloat16, "x")
+    _need(err_word, torch.int32, "err_word")
+    if tick_base is not None:
+        _need(tick_base, torch.int64, "tick_base")
+    T = x_bf16.shape[0]
+    check(load().moe355_decode_layer_static(ctypes.byref(desc), ctypes.byref(cache.struct),
+                                            _ptr(pool), layer, _ptr(tick_base), tick_add,
+                                            _ptr(logits), _ptr(x_bf16), T, ctypes.byref(policy),
+                                            _ptr(topk_ids), _ptr(topk_w), ctypes.byref(lists.struct),
+                                            _ptr(out), _ptr(err_word), _stream(stream)),
+          "moe355_decode_layer_static")
+
+
 def route_plan(desc, cache: DeviceCache, layer: int, logits, topk_ids, topk_w,
                lists: DeviceClassifyOut, stream=None):
     """Route + dedup + hit/miss + FFN plan (hits from slots, misses from the pool)."""

@@ -145,3 +145,22 @@ def test_cache_rebuild_rejects_overlapping_caches(lib):
         st = L.moe355_cache_rebuild(ctypes.byref(good_from), ctypes.byref(to), None)
         assert st == -1, name
         assert b"overlaps" in L.moe355_last_error(), (name, L.moe355_last_error())
+
+
+def test_static_decode_layer_host_checks(lib):
+    """The allocation-free layer call rejects, before touching any device, a
+    call whose h would not fit its fixed scratch and a missing error word."""
+    from moe_expert_layer_02_amd import abi
+    L = abi.load()
+    d = abi.LayerDesc(4096, 8192, 256, 8, 0, 1, 1, 1.0, 0)          # T*k*I = 32 * 8 * 8192 > 2^20
+    c = abi.Cache(64, 2, 256, 1, 1 << 40, 1 << 41, 1 << 42, 1 << 43)
+    pol = abi.EvictPolicy(8, 1, 1)
+    out = abi.ClassifyOut()
+    st = L.moe355_decode_layer_static(ctypes.byref(d), ctypes.byref(c), 1 << 44, 0, None, 1,
+                                      1 << 45, 1 << 46, 32, ctypes.byref(pol), 1 << 47, 1 << 47,
+                                      ctypes.byref(out), 1 << 47, 1 << 47, None)
+    assert st == -4 and b"scratch" in L.moe355_last_error()
+    st = L.moe355_decode_layer_static(ctypes.byref(d), ctypes.byref(c), 1 << 44, 0, None, 1,
+                                      1 << 45, 1 << 46, 1, ctypes.byref(pol), 1 << 47, 1 << 47,
+                                      ctypes.byref(out), 1 << 47, None, None)
+    assert st == -1 and b"error word" in L.moe355_last_error()
