@@ -47,23 +47,24 @@ def cpu_baseline_decode(w, trace, n_calls: int, budget_s: float):
     from workloads import traces as tr
     S = wx.expert_bytes(w.wfmt, w.hidden, w.inter)
     calls = [(s, l) for s in range(trace.steps) for l in range(w.n_layers)][:n_calls]
-    prepared = []
-    for s, l in calls:   # input generation is not timed
+    nbytes = 0
+    done = 0
+    dt = 0.0
+    for s, l in calls:
+        # inputs of one call (not timed), generated call by call: a DS-like call's
+        # experts alone are about 0.75 GB
         ids, wt = oroute.route(trace.logits[s, l], w.top_k, w.route, w.n_group, w.topk_group,
                                w.route_scale)
         blobs = {int(e): wx.expert_blob(C.seed(w.cid, 0), l * w.n_experts + int(e), w.wfmt,
                                         w.hidden, w.inter) for e in np.unique(ids)}
-        prepared.append((tr.x_as_f32(tr.decode_x(w, s, l)), ids, wt, blobs))
-    nbytes = 0
-    done = 0
-    t0 = time.perf_counter()
-    for x, ids, wt, blobs in prepared:
+        x = tr.x_as_f32(tr.decode_x(w, s, l))
+        t0 = time.perf_counter()
         offn.moe_layer(x, ids, wt, blobs.__getitem__, w.wfmt, w.hidden, w.inter, dtype=np.float32)
+        dt += time.perf_counter() - t0
         nbytes += len(blobs) * S
         done += 1
-        if time.perf_counter() - t0 > budget_s:
+        if dt > budget_s:
             break
-    dt = time.perf_counter() - t0
     try:
         from threadpoolctl import threadpool_info
         cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
@@ -305,13 +306,14 @@ def ffn_kernel_label(w, T):
 MFMA_PEAK_BF16_TFLOPS = 2500.0
 
 
-def cpu_baseline_prefill(w, x_bits, ids, wt, budget_s: float):
-    """The oracle (fp32, NumPy BLAS) on a bounded sample of the prefill layer's tokens."""
+def cpu_baseline_prefill(w, x_bits, ids, wt, budget_s: float, n_tok: int = 0):
+    """The oracle (fp32, NumPy BLAS) on the prefill layer: every token when
+    n_tok is 0, else the first n_tok tokens."""
     from oracle import ffn as offn
     from workloads import configs as C
     from workloads import experts as wx
     from workloads import traces as tr
-    n_tok = 256
+    n_tok = n_tok or w.t_prefill
     toks = np.arange(n_tok)
     blobs = {int(e): wx.expert_blob(C.seed(w.cid, 0), int(e), w.wfmt, w.hidden, w.inter)
              for e in np.unique(ids[toks])}
@@ -327,8 +329,9 @@ def cpu_baseline_prefill(w, x_bits, ids, wt, budget_s: float):
         cores = os.cpu_count() or 1
     return {"value": round(n_tok / dt, 2), "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"first {n_tok} of {w.t_prefill} tokens, fp32 NumPy dequant of their "
-                      f"{len(blobs)} experts + GEMMs + combine, {dt:.1f} s"}
+            "sample": (f"the whole layer ({n_tok} tokens)" if n_tok == w.t_prefill else
+                       f"first {n_tok} of {w.t_prefill} tokens") +
+                      f", fp32 NumPy dequant of {len(blobs)} experts + GEMMs + combine, {dt:.1f} s"}
 
 
 def bench_prefill(args, w):
@@ -401,8 +404,11 @@ def bench_prefill(args, w):
     }
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
+        # the whole Qwen-like layer finishes in seconds on the host; the DS-like one
+        # takes minutes, so it is timed on its first 512 tokens
+        n_tok = 0 if w.t_prefill * w.hidden * w.inter <= 8192 * 2048 * 512 else 512
         res["cpu_baseline"] = cpu_baseline_prefill(w, x_bits, ids.cpu().numpy(), wt.cpu().numpy(),
-                                                   args.cpu_budget)
+                                                   args.cpu_budget, n_tok)
     return res
 
 
@@ -458,6 +464,9 @@ def main():
     ap.add_argument("--order", default="auto", choices=["auto", "fused", "split"],
                     help="decode layer call order (auto: fused)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="print the selected workload alone (the default Qwen-like decode line "
+                         "also carries Qwen-like prefill and DS-like decode sub-records)")
     ap.add_argument("--cpu-calls", type=int, default=160)
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
@@ -476,6 +485,15 @@ def main():
     w = {"qwen_decode": C.QWEN_DECODE, "ds_decode": C.DS_DECODE, "qwen_prefill": C.QWEN_PREFILL,
          "ds_prefill": C.DS_STRESS}[args.workload]
     res = bench_prefill(args, w) if args.workload.endswith("prefill") else bench_decode(args, w)
+    if args.workload == "qwen_decode" and not args.no_sub:
+        # the same step definition, timing and roofline rules on two more workloads
+        import torch
+        res["sub_records"] = []
+        for name, fn, sw in (("qwen_prefill", bench_prefill, C.QWEN_PREFILL),
+                             ("ds_decode", bench_decode, C.DS_DECODE)):
+            torch.cuda.empty_cache()
+            print(f"bench: sub-record {name}", file=sys.stderr, flush=True)
+            res["sub_records"].append(fn(args, sw))
     print(json.dumps(res), flush=True)
 
 

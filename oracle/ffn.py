@@ -19,7 +19,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import dequant_expert
+from .formats import MXFP4, dequant_expert, mx_round_trip
 
 
 def silu(z: np.ndarray) -> np.ndarray:
@@ -69,6 +69,37 @@ def combine(y: np.ndarray, w: np.ndarray) -> np.ndarray:
     for j in range(y.shape[1]):
         out += w[:, j][:, None] * y[:, j]
     return out
+
+
+def moe_layer_mx8(x: np.ndarray, ids: np.ndarray, w: np.ndarray, expert_blob, H: int, I: int,
+                  tokens=None) -> np.ndarray:
+    """The layer over MXFP4 experts with MX FP8 E4M3 activations (OCP
+    Microscaling v1.0), the operand pair of the native fp4 matrix-core path.
+
+    Each token's x is quantised in blocks of 32 along H.  h = silu(g) * u is
+    carried into the down projection as two MX terms, h1 = MX(h) and
+    h2 = MX(h - h1), each quantised per routed pair in blocks of 32 along I:
+    y = W_d (h1 + h2).  Float64 otherwise.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ids = np.asarray(ids)
+    w = np.asarray(w, dtype=np.float64)
+    T, k = ids.shape
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    row_of = {int(t): r for r, t in enumerate(tokens)}
+    xq = mx_round_trip(x[tokens])
+    y = np.zeros((len(tokens), k, H))
+    for e in sorted({int(v) for v in ids[tokens].ravel()}):
+        wg, wu, wd = dequant_expert(expert_blob(e), MXFP4, H, I)
+        pairs = [(t, j) for t in tokens for j in range(k) if ids[t, j] == e]
+        rows = np.array([row_of[int(t)] for t, _ in pairs])
+        h = silu(xq[rows] @ wg.T) * (xq[rows] @ wu.T)
+        h1 = mx_round_trip(h)
+        h2 = mx_round_trip(h - h1)
+        ye = (h1 + h2) @ wd.T
+        for (t, j), yrow in zip(pairs, ye):
+            y[row_of[int(t)], j] = yrow
+    return combine(y, w[tokens])
 
 
 def permute(ids: np.ndarray, n_experts: int):

@@ -90,3 +90,80 @@ def dequant_expert(blob: np.ndarray, wfmt: int, H: int, I: int):
             raise ValueError(wfmt)
     assert off == blob.size
     return tuple(mats)
+
+
+# ---- MX activation quantisation (OCP Microscaling Formats v1.0) -------------
+# An MX block is 32 consecutive elements sharing one e8m0 scale X = 2**e; each
+# element is stored in a narrow format after division by X.  For FP8 E4M3 (one
+# sign bit, four exponent bits with bias 7, three mantissa bits; largest normal
+# 1.75 * 2**8 = 448, no infinities) the shared exponent is
+# e = floor(log2(max |v|)) - 8 (8 = the format's largest power of two), kept in
+# e8m0's range [-127, 127]; elements are rounded to nearest (ties to even) and
+# values beyond 448 saturate to 448.  A block of zeros takes e = -127.  This
+# build stores every zero element as +0 (code 0x00).
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one FP8 E4M3 code (0x7F and 0xFF are NaN)."""
+    s, e, m = code >> 7, (code >> 3) & 0xF, code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    mag = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return -mag if s else mag
+
+
+def mx_shared_exponent(amax: np.ndarray) -> np.ndarray:
+    """e = floor(log2(amax)) - 8 clamped to [-127, 127]; -127 for amax = 0."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))      # amax = f * 2**ex, f in [0.5, 1)
+    e = (ex - 1) - 8
+    return np.where(amax > 0, np.clip(e, -127, 127), -127).astype(np.int64)
+
+
+def e4m3_round(v: np.ndarray) -> np.ndarray:
+    """Round to the nearest E4M3 value (ties to even), saturating at +-448."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    step = np.ldexp(1.0, np.maximum(ex - 1, -6) - 3)     # subnormals share 2**-9
+    q = np.round(a / step) * step                         # numpy rounds halves to even
+    return np.where(v < 0, -q, q) + 0.0                   # -0 becomes +0
+
+
+def e4m3_encode(q: np.ndarray) -> np.ndarray:
+    """Codes of values already on the E4M3 grid (|q| <= 448); zero is 0x00."""
+    q = np.asarray(q, dtype=np.float64)
+    a = np.abs(q)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    E = ex - 1
+    normal = a >= 2.0 ** -6
+    m = np.where(normal, np.ldexp(a, -E) * 8 - 8, a / 2.0 ** -9)
+    e = np.where(normal, E + 7, 0)
+    code = (e.astype(np.int64) << 3) | m.astype(np.int64)
+    code = np.where(q < 0, code | 0x80, code)
+    return np.where(a == 0, 0, code).astype(np.uint8)
+
+
+def mx_quantize(v: np.ndarray, block: int = 32):
+    """MX FP8 E4M3 quantisation along the last axis: (codes uint8 [..., n],
+    scale bytes uint8 [..., n / 32] holding e + 127)."""
+    v = np.asarray(v, dtype=np.float64)
+    blocks = v.reshape(v.shape[:-1] + (v.shape[-1] // block, block))
+    e = mx_shared_exponent(np.abs(blocks).max(axis=-1))
+    q = e4m3_round(np.ldexp(blocks, -e[..., None]))
+    return e4m3_encode(q).reshape(v.shape), (e + 127).astype(np.uint8)
+
+
+def mx_dequantize(codes: np.ndarray, scales: np.ndarray, block: int = 32) -> np.ndarray:
+    """Values of MX FP8 E4M3 data: code value * 2**(scale byte - 127)."""
+    table = np.array([e4m3_value(c) for c in range(256)])
+    vals = table[np.asarray(codes)]
+    e = np.asarray(scales).astype(np.int64) - 127
+    return np.ldexp(vals, np.repeat(e, block, axis=-1))
+
+
+def mx_round_trip(v: np.ndarray) -> np.ndarray:
+    """The MX FP8 E4M3 value each element of v is stored as."""
+    return mx_dequantize(*mx_quantize(v))
