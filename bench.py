@@ -304,11 +304,14 @@ def ffn_kernel_label(w, T):
 
 
 MFMA_PEAK_BF16_TFLOPS = 2500.0
+# dense fp8 matrix-core peak: the rate of the scaled f8f6f4 MFMA when one operand is FP8
+MFMA_PEAK_FP8_TFLOPS = 5000.0
 
 
-def cpu_baseline_prefill(w, x_bits, ids, wt, budget_s: float, n_tok: int = 0):
+def cpu_baseline_prefill(w, x_bits, ids, wt, budget_s: float, n_tok: int = 0, mx: bool = False):
     """The oracle (fp32, NumPy BLAS) on the prefill layer: every token when
-    n_tok is 0, else the first n_tok tokens."""
+    n_tok is 0, else the first n_tok tokens.  mx: the MX-activation layer
+    (float64, as the oracle defines it)."""
     from oracle import ffn as offn
     from workloads import configs as C
     from workloads import experts as wx
@@ -319,8 +322,11 @@ def cpu_baseline_prefill(w, x_bits, ids, wt, budget_s: float, n_tok: int = 0):
              for e in np.unique(ids[toks])}
     x = tr.x_as_f32(x_bits[toks])
     t0 = time.perf_counter()
-    offn.moe_layer(x, ids[toks], wt[toks], blobs.__getitem__, w.wfmt, w.hidden, w.inter,
-                   dtype=np.float32)
+    if mx:
+        offn.moe_layer_mx8(x, ids[toks], wt[toks], blobs.__getitem__, w.hidden, w.inter)
+    else:
+        offn.moe_layer(x, ids[toks], wt[toks], blobs.__getitem__, w.wfmt, w.hidden, w.inter,
+                       dtype=np.float32)
     dt = time.perf_counter() - t0
     try:
         from threadpoolctl import threadpool_info
@@ -334,7 +340,7 @@ def cpu_baseline_prefill(w, x_bits, ids, wt, budget_s: float, n_tok: int = 0):
                       f", fp32 NumPy dequant of {len(blobs)} experts + GEMMs + combine, {dt:.1f} s"}
 
 
-def bench_prefill(args, w):
+def bench_prefill(args, w, mx=False):
     import torch
     import moe_expert_layer_02_amd as m
     from workloads import experts as wx
@@ -358,7 +364,9 @@ def bench_prefill(args, w):
     perm = torch.empty(T * k, dtype=torch.int32, device=dev)
     offsets = torch.empty(w.n_experts + 1, dtype=torch.int32, device=dev)
     wsp = torch.empty(m.workspace_bytes(desc, T, m.MODE_PERMUTE), dtype=torch.uint8, device=dev)
-    ws = torch.empty(m.workspace_bytes(desc, T, m.MODE_PREFILL), dtype=torch.uint8, device=dev)
+    ws = torch.empty(m.workspace_bytes(desc, T, m.MODE_PREFILL_MX if mx else m.MODE_PREFILL),
+                     dtype=torch.uint8, device=dev)
+    ffn = m.expert_ffn_prefill_mx if mx else m.expert_ffn_prefill
     out = torch.empty((T, w.hidden), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -367,7 +375,7 @@ def bench_prefill(args, w):
         m.permute(desc, ids, perm, offsets, wsp)
         if events is not None:
             events[0].record(stream)
-        m.expert_ffn_prefill(desc, x, ids, wt, layer, perm, offsets, out, ws)
+        ffn(desc, x, ids, wt, layer, perm, offsets, out, ws)
         if events is not None:
             events[1].record(stream)
 
@@ -385,19 +393,24 @@ def bench_prefill(args, w):
     ffn_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
     flops = 6.0 * w.hidden * w.inter * T * k          # algorithmic: gate, up, down
     achieved = flops / ffn_s / 1e12
+    peak = MFMA_PEAK_FP8_TFLOPS if mx else MFMA_PEAK_BF16_TFLOPS
     res = {
         "metric": METRIC, "value": round(T * args.steps / dt, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(dt / args.steps * 1e3, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f16" if w.wfmt == 0 else "bf16",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3 x fp4e2m1 (MX)" if mx else ("f16" if w.wfmt == 0 else "bf16"),
         "data": "synthetic",
-        "config": {"workload": w.name, "tokens": T, "hidden": w.hidden, "inter": w.inter,
+        "config": {"workload": w.name + ("_mx_activations" if mx else ""), "tokens": T,
+                   "hidden": w.hidden, "inter": w.inter,
                    "experts": w.n_experts, "top_k": k,
                    "weights": "int4_g64" if w.wfmt == 0 else "mxfp4",
                    "parallelism": "single_gpu"},
-        "roofline": {"bound": "mfma", "kernel": "expert_ffn_prefill",
-                     "achieved": round(achieved, 1), "peak": MFMA_PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma",
+                     "kernel": "expert_ffn_prefill_mx (mx8_x_kernel + gate_up_mx + down_mx)" if mx
+                     else "expert_ffn_prefill",
+                     "achieved": round(achieved, 1), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic_record(f"prefill_ffn_{w.name}_traffic.md", PREFILL_SOURCES),
                      "flops_per_launch": flops,
                      "avg_launch_us": round(ffn_s * 1e6, 1)},
@@ -407,8 +420,10 @@ def bench_prefill(args, w):
         # the whole Qwen-like layer finishes in seconds on the host; the DS-like one
         # takes minutes, so it is timed on its first 512 tokens
         n_tok = 0 if w.t_prefill * w.hidden * w.inter <= 8192 * 2048 * 512 else 512
+        if mx:
+            n_tok = 128
         res["cpu_baseline"] = cpu_baseline_prefill(w, x_bits, ids.cpu().numpy(), wt.cpu().numpy(),
-                                                   args.cpu_budget, n_tok)
+                                                   args.cpu_budget, n_tok, mx=mx)
     return res
 
 
@@ -460,7 +475,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen_decode",
-                    choices=["qwen_decode", "ds_decode", "qwen_prefill", "ds_prefill"])
+                    choices=["qwen_decode", "ds_decode", "qwen_prefill", "ds_prefill",
+                             "ds_prefill_mx"])
     ap.add_argument("--order", default="auto", choices=["auto", "fused", "split"],
                     help="decode layer call order (auto: fused)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -483,8 +499,11 @@ def main():
     m.check_build()         # the library under test was built from these sources
     from workloads import configs as C
     w = {"qwen_decode": C.QWEN_DECODE, "ds_decode": C.DS_DECODE, "qwen_prefill": C.QWEN_PREFILL,
-         "ds_prefill": C.DS_STRESS}[args.workload]
-    res = bench_prefill(args, w) if args.workload.endswith("prefill") else bench_decode(args, w)
+         "ds_prefill": C.DS_STRESS, "ds_prefill_mx": C.DS_STRESS}[args.workload]
+    if "prefill" in args.workload:
+        res = bench_prefill(args, w, mx=args.workload.endswith("_mx"))
+    else:
+        res = bench_decode(args, w)
     if args.workload == "qwen_decode" and not args.no_sub:
         # the same step definition, timing and roofline rules on two more workloads
         import torch

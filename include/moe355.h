@@ -431,6 +431,43 @@ moe355_status moe355_expert_ffn_prefill(const moe355_layer_desc* d, const void* 
                                         size_t ws_bytes, hipStream_t stream);
 
 /*
+ * MX FP8 E4M3 quantisation of bf16 activations (OCP Microscaling Formats v1.0;
+ * the activation operand of moe355_expert_ffn_prefill_mx): each row of x is cut
+ * into blocks of 32; a block's shared exponent is e = floor(log2(max |x|)) - 8
+ * (clamped to [-127, 127]; -127 for a zero block), stored as the byte e + 127;
+ * each element x / 2^e is rounded to the nearest E4M3 value (ties to even),
+ * saturating at +-448, and a zero element is stored as 0x00.
+ * x: device bf16 [rows, cols]; codes: device uint8 [rows, cols]; scales: device
+ * uint8 [rows, cols / 32].  Errors: MOE355_EINVAL for rows < 0, cols not a
+ * positive multiple of 32, or null pointers when rows > 0.
+ */
+moe355_status moe355_quantize_mx(const void* x_bf16, int64_t rows, int32_t cols, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t stream);
+
+/*
+ * Prefill expert FFN for MXFP4 experts on the native fp4 matrix cores
+ * (v_mfma_scale_f32_32x32x64_f8f6f4): the e2m1 weights with their e8m0 block
+ * scales against MX FP8 E4M3 activations.  The benchmark spec asks for native fp4
+ * MFMA where the path is MXFP4; the pages' MXFP4 models are the DeepSeek-V4-Flash
+ * rows of [FT-zh, Results].  Same call shape as moe355_expert_ffn_prefill, but
+ * a different result: x is quantised as moe355_quantize_mx does (per token,
+ * blocks of 32 along H), and h = silu(gate x) * (up x) is carried into the down
+ * projection as two MX FP8 terms per routed pair (blocks of 32 along I):
+ * h1 = MX(h), h2 = MX(h - h1), y = down (h1 + h2).  The output therefore
+ * differs from the bf16 path's by the quantisation of x (about 5e-2 relative
+ * L2 at the DS-like shape); it matches the exact layer evaluated on the same
+ * quantised operands.  ws: moe355_workspace_bytes(d, T, MOE355_MODE_PREFILL_MX)
+ * bytes, the error word at MOE355_PREFILL_ERR_BYTE (cleared by each call).
+ * Limits: wfmt MOE355_W_MXFP4 (else MOE355_ENOTSUP), H a multiple of 256,
+ * I a multiple of 128, both at most 16384, E <= 1024, T*H and T*k*I < 2^32.
+ */
+moe355_status moe355_expert_ffn_prefill_mx(const moe355_layer_desc* d, const void* x_bf16,
+                                           int32_t T, const int32_t* topk_ids, const float* topk_w,
+                                           const uint8_t* layer_w, const int32_t* perm,
+                                           const int32_t* offsets, float* out, void* ws,
+                                           size_t ws_bytes, hipStream_t stream);
+
+/*
  * Unfused combine [FT-zh, Core method: the partial sums of a token's experts
  * merge into its output exactly; Edge0, section 2 "MoE routing": the output is
  * the routing-weighted sum over the selected experts]:
@@ -446,6 +483,7 @@ moe355_status moe355_combine(int32_t T, int32_t H, int32_t k, const float* y,
 #define MOE355_MODE_DECODE   0
 #define MOE355_MODE_PREFILL  1
 #define MOE355_MODE_PERMUTE  2
+#define MOE355_MODE_PREFILL_MX 3
 /* Scratch bytes a call of the given mode needs for T tokens.  No page defines
  * this call; it sizes the caller-owned workspaces above.  Returns 0 for an
  * invalid descriptor, T < 0 or an unknown mode. */

@@ -13,6 +13,7 @@ W_MXFP4 = 1
 MODE_DECODE = 0
 MODE_PREFILL = 1
 MODE_PERMUTE = 2
+MODE_PREFILL_MX = 3
 
 c_i32 = ctypes.c_int32
 c_i64 = ctypes.c_int64
@@ -79,6 +80,9 @@ _SIGS = {
                                   _P(EvictPolicy), _P(ClassifyOut), c_ptr]),
     "moe355_expert_ffn_prefill": (c_i32, [_P(LayerDesc), c_ptr, c_i32, c_ptr, c_ptr, c_ptr,
                                           c_ptr, c_ptr, c_ptr, c_ptr, ctypes.c_size_t, c_ptr]),
+    "moe355_quantize_mx": (c_i32, [c_ptr, c_i64, c_i32, c_ptr, c_ptr, c_ptr]),
+    "moe355_expert_ffn_prefill_mx": (c_i32, [_P(LayerDesc), c_ptr, c_i32, c_ptr, c_ptr, c_ptr,
+                                             c_ptr, c_ptr, c_ptr, c_ptr, ctypes.c_size_t, c_ptr]),
     "moe355_combine": (c_i32, [c_i32, c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr]),
     "moe355_workspace_bytes": (ctypes.c_size_t, [_P(LayerDesc), c_i32, c_i32]),
 }

@@ -74,6 +74,7 @@ moe355_status check_desc(const moe355_layer_desc* d) {
 
 size_t permute_ws_bytes(int E, int T, int k);
 size_t prefill_ws_bytes(const moe355_layer_desc* d, int T);
+size_t prefill_mx_ws_bytes(const moe355_layer_desc* d, int T);
 size_t decode_ws_bytes(const moe355_layer_desc* d, int T);
 
 }  // namespace moe355
@@ -111,6 +112,7 @@ extern "C" size_t moe355_workspace_bytes(const moe355_layer_desc* d, int32_t T, 
         case MOE355_MODE_DECODE: return decode_ws_bytes(d, T);
         case MOE355_MODE_PREFILL: return prefill_ws_bytes(d, T);
         case MOE355_MODE_PERMUTE: return permute_ws_bytes(d->n_experts, T, d->top_k);
+        case MOE355_MODE_PREFILL_MX: return prefill_mx_ws_bytes(d, T);
         default: return 0;
     }
 }

@@ -745,6 +745,454 @@ __global__ void __launch_bounds__(256) down_mfma(PrefillParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Native fp4 matrix-core path for MXFP4 experts: v_mfma_scale_f32_32x32x64_f8f6f4
+// with the e2m1 weights (and their e8m0 block scales) as one operand and MX
+// FP8 E4M3 activations (OCP Microscaling v1.0: 32 elements per e8m0 scale) as
+// the other, so the products run on the fp8 x fp4 matrix-core rate.
+//   x is quantised once per call (mx8_x_kernel): blocks of 32 along H.
+//   gate/up: tile 128 pairs x 256 features, K = 128 per stage (two MFMAs of
+//     K = 64); h = silu(g) * u leaves the accumulators as two MX terms
+//     h1 = MX(h), h2 = MX(h - h1) per pair in blocks of 32 along I, so that a
+//     rounding decision that differs between implementations in h's last bits
+//     moves the sum h1 + h2 by at most one step of the second term.
+//   down: tile 128 pairs x 512 outputs, K = 64 per stage, both terms of h
+//     against the same weight operand; the combine adds into the output with
+//     fp32 atomics as in the f16/bf16 path.
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Shared exponent of an MX FP8 E4M3 block from its largest magnitude:
+// floor(log2(amax)) - 8, clamped to e8m0's range; -127 for zero (and for amax
+// below the normal range, whose floor(log2) is below -126).
+__device__ __forceinline__ int mx_exponent(float amax) {
+    const int ef = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFFu);
+    const int e = ef - 127 - 8;
+    return ef == 0 ? -127 : (e < -127 ? -127 : (e > 127 ? 127 : e));
+}
+// 2^-e for e in [-127, 119] (every block of finite bf16 or fp32 values), exact.
+__device__ __forceinline__ float mx_inv_scale(int e) {
+    return __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+}
+__device__ __forceinline__ float mx_scale(int e) {   // 2^e for e in [-127, 119], exact
+    return e >= -126 ? __uint_as_float(static_cast<uint32_t>(127 + e) << 23)
+                     : __uint_as_float(0x00400000u);   // 2^-127 (subnormal)
+}
+
+// FP8 E4M3 code of v (already divided by the block scale): round to nearest,
+// ties to even, saturating at +-448; zero (of either sign) is code 0.  *q gets
+// the code's value.  Done on the fp32 bits so the result is exact by construction.
+__device__ __forceinline__ uint32_t e4m3_rne(float v, float* q) {
+    const float a = fminf(__builtin_fabsf(v), 448.0f);
+    uint32_t code;
+    float mag;
+    if (a < 0.015625f) {                           // below 2^-6: steps of 2^-9
+        const float m = __builtin_rintf(a * 512.0f);   // 0 .. 8 (8 is 2^-6, code 0x08)
+        code = static_cast<uint32_t>(m);
+        mag = m * 0.001953125f;
+    } else {                                       // keep 3 mantissa bits, nearest even
+        const uint32_t b = __float_as_uint(a);
+        const uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u;
+        code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);   // biased exponent - 127 + 7
+        mag = __uint_as_float(r);
+    }
+    const bool neg = v < 0.0f && code != 0u;
+    *q = neg ? -mag : mag;
+    return code | (neg ? 0x80u : 0u);
+}
+
+// MX FP8 E4M3 copy of x: codes [T][H] and scale bytes [T][H / 32].  A thread
+// takes 8 bf16 values (one 16-byte load); 4 neighbouring threads form a block.
+__global__ void __launch_bounds__(256) mx8_x_kernel(const uint16_t* __restrict__ x, int64_t n8,
+                                                    uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ scales) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (i < n8) v = reinterpret_cast<const uint4*>(x)[i];
+    float f[8];
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = __uint_as_float(w4[j] << 16);
+        f[2 * j + 1] = __uint_as_float(w4[j] & 0xFFFF0000u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, __builtin_fabsf(f[j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, WAVE));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, WAVE));
+    const int e = mx_exponent(amax);
+    const float inv = mx_inv_scale(e);
+    uint32_t c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float q;
+        c[j] = e4m3_rne(f[j] * inv, &q);
+    }
+    if (i < n8) {
+        reinterpret_cast<uint2*>(codes)[i] = make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24,
+                                                        c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
+        if ((i & 3) == 0) scales[i >> 2] = static_cast<uint8_t>(e + 127);
+    }
+}
+
+// v_mfma_scale_f32_32x32x64_f8f6f4 operand layouts (measured on gfx950 with a
+// one-wavefront check of random operands): lane l serves row (or column)
+// l % 32 and half hf = l / 32 of the 64 inputs.
+//   e2m1 operand: 16 bytes, inputs 32 hf + [0, 32), low nibble first;
+//   E4M3 operand: 32 bytes, bytes 0-15 are inputs 16 hf + [0, 16) and bytes
+//     16-31 inputs 32 + 16 hf + [0, 16);
+//   scale: byte 0 of lane l's scale word is the e8m0 scale of inputs
+//     32 hf + [0, 32) of its row, whichever lanes hold them.
+__device__ __forceinline__ f32x16 mma_fp4_fp8(const uint4& w, uint32_t w_scale, const i32x8& x,
+                                              uint32_t x_scale, f32x16 c) {
+    const i32x8 a = {static_cast<int>(w.x), static_cast<int>(w.y), static_cast<int>(w.z),
+                     static_cast<int>(w.w), 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, x, c, 4, 0, 0, static_cast<int>(w_scale),
+                                                          0, static_cast<int>(x_scale));
+}
+// The same with the activation as the first operand (rows) and the weights as
+// the second (columns).
+__device__ __forceinline__ f32x16 mma_fp8_fp4(const i32x8& x, uint32_t x_scale, const uint4& w,
+                                              uint32_t w_scale, f32x16 c) {
+    const i32x8 b = {static_cast<int>(w.x), static_cast<int>(w.y), static_cast<int>(w.z),
+                     static_cast<int>(w.w), 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, b, c, 0, 4, 0, static_cast<int>(x_scale),
+                                                          0, static_cast<int>(w_scale));
+}
+
+struct MxParams {
+    const uint8_t* xq;       // [T][H] MX FP8 E4M3 codes of x
+    const uint8_t* xe;       // [T][H / 32] their scale bytes
+    const int32_t* perm;
+    const int32_t* offsets;
+    const float* topk_w;
+    const uint8_t* W;
+    int64_t S;
+    int64_t q_off[3], s_off[3];
+    int T, k, H, I, E;
+    const int32_t* tile_e;
+    const int32_t* tile_m0;
+    const int32_t* n_tiles;
+    uint8_t* hq[2];          // [T*k][I] the two MX terms of h (rows in bucket order)
+    uint8_t* he[2];          // [T*k][I / 32] their scale bytes
+    float* out;
+};
+
+// gate/up stage slot (K = 128): activation rows 128 x 128 bytes (16-byte chunk c
+// of row r at slot c ^ (r & 7)); weights [wavefront][4 column tiles][2 halves]
+// [64 lanes] x 16 bytes in MFMA operand order; weight scale dwords [wavefront]
+// [2][64] (row 64 j + i of load j); activation scale dwords [wavefront][64]
+// (row 32 w + i at i < 32).
+constexpr int MG_A = 0, MG_W = 16384, MG_WS = 49152, MG_XS = 51200, MG_SLOT = 52224, MG_PD = 3;
+constexpr int MG_K = 128;
+// down stage slot (K = 64): two h terms of 128 rows x 64 bytes (chunk c of row r
+// at slot c ^ (r & 3)); weights [wavefront][4][64] x 16 bytes; weight scale
+// dwords [wavefront][2][64]; h scale dwords per term [wavefront][64].
+constexpr int MD_A0 = 0, MD_A1 = 8192, MD_W = 16384, MD_WS = 32768, MD_HS = 34816,
+              MD_SLOT = 36864, MD_PD = 4;
+constexpr int MD_K = 64;
+
+__global__ void __launch_bounds__(256) gate_up_mx(MxParams p) {
+    constexpr int PD = MG_PD, D = PD - 1, OPS = 15;   // loads per stage per wavefront
+    extern __shared__ uint4 smem[];
+    uint8_t* ring = reinterpret_cast<uint8_t*>(smem);                  // [PD][MG_SLOT]
+    int32_t* rtok = reinterpret_cast<int32_t*>(ring + PD * MG_SLOT);   // token of each tile row
+    const int tid = threadIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / WAVE);
+    const int H = p.H, I = p.I, KS = H / MG_K;
+    const uint32_t ring_lds = lds_addr(ring);
+
+    {   // zero the layer output for the down kernel's atomics
+        const int64_t n = static_cast<int64_t>(p.T) * H;
+        for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + tid; i < n;
+             i += static_cast<int64_t>(gridDim.x) * 256)
+            p.out[i] = 0.0f;
+    }
+
+    const int FX = (I + GU_FEAT - 1) / GU_FEAT;
+    const TileRange tr = tile_range(*p.n_tiles * FX);
+    const void* xs = uniform_ptr(p.xq);
+    const void* xes = uniform_ptr(p.xe);
+    for (int t = tr.begin; t < tr.end; t += tr.step) {
+        const int y = t / FX;
+        const int e = p.tile_e[y], m0 = p.tile_m0[y];
+        const int pbase = p.offsets[e] + m0;
+        const int rows = min(BM, p.offsets[e + 1] - pbase);
+        const void* W = uniform_ptr(p.W + static_cast<int64_t>(e) * p.S);
+        const int fw = (t - y * FX) * GU_FEAT + 64 * wv;
+        int lane = tid & (WAVE - 1);
+        asm volatile("" : "+v"(lane));
+        const int ln = lane & 31, hh = lane >> 5;
+        const bool live = fw < I;
+        const int fr = live ? fw : 0;
+        __syncthreads();   // the previous tile is done with the LDS
+        if (tid < BM) rtok[tid] = p.perm[pbase + (tid < rows ? tid : 0)] / p.k;
+        __syncthreads();
+        uint32_t aoff[4];   // this lane's activation sources: 4 blocks of 8 rows
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 8 * (4 * wv + j) + lane / 8, c = (lane % 8) ^ (lane / 8);
+            aoff[j] = static_cast<uint32_t>(rtok[r]) * static_cast<uint32_t>(H) + c * 16;
+        }
+        // activation scale dwords: row 32 wv + ln (both lane halves load it)
+        const uint32_t xsoff = static_cast<uint32_t>(rtok[32 * wv + ln]) * static_cast<uint32_t>(H / 32);
+        uint32_t bq[4], bsc[2];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bq[c] = code_src(p.q_off[c >> 1], fr + 32 * (c & 1) + ln, H, hh);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bsc[j] = scale_src(p.s_off[j], fr + lane, H);
+
+        f32x16 R[4][4];   // [column tile][row tile]: features x tokens
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) R[c][i] = f32x16{};
+        auto issue = [&](int kk, int slot) {
+            const uint32_t sl = ring_lds + slot * MG_SLOT;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dma16(xs, aoff[j] + kk * MG_K, sl + MG_A + (4 * wv + j) * 1024);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    dma16(W, bq[c] + kk * 1024 + s * 512, sl + MG_W + ((4 * wv + c) * 2 + s) * 1024);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) dma4(W, bsc[j] + kk * 64, sl + MG_WS + (2 * wv + j) * 256);
+            dma4(xes, xsoff + kk * 4, sl + MG_XS + wv * 256);
+        };
+        auto compute = [&](int slot) {
+            const uint8_t* sp = ring + slot * MG_SLOT;
+            const uint4* A = reinterpret_cast<const uint4*>(sp + MG_A);
+            const uint4* Wq = reinterpret_cast<const uint4*>(sp + MG_W) + 4 * wv * 2 * 64 + lane;
+            const uint32_t* WS = reinterpret_cast<const uint32_t*>(sp + MG_WS);
+            const uint32_t* XS = reinterpret_cast<const uint32_t*>(sp + MG_XS);
+            uint32_t wsc[4], xsc[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) wsc[c] = tile_scale(WS, wv, c, ln);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) xsc[mt] = XS[mt * 64 + ln];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                i32x8 xb[4];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    // inputs 16 hh + [0, 16) and 32 + 16 hh + [0, 16) of half s
+                    const int r = mt * 32 + ln, c0 = 4 * s + hh;
+                    const uint4 u0 = A[r * 8 + (c0 ^ (r & 7))];
+                    const uint4 u1 = A[r * 8 + ((c0 + 2) ^ (r & 7))];
+                    xb[mt] = i32x8{static_cast<int>(u0.x), static_cast<int>(u0.y), static_cast<int>(u0.z),
+                                   static_cast<int>(u0.w), static_cast<int>(u1.x), static_cast<int>(u1.y),
+                                   static_cast<int>(u1.z), static_cast<int>(u1.w)};
+                }
+                const int sb = 8 * (2 * s + hh);   // this lane's block of the stage's 4
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint4 q = Wq[(c * 2 + s) * 64];
+                    const uint32_t ws = (wsc[c] >> sb) & 0xFFu;
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+                        R[c][mt] = mma_fp4_fp8(q, ws, xb[mt], (xsc[mt] >> sb) & 0xFFu, R[c][mt]);
+                }
+            }
+        };
+#pragma unroll
+        for (int kk = 0; kk < D; ++kk)
+            if (kk < KS) issue(kk, kk);
+        int slot = 0;
+#pragma nounroll
+        for (int kk = 0; kk < KS; ++kk) {
+            stage_wait<OPS, D - 1>(KS - 1 - kk);   // stage kk has landed everywhere
+            const int next = slot == 0 ? PD - 1 : slot - 1;   // the slot read last stage
+            if (kk + D < KS) issue(kk + D, next);
+            compute(slot);
+            slot = slot == PD - 1 ? 0 : slot + 1;
+        }
+
+        // h = silu(g) * u as two MX terms.  Lane (ln, hh) holds, for tile row
+        // 32 mt + ln, features fw + 32 ft + 8 (i / 4) + 4 hh + i % 4 in R[ft][mt][i]
+        // (g) and R[2 + ft][mt][i] (u): an MX block of 32 features is one column
+        // tile, 16 values here and 16 in lane ln + 32 (the other half).
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int r = mt * 32 + ln;
+            const bool keep = live && r < rows;
+            const int64_t prow = static_cast<int64_t>(pbase + r);
+#pragma unroll
+            for (int ft = 0; ft < 2; ++ft) {
+                float v[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float g = R[ft][mt][i], u = R[2 + ft][mt][i];
+                    v[i] = g / (1.0f + __expf(-g)) * u;
+                }
+                const int f0 = fw + 32 * ft;
+#pragma unroll
+                for (int term = 0; term < 2; ++term) {
+                    float amax = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, __builtin_fabsf(v[i]));
+                    amax = fmaxf(amax, __shfl_xor(amax, 32, WAVE));
+                    const int ex = mx_exponent(amax);
+                    const float inv = mx_inv_scale(ex), sc = mx_scale(ex);
+                    uint32_t cw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        float q;
+                        cw[i >> 2] |= e4m3_rne(v[i] * inv, &q) << (8 * (i & 3));
+                        v[i] -= q * sc;          // the residual, exact: the next term's input
+                    }
+                    if (keep) {
+                        uint8_t* dst = p.hq[term] + prow * I + f0 + 4 * hh;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) *reinterpret_cast<uint32_t*>(dst + 8 * j) = cw[j];
+                        if (hh == 0) p.he[term][prow * (I / 32) + f0 / 32] = static_cast<uint8_t>(ex + 127);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// down + combine on the two MX terms of h: A = the tile's 128 rows of h (each
+// term with its scale bytes); B = down rows nw + [0, 128) of wavefront w as 4
+// column tiles of e2m1 codes; fp32 atomics into the output as in down_mfma.
+__global__ void __launch_bounds__(256) down_mx(MxParams p) {
+    constexpr int PD = MD_PD, D = PD - 1, OPS = 12;   // loads per stage per wavefront
+    extern __shared__ uint4 smem[];
+    uint8_t* ring = reinterpret_cast<uint8_t*>(smem);                  // [PD][MD_SLOT]
+    int32_t* rtok = reinterpret_cast<int32_t*>(ring + PD * MD_SLOT);
+    float* rw = reinterpret_cast<float*>(rtok + BM);
+    const int tid = threadIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / WAVE);
+    const int H = p.H, I = p.I, KS = I / MD_K;
+    const int FX = (H + DN_COLS - 1) / DN_COLS;
+    const uint32_t ring_lds = lds_addr(ring);
+    const TileRange tr = tile_range(*p.n_tiles * FX);
+    for (int t = tr.begin; t < tr.end; t += tr.step) {
+        const int y = t / FX;
+        const int e = p.tile_e[y], m0 = p.tile_m0[y];
+        const int pbase = p.offsets[e] + m0;
+        const int rows = min(BM, p.offsets[e + 1] - pbase);
+        const void* W = uniform_ptr(p.W + static_cast<int64_t>(e) * p.S);
+        const int nw = (t - y * FX) * DN_COLS + 128 * wv;
+        int lane = tid & (WAVE - 1);
+        asm volatile("" : "+v"(lane));
+        const int ln = lane & 31, hh = lane >> 5;
+        const bool live = nw < H;
+        const int nr = live ? nw : 0;
+        const void* hb0 = uniform_ptr(p.hq[0] + static_cast<int64_t>(pbase) * I);
+        const void* hb1 = uniform_ptr(p.hq[1] + static_cast<int64_t>(pbase) * I);
+        const void* hs0 = uniform_ptr(p.he[0] + static_cast<int64_t>(pbase) * (I / 32));
+        const void* hs1 = uniform_ptr(p.he[1] + static_cast<int64_t>(pbase) * (I / 32));
+        __syncthreads();   // the previous tile is done with the LDS
+        if (tid < BM) {
+            if (tid < rows) {
+                const int pr = p.perm[pbase + tid];
+                rtok[tid] = pr / p.k;
+                rw[tid] = p.topk_w[pr];
+            } else {
+                rtok[tid] = -1;
+                rw[tid] = 0.0f;
+            }
+        }
+        uint32_t aoff[2];   // 2 blocks of 16 rows x 4 chunks; rows past the bucket re-read row 0
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = 16 * (2 * wv + j) + lane / 4, c = (lane % 4) ^ ((lane / 4) & 3);
+            aoff[j] = static_cast<uint32_t>(r < rows ? r : 0) * static_cast<uint32_t>(I) + c * 16;
+        }
+        const int srow = 32 * wv + ln;
+        const uint32_t hsoff = static_cast<uint32_t>(srow < rows ? srow : 0) * static_cast<uint32_t>(I / 32);
+        uint32_t bq[4], bsc[2];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bq[c] = code_src(p.q_off[2], nr + 32 * c + ln, I, hh);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bsc[j] = scale_src(p.s_off[2], nr + 64 * j + lane, I);
+
+        f32x16 R[4][4];   // [row tile][column tile]: pairs x outputs
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) R[i][c] = f32x16{};
+        auto issue = [&](int kk, int slot) {
+            const uint32_t sl = ring_lds + slot * MD_SLOT;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                dma16(hb0, aoff[j] + kk * MD_K, sl + MD_A0 + (2 * wv + j) * 1024);
+                dma16(hb1, aoff[j] + kk * MD_K, sl + MD_A1 + (2 * wv + j) * 1024);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) dma16(W, bq[c] + code_step(kk), sl + MD_W + (4 * wv + c) * 1024);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) dma4(W, bsc[j] + scale_step(kk), sl + MD_WS + (2 * wv + j) * 256);
+            dma4(hs0, hsoff + (kk >> 1) * 4, sl + MD_HS + wv * 256);
+            dma4(hs1, hsoff + (kk >> 1) * 4, sl + MD_HS + 1024 + wv * 256);
+        };
+        auto compute = [&](int kk, int slot) {
+            const uint8_t* sp = ring + slot * MD_SLOT;
+            const uint4* Wq = reinterpret_cast<const uint4*>(sp + MD_W) + 4 * wv * 64 + lane;
+            const uint32_t* WS = reinterpret_cast<const uint32_t*>(sp + MD_WS);
+            const int sb = 8 * (2 * (kk & 1) + hh);   // this lane's block of the dword's 4
+            uint4 q[4];
+            uint32_t wsc[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                q[c] = Wq[c * 64];
+                wsc[c] = (tile_scale(WS, wv, c, ln) >> sb) & 0xFFu;
+            }
+#pragma unroll
+            for (int term = 0; term < 2; ++term) {
+                const uint4* A = reinterpret_cast<const uint4*>(sp + (term ? MD_A1 : MD_A0));
+                const uint32_t* HS = reinterpret_cast<const uint32_t*>(sp + MD_HS + term * 1024);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const int r = mt * 32 + ln;
+                    const uint4 u0 = A[r * 4 + (hh ^ (r & 3))];         // inputs 16 hh + [0, 16)
+                    const uint4 u1 = A[r * 4 + ((2 + hh) ^ (r & 3))];   // 32 + 16 hh + [0, 16)
+                    const i32x8 xa = {static_cast<int>(u0.x), static_cast<int>(u0.y), static_cast<int>(u0.z),
+                                      static_cast<int>(u0.w), static_cast<int>(u1.x), static_cast<int>(u1.y),
+                                      static_cast<int>(u1.z), static_cast<int>(u1.w)};
+                    const uint32_t xsc = (HS[mt * 64 + ln] >> sb) & 0xFFu;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) R[mt][c] = mma_fp8_fp4(xa, xsc, q[c], wsc[c], R[mt][c]);
+                }
+            }
+        };
+#pragma unroll
+        for (int kk = 0; kk < D; ++kk)
+            if (kk < KS) issue(kk, kk);
+        int slot = 0;
+#pragma nounroll
+        for (int kk = 0; kk < KS; ++kk) {
+            stage_wait<OPS, D - 1>(KS - 1 - kk);
+            const int next = slot == 0 ? PD - 1 : slot - 1;
+            if (kk + D < KS) issue(kk + D, next);
+            compute(kk, slot);
+            slot = slot == PD - 1 ? 0 : slot + 1;
+        }
+
+        if (live) {   // combine, as in down_mfma
+            const int h4 = 4 * hh;
+            const int32_t* rt = rtok + h4;
+            const float* rwt = rw + h4;
+            float* obase = p.out + nw + ln;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int rc = mt * 32 + 8 * (i >> 2) + (i & 3);
+                    if (rc + h4 < rows) {
+                        const float wt = rwt[rc];
+                        float* orow = obase + static_cast<int64_t>(rt[rc]) * H;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) unsafeAtomicAdd(orow + 32 * c, wt * R[mt][c][i]);
+                    }
+                }
+        }
+    }
+}
+
 int max_tiles(int T, int k, int E) { return (T * k + BM - 1) / BM + E; }
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -766,6 +1214,16 @@ int prefill_blocks() {
 
 // h (hi, lo), the tile plan, the tile count, and for int4 the f16 copy of x,
 // its group sums and the group sums of h.
+// MX path workspace: the error word's 256 bytes, the tile plan and count, the
+// MX copy of x and its scales, the two MX terms of h and their scales.
+size_t prefill_mx_ws_bytes(const moe355_layer_desc* d, int T) {
+    const size_t tk = static_cast<size_t>(T) * d->top_k;
+    const size_t th = static_cast<size_t>(T) * d->hidden;
+    return 256 + align256(2 * static_cast<size_t>(max_tiles(T, d->top_k, d->n_experts)) * 4) + 256 +
+           align256(th) + align256(th / 32) + 2 * align256(tk * d->inter) +
+           2 * align256(tk * d->inter / 32);
+}
+
 size_t prefill_ws_bytes(const moe355_layer_desc* d, int T) {
     const size_t tk = static_cast<size_t>(T) * d->top_k;
     const size_t xb = d->wfmt == MOE355_W_INT4_G64
@@ -889,4 +1347,119 @@ extern "C" moe355_status moe355_expert_ffn_prefill(const moe355_layer_desc* d, c
     if (st) return st;
     dn<<<blocks, 256, lds_dn, stream>>>(p);
     return check_launch("expert_ffn_prefill down");
+}
+
+extern "C" moe355_status moe355_quantize_mx(const void* x_bf16, int64_t rows, int32_t cols,
+                                            uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+    MOE355_REQUIRE(rows >= 0 && cols > 0 && cols % 32 == 0, MOE355_EINVAL,
+                   "quantize_mx: rows=%lld cols=%d (a positive multiple of 32)",
+                   static_cast<long long>(rows), cols);
+    if (rows == 0) return ok();
+    MOE355_REQUIRE(x_bf16 && codes && scales, MOE355_EINVAL, "quantize_mx: null pointer");
+    const int64_t n8 = rows * cols / 8;
+    MOE355_REQUIRE((n8 + 255) / 256 <= 0x7FFFFFFFll, MOE355_ENOTSUP, "quantize_mx: too many values");
+    mx8_x_kernel<<<static_cast<unsigned>((n8 + 255) / 256), 256, 0, stream>>>(
+        static_cast<const uint16_t*>(x_bf16), n8, codes, scales);
+    return check_launch("quantize_mx");
+}
+
+extern "C" moe355_status moe355_expert_ffn_prefill_mx(const moe355_layer_desc* d, const void* x_bf16,
+                                                      int32_t T, const int32_t* topk_ids,
+                                                      const float* topk_w, const uint8_t* layer_w,
+                                                      const int32_t* perm, const int32_t* offsets,
+                                                      float* out, void* ws, size_t ws_bytes,
+                                                      hipStream_t stream) {
+    (void)topk_ids;
+    moe355_status st = check_desc(d);
+    if (st) return st;
+    MOE355_REQUIRE(d->wfmt == MOE355_W_MXFP4, MOE355_ENOTSUP,
+                   "expert_ffn_prefill_mx: MXFP4 experts only (wfmt=%d)", d->wfmt);
+    MOE355_REQUIRE(T >= 0 && static_cast<int64_t>(T) * d->top_k < (1ll << 28), MOE355_EINVAL,
+                   "expert_ffn_prefill_mx: T=%d", T);
+    if (T == 0) return ok();
+    MOE355_REQUIRE(x_bf16 && topk_w && layer_w && perm && offsets && out, MOE355_EINVAL,
+                   "expert_ffn_prefill_mx: null pointer");
+    MOE355_REQUIRE(d->hidden % 256 == 0 && d->inter % 128 == 0 && d->n_experts <= 1024 &&
+                       d->hidden <= 16384 && d->inter <= 16384,
+                   MOE355_ENOTSUP, "expert_ffn_prefill_mx: H=%d (multiple of 256), I=%d (of 128), E=%d",
+                   d->hidden, d->inter, d->n_experts);
+    // x rows and h rows are addressed by 32-bit byte offsets
+    MOE355_REQUIRE(static_cast<int64_t>(T) * d->hidden <= 0xFFFFFFFFll &&
+                       static_cast<int64_t>(T) * d->top_k * d->inter <= 0xFFFFFFFFll,
+                   MOE355_ENOTSUP, "expert_ffn_prefill_mx: T*H or T*k*I beyond 2^32 bytes");
+    const size_t need = prefill_mx_ws_bytes(d, T);
+    MOE355_REQUIRE(ws && ws_bytes >= need, MOE355_ECAPACITY,
+                   "expert_ffn_prefill_mx: workspace %zu < %zu bytes", ws_bytes, need);
+    ExpertLayout L;
+    expert_layout(d, &L);
+    const size_t tk = static_cast<size_t>(T) * d->top_k, th = static_cast<size_t>(T) * d->hidden;
+    const int mt = max_tiles(T, d->top_k, d->n_experts);
+    uint8_t* at = static_cast<uint8_t*>(ws);
+    uint32_t* err = reinterpret_cast<uint32_t*>(at);
+    at += 256;
+    int32_t* tiles = reinterpret_cast<int32_t*>(at);
+    at += align256(2 * static_cast<size_t>(mt) * 4);
+    int32_t* n_tiles = reinterpret_cast<int32_t*>(at);
+    at += 256;
+    MxParams p{};
+    uint8_t* xq = at;
+    at += align256(th);
+    uint8_t* xe = at;
+    at += align256(th / 32);
+    for (int term = 0; term < 2; ++term) {
+        p.hq[term] = at;
+        at += align256(tk * d->inter);
+    }
+    for (int term = 0; term < 2; ++term) {
+        p.he[term] = at;
+        at += align256(tk * d->inter / 32);
+    }
+    p.xq = xq;
+    p.xe = xe;
+    p.perm = perm;
+    p.offsets = offsets;
+    p.topk_w = topk_w;
+    p.W = layer_w;
+    p.S = L.bytes;
+    for (int m = 0; m < 3; ++m) {
+        p.q_off[m] = L.q_off[m];
+        p.s_off[m] = L.s_off[m];
+    }
+    p.T = T;
+    p.k = d->top_k;
+    p.H = d->hidden;
+    p.I = d->inter;
+    p.E = d->n_experts;
+    p.tile_e = tiles;
+    p.tile_m0 = tiles + mt;
+    p.n_tiles = n_tiles;
+    p.out = out;
+
+    plan_kernel<<<1, 1024, 0, stream>>>(offsets, d->n_experts, tiles, tiles + mt, n_tiles, err);
+    st = check_launch("expert_ffn_prefill_mx plan");
+    if (st) return st;
+    const int64_t n8 = static_cast<int64_t>(th / 8);
+    mx8_x_kernel<<<static_cast<unsigned>((n8 + 255) / 256), 256, 0, stream>>>(
+        static_cast<const uint16_t*>(x_bf16), n8, xq, xe);
+    st = check_launch("expert_ffn_prefill_mx quantise x");
+    if (st) return st;
+    const size_t lds_gu = MG_PD * MG_SLOT + BM * 4;
+    const size_t lds_dn = MD_PD * MD_SLOT + 2 * BM * 4;
+    static bool granted = false;
+    if (!granted) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(gate_up_mx),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                static_cast<int>(lds_gu)) != hipSuccess ||
+            hipFuncSetAttribute(reinterpret_cast<const void*>(down_mx),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                static_cast<int>(lds_dn)) != hipSuccess)
+            return fail(MOE355_EHIP, "expert_ffn_prefill_mx: LDS %zu / %zu bytes refused", lds_gu, lds_dn);
+        granted = true;
+    }
+    const int blocks = prefill_blocks();
+    gate_up_mx<<<blocks, 256, lds_gu, stream>>>(p);
+    st = check_launch("expert_ffn_prefill_mx gate_up");
+    if (st) return st;
+    down_mx<<<blocks, 256, lds_dn, stream>>>(p);
+    return check_launch("expert_ffn_prefill_mx down");
 }

@@ -11,7 +11,7 @@ import ctypes
 import torch
 
 from .abi import (Cache, ClassifyOut, EvictPolicy, LayerDesc, MODE_DECODE, MODE_PERMUTE,
-                  MODE_PREFILL, Moe355Error, check, load)
+                  MODE_PREFILL, MODE_PREFILL_MX, Moe355Error, check, load)
 
 
 def _ptr(t) -> int | None:
@@ -58,7 +58,7 @@ ERR_F16_RANGE = 2
 
 def error_word(ws, mode: int = MODE_DECODE) -> int:
     """The error word of a decode or prefill workspace (synchronises)."""
-    at = DECODE_ERR_BYTE if mode == MODE_DECODE else PREFILL_ERR_BYTE
+    at = DECODE_ERR_BYTE if mode == MODE_DECODE else PREFILL_ERR_BYTE   # both prefill forms
     return int(ws[at:at + 4].view(torch.int32).item()) & 0xFFFFFFFF
 
 
@@ -281,6 +281,31 @@ def expert_ffn_prefill(desc, x_bf16, topk_ids, topk_w, layer_w, perm, offsets, o
                                            _ptr(topk_w), _ptr(layer_w), _ptr(perm), _ptr(offsets),
                                            _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
                                            _stream(stream)), "moe355_expert_ffn_prefill")
+
+
+def quantize_mx(x_bf16, codes, scales, stream=None):
+    """MX FP8 E4M3 codes [rows, cols] and scale bytes [rows, cols / 32] of bf16 x."""
+    _need(x_bf16, torch.bfloat16, "x")
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    rows, cols = x_bf16.shape
+    if codes.numel() < rows * cols or scales.numel() < rows * cols // 32:
+        raise ValueError("quantize_mx: output buffers too small")
+    check(load().moe355_quantize_mx(_ptr(x_bf16), rows, cols, _ptr(codes), _ptr(scales),
+                                    _stream(stream)), "moe355_quantize_mx")
+
+
+def expert_ffn_prefill_mx(desc, x_bf16, topk_ids, topk_w, layer_w, perm, offsets, out, ws,
+                          stream=None):
+    """Prefill expert FFN for MXFP4 experts on the fp4 x fp8 matrix cores."""
+    _need(x_bf16, torch.bfloat16, "x")
+    _need(out, torch.float32, "out")
+    T = x_bf16.shape[0]
+    check(load().moe355_expert_ffn_prefill_mx(ctypes.byref(desc), _ptr(x_bf16), T, _ptr(topk_ids),
+                                              _ptr(topk_w), _ptr(layer_w), _ptr(perm),
+                                              _ptr(offsets), _ptr(out), _ptr(ws),
+                                              ws.numel() * ws.element_size(), _stream(stream)),
+          "moe355_expert_ffn_prefill_mx")
 
 
 def combine(y, topk_w, out, stream=None):

@@ -59,7 +59,7 @@ class BlobSource:
         return self.cache[g]
 
 
-def oracle_layer(x, ids, w, blob, wfmt, H, I, tokens=None, workers=8):
+def oracle_layer(x, ids, w, blob, wfmt, H, I, tokens=None, workers=8, mx=False):
     """``ffn.moe_layer`` for the given tokens, its distinct experts split into
     disjoint groups evaluated in parallel threads.
 
@@ -68,6 +68,9 @@ def oracle_layer(x, ids, w, blob, wfmt, H, I, tokens=None, workers=8):
     to its own experts (the others get weight 0 and point at one of the group's
     experts, so no other expert is dequantised).  NumPy releases the GIL in the
     dequantisation and the products, so the groups run concurrently.
+    mx=True evaluates ``ffn.moe_layer_mx8`` instead (MXFP4 experts, MX
+    activations): its x is quantised per token and h per pair, so the same
+    split holds.
     """
     from concurrent.futures import ThreadPoolExecutor
     from oracle import ffn as offn
@@ -82,8 +85,10 @@ def oracle_layer(x, ids, w, blob, wfmt, H, I, tokens=None, workers=8):
 
     def part(g):
         inside = np.isin(sid, g)
-        return offn.moe_layer(sx, np.where(inside, sid, g[0]), np.where(inside, sw, 0.0),
-                              blob, wfmt, H, I)
+        gid, gw = np.where(inside, sid, g[0]), np.where(inside, sw, 0.0)
+        if mx:
+            return offn.moe_layer_mx8(sx, gid, gw, blob, H, I)
+        return offn.moe_layer(sx, gid, gw, blob, wfmt, H, I)
 
     if n == 1:
         return part(groups[0])
