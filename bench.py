@@ -427,6 +427,135 @@ def bench_prefill(args, w, mx=False):
     return res
 
 
+def bench_miss_replay(args):
+    """Decode expert miss rate versus cache size (percent of the expert pool) for
+    the global LRU (the library's routing and bookkeeping calls on the GPU)
+    against static hot-expert pinning and static whole-layer placement, replayed
+    on identical synthetic routing traces (one token per step)."""
+    import torch
+    from moe_expert_layer_02_amd import replay
+    from workloads import configs as C
+    from workloads import traces as tr
+    fracs = (0.05, 0.11, 0.2, 0.37, 0.5, 0.75)
+    curves = {}
+    t0 = time.perf_counter()
+    for w in (C.QWEN_DECODE, C.DS_DECODE_SINGLE):
+        import moe_expert_layer_02_amd as m
+        desc = m.LayerDesc(w.hidden, w.inter, w.n_experts, w.top_k, w.route, w.n_group,
+                           w.topk_group, w.route_scale, w.wfmt)
+        trace = tr.DecodeTrace(w, w.steps)
+        L, E = w.n_layers, w.n_experts
+        rows = []
+        for f in fracs:
+            N = int(round(f * L * E))
+            K = min(w.t_decode * w.top_k, E, N)
+            lru, routed = replay.lru_misses(desc, trace.logits, N, K)
+            rows.append({"cache_frac": f, "slots": N,
+                         "lru": round(replay.miss_rate(lru), 4),
+                         # the second half of the trace: no cold-start first touches
+                         "lru_steady": round(replay.miss_rate(lru[w.steps // 2:]), 4),
+                         "hot_pinned": round(replay.miss_rate(replay.hot_pinned_misses(routed, E, N)), 4),
+                         "layer_static": round(replay.miss_rate(replay.layer_static_misses(routed, E, N)), 4)})
+            print(f"miss replay {w.name} {f:.0%}: {rows[-1]}", file=sys.stderr, flush=True)
+        curves[w.name] = {"layers": L, "experts": E, "top_k": w.top_k, "steps": w.steps,
+                          "calls": w.steps * L, "points": rows}
+        torch.cuda.synchronize()
+    return {"metric": "decode expert-cache miss rate vs cache size (fraction of the expert pool)",
+            "unit": "misses / distinct routed experts", "n_gpus": 1, "data": "synthetic",
+            "higher_is_better": False, "policies": {
+                "lru": "global LRU across layers (library routing + classify_evict on the GPU)",
+                "lru_steady": "the same LRU run, misses counted over the second half of the trace",
+                "hot_pinned": "the N most frequently routed (layer, expert) pairs of the replayed "
+                              "trace itself, fixed (a clairvoyant static placement)",
+                "layer_static": "whole layers 0.. resident while they fit, fixed"},
+            "curves": curves, "wall_s": round(time.perf_counter() - t0, 1)}
+
+
+def bench_prefill_pipeline(args, w, n_layers: int):
+    """Prefill of n_layers consecutive layers with the experts streamed from a
+    pinned host pool (moe355_prefill_layers): two whole-layer buffers (the
+    copy of layer l+1 overlaps layer l), one buffer (copies and compute in
+    series), the compute alone from a resident buffer, and the copies alone
+    (the pinned host-to-device bandwidth B_P).  Every timed region starts with
+    both streams idle and ends when both are done."""
+    import torch
+    import moe_expert_layer_02_amd as m
+    from workloads import experts as wx
+    from workloads import gpu as wg
+    from workloads import traces as tr
+    desc = m.LayerDesc(w.hidden, w.inter, w.n_experts, w.top_k, w.route, w.n_group,
+                       w.topk_group, w.route_scale, w.wfmt)
+    T, E, k = w.t_prefill, w.n_experts, w.top_k
+    S = wx.expert_bytes(w.wfmt, w.hidden, w.inter)
+    LB = E * S
+    pool_dev = wg.make_pool(w, n_layers=n_layers,
+                            pack=lambda src, dst, n: m.pack_experts(desc, src, dst, n))
+    host_pool = torch.empty(pool_dev.numel(), dtype=torch.uint8, pin_memory=True)
+    host_pool.copy_(pool_dev)
+    del pool_dev
+    logits = [torch.from_numpy(tr.prefill_logits_layer(w, l)).cuda() for l in range(n_layers)]
+    xs = [torch.from_numpy(tr.prefill_x_layer(w, l).view(np.int16)).cuda().view(torch.bfloat16)
+          for l in range(n_layers)]
+    outs = [torch.empty((T, w.hidden), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+    bufs = [torch.empty(LB, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(m.workspace_bytes(desc, T, m.MODE_PREFILL), dtype=torch.uint8, device="cuda")
+    wsp = torch.empty(m.workspace_bytes(desc, T, m.MODE_PERMUTE), dtype=torch.uint8, device="cuda")
+    main, copy = torch.cuda.current_stream(), torch.cuda.Stream()
+
+    def timed(fn, reps):
+        ts = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(main)
+            copy.wait_stream(main)
+            fn()
+            main.wait_stream(copy)
+            e1.record(main)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        return float(np.median(ts))
+
+    def pipeline(double):
+        return lambda: m.prefill_layers(desc, host_pool, bufs, logits, xs, outs, ids, wt, perm,
+                                        offsets, ws, wsp, double, copy_stream=copy)
+
+    def resident():
+        for l in range(n_layers):
+            m.route(desc, logits[l], ids, wt)
+            m.permute(desc, ids, perm, offsets, wsp)
+            m.expert_ffn_prefill(desc, xs[l], ids, wt, bufs[0], perm, offsets, outs[l], ws)
+
+    def copies():
+        with torch.cuda.stream(copy):
+            for l in range(n_layers):
+                bufs[l % 2].copy_(host_pool[l * LB:(l + 1) * LB], non_blocking=True)
+
+    reps = max(1, min(args.steps, 5))
+    pipeline(True)()          # warm-up: first launches, LDS attributes
+    torch.cuda.synchronize()
+    t2, t1 = timed(pipeline(True), reps), timed(pipeline(False), reps)
+    tc, tcopy = timed(resident, reps), timed(copies, reps)
+    m.check_error(ws, m.MODE_PREFILL, what="pipelined prefill")
+    tok = T * n_layers
+    return {"metric": "prefill tokens/s with the experts streamed from pinned host memory",
+            "value": round(tok / t2, 1), "unit": "tokens/s", "n_gpus": 1, "steps": reps,
+            "higher_is_better": True, "data": "synthetic",
+            "dtype": "f16" if w.wfmt == 0 else "bf16",
+            "config": {"workload": w.name + "_pipelined", "layers": n_layers, "tokens": T,
+                       "layer_bytes": LB, "parallelism": "single_gpu"},
+            "two_buffers_s": round(t2, 5), "one_buffer_s": round(t1, 5),
+            "compute_only_s": round(tc, 5), "copies_only_s": round(tcopy, 5),
+            "B_P_GBs": round(LB * n_layers / tcopy / 1e9, 2),
+            "one_buffer_tokens_per_s": round(tok / t1, 1),
+            "loss_without_second_buffer": round(1.0 - t2 / t1, 4),
+            "overlap_of_compute": round((tc + tcopy - t2) / tc, 4)}
+
+
 def C_seed(w):
     from workloads import configs as C
     return C.seed(w.cid, 0)
@@ -476,7 +605,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen_decode",
                     choices=["qwen_decode", "ds_decode", "qwen_prefill", "ds_prefill",
-                             "ds_prefill_mx"])
+                             "ds_prefill_mx", "miss_replay", "qwen_prefill_pipeline",
+                             "ds_prefill_pipeline"])
     ap.add_argument("--order", default="auto", choices=["auto", "fused", "split"],
                     help="decode layer call order (auto: fused)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -498,6 +628,13 @@ def main():
     import moe_expert_layer_02_amd as m
     m.check_build()         # the library under test was built from these sources
     from workloads import configs as C
+    if args.workload == "miss_replay":
+        print(json.dumps(bench_miss_replay(args)), flush=True)
+        return
+    if args.workload.endswith("_pipeline"):
+        w, n = (C.QWEN_PREFILL, 8) if args.workload.startswith("qwen") else (C.DS_STRESS, 4)
+        print(json.dumps(bench_prefill_pipeline(args, w, n)), flush=True)
+        return
     w = {"qwen_decode": C.QWEN_DECODE, "ds_decode": C.DS_DECODE, "qwen_prefill": C.QWEN_PREFILL,
          "ds_prefill": C.DS_STRESS, "ds_prefill_mx": C.DS_STRESS}[args.workload]
     if "prefill" in args.workload:

@@ -468,6 +468,36 @@ moe355_status moe355_expert_ffn_prefill_mx(const moe355_layer_desc* d, const voi
                                            size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Prefill of n_layers consecutive MoE layers with the experts streamed from a
+ * pinned host pool through whole-layer buffers [FT-zh, Core method and Method
+ * steps: two whole-layer buffers; while the GPU computes layer l from one, a
+ * transfer stream loads layer l+1 into the other over PCIe, then they swap;
+ * FT-en, System Architecture: the buffer A / buffer B ping-pong].
+ * For each layer l: copy host_pool's layer l (E * S bytes, device layout) into
+ * a buffer by DMA on copy_stream, then on `stream` route T tokens from
+ * logits[l], permute, and run moe355_expert_ffn_prefill on x[l] from that
+ * buffer into out[l].  double_buffer != 0: layers alternate between buf0 and
+ * buf1, so the copy of layer l+1 overlaps the compute of layer l; 0: buf0
+ * alone, every copy waits for the previous layer's compute (buf1 unused).
+ * host_pool: pinned host memory (hipHostMalloc) [n_layers * E * S]; buf0, buf1:
+ * device [E * S]; logits, x, out: host arrays of n_layers device pointers
+ * (fp32 [T, E], bf16 [T, H], fp32 [T, H]); topk_ids / topk_w / perm / offsets:
+ * device scratch as for moe355_route and moe355_permute, reused by every layer;
+ * ws / perm_ws: the MOE355_MODE_PREFILL and MOE355_MODE_PERMUTE workspaces.
+ * When the call returns, `stream` holds the last layer's work and copy_stream
+ * its copies.  Errors: MOE355_EINVAL for null pointers, a host_pool that is not
+ * pinned host memory, or stream == copy_stream; MOE355_ECAPACITY for short
+ * workspaces; otherwise as the calls above.
+ */
+moe355_status moe355_prefill_layers(const moe355_layer_desc* d, int32_t n_layers, int32_t T,
+                                    const uint8_t* host_pool, uint8_t* buf0, uint8_t* buf1,
+                                    const float* const* logits, const void* const* x,
+                                    float* const* out, int32_t* topk_ids, float* topk_w,
+                                    int32_t* perm, int32_t* offsets, void* ws, size_t ws_bytes,
+                                    void* perm_ws, size_t perm_ws_bytes, int32_t double_buffer,
+                                    hipStream_t stream, hipStream_t copy_stream);
+
+/*
  * Unfused combine [FT-zh, Core method: the partial sums of a token's experts
  * merge into its output exactly; Edge0, section 2 "MoE routing": the output is
  * the routing-weighted sum over the selected experts]:

@@ -17,7 +17,7 @@ from .abi import (LayerDesc, Cache, EvictPolicy, ClassifyOut, ROUTE_SOFTMAX_TOPK
 from .ops import (router_logits, route, dedup, classify_evict, cache_fill, cache_rebuild,
                   permute, expert_ffn_decode, decode_layer, decode_layer_static, route_plan,
                   evict_fill,
-                  expert_ffn_prefill, expert_ffn_prefill_mx, quantize_mx, combine,
+                  expert_ffn_prefill, expert_ffn_prefill_mx, quantize_mx, prefill_layers, combine,
                   workspace_bytes, pack_experts,
                   expert_bytes, version, check_build, error_word, check_error, ERR_WAIT,
                   ERR_F16_RANGE, DeviceCache, DeviceClassifyOut)
@@ -25,7 +25,7 @@ from .ops import (router_logits, route, dedup, classify_evict, cache_fill, cache
 __all__ = [
     "LayerDesc", "Cache", "EvictPolicy", "ClassifyOut", "ROUTE_SOFTMAX_TOPK",
     "ROUTE_SIGMOID_GROUP", "W_INT4_G64", "W_MXFP4", "MODE_DECODE", "MODE_PREFILL", "MODE_PERMUTE",
-    "MODE_PREFILL_MX", "expert_ffn_prefill_mx", "quantize_mx",
+    "MODE_PREFILL_MX", "expert_ffn_prefill_mx", "quantize_mx", "prefill_layers",
     "Moe355Error", "lib_path", "load", "router_logits", "route", "dedup", "classify_evict",
     "cache_fill", "cache_rebuild", "permute", "expert_ffn_decode", "decode_layer",
     "decode_layer_static", "route_plan",

@@ -83,6 +83,9 @@ _SIGS = {
     "moe355_quantize_mx": (c_i32, [c_ptr, c_i64, c_i32, c_ptr, c_ptr, c_ptr]),
     "moe355_expert_ffn_prefill_mx": (c_i32, [_P(LayerDesc), c_ptr, c_i32, c_ptr, c_ptr, c_ptr,
                                              c_ptr, c_ptr, c_ptr, c_ptr, ctypes.c_size_t, c_ptr]),
+    "moe355_prefill_layers": (c_i32, [_P(LayerDesc), c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
+                                      c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, ctypes.c_size_t,
+                                      c_ptr, ctypes.c_size_t, c_i32, c_ptr, c_ptr]),
     "moe355_combine": (c_i32, [c_i32, c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr]),
     "moe355_workspace_bytes": (ctypes.c_size_t, [_P(LayerDesc), c_i32, c_i32]),
 }

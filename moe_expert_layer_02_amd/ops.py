@@ -308,6 +308,32 @@ def expert_ffn_prefill_mx(desc, x_bf16, topk_ids, topk_w, layer_w, perm, offsets
           "moe355_expert_ffn_prefill_mx")
 
 
+def prefill_layers(desc, host_pool, bufs, logits, xs, outs, topk_ids, topk_w, perm, offsets, ws,
+                   perm_ws, double_buffer: bool, stream=None, copy_stream=None):
+    """Prefill of len(logits) layers, experts streamed from a pinned host pool
+    through one or two whole-layer device buffers (copies on copy_stream)."""
+    if host_pool.is_cuda or not host_pool.is_pinned():
+        raise ValueError("prefill_layers: host_pool must be pinned host memory")
+    n = len(logits)
+    if not (len(xs) == len(outs) == n):
+        raise ValueError("prefill_layers: one logits, x and out tensor per layer")
+    for t in xs:
+        _need(t, torch.bfloat16, "x")
+    arr = ctypes.c_void_p * n
+    lp, xp, op = arr(*[_ptr(t) for t in logits]), arr(*[_ptr(t) for t in xs]), arr(*[_ptr(t) for t in outs])
+    T = xs[0].shape[0]
+    if copy_stream is None:
+        raise ValueError("prefill_layers: a copy stream is required")
+    check(load().moe355_prefill_layers(ctypes.byref(desc), n, T, host_pool.data_ptr(), _ptr(bufs[0]),
+                                       _ptr(bufs[1]) if double_buffer else None, lp, xp, op,
+                                       _ptr(topk_ids), _ptr(topk_w), _ptr(perm), _ptr(offsets),
+                                       _ptr(ws), ws.numel() * ws.element_size(), _ptr(perm_ws),
+                                       perm_ws.numel() * perm_ws.element_size(),
+                                       1 if double_buffer else 0, _stream(stream),
+                                       ctypes.c_void_p(copy_stream.cuda_stream)),
+          "moe355_prefill_layers")
+
+
 def combine(y, topk_w, out, stream=None):
     T, k = topk_w.shape
     H = out.shape[1]

@@ -82,6 +82,16 @@ DS_STRESS = Workload(
 
 ALL = {w.cid: w for w in (TINY, QWEN_DECODE, QWEN_PREFILL, DS_DECODE, DS_STRESS)}
 
+# Single-stream (one token per step) DeepSeek-style decode trace, for the miss
+# rate versus cache size replay: the pages replay the routing of single agent
+# sessions, and a 16-token batch's working set (about 56 experts per layer call)
+# exceeds small caches by itself.
+DS_DECODE_SINGLE = Workload(
+    cid=10, name="dsv_like_decode_single_stream", hidden=4096, inter=2048, n_experts=256,
+    top_k=6, route=ROUTE_SIGMOID_GROUP, n_group=8, topk_group=4, route_scale=2.5,
+    wfmt=WFMT_MXFP4, n_layers=24, n_slots=1024, t_decode=1, steps=256, zipf_alpha=1.0,
+    keep_prob=0.6)
+
 
 def seed(cid: int, stream: int) -> int:
     """Seed of one input stream: 0 weights, 1 activations, 2 logits / trace."""

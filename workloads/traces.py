@@ -48,6 +48,17 @@ def prefill_logits(w: Workload) -> np.ndarray:
         (w.t_prefill, w.n_experts), dtype=np.float32)
 
 
+def prefill_x_layer(w: Workload, layer: int) -> np.ndarray:
+    """Activations of one layer of a multi-layer prefill, bf16 bits [T, H]
+    (independent per layer, like the decode draws)."""
+    return bf16_normal(_rng(seed(w.cid, 1), 0xFFFE, layer), (w.t_prefill, w.hidden))
+
+
+def prefill_logits_layer(w: Workload, layer: int) -> np.ndarray:
+    return _rng(seed(w.cid, 2), 0xFFFE, layer).standard_normal(
+        (w.t_prefill, w.n_experts), dtype=np.float32)
+
+
 def tiny_inputs(w: Workload):
     """x bf16 bits [T, H] and router weights fp32 N(0, 0.02) [E, H]."""
     x = bf16_normal(_rng(seed(w.cid, 1)), (w.t_decode, w.hidden))
