@@ -76,7 +76,7 @@ def cpu_baseline_decode(w, trace, n_calls: int, budget_s: float):
                       f"GEMV + combine, {dt:.1f} s"}
 
 
-def bench_decode(args, w):
+def bench_decode(args, w, pool=None, q=None, roofline=True):
     """Timed region: K decode steps, each one replay of a captured graph holding
     the step's 40 (or 24) layer calls, after the step's inputs (logits,
     activations, tick base) are staged in HBM.  Layer call order "fused":
@@ -102,9 +102,10 @@ def bench_decode(args, w):
     L, T = w.n_layers, w.t_decode
     n_trace = w.steps
     trace = tr.DecodeTrace(w, n_trace)
-    pool = wg.make_pool(w, pack=lambda src, dst, n: m.pack_experts(desc, src, dst, n))
+    if pool is None:
+        pool = wg.make_pool(w, pack=lambda src, dst, n: m.pack_experts(desc, src, dst, n))
     K = w.victims_k
-    policy = m.EvictPolicy(K, w.q_num, w.q_den)
+    policy = m.EvictPolicy(K, *(q if q is not None else (w.q_num, w.q_den)))
     cap = max(K, min(T * w.top_k, w.n_experts))
     logits_all = torch.from_numpy(trace.logits).to(dev)                      # [steps, L, T, E]
     xs_all = torch.stack([torch.stack([_x_dev(tr.decode_x(w, s, l), torch) for l in range(L)])
@@ -197,6 +198,10 @@ def bench_decode(args, w):
     bytes_total = n_uniq * S
     n_calls = args.steps * L
     value = bytes_total / dt / 1e9
+    if not roofline:
+        return {"value": round(value, 2), "unit": "GB/s", "ms_per_step": round(dt / args.steps * 1e3, 4),
+                "replay_ms_per_step": round(replay_s / args.steps * 1e3, 4), "steps": args.steps,
+                "policy_q": [policy.q_num, policy.q_den]}
 
     # roofline pass: the FFN kernels alone.  Each step's bookkeeping (route,
     # classify_evict, cache_fill) runs eagerly for all layers first; then the
@@ -556,6 +561,90 @@ def bench_prefill_pipeline(args, w, n_layers: int):
             "overlap_of_compute": round((tc + tcopy - t2) / tc, 4)}
 
 
+def bench_decode_host_pool(args):
+    """The Qwen-like decode stream with the expert pool in pinned host memory
+    (the host tier): B_P is the pinned host-to-device DMA rate of one layer of
+    experts; B_H the rate at which the decode FFN computes experts in place
+    straight from that pool (every expert of a step's calls read over PCIe);
+    q* = m * B_P / B_H (rounded, clamped to m).  The step is then timed under
+    that split, under pure fill (q = m) and under no fill (q = 0: every miss
+    computed in place from host memory, the cache never filled)."""
+    import torch
+    from fractions import Fraction
+    import moe_expert_layer_02_amd as m
+    from workloads import configs as C
+    from workloads import experts as wx
+    from workloads import gpu as wg
+    from workloads import traces as tr
+    w = C.QWEN_DECODE
+    desc = m.LayerDesc(w.hidden, w.inter, w.n_experts, w.top_k, w.route, w.n_group,
+                       w.topk_group, w.route_scale, w.wfmt)
+    S, E, L = wx.expert_bytes(w.wfmt, w.hidden, w.inter), w.n_experts, w.n_layers
+    t0 = time.perf_counter()
+    pool_dev = wg.make_pool(w, pack=lambda src, dst, n: m.pack_experts(desc, src, dst, n))
+    host = torch.empty(pool_dev.numel(), dtype=torch.uint8, pin_memory=True)
+    host.copy_(pool_dev)
+    del pool_dev
+    torch.cuda.empty_cache()
+    setup_s = time.perf_counter() - t0
+    stream = torch.cuda.current_stream()
+
+    def med_time(fn, reps=5):
+        ts = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        return float(np.median(ts))
+
+    # B_P: one layer of experts (E * S bytes) by DMA
+    buf = torch.empty(E * S, dtype=torch.uint8, device="cuda")
+    t_copy = med_time(lambda: buf.copy_(host[:E * S], non_blocking=True))
+    B_P = E * S / t_copy / 1e9
+    del buf
+    # B_H: one step's 40 FFN calls with every routed expert read in place from the host pool
+    trace = tr.DecodeTrace(w, 2)
+    T = w.t_decode
+    ids = torch.empty((L, T, w.top_k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((L, T, w.top_k), dtype=torch.float32, device="cuda")
+    lg = torch.from_numpy(trace.logits[0]).cuda()
+    xs = torch.stack([_x_dev(tr.decode_x(w, 0, l), torch) for l in range(L)])
+    outs = torch.empty((L, T, w.hidden), dtype=torch.float32, device="cuda")
+    lists = [m.DeviceClassifyOut(min(T * w.top_k, E)) for _ in range(L)]
+    ws = torch.zeros(m.workspace_bytes(desc, T, m.MODE_DECODE), dtype=torch.uint8, device="cuda")
+    for l in range(L):
+        m.route(desc, lg[l], ids[l], wt[l])
+        m.dedup(ids[l], E, lists[l])
+
+    def in_place_step():
+        for l in range(L):
+            m.expert_ffn_decode(desc, xs[l], ids[l], wt[l], None, host, l, lists[l], outs[l], ws)
+    in_place_step()
+    t_inplace = med_time(in_place_step)
+    m.check_error(ws, what="in-place FFN calls from host memory")
+    n_uniq = sum(int(lists[l].counts[0].item()) for l in range(L))
+    B_H = n_uniq * S / t_inplace / 1e9
+    ratio = Fraction(B_P / B_H).limit_denominator(64)
+    q_star = (ratio.numerator, ratio.denominator)
+    policies = {"q_star": q_star, "pure_fill": (1, 1), "no_fill": (0, 1)}
+    res = {"metric": "decode MoE-layer steps with the expert pool in pinned host memory",
+           "unit": "ms per step", "n_gpus": 1, "higher_is_better": False, "data": "synthetic",
+           "config": {"workload": w.name + "_host_pool", "layers": L, "tokens_per_step": T,
+                      "pool_bytes": int(host.numel()), "cache_slots": w.n_slots},
+           "B_P_GBs": round(B_P, 2), "B_H_GBs": round(B_H, 2),
+           "q_star": f"q = round(m * {q_star[0]} / {q_star[1]}), clamped to m",
+           "setup_s": round(setup_s, 1), "policies": {}}
+    for name, q in policies.items():
+        r = bench_decode(args, w, pool=host, q=q, roofline=False)
+        res["policies"][name] = r
+        print(f"host pool {name}: {r}", file=sys.stderr, flush=True)
+    return res
+
+
 def C_seed(w):
     from workloads import configs as C
     return C.seed(w.cid, 0)
@@ -606,7 +695,7 @@ def main():
     ap.add_argument("--workload", default="qwen_decode",
                     choices=["qwen_decode", "ds_decode", "qwen_prefill", "ds_prefill",
                              "ds_prefill_mx", "miss_replay", "qwen_prefill_pipeline",
-                             "ds_prefill_pipeline"])
+                             "ds_prefill_pipeline", "qwen_decode_host_pool"])
     ap.add_argument("--order", default="auto", choices=["auto", "fused", "split"],
                     help="decode layer call order (auto: fused)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -630,6 +719,9 @@ def main():
     from workloads import configs as C
     if args.workload == "miss_replay":
         print(json.dumps(bench_miss_replay(args)), flush=True)
+        return
+    if args.workload == "qwen_decode_host_pool":
+        print(json.dumps(bench_decode_host_pool(args)), flush=True)
         return
     if args.workload.endswith("_pipeline"):
         w, n = (C.QWEN_PREFILL, 8) if args.workload.startswith("qwen") else (C.DS_STRESS, 4)

@@ -24,6 +24,18 @@ def _ptr(t) -> int | None:
     return t.data_ptr()
 
 
+def _pool_ptr(t) -> int:
+    """The expert pool: device memory, or pinned host memory (the host tier, read
+    by the kernels over PCIe)."""
+    if t.is_cuda:
+        return _ptr(t)
+    if not t.is_pinned():
+        raise ValueError("libmoe355: a host expert pool must be pinned memory")
+    if not t.is_contiguous():
+        raise ValueError("libmoe355 takes contiguous tensors")
+    return t.data_ptr()
+
+
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
@@ -181,7 +193,7 @@ def classify_evict(cache: DeviceCache, layer: int, tick: int, ids, policy: Evict
 def cache_fill(cache: DeviceCache, pool, layer: int, out: DeviceClassifyOut, max_fill: int,
                stream=None):
     _need(pool, torch.uint8, "pool")
-    check(load().moe355_cache_fill(ctypes.byref(cache.struct), _ptr(pool), layer,
+    check(load().moe355_cache_fill(ctypes.byref(cache.struct), _pool_ptr(pool), layer,
                                    ctypes.byref(out.struct), max_fill, _stream(stream)),
           "moe355_cache_fill")
 
@@ -206,7 +218,7 @@ def expert_ffn_decode(desc, x_bf16, topk_ids, topk_w, cache, pool, layer: int,
     T = x_bf16.shape[0]
     cptr = ctypes.byref(cache.struct) if cache is not None else None
     check(load().moe355_expert_ffn_decode(ctypes.byref(desc), _ptr(x_bf16), T, _ptr(topk_ids),
-                                          _ptr(topk_w), cptr, _ptr(pool), layer,
+                                          _ptr(topk_w), cptr, _pool_ptr(pool), layer,
                                           ctypes.byref(experts.struct), _ptr(out), _ptr(ws),
                                           ws.numel() * ws.element_size(), _stream(stream)),
           "moe355_expert_ffn_decode")
@@ -221,7 +233,7 @@ def decode_layer(desc, cache: DeviceCache, pool, layer: int, tick_base, tick_add
     if tick_base is not None:
         _need(tick_base, torch.int64, "tick_base")
     T = x_bf16.shape[0]
-    check(load().moe355_decode_layer(ctypes.byref(desc), ctypes.byref(cache.struct), _ptr(pool),
+    check(load().moe355_decode_layer(ctypes.byref(desc), ctypes.byref(cache.struct), _pool_ptr(pool),
                                      layer, _ptr(tick_base), tick_add, _ptr(logits), _ptr(x_bf16),
                                      T, ctypes.byref(policy), _ptr(topk_ids), _ptr(topk_w),
                                      ctypes.byref(lists.struct), _ptr(out), _ptr(ws),
@@ -241,7 +253,7 @@ def decode_layer_static(desc, cache: DeviceCache, pool, layer: int, tick_base, t
         _need(tick_base, torch.int64, "tick_base")
     T = x_bf16.shape[0]
     check(load().moe355_decode_layer_static(ctypes.byref(desc), ctypes.byref(cache.struct),
-                                            _ptr(pool), layer, _ptr(tick_base), tick_add,
+                                            _pool_ptr(pool), layer, _ptr(tick_base), tick_add,
                                             _ptr(logits), _ptr(x_bf16), T, ctypes.byref(policy),
                                             _ptr(topk_ids), _ptr(topk_w), ctypes.byref(lists.struct),
                                             _ptr(out), _ptr(err_word), _stream(stream)),
@@ -266,7 +278,7 @@ def evict_fill(desc, cache: DeviceCache, pool, layer: int, tick_base, tick_add: 
     if tick_base is not None:
         _need(tick_base, torch.int64, "tick_base")
     T = topk_ids.shape[0]
-    check(load().moe355_evict_fill(ctypes.byref(desc), ctypes.byref(cache.struct), _ptr(pool),
+    check(load().moe355_evict_fill(ctypes.byref(desc), ctypes.byref(cache.struct), _pool_ptr(pool),
                                    layer, _ptr(tick_base), tick_add, _ptr(topk_ids), T,
                                    ctypes.byref(policy), ctypes.byref(lists.struct),
                                    _stream(stream)), "moe355_evict_fill")

@@ -228,20 +228,28 @@ def _sampler(cid, steps, mode):
 
 
 CASES = [
-    # (workload, steps, tick base)
-    (2, 64, 0), (4, 24, 0), (5, 24, 0), (6, 40, 0), (7, 40, 0), (8, 40, 0), (9, 40, 0),
-    (2, 16, WIDE_TICK), (9, 40, WIDE_TICK), (4, 8, WIDE_TICK),
+    # (workload, steps, tick base, pool in pinned host memory)
+    (2, 64, 0, False), (4, 24, 0, False), (5, 24, 0, False), (6, 40, 0, False), (7, 40, 0, False),
+    (8, 40, 0, False), (9, 40, 0, False),
+    (2, 16, WIDE_TICK, False), (9, 40, WIDE_TICK, False), (4, 8, WIDE_TICK, False),
+    # the host tier: misses read (in place, or while filling) over PCIe from pinned memory
+    (9, 40, 0, True), (7, 40, 0, True), (6, 40, 0, True),
 ]
 
 
-def _run_decode_trace(cid, steps, mode, tick0):
+def _run_decode_trace(cid, steps, mode, tick0, host_pool=False):
     import torch
     import moe_expert_layer_02_amd as m
     from workloads import gpu as wg
     w = _workload(cid)
-    say(f"decode_layer trace {w.name} ({mode}): {steps} steps, tick base {tick0}")
+    say(f"decode_layer trace {w.name} ({mode}): {steps} steps, tick base {tick0}, "
+        f"pool in {'pinned host' if host_pool else 'device'} memory")
     trace = tr.DecodeTrace(w, steps)
-    pool = wg.make_pool(w, pack=packer(desc_of(w)))
+    pool_dev = wg.make_pool(w, pack=packer(desc_of(w)))
+    pool = pool_dev
+    if host_pool:
+        pool = torch.empty(pool_dev.numel(), dtype=torch.uint8, pin_memory=True)
+        pool.copy_(pool_dev)
     run = LayerRunner(w, w.n_slots, pool, mode, tick0=tick0)
     sim = ocache.CacheSim(w.n_slots, w.n_layers, w.n_experts)
     sampler = _sampler(cid, steps, mode)
@@ -260,15 +268,15 @@ def _run_decode_trace(cid, steps, mode, tick0):
         sampler.take(run, s, routed)
         if s % 64 == 63:
             say(f"{w.name}: step {s + 1}/{steps}")
-    n_occ = _check_cache_state(run, sim, pool)
+    n_occ = _check_cache_state(run, sim, pool_dev)
     say(f"{w.name}: {steps * w.n_layers} calls bit-exact, {n_occ} slots hold their pool bytes")
     sampler.verify(w, BlobSource(w), f"{w.name} ({mode})")
 
 
 @pytest.mark.parametrize("mode", ["fused", "split"])
-@pytest.mark.parametrize("cid,steps,tick0", CASES)
-def test_decode_layer_trace(cid, steps, tick0, mode):
-    _run_decode_trace(cid, steps, mode, tick0)
+@pytest.mark.parametrize("cid,steps,tick0,host_pool", CASES)
+def test_decode_layer_trace(cid, steps, tick0, host_pool, mode):
+    _run_decode_trace(cid, steps, mode, tick0, host_pool)
 
 
 @pytest.mark.timeout(900)
