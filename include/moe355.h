@@ -447,9 +447,8 @@ moe355_status moe355_quantize_mx(const void* x_bf16, int64_t rows, int32_t cols,
 /*
  * Prefill expert FFN for MXFP4 experts on the native fp4 matrix cores
  * (v_mfma_scale_f32_32x32x64_f8f6f4): the e2m1 weights with their e8m0 block
- * scales against MX FP8 E4M3 activations.  The benchmark spec asks for native fp4
- * MFMA where the path is MXFP4; the pages' MXFP4 models are the DeepSeek-V4-Flash
- * rows of [FT-zh, Results].  Same call shape as moe355_expert_ffn_prefill, but
+ * scales against MX FP8 E4M3 activations (the pages' MXFP4 models are the
+ * DeepSeek-V4-Flash rows of [FT-zh, Results]).  Same call shape as moe355_expert_ffn_prefill, but
  * a different result: x is quantised as moe355_quantize_mx does (per token,
  * blocks of 32 along H), and h = silu(gate x) * (up x) is carried into the down
  * projection as two MX FP8 terms per routed pair (blocks of 32 along I):

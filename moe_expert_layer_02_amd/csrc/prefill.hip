@@ -245,7 +245,7 @@ __global__ void __launch_bounds__(256) x16_kernel(const uint16_t* __restrict__ x
 // for a dword load, past the LDS address in M0) into a ring of PD stage slots,
 // PD - 1 stages ahead of the MFMAs; one barrier per stage.
 //   A (activation rows): 128 rows x 64 inputs; 16-byte chunk c of row r sits at
-//     chunk (c ^ (r & 7)) of the row, so each lane fetches the chunk that belongs
+//     chunk (c ^ swz8(r)) of the row, so each lane fetches the chunk that belongs
 //     where it lands and the MFMA reads are free of bank conflicts.
 //   B (weight rows): per wavefront 2 column tiles x 64 lanes x 16 bytes of codes
 //     in MFMA operand order, then one dword per lane and tile holding its scale.
@@ -320,10 +320,23 @@ __device__ __forceinline__ uint4 b_operand(const uint4& q, uint32_t sc, int kk, 
         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3)));
 }
 
+// LDS swizzles of staged activation rows.  A 16-byte read by 64 lanes is served
+// 16 lanes (256 bytes, the LDS's 64 four-byte banks) at a time; the 16 lanes of
+// a group read 16 consecutive rows at one chunk index, so a row's chunks are
+// permuted to put those rows on distinct banks:
+//   128-byte rows (8 chunks): chunk c at slot c ^ ((r >> 1) & 7) -- rows of one
+//     parity share a 128-byte bank half and differ in (r >> 1) & 7;
+//   64-byte rows (4 chunks): chunk c at slot c ^ ((r >> 2) & 3) -- four
+//     consecutive rows fill 256 bytes and the next four move to other slots.
+// (XOR with r & 7 or r & 3 puts rows r and r + 8, or r + 4, on the same banks:
+// measured 1.2e8 and 1.7e8 bank-conflict cycles per call on the DS-like layer.)
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz4(int r) { return (r >> 2) & 3; }
+
 // A operand of MFMA step s for row tile mt from a staged 128 x 64 tile.
 __device__ __forceinline__ uint4 a_operand(const uint4* A, int mt, int ln, int hh, int s) {
     const int r = mt * 32 + ln, c = 4 * hh + s;
-    return A[r * 8 + (c ^ (r & 7))];
+    return A[r * 8 + (c ^ swz8(r))];
 }
 
 // Byte offsets (from the expert's blob) of weight sources in the device
@@ -409,7 +422,7 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
         uint32_t aoff[4];   // this lane's A sources: 4 blocks of 8 rows of the tile
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int r = 8 * (4 * wv + j) + lane / 8, c = (lane % 8) ^ (lane / 8);
+            const int r = 8 * (4 * wv + j) + lane / 8, c = (lane % 8) ^ swz8(r);
             aoff[j] = static_cast<uint32_t>(rtok[r]) * static_cast<uint32_t>(2 * H) + c * 16;
         }
         uint32_t bq[4], bsc[2];
@@ -627,7 +640,7 @@ __global__ void __launch_bounds__(256) down_mfma(PrefillParams p) {
         uint32_t aoff[4];   // rows past the bucket re-read its first row
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int r = 8 * (4 * wv + j) + lane / 8, c = (lane % 8) ^ (lane / 8);
+            const int r = 8 * (4 * wv + j) + lane / 8, c = (lane % 8) ^ swz8(r);
             aoff[j] = static_cast<uint32_t>(r < rows ? r : 0) * static_cast<uint32_t>(2 * I) + c * 16;
         }
         uint32_t bq[4], bsc[2];
@@ -880,14 +893,14 @@ struct MxParams {
 };
 
 // gate/up stage slot (K = 128): activation rows 128 x 128 bytes (16-byte chunk c
-// of row r at slot c ^ (r & 7)); weights [wavefront][4 column tiles][2 halves]
+// of row r at slot c ^ swz8(r)); weights [wavefront][4 column tiles][2 halves]
 // [64 lanes] x 16 bytes in MFMA operand order; weight scale dwords [wavefront]
 // [2][64] (row 64 j + i of load j); activation scale dwords [wavefront][64]
 // (row 32 w + i at i < 32).
 constexpr int MG_A = 0, MG_W = 16384, MG_WS = 49152, MG_XS = 51200, MG_SLOT = 52224, MG_PD = 3;
 constexpr int MG_K = 128;
 // down stage slot (K = 64): two h terms of 128 rows x 64 bytes (chunk c of row r
-// at slot c ^ (r & 3)); weights [wavefront][4][64] x 16 bytes; weight scale
+// at slot c ^ swz4(r)); weights [wavefront][4][64] x 16 bytes; weight scale
 // dwords [wavefront][2][64]; h scale dwords per term [wavefront][64].
 constexpr int MD_A0 = 0, MD_A1 = 8192, MD_W = 16384, MD_WS = 32768, MD_HS = 34816,
               MD_SLOT = 36864, MD_PD = 4;
@@ -932,7 +945,7 @@ __global__ void __launch_bounds__(256) gate_up_mx(MxParams p) {
         uint32_t aoff[4];   // this lane's activation sources: 4 blocks of 8 rows
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int r = 8 * (4 * wv + j) + lane / 8, c = (lane % 8) ^ (lane / 8);
+            const int r = 8 * (4 * wv + j) + lane / 8, c = (lane % 8) ^ swz8(r);
             aoff[j] = static_cast<uint32_t>(rtok[r]) * static_cast<uint32_t>(H) + c * 16;
         }
         // activation scale dwords: row 32 wv + ln (both lane halves load it)
@@ -979,8 +992,8 @@ __global__ void __launch_bounds__(256) gate_up_mx(MxParams p) {
                 for (int mt = 0; mt < 4; ++mt) {
                     // inputs 16 hh + [0, 16) and 32 + 16 hh + [0, 16) of half s
                     const int r = mt * 32 + ln, c0 = 4 * s + hh;
-                    const uint4 u0 = A[r * 8 + (c0 ^ (r & 7))];
-                    const uint4 u1 = A[r * 8 + ((c0 + 2) ^ (r & 7))];
+                    const uint4 u0 = A[r * 8 + (c0 ^ swz8(r))];
+                    const uint4 u1 = A[r * 8 + ((c0 + 2) ^ swz8(r))];
                     xb[mt] = i32x8{static_cast<int>(u0.x), static_cast<int>(u0.y), static_cast<int>(u0.z),
                                    static_cast<int>(u0.w), static_cast<int>(u1.x), static_cast<int>(u1.y),
                                    static_cast<int>(u1.z), static_cast<int>(u1.w)};
@@ -1099,7 +1112,7 @@ __global__ void __launch_bounds__(256) down_mx(MxParams p) {
         uint32_t aoff[2];   // 2 blocks of 16 rows x 4 chunks; rows past the bucket re-read row 0
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int r = 16 * (2 * wv + j) + lane / 4, c = (lane % 4) ^ ((lane / 4) & 3);
+            const int r = 16 * (2 * wv + j) + lane / 4, c = (lane % 4) ^ swz4(r);
             aoff[j] = static_cast<uint32_t>(r < rows ? r : 0) * static_cast<uint32_t>(I) + c * 16;
         }
         const int srow = 32 * wv + ln;
@@ -1148,8 +1161,8 @@ __global__ void __launch_bounds__(256) down_mx(MxParams p) {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     const int r = mt * 32 + ln;
-                    const uint4 u0 = A[r * 4 + (hh ^ (r & 3))];         // inputs 16 hh + [0, 16)
-                    const uint4 u1 = A[r * 4 + ((2 + hh) ^ (r & 3))];   // 32 + 16 hh + [0, 16)
+                    const uint4 u0 = A[r * 4 + (hh ^ swz4(r))];         // inputs 16 hh + [0, 16)
+                    const uint4 u1 = A[r * 4 + ((2 + hh) ^ swz4(r))];   // 32 + 16 hh + [0, 16)
                     const i32x8 xa = {static_cast<int>(u0.x), static_cast<int>(u0.y), static_cast<int>(u0.z),
                                       static_cast<int>(u0.w), static_cast<int>(u1.x), static_cast<int>(u1.y),
                                       static_cast<int>(u1.z), static_cast<int>(u1.w)};

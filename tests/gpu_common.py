@@ -8,7 +8,7 @@ import numpy as np
 from workloads import configs as C
 from workloads import experts as wx
 
-# spec tolerances for the layer output
+# parity tolerances for the layer output (relative L2 and absolute)
 REL_L2 = 1e-2
 MAX_ABS = 2e-2
 
