@@ -17,8 +17,11 @@
 //     with the scale) and x is bf16 already.
 //   * down projection: h = silu(g) * u enters as two 16-bit terms (hi + lo)
 //     accumulated into the same registers.
-//   * combine: out[t] += w * y with fp32 atomics in the down kernel's epilogue
-//     (the gate/up kernel zeroes `out` first), so no [T*k, H] intermediate.
+//   * combine: the down kernel stores each pair's y row (fp32, plain stores)
+//     at row t k + j of a [T*k, H] workspace array; a last pass sums a token's
+//     k rows with its weights, j ascending.  An fp32 atomic add per output
+//     element would avoid the intermediate but runs at one element per L2
+//     channel per clock, several times slower than the store and re-read.
 //
 // Tiling: v_mfma_f32_32x32x16 (f16 for int4, bf16 for MXFP4), 4 wavefronts per
 // block, tiles of 128 pair rows x 256 weight rows, K staged 64 at a time through
@@ -27,6 +30,8 @@
 // the other buffer after them.  Blocks are persistent (one per CU); the tiles of
 // a call are split into 8 contiguous ranges, one per XCD (block id mod 8), so
 // tiles that share activation rows or an expert's weights share an L2.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace moe355 {
@@ -57,7 +62,7 @@ struct PrefillParams {
     uint16_t* h_hi;          // [T*k][I] h = silu(g) * u, high half (f16 int4, bf16 MXFP4)
     uint16_t* h_lo;          // [T*k][I] remainder
     float* hsum;             // int4: [T*k][I / 64] group sums of h
-    float* out;
+    float* y;                // [T*k][H] down outputs by pair id t k + j
     uint32_t* err;           // the call's error word (cleared by the plan kernel)
 };
 
@@ -112,6 +117,12 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // Shared pieces of the two GEMMs.
+
+// silu(g) = g / (1 + e^-g) with the hardware reciprocal (1 ulp); e^-g = inf
+// gives -0 for very negative g.
+__device__ __forceinline__ float silu(float g) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
 
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -389,13 +400,6 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
     const int H = p.H, I = p.I, G = H / 64, KS = H / BK;
     const uint32_t ring_lds = lds_addr(ring);
 
-    {   // zero the layer output for the down kernel's atomics
-        const int64_t n = static_cast<int64_t>(p.T) * H;
-        for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + tid; i < n;
-             i += static_cast<int64_t>(gridDim.x) * 256)
-            p.out[i] = 0.0f;
-    }
-
     const int FX = (I + GU_FEAT - 1) / GU_FEAT;
     const TileRange tr = tile_range(*p.n_tiles * FX);
     const void* xs = uniform_ptr(FMT == MOE355_W_INT4_G64 ? p.xf : p.x);
@@ -445,7 +449,8 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) dma4(W, bsc[j] + scale_step(kk), sl + GU_S + (2 * wv + j) * 256);
         };
-        auto compute = [&](int kk, int slot) {
+        auto compute = [&](auto NMTc, int kk, int slot) {
+            constexpr int NMT = decltype(NMTc)::value;
             const uint8_t* sp = ring + slot * GU_SLOT;
             const uint4* A = reinterpret_cast<const uint4*>(sp + GU_A);
             const uint4* Bq = reinterpret_cast<const uint4*>(sp + GU_B) + 4 * wv * 64 + lane;
@@ -461,34 +466,44 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
             // wavefront per SIMD nothing else hides the LDS latency
             uint4 a[2][4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) a[0][mt] = a_operand(A, mt, ln, hh, 0);
+            for (int mt = 0; mt < NMT; ++mt) a[0][mt] = a_operand(A, mt, ln, hh, 0);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 if (s + 1 < 4) {
 #pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) a[(s + 1) & 1][mt] = a_operand(A, mt, ln, hh, s + 1);
+                    for (int mt = 0; mt < NMT; ++mt) a[(s + 1) & 1][mt] = a_operand(A, mt, ln, hh, s + 1);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const uint4 b = b_operand<FMT>(q[c], sc[c], kk, hh, s);
 #pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) R[c][mt] = mma<FMT>(b, a[s & 1][mt], R[c][mt]);
+                    for (int mt = 0; mt < NMT; ++mt) R[c][mt] = mma<FMT>(b, a[s & 1][mt], R[c][mt]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
+        // the row tiles past the bucket's last row are skipped (a bucket's last
+        // tile is often short); NMT = row tiles of 32 the MFMAs cover
+        auto kloop = [&](auto NMTc) {
 #pragma unroll
-        for (int kk = 0; kk < D; ++kk)
-            if (kk < KS) issue(kk, kk);
-        int slot = 0;
+            for (int kk = 0; kk < D; ++kk)
+                if (kk < KS) issue(kk, kk);
+            int slot = 0;
 #pragma nounroll
-        for (int kk = 0; kk < KS; ++kk) {
-            stage_wait<OPS, D - 1>(KS - 1 - kk);   // stage kk has landed everywhere
-            const int next = slot == 0 ? PD - 1 : slot - 1;   // (slot + D) % PD: the slot read last stage
-            if (kk + D < KS) issue(kk + D, next);
-            compute(kk, slot);
-            slot = slot == PD - 1 ? 0 : slot + 1;
+            for (int kk = 0; kk < KS; ++kk) {
+                stage_wait<OPS, D - 1>(KS - 1 - kk);   // stage kk has landed everywhere
+                const int next = slot == 0 ? PD - 1 : slot - 1;   // (slot + D) % PD: the slot read last stage
+                if (kk + D < KS) issue(kk + D, next);
+                compute(NMTc, kk, slot);
+                slot = slot == PD - 1 ? 0 : slot + 1;
+            }
+        };
+        switch (__builtin_amdgcn_readfirstlane((rows + 31) / 32)) {
+            case 1: kloop(std::integral_constant<int, 1>{}); break;
+            case 2: kloop(std::integral_constant<int, 2>{}); break;
+            case 3: kloop(std::integral_constant<int, 3>{}); break;
+            default: kloop(std::integral_constant<int, 4>{}); break;
         }
 
         if (FMT == MOE355_W_INT4_G64) {
@@ -533,7 +548,7 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const float g = R[ft][mt][4 * q + j], u = R[2 + ft][mt][4 * q + j];
-                        const float hv = g / (1.0f + __expf(-g)) * u;
+                        const float hv = silu(g) * u;
                         if (FMT == MOE355_W_INT4_G64) {
                             const _Float16 x1 = static_cast<_Float16>(hv);
                             const _Float16 x2 = static_cast<_Float16>(hv - static_cast<float>(x1));
@@ -589,18 +604,72 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// down + combine: A = the tile's 128 rows of h (hi and lo); B = down rows
-// nw + [0, 128) for wavefront w, nw = n0 + 128 w, as 4 column tiles; the
-// weighted rows are added into the output with fp32 atomics (a lane holds one
-// output column of 16 rows per row tile, so each atomic instruction covers 128
-// contiguous bytes of 2 rows).
+// Down epilogue: accumulator R[mt][c] of a wavefront holds rows 32 mt + 8 (i / 4)
+// + 4 hh + i % 4 (element i, lane half hh) of output column nw + 32 c + ln;
+// each row is stored at its pair id's row of y.  Every pair of the layer
+// belongs to exactly one tile row, so the down kernel writes all of y.
+__device__ __forceinline__ void store_y_rows(float* y, int H, int nw, const int32_t* rpair, int rows,
+                                             int lane, const f32x16 (&R)[4][4]) {
+    const int ln = lane & 31, h4 = 4 * (lane >> 5);
+    const int32_t* rp = rpair + h4;
+    float* ybase = y + nw + ln;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int rc = mt * 32 + 8 * (i >> 2) + (i & 3);
+            if (rc + h4 < rows) {
+                float* yrow = ybase + static_cast<int64_t>(rp[rc]) * H;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) __builtin_nontemporal_store(R[mt][c][i], yrow + 32 * c);
+            }
+        }
+}
+
+// Combine [FT-zh, Core method: a token's expert outputs merge into one sum]:
+// out[t] = sum over j ascending of w[t, j] y[t k + j], fp32, 4 columns a thread.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__global__ void __launch_bounds__(256) combine_rows_kernel(const f32x4* __restrict__ y,
+                                                           const float* __restrict__ w, int k,
+                                                           uint32_t H4, uint32_t n4,
+                                                           f32x4* __restrict__ out) {
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i >= n4) return;
+    const uint32_t t = i / H4, c = i - t * H4;
+    const f32x4* yr = y + static_cast<int64_t>(t) * k * H4 + c;
+    const float* wt = w + static_cast<int64_t>(t) * k;
+    f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < k; ++j) {
+        const float wj = wt[j];
+        const f32x4 v = __builtin_nontemporal_load(yr + static_cast<int64_t>(j) * H4);
+        a.x = fmaf(wj, v.x, a.x);
+        a.y = fmaf(wj, v.y, a.y);
+        a.z = fmaf(wj, v.z, a.z);
+        a.w = fmaf(wj, v.w, a.w);
+    }
+    out[i] = a;
+}
+
+moe355_status launch_combine(const float* y, const float* w, int T, int k, int H, float* out,
+                             hipStream_t stream, const char* what) {
+    const uint32_t H4 = static_cast<uint32_t>(H / 4);
+    const uint32_t n4 = static_cast<uint32_t>(T) * H4;
+    combine_rows_kernel<<<(n4 + 255) / 256, 256, 0, stream>>>(reinterpret_cast<const f32x4*>(y), w, k,
+                                                              H4, n4, reinterpret_cast<f32x4*>(out));
+    return check_launch(what);
+}
+
+// ---------------------------------------------------------------------------
+// down: A = the tile's 128 rows of h (hi and lo); B = down rows nw + [0, 128)
+// for wavefront w, nw = n0 + 128 w, as 4 column tiles; the y rows go to the
+// pair-indexed array (a lane holds one output column of 16 rows per row tile,
+// so each store instruction covers 128 contiguous bytes of 2 rows).
 template <int FMT>
 __global__ void __launch_bounds__(256) down_mfma(PrefillParams p) {
     constexpr int PD = DN_PD, D = PD - 1, OPS = 14;   // loads per stage per wavefront
     extern __shared__ uint4 smem[];
     uint8_t* ring = reinterpret_cast<uint8_t*>(smem);                  // [PD][DN_SLOT]
-    int32_t* rtok = reinterpret_cast<int32_t*>(ring + PD * DN_SLOT);
-    float* rw = reinterpret_cast<float*>(rtok + BM);
+    int32_t* rpair = reinterpret_cast<int32_t*>(ring + PD * DN_SLOT);
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int H = p.H, I = p.I, Gd = I / 64, KS = I / BK;
@@ -627,16 +696,7 @@ __global__ void __launch_bounds__(256) down_mfma(PrefillParams p) {
         const void* hb = uniform_ptr(p.h_hi + static_cast<int64_t>(pbase) * I);   // h rows are the bucket's pairs
         const void* lb = uniform_ptr(p.h_lo + static_cast<int64_t>(pbase) * I);
         __syncthreads();   // the previous tile is done with the LDS
-        if (tid < BM) {
-            if (tid < rows) {
-                const int pr = p.perm[pbase + tid];
-                rtok[tid] = pr / p.k;
-                rw[tid] = p.topk_w[pr];
-            } else {
-                rtok[tid] = -1;
-                rw[tid] = 0.0f;
-            }
-        }
+        if (tid < BM) rpair[tid] = tid < rows ? p.perm[pbase + tid] : -1;   // pair id t k + j
         uint32_t aoff[4];   // rows past the bucket re-read its first row
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -666,7 +726,8 @@ __global__ void __launch_bounds__(256) down_mfma(PrefillParams p) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) dma4(W, bsc[j] + scale_step(kk), sl + DN_S + (2 * wv + j) * 256);
         };
-        auto compute = [&](int kk, int slot) {
+        auto compute = [&](auto NMTc, int kk, int slot) {
+            constexpr int NMT = decltype(NMTc)::value;
             const uint8_t* sp = ring + slot * DN_SLOT;
             const uint4* Ah = reinterpret_cast<const uint4*>(sp + DN_AH);
             const uint4* Al = reinterpret_cast<const uint4*>(sp + DN_AL);
@@ -683,35 +744,45 @@ __global__ void __launch_bounds__(256) down_mfma(PrefillParams p) {
             // h; its A fragments are read one half-step ahead of their use
             uint4 a[2][4], b[4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) a[0][mt] = a_operand(Ah, mt, ln, hh, 0);
+            for (int mt = 0; mt < NMT; ++mt) a[0][mt] = a_operand(Ah, mt, ln, hh, 0);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 if (u + 1 < 8) {
                     const uint4* An = ((u + 1) & 1) ? Al : Ah;
 #pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) a[(u + 1) & 1][mt] = a_operand(An, mt, ln, hh, (u + 1) >> 1);
+                    for (int mt = 0; mt < NMT; ++mt) a[(u + 1) & 1][mt] = a_operand(An, mt, ln, hh, (u + 1) >> 1);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     if ((u & 1) == 0) b[c] = b_operand<FMT>(q[c], sc[c], kk, hh, u >> 1);
 #pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) R[mt][c] = mma<FMT>(a[u & 1][mt], b[c], R[mt][c]);
+                    for (int mt = 0; mt < NMT; ++mt) R[mt][c] = mma<FMT>(a[u & 1][mt], b[c], R[mt][c]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
+        // the row tiles past the bucket's last row are skipped (a bucket's last
+        // tile is often short); NMT = row tiles of 32 the MFMAs cover
+        auto kloop = [&](auto NMTc) {
 #pragma unroll
-        for (int kk = 0; kk < D; ++kk)
-            if (kk < KS) issue(kk, kk);
-        int slot = 0;
+            for (int kk = 0; kk < D; ++kk)
+                if (kk < KS) issue(kk, kk);
+            int slot = 0;
 #pragma nounroll
-        for (int kk = 0; kk < KS; ++kk) {
-            stage_wait<OPS, D - 1>(KS - 1 - kk);
-            const int next = slot == 0 ? PD - 1 : slot - 1;
-            if (kk + D < KS) issue(kk + D, next);
-            compute(kk, slot);
-            slot = slot == PD - 1 ? 0 : slot + 1;
+            for (int kk = 0; kk < KS; ++kk) {
+                stage_wait<OPS, D - 1>(KS - 1 - kk);
+                const int next = slot == 0 ? PD - 1 : slot - 1;
+                if (kk + D < KS) issue(kk + D, next);
+                compute(NMTc, kk, slot);
+                slot = slot == PD - 1 ? 0 : slot + 1;
+            }
+        };
+        switch (__builtin_amdgcn_readfirstlane((rows + 31) / 32)) {
+            case 1: kloop(std::integral_constant<int, 1>{}); break;
+            case 2: kloop(std::integral_constant<int, 2>{}); break;
+            case 3: kloop(std::integral_constant<int, 3>{}); break;
+            default: kloop(std::integral_constant<int, 4>{}); break;
         }
 
         if (FMT == MOE355_W_INT4_G64) {
@@ -735,26 +806,7 @@ __global__ void __launch_bounds__(256) down_mfma(PrefillParams p) {
             }
         }
 
-        // combine: out[t, n] += w * y; lane (ln, hh) holds rows rc + 4 hh of
-        // column nw + 32 c + ln, rc = 32 mt + 8 (i / 4) + i % 4
-        if (live) {
-            const int h4 = 4 * hh;
-            const int32_t* rt = rtok + h4;
-            const float* rwt = rw + h4;
-            float* obase = p.out + nw + ln;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int rc = mt * 32 + 8 * (i >> 2) + (i & 3);
-                    if (rc + h4 < rows) {
-                        const float wt = rwt[rc];
-                        float* orow = obase + static_cast<int64_t>(rt[rc]) * H;
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) unsafeAtomicAdd(orow + 32 * c, wt * R[mt][c][i]);
-                    }
-                }
-        }
+        if (live) store_y_rows(p.y, H, nw, rpair, rows, lane, R);
     }
 }
 
@@ -770,8 +822,8 @@ __global__ void __launch_bounds__(256) down_mfma(PrefillParams p) {
 //     rounding decision that differs between implementations in h's last bits
 //     moves the sum h1 + h2 by at most one step of the second term.
 //   down: tile 128 pairs x 512 outputs, K = 64 per stage, both terms of h
-//     against the same weight operand; the combine adds into the output with
-//     fp32 atomics as in the f16/bf16 path.
+//     against the same weight operand; y rows and the combine as in the
+//     f16/bf16 path.
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -812,6 +864,27 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v, float* q) {
     const bool neg = v < 0.0f && code != 0u;
     *q = neg ? -mag : mag;
     return code | (neg ? 0x80u : 0u);
+}
+
+// Four E4M3 codes of values already divided by their block scale, by gfx950's
+// conversion (round to nearest, ties to even; checked against the rounding
+// above on every bf16 pattern, tie neighbourhoods from 2^-16 to 2^9 and 2e6
+// log-uniform draws: no difference except that a negative value that rounds
+// to zero gets code 0x80, -0, which the down GEMM reads as zero).  Inputs are
+// clamped to +-448 first, so the conversion never sees a value it would not
+// saturate.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+    d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
+}
+// The value of byte B of four E4M3 codes (exact).
+template <int B>
+__device__ __forceinline__ float e4m3_byte_value(uint32_t w) {
+    return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), B);
 }
 
 // MX FP8 E4M3 copy of x: codes [T][H] and scale bytes [T][H / 32].  A thread
@@ -889,16 +962,17 @@ struct MxParams {
     const int32_t* n_tiles;
     uint8_t* hq[2];          // [T*k][I] the two MX terms of h (rows in bucket order)
     uint8_t* he[2];          // [T*k][I / 32] their scale bytes
-    float* out;
+    float* y;                // [T*k][H] down outputs by pair id t k + j
 };
 
-// gate/up stage slot (K = 128): activation rows 128 x 128 bytes (16-byte chunk c
-// of row r at slot c ^ swz8(r)); weights [wavefront][4 column tiles][2 halves]
-// [64 lanes] x 16 bytes in MFMA operand order; weight scale dwords [wavefront]
-// [2][64] (row 64 j + i of load j); activation scale dwords [wavefront][64]
-// (row 32 w + i at i < 32).
-constexpr int MG_A = 0, MG_W = 16384, MG_WS = 49152, MG_XS = 51200, MG_SLOT = 52224, MG_PD = 3;
-constexpr int MG_K = 128;
+// gate/up stage slot (K = 64): activation rows 128 x 64 bytes (16-byte chunk c of
+// row r at slot c ^ swz4(r)); weights [wavefront][4 column tiles][64 lanes] x 16
+// bytes in MFMA operand order; weight scale dwords [wavefront][2][64] (row
+// 64 j + i of load j); activation scale dwords [wavefront][64] (row 32 w + i at
+// i < 32).  A scale dword holds the e8m0 bytes of 128 inputs: stage kk uses
+// bytes 2 (kk & 1) + {0, 1}.
+constexpr int MG_A = 0, MG_W = 8192, MG_WS = 24576, MG_XS = 26624, MG_SLOT = 27648, MG_PD = 5;
+constexpr int MG_K = 64;
 // down stage slot (K = 64): two h terms of 128 rows x 64 bytes (chunk c of row r
 // at slot c ^ swz4(r)); weights [wavefront][4][64] x 16 bytes; weight scale
 // dwords [wavefront][2][64]; h scale dwords per term [wavefront][64].
@@ -906,8 +980,44 @@ constexpr int MD_A0 = 0, MD_A1 = 8192, MD_W = 16384, MD_WS = 32768, MD_HS = 3481
               MD_SLOT = 36864, MD_PD = 4;
 constexpr int MD_K = 64;
 
+// One stage's MFMA operands of a lane: the weight codes of the 4 column tiles,
+// the activations of the 4 row tiles, and the raw scale dwords.
+// An accumulator element read out of its AGPR at this point of the program.
+// Left to itself the compiler copies all 256 accumulators of a tile to VGPRs
+// right after the K loop, which spills other values (and a spill reload waits
+// for every memory operation in flight, the next tile's loads included).  The
+// caller guarantees that the MFMA that wrote the element finished (the
+// epilogue starts with enough wait states, see mfma_drain).
+__device__ __forceinline__ float acc_read(float a) {
+    float v;
+    asm("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
+// Wait states after the last MFMA before acc_read may read its result (more
+// than a 16-pass MFMA needs).
+__device__ __forceinline__ void mfma_drain() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+struct MxOps {
+    uint4 q[4];
+    i32x8 x[4];
+    uint32_t ws[4], xs[4];
+};
+
+// gate/up on the MX operands.  Per tile, stages of K = 64 flow through a ring of
+// PD slots filled by direct loads: at the top of iteration kk every wavefront
+// waits for stage kk + 1 and meets the others, after which stage kk's slot
+// (already copied to registers) takes stage kk + PD; the 16 MFMAs of stage kk
+// then run from registers while, between them, the next stage's operands are
+// read from LDS into the other register set and the loads of stage kk + PD are
+// issued.  The MFMA pipe so never waits on LDS, and the one barrier per stage
+// finds the next stage already landed as long as the loads of PD - 2 stages
+// cover the memory latency.  Past the last stage the loads repeat it (in
+// bounds, never read), which keeps every wait count uniform; they drain before
+// the next tile reuses the ring.
 __global__ void __launch_bounds__(256) gate_up_mx(MxParams p) {
-    constexpr int PD = MG_PD, D = PD - 1, OPS = 15;   // loads per stage per wavefront
+    constexpr int PD = MG_PD, OPS = 9;   // loads per stage per wavefront
     extern __shared__ uint4 smem[];
     uint8_t* ring = reinterpret_cast<uint8_t*>(smem);                  // [PD][MG_SLOT]
     int32_t* rtok = reinterpret_cast<int32_t*>(ring + PD * MG_SLOT);   // token of each tile row
@@ -916,112 +1026,177 @@ __global__ void __launch_bounds__(256) gate_up_mx(MxParams p) {
     const int H = p.H, I = p.I, KS = H / MG_K;
     const uint32_t ring_lds = lds_addr(ring);
 
-    {   // zero the layer output for the down kernel's atomics
-        const int64_t n = static_cast<int64_t>(p.T) * H;
-        for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + tid; i < n;
-             i += static_cast<int64_t>(gridDim.x) * 256)
-            p.out[i] = 0.0f;
-    }
-
     const int FX = (I + GU_FEAT - 1) / GU_FEAT;
     const TileRange tr = tile_range(*p.n_tiles * FX);
     const void* xs = uniform_ptr(p.xq);
     const void* xes = uniform_ptr(p.xe);
-    for (int t = tr.begin; t < tr.end; t += tr.step) {
+    // The lane index is made opaque again for every tile (below), so that the
+    // compiler recomputes lane-derived addresses per tile instead of hoisting
+    // dozens of them out of the tile loop (they would spill, and a spill reload
+    // waits for every memory operation in flight, the next tile's loads too).
+    int lane = tid & (WAVE - 1), ln = 0, hh = 0;
+    auto refresh_lane = [&]() {
+        asm volatile("" : "+v"(lane));
+        ln = lane & 31;
+        hh = lane >> 5;
+    };
+
+    // A tile's load sources for this lane (the expert's blob, activation rows,
+    // activation scale dwords, weight codes and scale dwords).  Setting them up
+    // writes the tile's row tokens to LDS between two barriers.
+    struct Src {
+        const void* W;
+        uint32_t aoff[2], xsoff, bq[4], bsc[2];
+    };
+    auto setup = [&](int t, Src& src) {
         const int y = t / FX;
         const int e = p.tile_e[y], m0 = p.tile_m0[y];
         const int pbase = p.offsets[e] + m0;
         const int rows = min(BM, p.offsets[e + 1] - pbase);
-        const void* W = uniform_ptr(p.W + static_cast<int64_t>(e) * p.S);
         const int fw = (t - y * FX) * GU_FEAT + 64 * wv;
-        int lane = tid & (WAVE - 1);
-        asm volatile("" : "+v"(lane));
-        const int ln = lane & 31, hh = lane >> 5;
-        const bool live = fw < I;
-        const int fr = live ? fw : 0;
-        __syncthreads();   // the previous tile is done with the LDS
+        const int fr = fw < I ? fw : 0;   // idle wavefronts of a small I compute on row 0
+        src.W = uniform_ptr(p.W + static_cast<int64_t>(e) * p.S);
+        __syncthreads();   // nobody reads the previous tokens any more
         if (tid < BM) rtok[tid] = p.perm[pbase + (tid < rows ? tid : 0)] / p.k;
         __syncthreads();
-        uint32_t aoff[4];   // this lane's activation sources: 4 blocks of 8 rows
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 8 * (4 * wv + j) + lane / 8, c = (lane % 8) ^ swz8(r);
-            aoff[j] = static_cast<uint32_t>(rtok[r]) * static_cast<uint32_t>(H) + c * 16;
+        for (int j = 0; j < 2; ++j) {   // 2 blocks of 16 rows x 4 chunks
+            const int r = 16 * (2 * wv + j) + lane / 4, c = (lane % 4) ^ swz4(r);
+            src.aoff[j] = static_cast<uint32_t>(rtok[r]) * static_cast<uint32_t>(H) + c * 16;
         }
         // activation scale dwords: row 32 wv + ln (both lane halves load it)
-        const uint32_t xsoff = static_cast<uint32_t>(rtok[32 * wv + ln]) * static_cast<uint32_t>(H / 32);
-        uint32_t bq[4], bsc[2];
+        src.xsoff = static_cast<uint32_t>(rtok[32 * wv + ln]) * static_cast<uint32_t>(H / 32);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) bq[c] = code_src(p.q_off[c >> 1], fr + 32 * (c & 1) + ln, H, hh);
+        for (int c = 0; c < 4; ++c) src.bq[c] = code_src(p.q_off[c >> 1], fr + 32 * (c & 1) + ln, H, hh);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) bsc[j] = scale_src(p.s_off[j], fr + lane, H);
+        for (int j = 0; j < 2; ++j) src.bsc[j] = scale_src(p.s_off[j], fr + lane, H);
+    };
+    // load i (of OPS) of stage kk into the slot at LDS address sl
+    auto load_op = [&](const Src& src, int kk, uint32_t sl, int i) {
+        if (i < 2) {
+            dma16(xs, src.aoff[i] + kk * MG_K, sl + MG_A + (2 * wv + i) * 1024);
+        } else if (i < 6) {
+            dma16(src.W, src.bq[i - 2] + code_step(kk), sl + MG_W + (4 * wv + i - 2) * 1024);
+        } else if (i < 8) {
+            dma4(src.W, src.bsc[i - 6] + scale_step(kk), sl + MG_WS + (2 * wv + i - 6) * 256);
+        } else {
+            dma4(xes, src.xsoff + (kk >> 1) * 4, sl + MG_XS + wv * 256);
+        }
+    };
+    // the first PD stages of a tile (the last stage again where KS < PD)
+    auto prologue = [&](const Src& src) {
+#pragma unroll
+        for (int s = 0; s < PD; ++s)
+#pragma unroll
+            for (int i = 0; i < OPS; ++i) load_op(src, s < KS ? s : KS - 1, ring_lds + s * MG_SLOT, i);
+    };
+    // read piece i (of 16) of the stage in slot sp into o
+    auto read_op = [&](const uint8_t* sp, int i, MxOps& o) {
+        if (i < 4) {
+            o.ws[i] = tile_scale(reinterpret_cast<const uint32_t*>(sp + MG_WS), wv, i, ln);
+        } else if (i < 8) {
+            o.xs[i - 4] = reinterpret_cast<const uint32_t*>(sp + MG_XS)[(i - 4) * 64 + ln];
+        } else if (i < 12) {
+            o.q[i - 8] = (reinterpret_cast<const uint4*>(sp + MG_W) + 4 * wv * 64 + lane)[(i - 8) * 64];
+        } else {
+            // inputs 16 hh + [0, 16) and 32 + 16 hh + [0, 16) of row tile i - 12
+            const uint4* A = reinterpret_cast<const uint4*>(sp + MG_A);
+            const int r = (i - 12) * 32 + ln;
+            const uint4 u0 = A[r * 4 + (hh ^ swz4(r))];
+            const uint4 u1 = A[r * 4 + ((2 + hh) ^ swz4(r))];
+            o.x[i - 12] = i32x8{static_cast<int>(u0.x), static_cast<int>(u0.y), static_cast<int>(u0.z),
+                                static_cast<int>(u0.w), static_cast<int>(u1.x), static_cast<int>(u1.y),
+                                static_cast<int>(u1.z), static_cast<int>(u1.w)};
+        }
+    };
+
+    Src src;
+    if (tr.begin < tr.end) {
+        refresh_lane();
+        setup(tr.begin, src);
+        prologue(src);
+    }
+    for (int t = tr.begin; t < tr.end; t += tr.step) {
+        refresh_lane();
+        const int y = t / FX;
+        const int e = p.tile_e[y], m0 = p.tile_m0[y];
+        const int pbase = p.offsets[e] + m0;
+        const int rows = min(BM, p.offsets[e + 1] - pbase);
+        const int fw = (t - y * FX) * GU_FEAT + 64 * wv;
+        const bool live = fw < I;
+        // row tiles of 32 the MFMAs cover: a bucket's last tile is often short,
+        // and its empty row tiles are skipped
+        const int nmt = __builtin_amdgcn_readfirstlane((rows + 31) / 32);
 
         f32x16 R[4][4];   // [column tile][row tile]: features x tokens
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) R[c][i] = f32x16{};
-        auto issue = [&](int kk, int slot) {
+        // iteration kk: MFMAs of stage kk from cur, reads of stage kk + 1 into nxt,
+        // loads of stage kk + PD (the last stage again past the end)
+        auto iter = [&](auto NMTc, int kk, int slot, const MxOps& cur, MxOps& nxt) {
+            constexpr int NMT = decltype(NMTc)::value;
+            stage_barrier<OPS * (PD - 2)>();   // stage kk + 1 has landed everywhere
+            const int nslot = slot == PD - 1 ? 0 : slot + 1;
+            const uint8_t* spn = ring + nslot * MG_SLOT;
             const uint32_t sl = ring_lds + slot * MG_SLOT;
+            const int kl = min(kk + PD, KS - 1);
+            const int sb = 8 * (2 * (kk & 1) + hh);   // this lane's scale byte
+            uint32_t wsb[4], xsb[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dma16(xs, aoff[j] + kk * MG_K, sl + MG_A + (4 * wv + j) * 1024);
+            for (int c = 0; c < 4; ++c) wsb[c] = (cur.ws[c] >> sb) & 0xFFu;
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+            for (int mt = 0; mt < NMT; ++mt) xsb[mt] = (cur.xs[mt] >> sb) & 0xFFu;
+            __builtin_amdgcn_sched_barrier(0);
+            // the reads go out with the first 8 MFMAs (done long before the next
+            // barrier's wait for them), the loads with MFMAs 4 to 12
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    dma16(W, bq[c] + kk * 1024 + s * 512, sl + MG_W + ((4 * wv + c) * 2 + s) * 1024);
+            for (int j = 0; j < 16; ++j) {
+                const int c = j >> 2, mt = j & 3;
+                if (mt < NMT) R[c][mt] = mma_fp4_fp8(cur.q[c], wsb[c], cur.x[mt], xsb[mt], R[c][mt]);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) dma4(W, bsc[j] + kk * 64, sl + MG_WS + (2 * wv + j) * 256);
-            dma4(xes, xsoff + kk * 4, sl + MG_XS + wv * 256);
-        };
-        auto compute = [&](int slot) {
-            const uint8_t* sp = ring + slot * MG_SLOT;
-            const uint4* A = reinterpret_cast<const uint4*>(sp + MG_A);
-            const uint4* Wq = reinterpret_cast<const uint4*>(sp + MG_W) + 4 * wv * 2 * 64 + lane;
-            const uint32_t* WS = reinterpret_cast<const uint32_t*>(sp + MG_WS);
-            const uint32_t* XS = reinterpret_cast<const uint32_t*>(sp + MG_XS);
-            uint32_t wsc[4], xsc[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) wsc[c] = tile_scale(WS, wv, c, ln);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) xsc[mt] = XS[mt * 64 + ln];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                i32x8 xb[4];
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    // inputs 16 hh + [0, 16) and 32 + 16 hh + [0, 16) of half s
-                    const int r = mt * 32 + ln, c0 = 4 * s + hh;
-                    const uint4 u0 = A[r * 8 + (c0 ^ swz8(r))];
-                    const uint4 u1 = A[r * 8 + ((c0 + 2) ^ swz8(r))];
-                    xb[mt] = i32x8{static_cast<int>(u0.x), static_cast<int>(u0.y), static_cast<int>(u0.z),
-                                   static_cast<int>(u0.w), static_cast<int>(u1.x), static_cast<int>(u1.y),
-                                   static_cast<int>(u1.z), static_cast<int>(u1.w)};
-                }
-                const int sb = 8 * (2 * s + hh);   // this lane's block of the stage's 4
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const uint4 q = Wq[(c * 2 + s) * 64];
-                    const uint32_t ws = (wsc[c] >> sb) & 0xFFu;
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt)
-                        R[c][mt] = mma_fp4_fp8(q, ws, xb[mt], (xsc[mt] >> sb) & 0xFFu, R[c][mt]);
-                }
+                for (int i = 2 * j; i < 2 * j + 2; ++i)
+                    if (i < 12 || (i < 16 && i - 12 < NMT)) read_op(spn, i, nxt);
+                if (j >= 4 && j - 4 < OPS) load_op(src, kl, sl, j - 4);
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
+        // The tile's stages.  Its first PD stages were issued before the previous
+        // tile's epilogue (or above, for the first tile); the wait for stage 0
+        // also covers the memory operations issued in between (vector memory
+        // operations of a wavefront complete in issue order).
+        auto kloop = [&](auto NMTc) {
+            MxOps o0, o1;
+            stage_barrier<OPS * (PD - 1)>();   // stage 0 has landed everywhere
 #pragma unroll
-        for (int kk = 0; kk < D; ++kk)
-            if (kk < KS) issue(kk, kk);
-        int slot = 0;
+            for (int i = 0; i < 16; ++i) read_op(ring, i, o0);
+            int slot = 0;
 #pragma nounroll
-        for (int kk = 0; kk < KS; ++kk) {
-            stage_wait<OPS, D - 1>(KS - 1 - kk);   // stage kk has landed everywhere
-            const int next = slot == 0 ? PD - 1 : slot - 1;   // the slot read last stage
-            if (kk + D < KS) issue(kk + D, next);
-            compute(slot);
-            slot = slot == PD - 1 ? 0 : slot + 1;
+            for (int kk = 0; kk < KS; kk += 2) {   // KS is even
+                iter(NMTc, kk, slot, o0, o1);
+                slot = slot == PD - 1 ? 0 : slot + 1;
+                iter(NMTc, kk + 1, slot, o1, o0);
+                slot = slot == PD - 1 ? 0 : slot + 1;
+            }
+            // the repeated loads have landed and every read of the ring is done
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        };
+        switch (nmt) {
+            case 1: kloop(std::integral_constant<int, 1>{}); break;
+            case 2: kloop(std::integral_constant<int, 2>{}); break;
+            case 3: kloop(std::integral_constant<int, 3>{}); break;
+            default: kloop(std::integral_constant<int, 4>{}); break;
         }
+        // the next tile's first stages load while this one's epilogue runs
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + tr.step < tr.end) {
+            setup(t + tr.step, src);   // its first barrier: every wavefront is past the ring
+            prologue(src);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 
+        mfma_drain();
         // h = silu(g) * u as two MX terms.  Lane (ln, hh) holds, for tile row
         // 32 mt + ln, features fw + 32 ft + 8 (i / 4) + 4 hh + i % 4 in R[ft][mt][i]
         // (g) and R[2 + ft][mt][i] (u): an MX block of 32 features is one column
@@ -1033,11 +1208,12 @@ __global__ void __launch_bounds__(256) gate_up_mx(MxParams p) {
             const int64_t prow = static_cast<int64_t>(pbase + r);
 #pragma unroll
             for (int ft = 0; ft < 2; ++ft) {
+                __builtin_amdgcn_sched_barrier(0);   // one block at a time: few live registers
                 float v[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float g = R[ft][mt][i], u = R[2 + ft][mt][i];
-                    v[i] = g / (1.0f + __expf(-g)) * u;
+                    const float g = acc_read(R[ft][mt][i]), u = acc_read(R[2 + ft][mt][i]);
+                    v[i] = silu(g) * u;
                 }
                 const int f0 = fw + 32 * ft;
 #pragma unroll
@@ -1048,12 +1224,16 @@ __global__ void __launch_bounds__(256) gate_up_mx(MxParams p) {
                     amax = fmaxf(amax, __shfl_xor(amax, 32, WAVE));
                     const int ex = mx_exponent(amax);
                     const float inv = mx_inv_scale(ex), sc = mx_scale(ex);
-                    uint32_t cw[4] = {0u, 0u, 0u, 0u};
+                    uint32_t cw[4];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        float q;
-                        cw[i >> 2] |= e4m3_rne(v[i] * inv, &q) << (8 * (i & 3));
-                        v[i] -= q * sc;          // the residual, exact: the next term's input
+                    for (int j = 0; j < 4; ++j) {
+                        cw[j] = e4m3x4(v[4 * j] * inv, v[4 * j + 1] * inv, v[4 * j + 2] * inv,
+                                       v[4 * j + 3] * inv);
+                        // the residual (exact): the next term's input
+                        v[4 * j] -= e4m3_byte_value<0>(cw[j]) * sc;
+                        v[4 * j + 1] -= e4m3_byte_value<1>(cw[j]) * sc;
+                        v[4 * j + 2] -= e4m3_byte_value<2>(cw[j]) * sc;
+                        v[4 * j + 3] -= e4m3_byte_value<3>(cw[j]) * sc;
                     }
                     if (keep) {
                         uint8_t* dst = p.hq[term] + prow * I + f0 + 4 * hh;
@@ -1067,142 +1247,209 @@ __global__ void __launch_bounds__(256) gate_up_mx(MxParams p) {
     }
 }
 
-// down + combine on the two MX terms of h: A = the tile's 128 rows of h (each
-// term with its scale bytes); B = down rows nw + [0, 128) of wavefront w as 4
-// column tiles of e2m1 codes; fp32 atomics into the output as in down_mfma.
+// down on the two MX terms of h: A = the tile's 128 rows of h (each term with
+// its scale bytes); B = down rows nw + [0, 128) of wavefront w as 4 column tiles
+// of e2m1 codes; the y rows go to the pair-indexed array as in down_mfma.
+// Pipelined as gate_up_mx, with each K = 64 stage in two halves: the MFMAs of
+// term 0 run while term 1's operands are read; then, past the stage's barrier
+// (the next stage has landed, this one is read out), the MFMAs of term 1 run
+// while the next stage's weights and term-0 operands are read and a later
+// stage's loads are issued.
+struct MxDnOps {   // a stage's weight codes and scales, one term's h operands
+    uint4 q[4];
+    uint32_t ws[4];
+    i32x8 a[4];
+    uint32_t hs[4];
+};
+
 __global__ void __launch_bounds__(256) down_mx(MxParams p) {
-    constexpr int PD = MD_PD, D = PD - 1, OPS = 12;   // loads per stage per wavefront
+    constexpr int PD = MD_PD, OPS = 12;   // loads per stage per wavefront
     extern __shared__ uint4 smem[];
     uint8_t* ring = reinterpret_cast<uint8_t*>(smem);                  // [PD][MD_SLOT]
-    int32_t* rtok = reinterpret_cast<int32_t*>(ring + PD * MD_SLOT);
-    float* rw = reinterpret_cast<float*>(rtok + BM);
+    int32_t* rpair = reinterpret_cast<int32_t*>(ring + PD * MD_SLOT);
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int H = p.H, I = p.I, KS = I / MD_K;
     const int FX = (H + DN_COLS - 1) / DN_COLS;
     const uint32_t ring_lds = lds_addr(ring);
     const TileRange tr = tile_range(*p.n_tiles * FX);
-    for (int t = tr.begin; t < tr.end; t += tr.step) {
+    int lane = tid & (WAVE - 1), ln = 0, hh = 0;   // opaque per tile, as in gate_up_mx
+    auto refresh_lane = [&]() {
+        asm volatile("" : "+v"(lane));
+        ln = lane & 31;
+        hh = lane >> 5;
+    };
+
+    // A tile's load sources for this lane: both h terms with their scales, the
+    // expert's blob with the down codes and scales.
+    struct Src {
+        const void *W, *hb0, *hb1, *hs0, *hs1;
+        uint32_t aoff[2], hsoff, bq[4], bsc[2];
+    };
+    auto setup = [&](int t, Src& src) {
         const int y = t / FX;
         const int e = p.tile_e[y], m0 = p.tile_m0[y];
         const int pbase = p.offsets[e] + m0;
         const int rows = min(BM, p.offsets[e + 1] - pbase);
-        const void* W = uniform_ptr(p.W + static_cast<int64_t>(e) * p.S);
         const int nw = (t - y * FX) * DN_COLS + 128 * wv;
-        int lane = tid & (WAVE - 1);
-        asm volatile("" : "+v"(lane));
-        const int ln = lane & 31, hh = lane >> 5;
-        const bool live = nw < H;
-        const int nr = live ? nw : 0;
-        const void* hb0 = uniform_ptr(p.hq[0] + static_cast<int64_t>(pbase) * I);
-        const void* hb1 = uniform_ptr(p.hq[1] + static_cast<int64_t>(pbase) * I);
-        const void* hs0 = uniform_ptr(p.he[0] + static_cast<int64_t>(pbase) * (I / 32));
-        const void* hs1 = uniform_ptr(p.he[1] + static_cast<int64_t>(pbase) * (I / 32));
-        __syncthreads();   // the previous tile is done with the LDS
-        if (tid < BM) {
-            if (tid < rows) {
-                const int pr = p.perm[pbase + tid];
-                rtok[tid] = pr / p.k;
-                rw[tid] = p.topk_w[pr];
-            } else {
-                rtok[tid] = -1;
-                rw[tid] = 0.0f;
-            }
-        }
-        uint32_t aoff[2];   // 2 blocks of 16 rows x 4 chunks; rows past the bucket re-read row 0
+        const int nr = nw < H ? nw : 0;   // idle wavefronts of a small H compute on row 0
+        src.W = uniform_ptr(p.W + static_cast<int64_t>(e) * p.S);
+        src.hb0 = uniform_ptr(p.hq[0] + static_cast<int64_t>(pbase) * I);
+        src.hb1 = uniform_ptr(p.hq[1] + static_cast<int64_t>(pbase) * I);
+        src.hs0 = uniform_ptr(p.he[0] + static_cast<int64_t>(pbase) * (I / 32));
+        src.hs1 = uniform_ptr(p.he[1] + static_cast<int64_t>(pbase) * (I / 32));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < 2; ++j) {   // 2 blocks of 16 rows x 4 chunks; rows past the bucket re-read row 0
             const int r = 16 * (2 * wv + j) + lane / 4, c = (lane % 4) ^ swz4(r);
-            aoff[j] = static_cast<uint32_t>(r < rows ? r : 0) * static_cast<uint32_t>(I) + c * 16;
+            src.aoff[j] = static_cast<uint32_t>(r < rows ? r : 0) * static_cast<uint32_t>(I) + c * 16;
         }
         const int srow = 32 * wv + ln;
-        const uint32_t hsoff = static_cast<uint32_t>(srow < rows ? srow : 0) * static_cast<uint32_t>(I / 32);
-        uint32_t bq[4], bsc[2];
+        src.hsoff = static_cast<uint32_t>(srow < rows ? srow : 0) * static_cast<uint32_t>(I / 32);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) bq[c] = code_src(p.q_off[2], nr + 32 * c + ln, I, hh);
+        for (int c = 0; c < 4; ++c) src.bq[c] = code_src(p.q_off[2], nr + 32 * c + ln, I, hh);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) bsc[j] = scale_src(p.s_off[2], nr + 64 * j + lane, I);
+        for (int j = 0; j < 2; ++j) src.bsc[j] = scale_src(p.s_off[2], nr + 64 * j + lane, I);
+    };
+    // load i (of OPS) of stage kk into the slot at LDS address sl
+    auto load_op = [&](const Src& src, int kk, uint32_t sl, int i) {
+        if (i < 4) {
+            const int j = i & 1;
+            dma16(i < 2 ? src.hb0 : src.hb1, src.aoff[j] + kk * MD_K,
+                  sl + (i < 2 ? MD_A0 : MD_A1) + (2 * wv + j) * 1024);
+        } else if (i < 8) {
+            dma16(src.W, src.bq[i - 4] + code_step(kk), sl + MD_W + (4 * wv + i - 4) * 1024);
+        } else if (i < 10) {
+            dma4(src.W, src.bsc[i - 8] + scale_step(kk), sl + MD_WS + (2 * wv + i - 8) * 256);
+        } else {
+            dma4(i == 10 ? src.hs0 : src.hs1, src.hsoff + (kk >> 1) * 4,
+                 sl + MD_HS + (i - 10) * 1024 + wv * 256);
+        }
+    };
+    auto prologue = [&](const Src& src) {
+#pragma unroll
+        for (int s = 0; s < PD; ++s)
+#pragma unroll
+            for (int i = 0; i < OPS; ++i) load_op(src, s < KS ? s : KS - 1, ring_lds + s * MD_SLOT, i);
+    };
+    // term te's h operand of row tile mt, and its scale dword
+    auto read_a = [&](const uint8_t* sp, int te, int mt, MxDnOps& o) {
+        const uint4* A = reinterpret_cast<const uint4*>(sp + (te ? MD_A1 : MD_A0));
+        const int r = mt * 32 + ln;
+        const uint4 u0 = A[r * 4 + (hh ^ swz4(r))];         // inputs 16 hh + [0, 16)
+        const uint4 u1 = A[r * 4 + ((2 + hh) ^ swz4(r))];   // 32 + 16 hh + [0, 16)
+        o.a[mt] = i32x8{static_cast<int>(u0.x), static_cast<int>(u0.y), static_cast<int>(u0.z),
+                        static_cast<int>(u0.w), static_cast<int>(u1.x), static_cast<int>(u1.y),
+                        static_cast<int>(u1.z), static_cast<int>(u1.w)};
+    };
+    auto read_hs = [&](const uint8_t* sp, int te, int mt, MxDnOps& o) {
+        o.hs[mt] = reinterpret_cast<const uint32_t*>(sp + MD_HS + te * 1024)[mt * 64 + ln];
+    };
+    auto read_w = [&](const uint8_t* sp, int c, MxDnOps& o) {
+        o.q[c] = (reinterpret_cast<const uint4*>(sp + MD_W) + 4 * wv * 64 + lane)[c * 64];
+        o.ws[c] = tile_scale(reinterpret_cast<const uint32_t*>(sp + MD_WS), wv, c, ln);
+    };
 
+    Src src;
+    for (int t = tr.begin; t < tr.end; t += tr.step) {
+        refresh_lane();
+        const int y = t / FX;
+        const int e = p.tile_e[y], m0 = p.tile_m0[y];
+        const int pbase = p.offsets[e] + m0;
+        const int rows = min(BM, p.offsets[e + 1] - pbase);
+        const int nw = (t - y * FX) * DN_COLS + 128 * wv;
+        const bool live = nw < H;
+        const int nmt = __builtin_amdgcn_readfirstlane((rows + 31) / 32);   // row tiles with rows
+        __syncthreads();   // the previous tile is done with the ring and the pair ids
+        setup(t, src);
+        prologue(src);
+        if (tid < BM) rpair[tid] = tid < rows ? p.perm[pbase + tid] : -1;   // pair id t k + j
+
+        // The MFMAs take h as their first operand: a lane holds one output column
+        // of 16 pairs per row tile, so each store instruction writes 128
+        // contiguous bytes of 2 rows (whole cache lines; the transposed layout,
+        // 16-byte runs of 32 rows per instruction, measured twice as slow).
         f32x16 R[4][4];   // [row tile][column tile]: pairs x outputs
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int c = 0; c < 4; ++c) R[i][c] = f32x16{};
-        auto issue = [&](int kk, int slot) {
-            const uint32_t sl = ring_lds + slot * MD_SLOT;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                dma16(hb0, aoff[j] + kk * MD_K, sl + MD_A0 + (2 * wv + j) * 1024);
-                dma16(hb1, aoff[j] + kk * MD_K, sl + MD_A1 + (2 * wv + j) * 1024);
-            }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) dma16(W, bq[c] + code_step(kk), sl + MD_W + (4 * wv + c) * 1024);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) dma4(W, bsc[j] + scale_step(kk), sl + MD_WS + (2 * wv + j) * 256);
-            dma4(hs0, hsoff + (kk >> 1) * 4, sl + MD_HS + wv * 256);
-            dma4(hs1, hsoff + (kk >> 1) * 4, sl + MD_HS + 1024 + wv * 256);
-        };
-        auto compute = [&](int kk, int slot) {
+        // iteration kk: term 0 from cur (with term 1 read into t1), the barrier,
+        // term 1 (with stage kk + 1's weights and term 0 read into nxt and the
+        // loads of stage kk + PD)
+        auto iter = [&](auto NMTc, int kk, int slot, const MxDnOps& cur, MxDnOps& t1, MxDnOps& nxt) {
+            constexpr int NMT = decltype(NMTc)::value;
             const uint8_t* sp = ring + slot * MD_SLOT;
-            const uint4* Wq = reinterpret_cast<const uint4*>(sp + MD_W) + 4 * wv * 64 + lane;
-            const uint32_t* WS = reinterpret_cast<const uint32_t*>(sp + MD_WS);
-            const int sb = 8 * (2 * (kk & 1) + hh);   // this lane's block of the dword's 4
-            uint4 q[4];
-            uint32_t wsc[4];
+            const int nslot = slot == PD - 1 ? 0 : slot + 1;
+            const uint8_t* spn = ring + nslot * MD_SLOT;
+            const uint32_t sl = ring_lds + slot * MD_SLOT;
+            const int kl = min(kk + PD, KS - 1);
+            const int sb = 8 * (2 * (kk & 1) + hh);
+            uint32_t wsb[4], hsb[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                q[c] = Wq[c * 64];
-                wsc[c] = (tile_scale(WS, wv, c, ln) >> sb) & 0xFFu;
-            }
+            for (int c = 0; c < 4; ++c) wsb[c] = (cur.ws[c] >> sb) & 0xFFu;
 #pragma unroll
-            for (int term = 0; term < 2; ++term) {
-                const uint4* A = reinterpret_cast<const uint4*>(sp + (term ? MD_A1 : MD_A0));
-                const uint32_t* HS = reinterpret_cast<const uint32_t*>(sp + MD_HS + term * 1024);
+            for (int mt = 0; mt < NMT; ++mt) hsb[mt] = (cur.hs[mt] >> sb) & 0xFFu;
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    const int r = mt * 32 + ln;
-                    const uint4 u0 = A[r * 4 + (hh ^ swz4(r))];         // inputs 16 hh + [0, 16)
-                    const uint4 u1 = A[r * 4 + ((2 + hh) ^ swz4(r))];   // 32 + 16 hh + [0, 16)
-                    const i32x8 xa = {static_cast<int>(u0.x), static_cast<int>(u0.y), static_cast<int>(u0.z),
-                                      static_cast<int>(u0.w), static_cast<int>(u1.x), static_cast<int>(u1.y),
-                                      static_cast<int>(u1.z), static_cast<int>(u1.w)};
-                    const uint32_t xsc = (HS[mt * 64 + ln] >> sb) & 0xFFu;
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) R[mt][c] = mma_fp8_fp4(xa, xsc, q[c], wsc[c], R[mt][c]);
+            for (int j = 0; j < 16; ++j) {   // term 0
+                const int mt = j >> 2, c = j & 3;
+                if (mt < NMT) R[mt][c] = mma_fp8_fp4(cur.a[mt], hsb[mt], cur.q[c], wsb[c], R[mt][c]);
+                if (j < 2 * NMT) {
+                    if (j & 1) read_hs(sp, 1, j >> 1, t1);
+                    else read_a(sp, 1, j >> 1, t1);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            stage_barrier<OPS * (PD - 2)>();   // stage kk + 1 has landed; stage kk is read out
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) hsb[mt] = (t1.hs[mt] >> sb) & 0xFFu;
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {   // term 1
+                const int mt = j >> 2, c = j & 3;
+                if (mt < NMT) R[mt][c] = mma_fp8_fp4(t1.a[mt], hsb[mt], cur.q[c], wsb[c], R[mt][c]);
+                if (j < 4) {
+                    read_w(spn, j, nxt);
+                } else if (j < 4 + 2 * NMT) {
+                    if (j & 1) read_hs(spn, 0, (j - 4) >> 1, nxt);
+                    else read_a(spn, 0, (j - 4) >> 1, nxt);
+                }
+                if (j >= 2 && j - 2 < OPS) load_op(src, kl, sl, j - 2);
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
+        auto kloop = [&](auto NMTc) {   // the tile's stages
+            constexpr int NMT = decltype(NMTc)::value;
+            MxDnOps o0, o1, ot;
+            stage_barrier<OPS * (PD - 1)>();   // stage 0 has landed everywhere
 #pragma unroll
-        for (int kk = 0; kk < D; ++kk)
-            if (kk < KS) issue(kk, kk);
-        int slot = 0;
+            for (int c = 0; c < 4; ++c) read_w(ring, c, o0);
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) {
+                read_a(ring, 0, mt, o0);
+                read_hs(ring, 0, mt, o0);
+            }
+            int slot = 0;
 #pragma nounroll
-        for (int kk = 0; kk < KS; ++kk) {
-            stage_wait<OPS, D - 1>(KS - 1 - kk);
-            const int next = slot == 0 ? PD - 1 : slot - 1;
-            if (kk + D < KS) issue(kk + D, next);
-            compute(kk, slot);
-            slot = slot == PD - 1 ? 0 : slot + 1;
+            for (int kk = 0; kk < KS; kk += 2) {   // KS is even
+                iter(NMTc, kk, slot, o0, ot, o1);
+                slot = slot == PD - 1 ? 0 : slot + 1;
+                iter(NMTc, kk + 1, slot, o1, ot, o0);
+                slot = slot == PD - 1 ? 0 : slot + 1;
+            }
+            // the repeated loads have landed and every read of the ring is done
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        };
+        switch (nmt) {
+            case 1: kloop(std::integral_constant<int, 1>{}); break;
+            case 2: kloop(std::integral_constant<int, 2>{}); break;
+            case 3: kloop(std::integral_constant<int, 3>{}); break;
+            default: kloop(std::integral_constant<int, 4>{}); break;
         }
-
-        if (live) {   // combine, as in down_mfma
-            const int h4 = 4 * hh;
-            const int32_t* rt = rtok + h4;
-            const float* rwt = rw + h4;
-            float* obase = p.out + nw + ln;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int rc = mt * 32 + 8 * (i >> 2) + (i & 3);
-                    if (rc + h4 < rows) {
-                        const float wt = rwt[rc];
-                        float* orow = obase + static_cast<int64_t>(rt[rc]) * H;
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) unsafeAtomicAdd(orow + 32 * c, wt * R[mt][c][i]);
-                    }
-                }
-        }
+        // (a next tile's first loads issued here would wait behind these stores
+        // in the wavefront's 63-entry memory counter: measured slower)
+        mfma_drain();
+        if (live) store_y_rows(p.y, H, nw, rpair, rows, lane, R);
     }
 }
 
@@ -1225,16 +1472,15 @@ int prefill_blocks() {
 
 }  // namespace
 
-// h (hi, lo), the tile plan, the tile count, and for int4 the f16 copy of x,
-// its group sums and the group sums of h.
 // MX path workspace: the error word's 256 bytes, the tile plan and count, the
-// MX copy of x and its scales, the two MX terms of h and their scales.
+// MX copy of x and its scales, the two MX terms of h and their scales, the
+// pair-indexed y rows.
 size_t prefill_mx_ws_bytes(const moe355_layer_desc* d, int T) {
     const size_t tk = static_cast<size_t>(T) * d->top_k;
     const size_t th = static_cast<size_t>(T) * d->hidden;
     return 256 + align256(2 * static_cast<size_t>(max_tiles(T, d->top_k, d->n_experts)) * 4) + 256 +
            align256(th) + align256(th / 32) + 2 * align256(tk * d->inter) +
-           2 * align256(tk * d->inter / 32);
+           2 * align256(tk * d->inter / 32) + align256(tk * d->hidden * sizeof(float));
 }
 
 size_t prefill_ws_bytes(const moe355_layer_desc* d, int T) {
@@ -1244,10 +1490,11 @@ size_t prefill_ws_bytes(const moe355_layer_desc* d, int T) {
                                 align256(static_cast<size_t>(T) * (d->hidden / 64) * 4) +
                                 align256(tk * (d->inter / 64) * 4)
                           : 0;
-    // the error word's 256 bytes, h, the tile plan, the tile count, int4's x copy and sums
+    // the error word's 256 bytes, h, the tile plan, the tile count, int4's x copy
+    // and sums, the pair-indexed y rows
     return 256 + align256(tk * d->inter * sizeof(float)) +
            align256(2 * static_cast<size_t>(max_tiles(T, d->top_k, d->n_experts)) * sizeof(int32_t)) +
-           256 + xb;
+           256 + xb + align256(tk * d->hidden * sizeof(float));
 }
 
 }  // namespace moe355
@@ -1283,6 +1530,7 @@ extern "C" moe355_status moe355_expert_ffn_prefill(const moe355_layer_desc* d, c
     ExpertLayout L;
     expert_layout(d, &L);
     const size_t tk = static_cast<size_t>(T) * d->top_k;
+    const bool int4 = d->wfmt == MOE355_W_INT4_G64;
     PrefillParams p{};
     p.err = static_cast<uint32_t*>(ws);            // first 256 bytes: the error word
     uint8_t* wsb = static_cast<uint8_t*>(ws) + 256;
@@ -1310,7 +1558,6 @@ extern "C" moe355_status moe355_expert_ffn_prefill(const moe355_layer_desc* d, c
     p.tile_e = tiles;
     p.tile_m0 = tiles + mt;
     p.n_tiles = reinterpret_cast<int32_t*>(wsb + off_tiles + align256(2 * static_cast<size_t>(mt) * 4));
-    p.out = out;
     const size_t off_x = off_tiles + align256(2 * static_cast<size_t>(mt) * 4) + 256;
     uint16_t* xf = reinterpret_cast<uint16_t*>(wsb + off_x);
     float* xsum = reinterpret_cast<float*>(wsb + off_x + align256(static_cast<size_t>(T) * d->hidden * 2));
@@ -1318,13 +1565,17 @@ extern "C" moe355_status moe355_expert_ffn_prefill(const moe355_layer_desc* d, c
     p.xsum = xsum;
     p.hsum = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(xsum) +
                                       align256(static_cast<size_t>(T) * (d->hidden / 64) * 4));
+    const size_t xb = int4 ? align256(static_cast<size_t>(T) * d->hidden * 2) +
+                                 align256(static_cast<size_t>(T) * (d->hidden / 64) * 4) +
+                                 align256(tk * (d->inter / 64) * 4)
+                           : 0;
+    p.y = reinterpret_cast<float*>(wsb + off_x + xb);
 
     plan_kernel<<<1, 1024, 0, stream>>>(offsets, d->n_experts, tiles, tiles + mt,
                                         const_cast<int32_t*>(p.n_tiles), p.err);
     st = check_launch("expert_ffn_prefill plan");
     if (st) return st;
     const int blocks = prefill_blocks();
-    const bool int4 = d->wfmt == MOE355_W_INT4_G64;
     if (int4) {
         const int64_t n8 = static_cast<int64_t>(T) * d->hidden / 8;
         x16_kernel<<<static_cast<unsigned>((n8 + 255) / 256), 256, 0, stream>>>(
@@ -1333,7 +1584,7 @@ extern "C" moe355_status moe355_expert_ffn_prefill(const moe355_layer_desc* d, c
         if (st) return st;
     }
     const size_t lds_gu = GU_PD * GU_SLOT + BM * 4;
-    const size_t lds_dn = DN_PD * DN_SLOT + 2 * BM * 4;
+    const size_t lds_dn = DN_PD * DN_SLOT + BM * 4;
     MOE355_REQUIRE(lds_gu <= 160 * 1024 && lds_dn <= 160 * 1024, MOE355_ENOTSUP,
                    "expert_ffn_prefill: LDS need %zu / %zu bytes", lds_gu, lds_dn);
     auto gu = int4 ? gate_up_mfma<MOE355_W_INT4_G64> : gate_up_mfma<MOE355_W_MXFP4>;
@@ -1359,7 +1610,9 @@ extern "C" moe355_status moe355_expert_ffn_prefill(const moe355_layer_desc* d, c
     st = check_launch("expert_ffn_prefill gate_up");
     if (st) return st;
     dn<<<blocks, 256, lds_dn, stream>>>(p);
-    return check_launch("expert_ffn_prefill down");
+    st = check_launch("expert_ffn_prefill down");
+    if (st) return st;
+    return launch_combine(p.y, topk_w, T, d->top_k, d->hidden, out, stream, "expert_ffn_prefill combine");
 }
 
 extern "C" moe355_status moe355_quantize_mx(const void* x_bf16, int64_t rows, int32_t cols,
@@ -1427,6 +1680,7 @@ extern "C" moe355_status moe355_expert_ffn_prefill_mx(const moe355_layer_desc* d
         p.he[term] = at;
         at += align256(tk * d->inter / 32);
     }
+    p.y = reinterpret_cast<float*>(at);
     p.xq = xq;
     p.xe = xe;
     p.perm = perm;
@@ -1446,7 +1700,6 @@ extern "C" moe355_status moe355_expert_ffn_prefill_mx(const moe355_layer_desc* d
     p.tile_e = tiles;
     p.tile_m0 = tiles + mt;
     p.n_tiles = n_tiles;
-    p.out = out;
 
     plan_kernel<<<1, 1024, 0, stream>>>(offsets, d->n_experts, tiles, tiles + mt, n_tiles, err);
     st = check_launch("expert_ffn_prefill_mx plan");
@@ -1457,7 +1710,7 @@ extern "C" moe355_status moe355_expert_ffn_prefill_mx(const moe355_layer_desc* d
     st = check_launch("expert_ffn_prefill_mx quantise x");
     if (st) return st;
     const size_t lds_gu = MG_PD * MG_SLOT + BM * 4;
-    const size_t lds_dn = MD_PD * MD_SLOT + 2 * BM * 4;
+    const size_t lds_dn = MD_PD * MD_SLOT + BM * 4;
     static bool granted = false;
     if (!granted) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(gate_up_mx),
@@ -1474,5 +1727,8 @@ extern "C" moe355_status moe355_expert_ffn_prefill_mx(const moe355_layer_desc* d
     st = check_launch("expert_ffn_prefill_mx gate_up");
     if (st) return st;
     down_mx<<<blocks, 256, lds_dn, stream>>>(p);
-    return check_launch("expert_ffn_prefill_mx down");
+    st = check_launch("expert_ffn_prefill_mx down");
+    if (st) return st;
+    return launch_combine(p.y, topk_w, T, d->top_k, d->hidden, out, stream,
+                          "expert_ffn_prefill_mx combine");
 }
