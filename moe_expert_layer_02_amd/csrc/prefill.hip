@@ -118,6 +118,23 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // Shared pieces of the two GEMMs.
 
+// An accumulator element read out of its AGPR at this point of the program.
+// Left to itself the compiler copies all 256 accumulators of a tile to VGPRs
+// right after the K loop, which spills other values (and a spill reload waits
+// for every memory operation in flight, the next tile's loads included).  The
+// caller guarantees that the MFMA that wrote the element finished (the
+// epilogue starts with enough wait states, see mfma_drain).
+__device__ __forceinline__ float acc_read(float a) {
+    float v;
+    asm("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
+// Wait states after the last MFMA before acc_read may read its result (more
+// than a 16-pass MFMA needs).
+__device__ __forceinline__ void mfma_drain() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
 // silu(g) = g / (1 + e^-g) with the hardware reciprocal (1 ulp); e^-g = inf
 // gives -0 for very negative g.
 __device__ __forceinline__ float silu(float g) {
@@ -391,7 +408,7 @@ __device__ __forceinline__ uint32_t tile_scale(const uint32_t* S, int wv, int c,
 // group sums of h need one exchange between the lane halves.
 template <int FMT>
 __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
-    constexpr int PD = GU_PD, D = PD - 1, OPS = 10;   // loads per stage per wavefront
+    constexpr int PD = GU_PD, OPS = 10;   // loads per stage per wavefront
     extern __shared__ uint4 smem[];
     uint8_t* ring = reinterpret_cast<uint8_t*>(smem);                  // [PD][GU_SLOT]
     int32_t* rtok = reinterpret_cast<int32_t*>(ring + PD * GU_SLOT);   // token of each tile row
@@ -440,64 +457,84 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
         for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) R[c][i] = f32x16{};
-        auto issue = [&](int kk, int slot) {
-            const uint32_t sl = ring_lds + slot * GU_SLOT;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dma16(xs, aoff[j] + kk * 128, sl + GU_A + (4 * wv + j) * 1024);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) dma16(W, bq[c] + code_step(kk), sl + GU_B + (4 * wv + c) * 1024);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) dma4(W, bsc[j] + scale_step(kk), sl + GU_S + (2 * wv + j) * 256);
-        };
-        auto compute = [&](auto NMTc, int kk, int slot) {
-            constexpr int NMT = decltype(NMTc)::value;
-            const uint8_t* sp = ring + slot * GU_SLOT;
-            const uint4* A = reinterpret_cast<const uint4*>(sp + GU_A);
-            const uint4* Bq = reinterpret_cast<const uint4*>(sp + GU_B) + 4 * wv * 64 + lane;
-            const uint32_t* S = reinterpret_cast<const uint32_t*>(sp + GU_S);
+        // One stage's operands of a lane: A fragments [MFMA step][row tile], the
+        // codes and scale dwords of the 4 column tiles.
+        struct Ops {
+            uint4 a[4][4];
             uint4 q[4];
             uint32_t sc[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                q[c] = Bq[c * 64];
-                sc[c] = tile_scale(S, wv, c, ln);
-            }
-            // A fragments are read one MFMA step ahead of their use: with one
-            // wavefront per SIMD nothing else hides the LDS latency
-            uint4 a[2][4];
-#pragma unroll
-            for (int mt = 0; mt < NMT; ++mt) a[0][mt] = a_operand(A, mt, ln, hh, 0);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                if (s + 1 < 4) {
-#pragma unroll
-                    for (int mt = 0; mt < NMT; ++mt) a[(s + 1) & 1][mt] = a_operand(A, mt, ln, hh, s + 1);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const uint4 b = b_operand<FMT>(q[c], sc[c], kk, hh, s);
-#pragma unroll
-                    for (int mt = 0; mt < NMT; ++mt) R[c][mt] = mma<FMT>(b, a[s & 1][mt], R[c][mt]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+        };
+        // load i (of OPS) of stage kk into the slot at LDS address sl
+        auto load_op = [&](int kk, uint32_t sl, int i) {
+            if (i < 4) {
+                dma16(xs, aoff[i] + kk * 128, sl + GU_A + (4 * wv + i) * 1024);
+            } else if (i < 8) {
+                dma16(W, bq[i - 4] + code_step(kk), sl + GU_B + (4 * wv + i - 4) * 1024);
+            } else {
+                dma4(W, bsc[i - 8] + scale_step(kk), sl + GU_S + (2 * wv + i - 8) * 256);
             }
         };
-        // the row tiles past the bucket's last row are skipped (a bucket's last
-        // tile is often short); NMT = row tiles of 32 the MFMAs cover
-        auto kloop = [&](auto NMTc) {
+        // read piece i of a stage: 0..3 the codes and scale of column tile i,
+        // then A fragment (s, mt) as piece 4 + 4 s + mt
+        auto read_op = [&](const uint8_t* sp, int i, Ops& o) {
+            if (i < 4) {
+                o.q[i] = (reinterpret_cast<const uint4*>(sp + GU_B) + 4 * wv * 64 + lane)[i * 64];
+                o.sc[i] = tile_scale(reinterpret_cast<const uint32_t*>(sp + GU_S), wv, i, ln);
+            } else {
+                const int s4 = (i - 4) >> 2, mt = (i - 4) & 3;
+                o.a[s4][mt] = a_operand(reinterpret_cast<const uint4*>(sp + GU_A), mt, ln, hh, s4);
+            }
+        };
+        // Iteration kk, as in gate_up_mx: the MFMAs of stage kk from cur (the
+        // weight operand of each (step, column tile) dequantised in registers
+        // one group ahead), between them the reads of stage kk + 1 into nxt and
+        // the loads of stage kk + PD (the last stage again past the end).
+        auto iter = [&](auto NMTc, int kk, int slot, const Ops& cur, Ops& nxt) {
+            constexpr int NMT = decltype(NMTc)::value;
+            constexpr int NP = 4 + 4 * NMT;   // pieces the next stage needs
+            stage_barrier<OPS * (PD - 2)>();  // stage kk + 1 has landed everywhere
+            const int nslot = slot == PD - 1 ? 0 : slot + 1;
+            const uint8_t* spn = ring + nslot * GU_SLOT;
+            const uint32_t sl = ring_lds + slot * GU_SLOT;
+            const int kl = min(kk + PD, KS - 1);
+            uint4 b[2];
+            b[0] = b_operand<FMT>(cur.q[0], cur.sc[0], kk, hh, 0);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kk = 0; kk < D; ++kk)
-                if (kk < KS) issue(kk, kk);
+            for (int g = 0; g < 16; ++g) {   // group g: MFMA step g / 4, column tile g % 4
+#pragma unroll
+                for (int mt = 0; mt < NMT; ++mt) {
+                    R[g & 3][mt] = mma<FMT>(b[g & 1], cur.a[g >> 2][mt], R[g & 3][mt]);
+                    if (mt == 0 && g + 1 < 16)
+                        b[(g + 1) & 1] = b_operand<FMT>(cur.q[(g + 1) & 3], cur.sc[(g + 1) & 3], kk, hh, (g + 1) >> 2);
+                    const int j = g * NMT + mt;
+#pragma unroll
+                    for (int u = 2 * j; u < 2 * j + 2; ++u)
+                        if (u < NP) read_op(spn, u < 4 ? u : 4 + 4 * ((u - 4) / NMT) + (u - 4) % NMT, nxt);
+                    if (j >= 4 && j - 4 < OPS) load_op(kl, sl, j - 4);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        };
+        auto kloop = [&](auto NMTc) {
+            constexpr int NMT = decltype(NMTc)::value;
+            Ops o0, o1;
+#pragma unroll
+            for (int s4 = 0; s4 < PD; ++s4)
+#pragma unroll
+                for (int i = 0; i < OPS; ++i) load_op(s4 < KS ? s4 : KS - 1, ring_lds + s4 * GU_SLOT, i);
+            stage_barrier<OPS * (PD - 1)>();   // stage 0 has landed everywhere
+#pragma unroll
+            for (int u = 0; u < 4 + 4 * NMT; ++u) read_op(ring, u < 4 ? u : 4 + 4 * ((u - 4) / NMT) + (u - 4) % NMT, o0);
             int slot = 0;
 #pragma nounroll
-            for (int kk = 0; kk < KS; ++kk) {
-                stage_wait<OPS, D - 1>(KS - 1 - kk);   // stage kk has landed everywhere
-                const int next = slot == 0 ? PD - 1 : slot - 1;   // (slot + D) % PD: the slot read last stage
-                if (kk + D < KS) issue(kk + D, next);
-                compute(NMTc, kk, slot);
+            for (int kk = 0; kk < KS; kk += 2) {   // KS is even
+                iter(NMTc, kk, slot, o0, o1);
+                slot = slot == PD - 1 ? 0 : slot + 1;
+                iter(NMTc, kk + 1, slot, o1, o0);
                 slot = slot == PD - 1 ? 0 : slot + 1;
             }
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // the repeated loads have landed
         };
         switch (__builtin_amdgcn_readfirstlane((rows + 31) / 32)) {
             case 1: kloop(std::integral_constant<int, 1>{}); break;
@@ -527,6 +564,7 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
             }
         }
 
+        mfma_drain();
         // h = silu(g) * u.  Lane (ln, hh) holds, for token row 32 mt + ln, features
         // fw + 32 ft + 8 q + 4 hh + [0, 4) in R[ft][mt][4 q + 0..3] (g) and R[2 + ft] (u).
         // int4 stores each block of 8 features in the down GEMM's operand order
@@ -547,7 +585,7 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
                     uint16_t hi[4], lo[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const float g = R[ft][mt][4 * q + j], u = R[2 + ft][mt][4 * q + j];
+                        const float g = acc_read(R[ft][mt][4 * q + j]), u = acc_read(R[2 + ft][mt][4 * q + j]);
                         const float hv = silu(g) * u;
                         if (FMT == MOE355_W_INT4_G64) {
                             const _Float16 x1 = static_cast<_Float16>(hv);
@@ -666,7 +704,7 @@ moe355_status launch_combine(const float* y, const float* w, int T, int k, int H
 // so each store instruction covers 128 contiguous bytes of 2 rows).
 template <int FMT>
 __global__ void __launch_bounds__(256) down_mfma(PrefillParams p) {
-    constexpr int PD = DN_PD, D = PD - 1, OPS = 14;   // loads per stage per wavefront
+    constexpr int PD = DN_PD, OPS = 14;   // loads per stage per wavefront
     extern __shared__ uint4 smem[];
     uint8_t* ring = reinterpret_cast<uint8_t*>(smem);                  // [PD][DN_SLOT]
     int32_t* rpair = reinterpret_cast<int32_t*>(ring + PD * DN_SLOT);
@@ -714,69 +752,103 @@ __global__ void __launch_bounds__(256) down_mfma(PrefillParams p) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int c = 0; c < 4; ++c) R[i][c] = f32x16{};
-        auto issue = [&](int kk, int slot) {
-            const uint32_t sl = ring_lds + slot * DN_SLOT;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                dma16(hb, aoff[j] + kk * 128, sl + DN_AH + (4 * wv + j) * 1024);
-                dma16(lb, aoff[j] + kk * 128, sl + DN_AL + (4 * wv + j) * 1024);
-            }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) dma16(W, bq[c] + code_step(kk), sl + DN_B + (4 * wv + c) * 1024);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) dma4(W, bsc[j] + scale_step(kk), sl + DN_S + (2 * wv + j) * 256);
-        };
-        auto compute = [&](auto NMTc, int kk, int slot) {
-            constexpr int NMT = decltype(NMTc)::value;
-            const uint8_t* sp = ring + slot * DN_SLOT;
-            const uint4* Ah = reinterpret_cast<const uint4*>(sp + DN_AH);
-            const uint4* Al = reinterpret_cast<const uint4*>(sp + DN_AL);
-            const uint4* Bq = reinterpret_cast<const uint4*>(sp + DN_B) + 4 * wv * 64 + lane;
-            const uint32_t* S = reinterpret_cast<const uint32_t*>(sp + DN_S);
+        // Operands: a stage's weight codes and scale dwords, and the A fragments of
+        // two MFMA steps [step][part hi / lo][row tile].
+        struct WOps {
             uint4 q[4];
             uint32_t sc[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                q[c] = Bq[c * 64];
-                sc[c] = tile_scale(S, wv, c, ln);
-            }
-            // half-step u: MFMA step u / 2 on the hi (u even) or lo (u odd) part of
-            // h; its A fragments are read one half-step ahead of their use
-            uint4 a[2][4], b[4];
-#pragma unroll
-            for (int mt = 0; mt < NMT; ++mt) a[0][mt] = a_operand(Ah, mt, ln, hh, 0);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                if (u + 1 < 8) {
-                    const uint4* An = ((u + 1) & 1) ? Al : Ah;
-#pragma unroll
-                    for (int mt = 0; mt < NMT; ++mt) a[(u + 1) & 1][mt] = a_operand(An, mt, ln, hh, (u + 1) >> 1);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    if ((u & 1) == 0) b[c] = b_operand<FMT>(q[c], sc[c], kk, hh, u >> 1);
-#pragma unroll
-                    for (int mt = 0; mt < NMT; ++mt) R[mt][c] = mma<FMT>(a[u & 1][mt], b[c], R[mt][c]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+        };
+        struct AOps {
+            uint4 a[2][2][4];
+        };
+        // load i (of OPS) of stage kk into the slot at LDS address sl
+        auto load_op = [&](int kk, uint32_t sl, int i) {
+            if (i < 8) {
+                const int j = i >> 1;
+                dma16((i & 1) ? lb : hb, aoff[j] + kk * 128, sl + ((i & 1) ? DN_AL : DN_AH) + (4 * wv + j) * 1024);
+            } else if (i < 12) {
+                dma16(W, bq[i - 8] + code_step(kk), sl + DN_B + (4 * wv + i - 8) * 1024);
+            } else {
+                dma4(W, bsc[i - 12] + scale_step(kk), sl + DN_S + (2 * wv + i - 12) * 256);
             }
         };
-        // the row tiles past the bucket's last row are skipped (a bucket's last
-        // tile is often short); NMT = row tiles of 32 the MFMAs cover
-        auto kloop = [&](auto NMTc) {
+        auto read_w = [&](const uint8_t* sp, int c, WOps& o) {
+            o.q[c] = (reinterpret_cast<const uint4*>(sp + DN_B) + 4 * wv * 64 + lane)[c * 64];
+            o.sc[c] = tile_scale(reinterpret_cast<const uint32_t*>(sp + DN_S), wv, c, ln);
+        };
+        // A fragment (step s0 + sx, part pt, row tile mt) into o.a[sx][pt][mt]
+        auto read_a = [&](const uint8_t* sp, int s0, int i, AOps& o) {
+            const int sx = i >> 3, pt = (i >> 2) & 1, mt = i & 3;
+            o.a[sx][pt][mt] = a_operand(reinterpret_cast<const uint4*>(sp + (pt ? DN_AL : DN_AH)), mt, ln, hh, s0 + sx);
+        };
+        // The MFMAs of steps s0, s0 + 1 of stage kk: per step and column tile the
+        // weight operand is dequantised (one group ahead) and used by the hi and
+        // lo parts of every row tile; between the MFMAs, extra(j) issues reads
+        // and loads.
+        auto half = [&](auto NMTc, int kk, int s0, const WOps& w, const AOps& A, auto extra) {
+            constexpr int NMT = decltype(NMTc)::value;
+            uint4 b[2];
+            b[0] = b_operand<FMT>(w.q[0], w.sc[0], kk, hh, s0);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kk = 0; kk < D; ++kk)
-                if (kk < KS) issue(kk, kk);
+            for (int g = 0; g < 8; ++g) {   // group g: step s0 + g / 4, column tile g % 4
+#pragma unroll
+                for (int m = 0; m < 2 * NMT; ++m) {
+                    const int mt = m >> 1, pt = m & 1;
+                    R[mt][g & 3] = mma<FMT>(A.a[g >> 2][pt][mt], b[g & 1], R[mt][g & 3]);
+                    if (m == 0 && g + 1 < 8)
+                        b[(g + 1) & 1] = b_operand<FMT>(w.q[(g + 1) & 3], w.sc[(g + 1) & 3], kk, hh, s0 + ((g + 1) >> 2));
+                    extra(g * 2 * NMT + m);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        };
+        // Iteration kk: steps 0, 1 of stage kk (from X) while steps 2, 3 are read
+        // into Y; the barrier (stage kk + 1 has landed, stage kk is read out);
+        // steps 2, 3 (from Y) while stage kk + 1's weights and steps 0, 1 are read
+        // into nw_ and X and the loads of stage kk + PD are issued.
+        auto iter = [&](auto NMTc, int kk, int slot, const WOps& w, WOps& wn, AOps& X, AOps& Y) {
+            constexpr int NMT = decltype(NMTc)::value;
+            const uint8_t* sp = ring + slot * DN_SLOT;
+            const int nslot = slot == PD - 1 ? 0 : slot + 1;
+            const uint8_t* spn = ring + nslot * DN_SLOT;
+            const uint32_t sl = ring_lds + slot * DN_SLOT;
+            const int kl = min(kk + PD, KS - 1);
+            // the 2 x 2 x NMT fragments of a half, in the order [step][part][row tile]
+            auto frag = [&](int u) { return (u / (2 * NMT)) * 8 + ((u / NMT) & 1) * 4 + u % NMT; };
+            half(NMTc, kk, 0, w, X, [&](int j) {
+                if (j < 4 * NMT) read_a(sp, 2, frag(j), Y);
+            });
+            stage_barrier<OPS * (PD - 2)>();
+            half(NMTc, kk, 2, w, Y, [&](int j) {
+                if (j < 4) read_w(spn, j, wn);
+                else if (j < 4 + 4 * NMT) read_a(spn, 0, frag(j - 4), X);
+                if (j >= 2 && j - 2 < OPS) load_op(kl, sl, j - 2);
+            });
+        };
+        auto kloop = [&](auto NMTc) {
+            constexpr int NMT = decltype(NMTc)::value;
+            WOps w0, w1;
+            AOps X, Y;
+#pragma unroll
+            for (int s4 = 0; s4 < PD; ++s4)
+#pragma unroll
+                for (int i = 0; i < OPS; ++i) load_op(s4 < KS ? s4 : KS - 1, ring_lds + s4 * DN_SLOT, i);
+            stage_barrier<OPS * (PD - 1)>();   // stage 0 has landed everywhere
+#pragma unroll
+            for (int c = 0; c < 4; ++c) read_w(ring, c, w0);
+#pragma unroll
+            for (int u = 0; u < 4 * NMT; ++u)
+                read_a(ring, 0, (u / (2 * NMT)) * 8 + ((u / NMT) & 1) * 4 + u % NMT, X);
             int slot = 0;
 #pragma nounroll
-            for (int kk = 0; kk < KS; ++kk) {
-                stage_wait<OPS, D - 1>(KS - 1 - kk);
-                const int next = slot == 0 ? PD - 1 : slot - 1;
-                if (kk + D < KS) issue(kk + D, next);
-                compute(NMTc, kk, slot);
+            for (int kk = 0; kk < KS; kk += 2) {   // KS is even
+                iter(NMTc, kk, slot, w0, w1, X, Y);
+                slot = slot == PD - 1 ? 0 : slot + 1;
+                iter(NMTc, kk + 1, slot, w1, w0, X, Y);
                 slot = slot == PD - 1 ? 0 : slot + 1;
             }
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // the repeated loads have landed
         };
         switch (__builtin_amdgcn_readfirstlane((rows + 31) / 32)) {
             case 1: kloop(std::integral_constant<int, 1>{}); break;
@@ -982,23 +1054,6 @@ constexpr int MD_K = 64;
 
 // One stage's MFMA operands of a lane: the weight codes of the 4 column tiles,
 // the activations of the 4 row tiles, and the raw scale dwords.
-// An accumulator element read out of its AGPR at this point of the program.
-// Left to itself the compiler copies all 256 accumulators of a tile to VGPRs
-// right after the K loop, which spills other values (and a spill reload waits
-// for every memory operation in flight, the next tile's loads included).  The
-// caller guarantees that the MFMA that wrote the element finished (the
-// epilogue starts with enough wait states, see mfma_drain).
-__device__ __forceinline__ float acc_read(float a) {
-    float v;
-    asm("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
-    return v;
-}
-// Wait states after the last MFMA before acc_read may read its result (more
-// than a 16-pass MFMA needs).
-__device__ __forceinline__ void mfma_drain() {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-}
-
 struct MxOps {
     uint4 q[4];
     i32x8 x[4];
