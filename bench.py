@@ -412,11 +412,14 @@ def bench_prefill(args, w, mx=False):
                    "weights": "int4_g64" if w.wfmt == 0 else "mxfp4",
                    "parallelism": "single_gpu"},
         "roofline": {"bound": "mfma",
-                     "kernel": "expert_ffn_prefill_mx (mx8_x_kernel + gate_up_mx + down_mx)" if mx
-                     else "expert_ffn_prefill",
+                     "kernel": "expert_ffn_prefill_mx (plan_kernel + mx8_x_kernel + gate_up_mx + "
+                               "down_mx + combine_rows_kernel)" if mx
+                     else ("expert_ffn_prefill (plan_kernel + " + ("x16_kernel + " if w.wfmt == 0 else "") +
+                           "gate_up_mfma + down_mfma + combine_rows_kernel)"),
                      "achieved": round(achieved, 1), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic_record(f"prefill_ffn_{w.name}_traffic.md", PREFILL_SOURCES),
+                     "traffic": traffic_record(f"prefill_ffn_{w.name}{'_mx' if mx else ''}_traffic.md",
+                                              PREFILL_SOURCES),
                      "flops_per_launch": flops,
                      "avg_launch_us": round(ffn_s * 1e6, 1)},
     }
