@@ -201,25 +201,33 @@ __device__ __forceinline__ float f16x8_sum(uint4 v, float s) {
 // as an f16 hi/lo pair (B side), and 8 group sums of one A row (A side).  In the
 // device layout group g of row n sits in the scale (bias) word of block
 // (n / 16, g / 2), half g % 2.
-__device__ __forceinline__ void bias_b(const uint8_t* W, const PrefillParams& p, int m, int n,
-                                       int G, int g0, uint4* hi, uint4* lo) {
+// Loads and conversions are separate calls, so that a tile issues all the
+// loads of 16 groups before it waits for any (one round trip, not one per call).
+struct BiasRaw {
+    uint32_t bw[4], sw[4];   // B side: bias and scale words of 8 groups
+    float x[8];              // A side: 8 group sums
+};
+__device__ __forceinline__ void bias_b_load(const uint8_t* W, const PrefillParams& p, int m, int n,
+                                            int G, int g0, BiasRaw& r) {
     const int64_t row = static_cast<int64_t>(n / 16) * (G / 2) * 64 + (n & 15) * 4;
     const uint8_t* bp = W + p.b_off[m] + row;
     const uint8_t* sp = W + p.s_off[m] + row;
-    uint32_t bw[4] = {0u, 0u, 0u, 0u}, sw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (g0 + 2 * j < G) {   // a short row (G = 2 or 4 groups, always even) stops early
-            const int64_t o = static_cast<int64_t>(g0 / 2 + j) * 64;
-            bw[j] = *reinterpret_cast<const uint32_t*>(bp + o);
-            sw[j] = *reinterpret_cast<const uint32_t*>(sp + o);
-        }
+    for (int j = 0; j < 4; ++j) {   // groups past G read group 0 (zeroed by bias_b_cvt)
+        const int64_t o = static_cast<int64_t>(g0 + 2 * j < G ? g0 / 2 + j : 0) * 64;
+        r.bw[j] = *reinterpret_cast<const uint32_t*>(bp + o);
+        r.sw[j] = *reinterpret_cast<const uint32_t*>(sp + o);
     }
+}
+// a short row (G = 2, 4 or 6 groups, always even) ends inside the 8
+__device__ __forceinline__ void bias_b_cvt(const BiasRaw& r, int G, int g0, uint4* hi, uint4* lo) {
     uint32_t h[4], l[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float v0 = __uint_as_float(bw[i] << 16) + 8.0f * __uint_as_float(sw[i] << 16);
-        const float v1 = __uint_as_float(bw[i] & 0xFFFF0000u) + 8.0f * __uint_as_float(sw[i] & 0xFFFF0000u);
+        const bool in = g0 + 2 * i < G;
+        const uint32_t bw = in ? r.bw[i] : 0u, sw = in ? r.sw[i] : 0u;
+        const float v0 = __uint_as_float(bw << 16) + 8.0f * __uint_as_float(sw << 16);
+        const float v1 = __uint_as_float(bw & 0xFFFF0000u) + 8.0f * __uint_as_float(sw & 0xFFFF0000u);
         const _Float16 a = static_cast<_Float16>(v0), b = static_cast<_Float16>(v1);
         h[i] = __builtin_bit_cast(uint32_t, half2v{a, b});
         l[i] = __builtin_bit_cast(uint32_t, half2v{static_cast<_Float16>(v0 - static_cast<float>(a)),
@@ -228,17 +236,27 @@ __device__ __forceinline__ void bias_b(const uint8_t* W, const PrefillParams& p,
     *hi = make_uint4(h[0], h[1], h[2], h[3]);
     *lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
-__device__ __forceinline__ void bias_a(const float* sums, int G, int g0, uint4* hi, uint4* lo) {
-    float v[8];
+// 8 group sums [g0, g0 + 8) of a row of G (even) sums, 8-byte loads; sums past
+// G read sum 0 and are zeroed by bias_a_cvt.
+__device__ __forceinline__ void bias_a_load(const float* sums, int G, int g0, BiasRaw& r) {
+    const float2* s2 = reinterpret_cast<const float2*>(sums);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = g0 + i < G ? sums[g0 + i] : 0.0f;
+    for (int i = 0; i < 4; ++i) {
+        const float2 v = s2[g0 + 2 * i < G ? g0 / 2 + i : 0];
+        r.x[2 * i] = v.x;
+        r.x[2 * i + 1] = v.y;
+    }
+}
+__device__ __forceinline__ void bias_a_cvt(const BiasRaw& r, int G, int g0, uint4* hi, uint4* lo) {
     uint32_t h[4], l[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const _Float16 a = static_cast<_Float16>(v[2 * i]), b = static_cast<_Float16>(v[2 * i + 1]);
+        const bool in = g0 + 2 * i < G;
+        const float x0 = in ? r.x[2 * i] : 0.0f, x1 = in ? r.x[2 * i + 1] : 0.0f;
+        const _Float16 a = static_cast<_Float16>(x0), b = static_cast<_Float16>(x1);
         h[i] = __builtin_bit_cast(uint32_t, half2v{a, b});
-        l[i] = __builtin_bit_cast(uint32_t, half2v{static_cast<_Float16>(v[2 * i] - static_cast<float>(a)),
-                                                  static_cast<_Float16>(v[2 * i + 1] - static_cast<float>(b))});
+        l[i] = __builtin_bit_cast(uint32_t, half2v{static_cast<_Float16>(x0 - static_cast<float>(a)),
+                                                  static_cast<_Float16>(x1 - static_cast<float>(b))});
     }
     *hi = make_uint4(h[0], h[1], h[2], h[3]);
     *lo = make_uint4(l[0], l[1], l[2], l[3]);
@@ -546,14 +564,21 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
         if (FMT == MOE355_W_INT4_G64) {
             // bias: R += sum_g (b + 8 s)[n, g] * xsum[m, g], both factors as f16 hi + lo
             for (int g0 = 0; g0 < G; g0 += 16) {
-                const int gl = g0 + 8 * hh;
+                const int gl = g0 + 8 * hh, BG = G;
+                BiasRaw rb[4], ra[4];   // every load of the 16 groups first, then one wait
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    bias_b_load(static_cast<const uint8_t*>(W), p, c >> 1, fr + 32 * (c & 1) + ln, G, gl, rb[c]);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+                    bias_a_load(p.xsum + static_cast<int64_t>(rtok[mt * 32 + ln]) * G, G, gl, ra[mt]);
                 uint4 bh[4], bl[4];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) bias_b(static_cast<const uint8_t*>(W), p, c >> 1, fr + 32 * (c & 1) + ln, G, gl, &bh[c], &bl[c]);
+                for (int c = 0; c < 4; ++c) bias_b_cvt(rb[c], BG, gl, &bh[c], &bl[c]);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     uint4 xh, xl;
-                    bias_a(p.xsum + static_cast<int64_t>(rtok[mt * 32 + ln]) * G, G, gl, &xh, &xl);
+                    bias_a_cvt(ra[mt], BG, gl, &xh, &xl);
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         R[c][mt] = mma<FMT>(bh[c], xh, R[c][mt]);
@@ -859,15 +884,22 @@ __global__ void __launch_bounds__(256) down_mfma(PrefillParams p) {
 
         if (FMT == MOE355_W_INT4_G64) {
             for (int g0 = 0; g0 < Gd; g0 += 16) {
-                const int gl = g0 + 8 * hh;
-                uint4 bh[4], bl[4];
+                const int gl = g0 + 8 * hh, BG = Gd;
+                BiasRaw rb[4], ra[4];   // every load of the 16 groups first, then one wait
 #pragma unroll
-                for (int c = 0; c < 4; ++c) bias_b(Wb, p, 2, nr + 32 * c + ln, Gd, gl, &bh[c], &bl[c]);
+                for (int c = 0; c < 4; ++c) bias_b_load(Wb, p, 2, nr + 32 * c + ln, Gd, gl, rb[c]);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     const int r = mt * 32 + ln;
+                    bias_a_load(p.hsum + static_cast<int64_t>(pbase + (r < rows ? r : 0)) * Gd, Gd, gl, ra[mt]);
+                }
+                uint4 bh[4], bl[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) bias_b_cvt(rb[c], BG, gl, &bh[c], &bl[c]);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
                     uint4 xh, xl;
-                    bias_a(p.hsum + static_cast<int64_t>(pbase + (r < rows ? r : 0)) * Gd, Gd, gl, &xh, &xl);
+                    bias_a_cvt(ra[mt], BG, gl, &xh, &xl);
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         R[mt][c] = mma<FMT>(xh, bh[c], R[mt][c]);
