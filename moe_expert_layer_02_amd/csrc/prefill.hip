@@ -135,6 +135,22 @@ __device__ __forceinline__ void mfma_drain() {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
+// The values of lanes l and l ^ 32 by gfx950's v_permlane32_swap (a VALU op,
+// no LDS round trip): lanes 0-31 get (v[l], v[l + 32]), lanes 32-63
+// (v[l - 32], v[l]) (checked with a one-wavefront probe).
+__device__ __forceinline__ uint32_t half_partner(uint32_t v, int hh) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return hh ? r[0] : r[1];
+}
+__device__ __forceinline__ float max_with_partner(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_partner(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // silu(g) = g / (1 + e^-g) with the hardware reciprocal (1 ulp); e^-g = inf
 // gives -0 for very negative g.
 __device__ __forceinline__ float silu(float g) {
@@ -163,10 +179,14 @@ __device__ __forceinline__ half2v as_h2(uint32_t v) { return __builtin_bit_cast(
 // exact for any bf16 scale (|q - 8| <= 8 keeps the product within 11 bits).
 __device__ __forceinline__ uint4 int4_dword_f16(uint32_t d, half2v s2) {
     const half2v off = {static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
+    // the two masks live in registers, so that (x & mask) | magic is one
+    // v_and_or_b32 (gfx9 encodes at most one literal per VALU instruction)
+    uint32_t mask = 0x000F000Fu, magic = 0x64006400u;
+    asm("" : "+v"(mask), "+v"(magic));
     uint32_t v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const half2v q = as_h2(((d >> (4 * i)) & 0x000F000Fu) | 0x64006400u);  // 1024 + q
+        const half2v q = as_h2(((d >> (4 * i)) & mask) | magic);  // 1024 + q
         v[i] = __builtin_bit_cast(uint32_t, (q + off) * s2);
     }
     return make_uint4(v[0], v[1], v[2], v[3]);
@@ -629,7 +649,7 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
                                                : (hi[2] | (static_cast<uint32_t>(hi[3]) << 16));
                         const uint32_t gl = hh ? (lo[0] | (static_cast<uint32_t>(lo[1]) << 16))
                                                : (lo[2] | (static_cast<uint32_t>(lo[3]) << 16));
-                        const uint32_t rh = __shfl_xor(gh, 32, WAVE), rl = __shfl_xor(gl, 32, WAVE);
+                        const uint32_t rh = half_partner(gh, hh), rl = half_partner(gl, hh);
                         if (hh == 0) {
                             hw[0] = hi[0] | (rh << 16);
                             hw[1] = hi[1] | (rh & 0xFFFF0000u);
@@ -657,7 +677,7 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
             if (FMT == MOE355_W_INT4_G64) {
                 // the row's sum over the wavefront's 64 features: one int4 group of h
                 // (not finite when an h value left f16's range: flag the call)
-                gsum += __shfl_xor(gsum, 32, WAVE);
+                gsum = sum_with_partner(gsum);
                 if (keep && !(__builtin_fabsf(gsum) <= 3.0e38f))
                     __hip_atomic_fetch_or(p.err, ERR_F16_RANGE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (keep && hh == 0) p.hsum[static_cast<int64_t>(pbase + r) * (I / 64) + fw / 64] = gsum;
@@ -1308,7 +1328,7 @@ __global__ void __launch_bounds__(256) gate_up_mx(MxParams p) {
                     float amax = 0.0f;
 #pragma unroll
                     for (int i = 0; i < 16; ++i) amax = fmaxf(amax, __builtin_fabsf(v[i]));
-                    amax = fmaxf(amax, __shfl_xor(amax, 32, WAVE));
+                    amax = max_with_partner(amax);
                     const int ex = mx_exponent(amax);
                     const float inv = mx_inv_scale(ex), sc = mx_scale(ex);
                     uint32_t cw[4];
