@@ -66,6 +66,16 @@ struct PrefillParams {
     uint32_t* err;           // the call's error word (cleared by the plan kernel)
 };
 
+// A load of memory that no kernel of the launch writes (the tile plan, the
+// bucket offsets) through the constant address space: at a wavefront-uniform
+// address the compiler makes it a scalar load, whose wait (lgkmcnt) does not
+// also wait for the vector-memory stores and direct loads in flight.
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* q) {
+    typedef const __attribute__((address_space(4))) T* ConstPtr;
+    return *(ConstPtr)(q);
+}
+
 // Persistent tile loop: the work of a call split into NXCD contiguous ranges.
 struct TileRange {
     int begin, end, step;
@@ -456,13 +466,13 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
     const uint32_t ring_lds = lds_addr(ring);
 
     const int FX = (I + GU_FEAT - 1) / GU_FEAT;
-    const TileRange tr = tile_range(*p.n_tiles * FX);
+    const TileRange tr = tile_range(ld_const(p.n_tiles) * FX);
     const void* xs = uniform_ptr(FMT == MOE355_W_INT4_G64 ? p.xf : p.x);
     for (int t = tr.begin; t < tr.end; t += tr.step) {
         const int y = t / FX;
-        const int e = p.tile_e[y], m0 = p.tile_m0[y];
-        const int pbase = p.offsets[e] + m0;
-        const int rows = min(BM, p.offsets[e + 1] - pbase);
+        const int e = ld_const(p.tile_e + y), m0 = ld_const(p.tile_m0 + y);
+        const int pbase = ld_const(p.offsets + e) + m0;
+        const int rows = min(BM, ld_const(p.offsets + e + 1) - pbase);
         const void* W = uniform_ptr(p.W + static_cast<int64_t>(e) * p.S);
         const int fw = (t - y * FX) * GU_FEAT + 64 * wv;
         // The lane index is made opaque once per tile so that the compiler
@@ -758,12 +768,12 @@ __global__ void __launch_bounds__(256) down_mfma(PrefillParams p) {
     const int H = p.H, I = p.I, Gd = I / 64, KS = I / BK;
     const int FX = (H + DN_COLS - 1) / DN_COLS;
     const uint32_t ring_lds = lds_addr(ring);
-    const TileRange tr = tile_range(*p.n_tiles * FX);
+    const TileRange tr = tile_range(ld_const(p.n_tiles) * FX);
     for (int t = tr.begin; t < tr.end; t += tr.step) {
         const int y = t / FX;
-        const int e = p.tile_e[y], m0 = p.tile_m0[y];
-        const int pbase = p.offsets[e] + m0;
-        const int rows = min(BM, p.offsets[e + 1] - pbase);
+        const int e = ld_const(p.tile_e + y), m0 = ld_const(p.tile_m0 + y);
+        const int pbase = ld_const(p.offsets + e) + m0;
+        const int rows = min(BM, ld_const(p.offsets + e + 1) - pbase);
         const void* W = uniform_ptr(p.W + static_cast<int64_t>(e) * p.S);
         const uint8_t* Wb = p.W + static_cast<int64_t>(e) * p.S;
         const int nw = (t - y * FX) * DN_COLS + 128 * wv;
@@ -1134,7 +1144,7 @@ __global__ void __launch_bounds__(256) gate_up_mx(MxParams p) {
     const uint32_t ring_lds = lds_addr(ring);
 
     const int FX = (I + GU_FEAT - 1) / GU_FEAT;
-    const TileRange tr = tile_range(*p.n_tiles * FX);
+    const TileRange tr = tile_range(ld_const(p.n_tiles) * FX);
     const void* xs = uniform_ptr(p.xq);
     const void* xes = uniform_ptr(p.xe);
     // The lane index is made opaque again for every tile (below), so that the
@@ -1155,16 +1165,23 @@ __global__ void __launch_bounds__(256) gate_up_mx(MxParams p) {
         const void* W;
         uint32_t aoff[2], xsoff, bq[4], bsc[2];
     };
-    auto setup = [&](int t, Src& src) {
+    // this thread's pair of tile t (threads below BM; rows past the bucket
+    // re-read its first row), loaded ahead of its use in setup
+    auto tile_pair = [&](int t) {
         const int y = t / FX;
-        const int e = p.tile_e[y], m0 = p.tile_m0[y];
-        const int pbase = p.offsets[e] + m0;
-        const int rows = min(BM, p.offsets[e + 1] - pbase);
+        const int e = ld_const(p.tile_e + y), m0 = ld_const(p.tile_m0 + y);
+        const int pbase = ld_const(p.offsets + e) + m0;
+        const int rows = min(BM, ld_const(p.offsets + e + 1) - pbase);
+        return tid < BM ? p.perm[pbase + (tid < rows ? tid : 0)] : 0;
+    };
+    auto setup = [&](int t, Src& src, int pair) {
+        const int y = t / FX;
+        const int e = ld_const(p.tile_e + y);
         const int fw = (t - y * FX) * GU_FEAT + 64 * wv;
         const int fr = fw < I ? fw : 0;   // idle wavefronts of a small I compute on row 0
         src.W = uniform_ptr(p.W + static_cast<int64_t>(e) * p.S);
         __syncthreads();   // nobody reads the previous tokens any more
-        if (tid < BM) rtok[tid] = p.perm[pbase + (tid < rows ? tid : 0)] / p.k;
+        if (tid < BM) rtok[tid] = pair / p.k;
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < 2; ++j) {   // 2 blocks of 16 rows x 4 chunks
@@ -1220,15 +1237,17 @@ __global__ void __launch_bounds__(256) gate_up_mx(MxParams p) {
     Src src;
     if (tr.begin < tr.end) {
         refresh_lane();
-        setup(tr.begin, src);
+        setup(tr.begin, src, tile_pair(tr.begin));
         prologue(src);
     }
     for (int t = tr.begin; t < tr.end; t += tr.step) {
         refresh_lane();
+        // the next tile's pair ids: loaded now, used after this tile's K loop
+        const int next_pair = t + tr.step < tr.end ? tile_pair(t + tr.step) : 0;
         const int y = t / FX;
-        const int e = p.tile_e[y], m0 = p.tile_m0[y];
-        const int pbase = p.offsets[e] + m0;
-        const int rows = min(BM, p.offsets[e + 1] - pbase);
+        const int e = ld_const(p.tile_e + y), m0 = ld_const(p.tile_m0 + y);
+        const int pbase = ld_const(p.offsets + e) + m0;
+        const int rows = min(BM, ld_const(p.offsets + e + 1) - pbase);
         const int fw = (t - y * FX) * GU_FEAT + 64 * wv;
         const bool live = fw < I;
         // row tiles of 32 the MFMAs cover: a bucket's last tile is often short,
@@ -1298,7 +1317,7 @@ __global__ void __launch_bounds__(256) gate_up_mx(MxParams p) {
         // the next tile's first stages load while this one's epilogue runs
         __builtin_amdgcn_sched_barrier(0);
         if (t + tr.step < tr.end) {
-            setup(t + tr.step, src);   // its first barrier: every wavefront is past the ring
+            setup(t + tr.step, src, next_pair);   // its first barrier: every wavefront is past the ring
             prologue(src);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -1315,7 +1334,6 @@ __global__ void __launch_bounds__(256) gate_up_mx(MxParams p) {
             const int64_t prow = static_cast<int64_t>(pbase + r);
 #pragma unroll
             for (int ft = 0; ft < 2; ++ft) {
-                __builtin_amdgcn_sched_barrier(0);   // one block at a time: few live registers
                 float v[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -1379,7 +1397,7 @@ __global__ void __launch_bounds__(256) down_mx(MxParams p) {
     const int H = p.H, I = p.I, KS = I / MD_K;
     const int FX = (H + DN_COLS - 1) / DN_COLS;
     const uint32_t ring_lds = lds_addr(ring);
-    const TileRange tr = tile_range(*p.n_tiles * FX);
+    const TileRange tr = tile_range(ld_const(p.n_tiles) * FX);
     int lane = tid & (WAVE - 1), ln = 0, hh = 0;   // opaque per tile, as in gate_up_mx
     auto refresh_lane = [&]() {
         asm volatile("" : "+v"(lane));
@@ -1395,9 +1413,9 @@ __global__ void __launch_bounds__(256) down_mx(MxParams p) {
     };
     auto setup = [&](int t, Src& src) {
         const int y = t / FX;
-        const int e = p.tile_e[y], m0 = p.tile_m0[y];
-        const int pbase = p.offsets[e] + m0;
-        const int rows = min(BM, p.offsets[e + 1] - pbase);
+        const int e = ld_const(p.tile_e + y), m0 = ld_const(p.tile_m0 + y);
+        const int pbase = ld_const(p.offsets + e) + m0;
+        const int rows = min(BM, ld_const(p.offsets + e + 1) - pbase);
         const int nw = (t - y * FX) * DN_COLS + 128 * wv;
         const int nr = nw < H ? nw : 0;   // idle wavefronts of a small H compute on row 0
         src.W = uniform_ptr(p.W + static_cast<int64_t>(e) * p.S);
@@ -1460,9 +1478,9 @@ __global__ void __launch_bounds__(256) down_mx(MxParams p) {
     for (int t = tr.begin; t < tr.end; t += tr.step) {
         refresh_lane();
         const int y = t / FX;
-        const int e = p.tile_e[y], m0 = p.tile_m0[y];
-        const int pbase = p.offsets[e] + m0;
-        const int rows = min(BM, p.offsets[e + 1] - pbase);
+        const int e = ld_const(p.tile_e + y), m0 = ld_const(p.tile_m0 + y);
+        const int pbase = ld_const(p.offsets + e) + m0;
+        const int rows = min(BM, ld_const(p.offsets + e + 1) - pbase);
         const int nw = (t - y * FX) * DN_COLS + 128 * wv;
         const bool live = nw < H;
         const int nmt = __builtin_amdgcn_readfirstlane((rows + 31) / 32);   // row tiles with rows
