@@ -651,10 +651,12 @@ __device__ __forceinline__ void gate_up_body(const DecodeParams& p, PlanLds& pl,
     const int tile_rows = RW * RT * 16;
     const int tiles = p.I / tile_rows;
     const int n_items = pl.n_uniq * tiles;
-    const int per = (n_items + nblk - 1) / nblk;
-    const int i_beg = bid * per;
-    const int i_end = min(n_items, i_beg + per);
-    if (i_beg >= i_end) return;
+    // items bid, bid + nblk, ...: every block gets floor or ceil(n_items / nblk)
+    // (contiguous ranges of ceil(n_items / nblk) left the last blocks empty,
+    // and the CUs that held two full blocks set the time)
+    const int i_beg = bid;
+    if (i_beg >= n_items) return;
+    const int i_last = i_beg + (n_items - 1 - i_beg) / nblk * nblk;
 
     // unit = (item, token group); stage = (unit, slab)
     auto tokens_of = [&](int item) { return pl.plan[item / tiles].w; };
@@ -663,7 +665,7 @@ __device__ __forceinline__ void gate_up_body(const DecodeParams& p, PlanLds& pl,
     // columns with no pair read the expert's first token (their MFMA columns are
     // never used).
     auto load = [&](GuStage<FMT, KW, RT>& st, int item, int tg, int s) {
-        const int it = min(item, i_end - 1);
+        const int it = min(item, i_last);
         const int u = it / tiles, tile = it - u * tiles;
         const ExpertRef ref = expert_ref(p, pl, u);
         const int row0 = tile * tile_rows + rw * RT * 16;
@@ -826,7 +828,8 @@ __device__ __forceinline__ void gate_up_body(const DecodeParams& p, PlanLds& pl,
             return;
         }
         c.tg = 0;
-        c.valid = ++c.item < i_end;
+        c.item += nblk;
+        c.valid = c.item <= i_last;
     };
     // D stages in a ring: the loads of the next D-1 stages stay in flight while
     // one is computed
@@ -846,7 +849,7 @@ __device__ __forceinline__ void gate_up_body(const DecodeParams& p, PlanLds& pl,
     bool fresh = fill_sync == nullptr;
     bool need = false;
     if (!fresh)
-        for (int it = i_beg; it < i_end; ++it) need |= pl.plan[it / tiles].x < 0;
+        for (int it = i_beg; it <= i_last; it += nblk) need |= pl.plan[it / tiles].x < 0;
     bool done = false;
     while (!done) {
 #pragma unroll
@@ -1087,12 +1090,27 @@ __global__ void __launch_bounds__(NW * WAVE) down_lds_kernel(DecodeParams p) {
     auto stage_h = [&](int p0) {
         const int nr = min(nwin, n_pos - p0);
         const int rq = I / 4;   // uint4 of h per row
-        for (int i = threadIdx.x; i < nr * rq; i += NW * WAVE) {
-            const int r = i / rq, c = i - r * rq;
-            const int64_t pair = pl.pairs[p0 + r];
-            const uint4* src = c < I / 8 ? reinterpret_cast<const uint4*>(p.h_hi + pair * I) + c
-                                         : reinterpret_cast<const uint4*>(p.h_lo + pair * I) + (c - I / 8);
-            hsm[r * RSq + c] = *src;
+        const int n = nr * rq;
+        // eight loads in flight per thread before their LDS stores (one load,
+        // wait and store at a time made the window a chain of round trips)
+        constexpr int B = 8;
+        for (int i0 = threadIdx.x; i0 < n; i0 += B * NW * WAVE) {
+            uint4 v[B];
+            // without branches, so the compiler cannot sink each load next to its
+            // store: chunks past the window re-read and rewrite chunk 0 (the same
+            // value)
+            int at[B];
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                const int i = i0 + j * NW * WAVE < n ? i0 + j * NW * WAVE : 0;
+                const int r = i / rq, c = i - r * rq;
+                const int64_t pair = pl.pairs[p0 + r];
+                const uint16_t* base = c < I / 8 ? p.h_hi : p.h_lo;
+                v[j] = reinterpret_cast<const uint4*>(base + pair * I)[c < I / 8 ? c : c - I / 8];
+                at[j] = r * RSq + c;
+            }
+#pragma unroll
+            for (int j = 0; j < B; ++j) hsm[at[j]] = v[j];
         }
         if (threadIdx.x == 0) {
             win[0] = p0;
@@ -1161,16 +1179,18 @@ __global__ void __launch_bounds__(NW * WAVE) down_lds_kernel(DecodeParams p) {
     Cur lc, cc;
     set_item(lc, i_beg);
     cc = lc;
-    {
-        int a, nt;
-        group_of(cc, a, nt);
-        stage_h(a);
-    }
+    // the first weight stages do not depend on h: their loads go out before the
+    // window is staged
     WSlab<RT> ring[D];
 #pragma unroll
     for (int d = 0; d < D - 1; ++d) {
         load_stage(ring[d], lc);
         adv(lc);
+    }
+    {
+        int a, nt;
+        group_of(cc, a, nt);
+        stage_h(a);
     }
     bool done = false;
     while (!done) {
