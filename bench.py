@@ -648,6 +648,63 @@ def bench_decode_host_pool(args):
     return res
 
 
+def bench_decode_floor(args):
+    """What a decode step's 40 graph nodes cost before any expert work: graphs
+    of 40 dependent nodes on one stream, each replay preceded by a 1 GiB read
+    that evicts the lines the nodes touch (L2 and the memory-side cache), then
+    timed with HIP events around the replay alone.  Nodes: an empty-work kernel
+    of one workgroup (a one-element add), a 1 MiB fill (hundreds of
+    workgroups), one dependent cold read (a one-element copy from a separate
+    cold 2 MiB page per node: launch + one HBM round trip + the store), and a
+    7 MiB copy per node from 40 distinct sources (14 MiB moved, the size of a
+    Qwen-like layer call's expert bytes)."""
+    import torch
+    dev = torch.device("cuda:0")
+    L, reps = 40, max(5, args.steps)
+    page = 1 << 21
+    one = torch.zeros(1, dtype=torch.float32, device=dev)
+    fill = torch.empty(513 * 512, dtype=torch.float32, device=dev)
+    src = torch.zeros(L * page // 4, dtype=torch.float32, device=dev)
+    dst = torch.zeros(L, dtype=torch.float32, device=dev)
+    n7 = (7 << 20) // 2
+    big = torch.zeros((L, n7), dtype=torch.bfloat16, device=dev)
+    out7 = torch.empty(n7, dtype=torch.bfloat16, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)      # 1 GiB
+    nodes = {
+        "empty_node": lambda l: one.add_(1.0),
+        "fill_1MiB_node": lambda l: fill.fill_(float(l)),
+        "cold_read_node": lambda l: dst[l:l + 1].copy_(src[l * (page // 4):l * (page // 4) + 1]),
+        "copy_7MiB_node": lambda l: out7.copy_(big[l]),
+    }
+    stream = torch.cuda.current_stream()
+    res = {"metric": "decode graph-node floor", "unit": "us per node", "n_gpus": 1,
+           "nodes_per_graph": L, "replays": reps, "data": "synthetic",
+           "config": {"workload": "decode_floor", "parallelism": "single_gpu"}}
+    for name, fn in nodes.items():
+        for l in range(L):
+            fn(l)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for l in range(L):
+                fn(l)
+        torch.cuda.synchronize()
+        ts = []
+        for i in range(reps + 2):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(e0.elapsed_time(e1) * 1e3 / L)
+        res[name] = round(float(np.median(ts)), 3)
+        del g
+    res["copy_7MiB_GBs"] = round(2 * n7 * 2 / (res["copy_7MiB_node"] * 1e-6) / 1e9, 1)
+    return res
+
+
 def C_seed(w):
     from workloads import configs as C
     return C.seed(w.cid, 0)
@@ -698,7 +755,7 @@ def main():
     ap.add_argument("--workload", default="qwen_decode",
                     choices=["qwen_decode", "ds_decode", "qwen_prefill", "ds_prefill",
                              "ds_prefill_mx", "miss_replay", "qwen_prefill_pipeline",
-                             "ds_prefill_pipeline", "qwen_decode_host_pool"])
+                             "ds_prefill_pipeline", "qwen_decode_host_pool", "decode_floor"])
     ap.add_argument("--order", default="auto", choices=["auto", "fused", "split"],
                     help="decode layer call order (auto: fused)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -722,6 +779,9 @@ def main():
     from workloads import configs as C
     if args.workload == "miss_replay":
         print(json.dumps(bench_miss_replay(args)), flush=True)
+        return
+    if args.workload == "decode_floor":
+        print(json.dumps(bench_decode_floor(args)), flush=True)
         return
     if args.workload == "qwen_decode_host_pool":
         print(json.dumps(bench_decode_host_pool(args)), flush=True)
