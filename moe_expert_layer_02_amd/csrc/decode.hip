@@ -1063,7 +1063,6 @@ __global__ void __launch_bounds__(NW * WAVE) down_lds_kernel(DecodeParams p) {
     const int per = (n_items + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x);
     const int i_beg = static_cast<int>(blockIdx.x) * per, i_end = min(n_items, i_beg + per);
     if (i_beg >= i_end) return;   // block-uniform
-    const int n_pos = pl.plan[nu - 1].z + pl.plan[nu - 1].w;   // pair positions in use
 
     // cursor over (item, slab); an item past the block's end re-reads its last one
     struct Cur {
@@ -1086,6 +1085,15 @@ __global__ void __launch_bounds__(NW * WAVE) down_lds_kernel(DecodeParams p) {
     auto adv = [&](Cur& k) {
         if (++k.s == NS) set_item(k, k.it + 1);
     };
+    // pair positions this block's items use end at its last item's token group
+    // (a window staged beyond them would read h rows no item here multiplies)
+    int n_pos;
+    {
+        Cur k;
+        set_item(k, i_end - 1);
+        const int4 pr = pl.plan[k.u];
+        n_pos = pr.z + min(pr.w, TOK * (k.tg + 1));
+    }
     // the window from pair position p0 on (all threads; ends with a barrier)
     auto stage_h = [&](int p0) {
         const int nr = min(nwin, n_pos - p0);
