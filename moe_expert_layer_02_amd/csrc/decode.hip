@@ -1021,13 +1021,14 @@ __global__ void __launch_bounds__(256) down_kernel(DecodeParams p) {
 
 // ---------------------------------------------------------------------------
 // down + combine with h in LDS (many distinct experts, e.g. the DS-like decode).
-// A block of NW wavefronts takes items (distinct expert u, token group tg of up
-// to 16 of its pairs, NW * 16 RT consecutive output rows); wavefront w computes
-// rows r0 + 16 RT w (RT 16-row tiles) over all of I.  The block keeps the h rows
-// (hi and lo halves) of a window of consecutive pair positions in LDS, staged
-// before the first item and again only when an item's pairs leave the window
-// (the positions of consecutive items rise), so a wavefront's register ring
-// holds weights alone and runs D - 1 slabs ahead.  (With h in the ring, each
+// The work is cut into units (distinct expert u, token group tg of up to 16 of
+// its pairs, 16 RT consecutive output rows), each computed over all of I by one
+// wavefront (RT 16-row tiles); a block of NW wavefronts takes a contiguous,
+// balanced range of units.  The block keeps the h rows (hi and lo halves) of a
+// window of consecutive pair positions in LDS, staged before its first unit and
+// again only when a unit's pairs leave the window (the positions of
+// consecutive units rise), so a wavefront's register ring holds weights alone
+// and runs D - 1 slabs ahead.  (With h in the ring, each
 // stage also held 32 registers of h and two stages ahead filled the register
 // budget at two wavefronts per SIMD: half the bytes in flight of gate/up.)
 constexpr int DNL_LDS = 135168;   // bytes of staged h: 16 rows of I = 2048 with padding
@@ -1041,9 +1042,9 @@ __global__ void __launch_bounds__(NW * WAVE) down_lds_kernel(DecodeParams p) {
     __shared__ uint4 hsm[DNL_LDS / 16];
     stage_plan(p, pl);
     const int lane = threadIdx.x & (WAVE - 1), ln = lane & 15, gq = lane >> 4;
-    const int wv = threadIdx.x / WAVE;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);   // cursors in scalar registers
     constexpr int WR = 16 * RT;   // output rows per wavefront
-    const int I = p.I, NS = I / SLAB, CH = p.H / (NW * WR);
+    const int I = p.I, NS = I / SLAB;
     // row r of the window: hi halves (I / 8 uint4), lo halves, one uint4 of padding
     // (consecutive rows then start 4 banks apart, so 16 token rows do not collide)
     const int RSq = I / 4 + 1;
@@ -1059,20 +1060,33 @@ __global__ void __launch_bounds__(NW * WAVE) down_lds_kernel(DecodeParams p) {
         tgb[nu] = acc;
     }
     __syncthreads();
-    const int n_items = tgb[nu] * CH;
-    const int per = (n_items + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x);
-    const int i_beg = static_cast<int>(blockIdx.x) * per, i_end = min(n_items, i_beg + per);
-    if (i_beg >= i_end) return;   // block-uniform
+    // Units of WR rows: unit j = (token group q = j / NB, row band j % NB).  Block
+    // b owns units [jb, je) of a balanced split (one unit more or less than
+    // any other block), so a call with fewer 1024-row chunks than blocks still
+    // spreads its bytes over every CU; wavefront w takes units jb + w + NW i.
+    // A block's units visit the token groups q_first .. q_last in phases: a
+    // phase's units multiply the h rows of their group, which the window holds
+    // (it is restaged, between two barriers, only when a phase's group is
+    // outside it; every wavefront takes part in every phase change, including
+    // those of phases in which it has no unit).
+    const int NB = p.H / WR;
+    const int n_units = tgb[nu] * NB;
+    const int nb = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
+    const int jb = static_cast<int>(static_cast<int64_t>(n_units) * b / nb);
+    const int je = static_cast<int>(static_cast<int64_t>(n_units) * (b + 1) / nb);
+    if (jb >= je) return;   // block-uniform
+    const int q_first = jb / NB, q_last = (je - 1) / NB;
 
-    // cursor over (item, slab); an item past the block's end re-reads its last one
+    // cursor over the wavefront's (unit, slab) sequence; past its last unit it
+    // re-reads that unit's last slab
     struct Cur {
-        int it, s, u, tg, c;
+        int j, s, u, tg, band;
+        bool valid;
     };
-    auto set_item = [&](Cur& k, int it) {
-        k.it = it;
-        k.s = 0;
-        const int q = min(it, i_end - 1) / CH;
-        k.c = min(it, i_end - 1) - q * CH;
+    auto locate = [&](Cur& k, int j) {
+        k.j = j;
+        const int q = j / NB;
+        k.band = j - q * NB;
         int lo = 0, hi = nu - 1;   // the last u with tgb[u] <= q
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -1082,17 +1096,41 @@ __global__ void __launch_bounds__(NW * WAVE) down_lds_kernel(DecodeParams p) {
         k.u = lo;
         k.tg = q - tgb[lo];
     };
-    auto adv = [&](Cur& k) {
-        if (++k.s == NS) set_item(k, k.it + 1);
+    auto first = [&](Cur& k) {
+        k.s = 0;
+        k.valid = jb + wv < je;
+        locate(k, k.valid ? jb + wv : je - 1);
     };
-    // pair positions this block's items use end at its last item's token group
-    // (a window staged beyond them would read h rows no item here multiplies)
+    auto adv = [&](Cur& k) {
+        if (++k.s < NS) return;
+        if (k.valid && k.j + NW < je) {
+            k.s = 0;
+            locate(k, k.j + NW);
+        } else {
+            k.valid = false;
+            k.s = NS - 1;
+        }
+    };
+    auto q_of = [&](const Cur& k) { return k.j / NB; };
+    // pair positions of token group q: [a, a + nt)
+    auto group_at = [&](int q, int& a, int& nt) {
+        int lo = 0, hi = nu - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tgb[mid] <= q) lo = mid;
+            else hi = mid - 1;
+        }
+        const int4 pr = pl.plan[lo];
+        const int tg = q - tgb[lo];
+        a = pr.z + TOK * tg;
+        nt = min(TOK, pr.w - TOK * tg);
+    };
+    // pair positions this block's units use end at its last group
     int n_pos;
     {
-        Cur k;
-        set_item(k, i_end - 1);
-        const int4 pr = pl.plan[k.u];
-        n_pos = pr.z + min(pr.w, TOK * (k.tg + 1));
+        int a, nt;
+        group_at(q_last, a, nt);
+        n_pos = a + nt;
     }
     // the window from pair position p0 on (all threads; ends with a barrier)
     auto stage_h = [&](int p0) {
@@ -1126,6 +1164,15 @@ __global__ void __launch_bounds__(NW * WAVE) down_lds_kernel(DecodeParams p) {
         }
         __syncthreads();
     };
+    // phase change to group q (every wavefront, in phase order)
+    auto enter = [&](int q) {
+        int a, nt;
+        group_at(q, a, nt);
+        if (a < win[0] || a + nt > win[1]) {   // block-uniform
+            __syncthreads();   // every wavefront is done with the old window
+            stage_h(a);
+        }
+    };
     auto group_of = [&](const Cur& k, int& a, int& nt) {
         const int4 pr = pl.plan[k.u];
         a = pr.z + TOK * k.tg;
@@ -1137,7 +1184,7 @@ __global__ void __launch_bounds__(NW * WAVE) down_lds_kernel(DecodeParams p) {
     for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     auto load_stage = [&](WSlab<RT>& w, const Cur& k) {
         const ExpertRef ref = expert_ref(p, pl, k.u);
-        load_wslab<FMT, RT>(p, ref.src, 2, k.c * (NW * WR) + WR * wv, I, k.s * SLAB, ln, gq, w);
+        load_wslab<FMT, RT>(p, ref.src, 2, k.band * WR, I, k.s * SLAB, ln, gq, w);
     };
     auto compute = [&](const WSlab<RT>& w, const Cur& k) {
         int a, nt;
@@ -1165,7 +1212,7 @@ __global__ void __launch_bounds__(NW * WAVE) down_lds_kernel(DecodeParams p) {
         }
         if (k.tg == 0) {   // fill-through of the expert's down bytes
             const ExpertRef ref = expert_ref(p, pl, k.u);
-            if (ref.dst) store_wslab<FMT, RT>(p, ref.dst, 2, k.c * (NW * WR) + WR * wv, I, k.s * SLAB, ln, gq, w);
+            if (ref.dst) store_wslab<FMT, RT>(p, ref.dst, 2, k.band * WR, I, k.s * SLAB, ln, gq, w);
         }
     };
     auto epilogue = [&](const Cur& k) {
@@ -1174,7 +1221,7 @@ __global__ void __launch_bounds__(NW * WAVE) down_lds_kernel(DecodeParams p) {
         if (ln < nt) {
             const int pair = pl.pairs[a + ln];
             const float wt = pl.w[pair];
-            float* o = p.out + static_cast<int64_t>(pl.tok[a + ln]) * p.H + k.c * (NW * WR) + WR * wv;
+            float* o = p.out + static_cast<int64_t>(pl.tok[a + ln]) * p.H + k.band * WR;
 #pragma unroll
             for (int t = 0; t < RT; ++t)
 #pragma unroll
@@ -1185,43 +1232,41 @@ __global__ void __launch_bounds__(NW * WAVE) down_lds_kernel(DecodeParams p) {
     };
 
     Cur lc, cc;
-    set_item(lc, i_beg);
+    first(lc);
     cc = lc;
     // the first weight stages do not depend on h: their loads go out before the
     // window is staged
     WSlab<RT> ring[D];
+    if (cc.valid) {
 #pragma unroll
-    for (int d = 0; d < D - 1; ++d) {
-        load_stage(ring[d], lc);
-        adv(lc);
+        for (int d = 0; d < D - 1; ++d) {
+            load_stage(ring[d], lc);
+            adv(lc);
+        }
     }
     {
         int a, nt;
-        group_of(cc, a, nt);
+        group_at(q_first, a, nt);
         stage_h(a);
     }
-    bool done = false;
+    int cur_q = q_first;   // the phase every wavefront has entered
+    bool done = !cc.valid;
     while (!done) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             load_stage(ring[(d + D - 1) % D], lc);
             adv(lc);
             if (!done) {
-                if (cc.s == 0) {   // block-uniform: every wavefront walks the same items
-                    int a, nt;
-                    group_of(cc, a, nt);
-                    if (a < win[0] || a + nt > win[1]) {
-                        __syncthreads();   // every wavefront is done with the old window
-                        stage_h(a);
-                    }
-                }
+                if (cc.s == 0)
+                    while (cur_q < q_of(cc)) enter(++cur_q);
                 compute(ring[d], cc);
                 if (cc.s == NS - 1) epilogue(cc);
                 adv(cc);
-                done = cc.it >= i_end;
+                done = !cc.valid;
             }
         }
     }
+    while (cur_q < q_last) enter(++cur_q);   // the phases of the other wavefronts' units
 }
 
 // ---------------------------------------------------------------------------
