@@ -634,9 +634,11 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
             float gsum = 0.0f;
 #pragma unroll
             for (int ft = 0; ft < 2; ++ft) {
+                uint32_t HW[4][2], LW[4][2];   // per 8-feature block q: this lane's 4 values, hi and lo
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    uint32_t hw[2], lw[2];   // this lane's 4 values as packed hi and lo pairs
+                    uint32_t* hw = HW[q];
+                    uint32_t* lw = LW[q];
                     uint16_t hi[4], lo[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
@@ -677,10 +679,24 @@ __global__ void __launch_bounds__(256) gate_up_mfma(PrefillParams p) {
                         lw[0] = lo[0] | (static_cast<uint32_t>(lo[1]) << 16);
                         lw[1] = lo[2] | (static_cast<uint32_t>(lo[3]) << 16);
                     }
+                }
+                // lane half 0 holds positions 0-3 of each block, half 1 positions
+                // 4-7: half 0 trades its blocks 1, 3 for half 1's blocks 0, 2, and
+                // each lane stores two whole blocks (16 bytes each) of hi and of lo
+#pragma unroll
+                for (int qq = 0; qq < 2; ++qq) {
+                    const uint32_t rh0 = half_partner(hh ? HW[2 * qq][0] : HW[2 * qq + 1][0], hh);
+                    const uint32_t rh1 = half_partner(hh ? HW[2 * qq][1] : HW[2 * qq + 1][1], hh);
+                    const uint32_t rl0 = half_partner(hh ? LW[2 * qq][0] : LW[2 * qq + 1][0], hh);
+                    const uint32_t rl1 = half_partner(hh ? LW[2 * qq][1] : LW[2 * qq + 1][1], hh);
                     if (keep) {
-                        const int64_t at = row + fw + 32 * ft + 8 * q + 4 * hh;
-                        *reinterpret_cast<uint2*>(p.h_hi + at) = make_uint2(hw[0], hw[1]);
-                        *reinterpret_cast<uint2*>(p.h_lo + at) = make_uint2(lw[0], lw[1]);
+                        const int64_t at = row + fw + 32 * ft + 8 * (2 * qq + hh);
+                        const uint4 vh = hh ? make_uint4(rh0, rh1, HW[2 * qq + 1][0], HW[2 * qq + 1][1])
+                                            : make_uint4(HW[2 * qq][0], HW[2 * qq][1], rh0, rh1);
+                        const uint4 vl = hh ? make_uint4(rl0, rl1, LW[2 * qq + 1][0], LW[2 * qq + 1][1])
+                                            : make_uint4(LW[2 * qq][0], LW[2 * qq][1], rl0, rl1);
+                        *reinterpret_cast<uint4*>(p.h_hi + at) = vh;
+                        *reinterpret_cast<uint4*>(p.h_lo + at) = vl;
                     }
                 }
             }
@@ -1360,10 +1376,15 @@ __global__ void __launch_bounds__(256) gate_up_mx(MxParams p) {
                         v[4 * j + 2] -= e4m3_byte_value<2>(cw[j]) * sc;
                         v[4 * j + 3] -= e4m3_byte_value<3>(cw[j]) * sc;
                     }
+                    // lane half 0 holds features 8 j + 0..3 of the block, half 1
+                    // 8 j + 4..7: trading j = 2, 3 (half 0) for j = 0, 1 (half 1)
+                    // leaves each half 16 consecutive bytes, one store
+                    const uint32_t r0 = half_partner(hh ? cw[0] : cw[2], hh);
+                    const uint32_t r1 = half_partner(hh ? cw[1] : cw[3], hh);
                     if (keep) {
-                        uint8_t* dst = p.hq[term] + prow * I + f0 + 4 * hh;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) *reinterpret_cast<uint32_t*>(dst + 8 * j) = cw[j];
+                        uint8_t* dst = p.hq[term] + prow * I + f0 + 16 * hh;
+                        *reinterpret_cast<uint4*>(dst) = hh ? make_uint4(r0, cw[2], r1, cw[3])
+                                                            : make_uint4(cw[0], r0, cw[1], r1);
                         if (hh == 0) p.he[term][prow * (I / 32) + f0 / 32] = static_cast<uint8_t>(ex + 127);
                     }
                 }
