@@ -28,17 +28,22 @@ __global__ void __launch_bounds__(256) perm_count_kernel(const int32_t* __restri
     for (int e = threadIdx.x; e < E; e += blockDim.x) hist[static_cast<int64_t>(blockIdx.x) * E + e] = h[e];
 }
 
+// One thread per expert walks the chunks' counts twice, SB loads in flight at a
+// time (the counts come from other XCDs' stores, so each batch is a trip to the
+// memory side; one load at a time made this kernel a chain of nb trips).
+constexpr int SB = 16;
 __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ hist, int nb, int E,
                                                          int n, int32_t* __restrict__ offsets) {
-    __shared__ int32_t tot[1024];
     __shared__ int32_t wave_tot[16];
     const int e = threadIdx.x;
     int running = 0;
     if (e < E)
-        for (int b = 0; b < nb; ++b) {
-            const int v = hist[static_cast<int64_t>(b) * E + e];
-            hist[static_cast<int64_t>(b) * E + e] = running;
-            running += v;
+        for (int b0 = 0; b0 < nb; b0 += SB) {
+            int v[SB];
+#pragma unroll
+            for (int j = 0; j < SB; ++j) v[j] = b0 + j < nb ? hist[static_cast<int64_t>(b0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < SB; ++j) running += v[j];
         }
     // exclusive scan of the per-expert totals
     const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
@@ -53,10 +58,20 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ h
     int base = 0;
     for (int i = 0; i < w; ++i) base += wave_tot[i];
     const int excl = base + inc - running;
-    tot[e] = excl;
     if (e < E) {
         offsets[e] = excl;
-        for (int b = 0; b < nb; ++b) hist[static_cast<int64_t>(b) * E + e] += excl;
+        int acc = excl;   // chunk b's base for expert e: excl + the counts of chunks < b
+        for (int b0 = 0; b0 < nb; b0 += SB) {
+            int v[SB];
+#pragma unroll
+            for (int j = 0; j < SB; ++j) v[j] = b0 + j < nb ? hist[static_cast<int64_t>(b0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < SB; ++j)
+                if (b0 + j < nb) {
+                    hist[static_cast<int64_t>(b0 + j) * E + e] = acc;
+                    acc += v[j];
+                }
+        }
     }
     if (e == 0) offsets[E] = n;
 }
@@ -71,9 +86,20 @@ __global__ void __launch_bounds__(64) perm_scatter_kernel(const int32_t* __restr
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 1;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
     const int beg = blockIdx.x * PCHUNK;
-    for (int g = beg; g < beg + PCHUNK && g < n; g += WAVE) {
+    // the chunk's ids, all requested before the first is ranked
+    constexpr int NG = PCHUNK / WAVE;
+    int idv[NG];
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+        const int i = beg + q * WAVE + lane;
+        idv[q] = i < n ? ids[i] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+        const int g = beg + q * WAVE;
+        if (g >= n) break;
         const int i = g + lane;
-        int e = i < n ? ids[i] : -1;
+        int e = idv[q];
         const bool valid = e >= 0 && e < E;
         uint64_t peers = __ballot(valid);
         for (int b = 0; b < nbits; ++b) {
