@@ -28,8 +28,10 @@
 //     reduce their partial sums through LDS and write h.  It also zeroes the
 //     layer output.
 //   down + combine: a wavefront item is (distinct expert, tile of H rows) over
-//     all of I; each row's result meets the routing weight and is added into
-//     the fp32 layer output with an atomic (k additions per element).
+//     all of I (with many distinct experts, units of 64 rows dealt to the
+//     blocks in balanced ranges, h staged in LDS); each row's result meets the
+//     routing weight and is added into the fp32 layer output with an atomic
+//     (k additions per element).
 // Each block stages the call's plan (for each distinct expert: where its bytes
 // live, whether this call fills a cache slot with it, its routed pairs) in LDS
 // first, so every weight load is independent of the others, and each
@@ -1692,8 +1694,8 @@ moe355_status launch_decode(const DecodeParams& p, int max_uniq, uint32_t* sync,
     if (items2 >= 2 * slots && p.H % 512 == 0 && 16 * (p.I / 4 + 1) * 16 <= DNL_LDS) {
         // many distinct experts: h in LDS, one block per CU (a window holds a
         // full token group of any expert); four row tiles per wavefront, one
-        // slab ahead, sixteen wavefronts (four per SIMD) where H allows items of
-        // 1024 rows, else eight (DS-like: 154 us per FFN call with sixteen,
+        // slab ahead, sixteen wavefronts (four per SIMD) where H is a multiple
+        // of 1024, else eight (DS-like: 154 us per FFN call with sixteen,
         // 156 us with eight, against 168-172 us with two row tiles at any depth
         // and 159-164 us with four tiles 3-6 deep)
         if (p.H % 1024 == 0)
