@@ -179,6 +179,22 @@ def test_decode_many_experts_window_restage(wfmt):
     check_close(got[toks], want, f"many experts, window restage (fmt {wfmt})")
 
 
+def test_decode_many_experts_balanced_units():
+    """The h-in-LDS down pass with 36 distinct experts (fewer 1024-row chunks
+    than CUs): its 64-row units are dealt to the blocks in balanced ranges that
+    cross expert boundaries, each block entering several token groups as
+    phases.  Every token checked."""
+    w = C.Workload(cid=126, name="units", hidden=4096, inter=2048, n_experts=256, top_k=6,
+                   route=0, wfmt=C.WFMT_MXFP4)
+    T = 6
+    rng = np.random.default_rng(21)
+    x_bits = tr.bf16_normal(rng, (T, w.hidden))
+    ids = rng.permutation(256)[:T * 6].reshape(T, 6).astype(np.int32)   # 36 distinct experts
+    wt = (0.05 + rng.random((T, 6))).astype(np.float32)
+    got = _decode_whole_layer(w, x_bits, ids, wt)
+    check_close(got, _oracle_layer(w, x_bits, ids, wt), "36 experts, balanced down units")
+
+
 def test_decode_empty_batch_is_noop():
     import torch
     import moe_expert_layer_02_amd as m
